@@ -1,0 +1,8 @@
+"""CPU float64 oracle for FAVOR+ attention.
+
+TEST INFRASTRUCTURE ONLY: imported by the test-suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py``; never by the library.  It shares no code with the HIP
+path.  Every function is pinned by ``tests/test_oracle.py`` (no function here is
+"parity unpinned").
+"""
+from .favor_oracle import *  # noqa: F401,F403

@@ -1,0 +1,195 @@
+"""FAVOR+ attention oracle: plain, slow, float64, CPU only.
+
+TEST INFRASTRUCTURE.  Only the test-suite, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` may import or call this module.  The library's HIP path never does,
+and this module shares no code with it (it takes every input, W included, as an array).
+
+What it computes, and where that is defined
+-------------------------------------------
+Sources are the review pages of "Rethinking Attention with Performers" (Performer),
+"KDEformer: Accelerating Transformers via Kernel Density Estimation" (KDEformer) and
+"Fast Transformer Decoding: One Write-Head is All You Need" (MQA).
+
+* Performer, sections "요약" and "ABSTRACT": softmax attention is estimated in linear
+  space and time, with no sparsity or low-rank prior.
+* Performer, section "제안 방법": attention is written in kernelised form and the softmax
+  kernel exp(q.k) is approximated with positive random features, with orthogonal random
+  features to cut the variance; the estimate of the attention matrix is (nearly)
+  unbiased.  The page prints no formula.  The feature map used here is the positive one,
+        phi(x) = exp(W x - |x|^2 / 2) / sqrt(m),       W of shape (m, d),
+  chosen because for w ~ N(0, I_d) one has E[exp(w.z)] = exp(|z|^2 / 2), hence
+  E[phi(x).phi(y)] = exp(x.y) (see ``tests/test_oracle.py`` for the pin).  A constant c
+  subtracted inside the exponent cancels in the normalised output; the oracle uses c = 0
+  (float64 needs no stabiliser) and exposes c only so the invariance can be tested.
+* KDEformer, section "提出的方法": attention written as D^-1 A V with A the (unnormalised)
+  attention matrix and D the diagonal of its row sums.  With A_hat = phi(Q) phi(K)^T the
+  FAVOR+ output is D^-1 A_hat V.  ``favor_rows`` is that definition, row by row;
+  ``favor_attention`` is the linear-order evaluation phi(Q) (phi(K)^T [V, 1]) that the
+  Performer page's linear space/time claim rests on.  Both reach the same numbers up to
+  float64 rounding (pinned by the associativity test).
+* Causal (unidirectional) mode is not on the pages; the reading taken is the standard
+  inclusive mask j <= i, evaluated as a left-to-right running sum of phi(k_j) [v_j, 1]^T.
+* MQA, section "提出的方法": one K/V head may serve many query heads.  Query head hq reads
+  kv head hq // (Hq / Hkv); the feature matrix is per kv head (Hw == Hkv) or shared
+  (Hw == 1).
+
+Shapes: Q (B, Hq, L, d), K and V (B, Hkv, L, d), W (Hw, m, d); out (B, Hq, L, d).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "feature_map",
+    "kv_summary",
+    "favor_head",
+    "favor_head_rows",
+    "implied_attention",
+    "favor_attention",
+    "favor_rows",
+    "softmax_head",
+    "softmax_rows",
+    "head_maps",
+    "rowwise_rel_err",
+]
+
+_F = np.float64
+
+
+def feature_map(X, W, c=0.0):
+    """Positive random features phi(x) = exp(W x - |x|^2/2 - c) / sqrt(m) (Performer, "제안 방법").
+
+    X (..., d), W (m, d); c broadcastable to X[..., :1] (a stabiliser; 0 by default).
+    Returns (..., m) float64.
+    """
+    X = np.asarray(X, dtype=_F)
+    W = np.asarray(W, dtype=_F)
+    m = W.shape[0]
+    E = X @ W.T - 0.5 * np.sum(X * X, axis=-1, keepdims=True) - c
+    if not np.all(np.abs(E) < 700.0):
+        raise FloatingPointError("feature exponent outside the float64 exp range")
+    return np.exp(E) / np.sqrt(m)
+
+
+def kv_summary(phi_k, V):
+    """S = phi(K)^T [V, 1]: returns (S_v (m, d), S_1 (m,)) (Performer, "제안 방법": linear order)."""
+    V = np.asarray(V, dtype=_F)
+    return phi_k.T @ V, phi_k.sum(axis=0)
+
+
+def favor_head(q, k, v, W, causal=False, c_q=0.0, c_k=0.0):
+    """FAVOR+ on one head in linear order.  q, k, v (L, d); W (m, d).  Returns (L, d) float64.
+
+    Bidirectional: S = phi(K)^T [V, 1] once, then out_i = phi(q_i) S_v / phi(q_i) S_1.
+    Causal: S accumulated left to right over positions j <= i (inclusive).
+    """
+    v = np.asarray(v, dtype=_F)
+    pq = feature_map(q, W, c_q)
+    pk = feature_map(k, W, c_k)
+    if not causal:
+        Sv, S1 = kv_summary(pk, v)
+        return (pq @ Sv) / (pq @ S1)[:, None]
+    L, d = v.shape
+    m = pk.shape[1]
+    Sv = np.zeros((m, d))
+    S1 = np.zeros(m)
+    out = np.empty((L, d))
+    for i in range(L):
+        Sv += np.outer(pk[i], v[i])
+        S1 += pk[i]
+        out[i] = (pq[i] @ Sv) / (pq[i] @ S1)
+    return out
+
+
+def implied_attention(q, k, W, causal=False):
+    """A_hat = phi(Q) phi(K)^T (L x L), lower-triangular (j <= i) when causal."""
+    A = feature_map(q, W) @ feature_map(k, W).T
+    if causal:
+        A = np.tril(A)
+    return A
+
+
+def favor_head_rows(q_rows, pos, k, v, W, causal=False):
+    """Rows of D^-1 A_hat V for the query rows q_rows (n, d) sitting at positions pos (n,).
+
+    The definition written out row by row: weights a_j = phi(q_i) . phi(k_j) over
+    j <= pos_i (causal) or all j, then sum_j a_j v_j / sum_j a_j.
+    """
+    v = np.asarray(v, dtype=_F)
+    pk = feature_map(k, W)
+    pq = feature_map(q_rows, W)
+    out = np.empty((len(pos), v.shape[1]))
+    for r, i in enumerate(pos):
+        n = int(i) + 1 if causal else len(v)
+        a = pk[:n] @ pq[r]
+        out[r] = (a @ v[:n]) / a.sum()
+    return out
+
+
+def head_maps(Hq, Hkv, Hw):
+    """(kv head of each query head, W index of each kv head) (MQA page, "提出的方法")."""
+    if Hq % Hkv != 0 or Hw not in (1, Hkv):
+        raise ValueError("heads_q must be a multiple of heads_kv and heads_w in {1, heads_kv}")
+    G = Hq // Hkv
+    return [hq // G for hq in range(Hq)], [0 if Hw == 1 else h for h in range(Hkv)]
+
+
+def favor_attention(Q, K, V, W, causal=False):
+    """Full FAVOR+ output (B, Hq, L, d) float64, linear order, head by head."""
+    B, Hq, L, d = Q.shape
+    Hkv, Hw = K.shape[1], W.shape[0]
+    kv_of, w_of = head_maps(Hq, Hkv, Hw)
+    out = np.empty((B, Hq, L, d))
+    for b in range(B):
+        for hq in range(Hq):
+            hk = kv_of[hq]
+            out[b, hq] = favor_head(Q[b, hq], K[b, hk], V[b, hk], W[w_of[hk]], causal)
+    return out
+
+
+def favor_rows(Q, K, V, W, rows, causal=False):
+    """FAVOR+ output at the listed rows (n, 3) of (b, hq, i), by the row definition."""
+    B, Hq, L, d = Q.shape
+    Hkv, Hw = K.shape[1], W.shape[0]
+    kv_of, w_of = head_maps(Hq, Hkv, Hw)
+    rows = np.asarray(rows)
+    out = np.empty((len(rows), d))
+    for (b, hk) in sorted({(int(r[0]), kv_of[int(r[1])]) for r in rows}):
+        sel = [n for n, r in enumerate(rows) if int(r[0]) == b and kv_of[int(r[1])] == hk]
+        qr = np.stack([Q[rows[n][0], rows[n][1], rows[n][2]] for n in sel])
+        pos = [int(rows[n][2]) for n in sel]
+        out[sel] = favor_head_rows(qr, pos, K[b, hk], V[b, hk], W[w_of[hk]], causal)
+    return out
+
+
+def softmax_head(q, k, v, causal=False):
+    """Exact softmax attention softmax(q k^T) v on one head (no 1/sqrt(d): the data carry it)."""
+    q, k, v = (np.asarray(t, dtype=_F) for t in (q, k, v))
+    s = q @ k.T
+    if causal:
+        s = np.where(np.tril(np.ones(s.shape, dtype=bool)), s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p @ v) / p.sum(axis=1, keepdims=True)
+
+
+def softmax_rows(Q, K, V, rows, causal=False):
+    """Exact softmax attention at listed rows (b, hq, i); kv head by the MQA head map."""
+    B, Hq, L, d = Q.shape
+    G = Hq // K.shape[1]
+    out = np.empty((len(rows), d))
+    for n, (b, hq, i) in enumerate(np.asarray(rows)):
+        k = np.asarray(K[b, hq // G], dtype=_F)
+        v = np.asarray(V[b, hq // G], dtype=_F)
+        n_keys = int(i) + 1 if causal else L
+        s = k[:n_keys] @ np.asarray(Q[b, hq, i], dtype=_F)
+        p = np.exp(s - s.max())
+        out[n] = (p @ v[:n_keys]) / p.sum()
+    return out
+
+
+def rowwise_rel_err(y, r):
+    """max over rows of |y_i - r_i|_inf / |r_i|_inf (rows along the last axis)."""
+    y = np.asarray(y, dtype=_F).reshape(-1, np.shape(y)[-1])
+    r = np.asarray(r, dtype=_F).reshape(-1, np.shape(r)[-1])
+    return float(np.max(np.max(np.abs(y - r), axis=1) / np.max(np.abs(r), axis=1)))
