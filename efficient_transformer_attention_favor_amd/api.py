@@ -1,0 +1,90 @@
+"""Torch-tensor front end of the C ABI.
+
+PyTorch provides device memory and the current stream; every step of the attention
+runs in the library's HIP kernels.  Nothing here computes attention.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DTYPES = {torch.float32: _lib.FAVOR_F32, torch.bfloat16: _lib.FAVOR_BF16}
+
+
+def _problem(Q, K, W, causal, chunk):
+    if Q.dim() != 4 or K.dim() != 4 or W.dim() != 3:
+        raise ValueError("expected Q, K, V of shape (B, H, L, d) and W of shape (Hw, m, d)")
+    if Q.dtype not in _DTYPES:
+        raise ValueError(f"unsupported dtype {Q.dtype}")
+    B, Hq, L, d = Q.shape
+    return _lib.problem(B, Hq, K.shape[1], W.shape[0], L, d, W.shape[1], _DTYPES[Q.dtype],
+                        _lib.FAVOR_CAUSAL if causal else _lib.FAVOR_BIDIRECTIONAL, chunk)
+
+
+def _check(Q, K, V, W):
+    dev = Q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    for name, t in (("K", K), ("V", V), ("W", W)):
+        if t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, Q on {dev}")
+    if K.dtype != Q.dtype or V.dtype != Q.dtype:
+        raise ValueError("Q, K and V must share one dtype")
+    if W.dtype != torch.float32:
+        raise ValueError("W must be float32")
+    if K.shape != V.shape or K.shape[0] != Q.shape[0] or K.shape[2:] != Q.shape[2:]:
+        raise ValueError("K and V must be (B, Hkv, L, d) matching Q")
+    if W.shape[2] != Q.shape[3]:
+        raise ValueError("W must be (Hw, m, d)")
+    for name, t in (("Q", Q), ("K", K), ("V", V), ("W", W)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def workspace_bytes(Q, K, W, causal=False, chunk=0) -> int:
+    return _lib.workspace_bytes(_problem(Q, K, W, causal, chunk))
+
+
+def attn_fwd(Q, K, V, W, causal=False, chunk=0, out=None, workspace=None, stream=None):
+    """FAVOR+ attention forward; returns out (B, Hq, L, d) in Q's dtype."""
+    _check(Q, K, V, W)
+    p = _problem(Q, K, W, causal, chunk)
+    nbytes = _lib.workspace_bytes(p)
+    if nbytes == 0:
+        st = _lib.attn_fwd(p, None, None, None, None, None, None, 0, None)
+        raise _lib.FavorError(st, "favor_attn_fwd")
+    if out is None:
+        out = torch.empty_like(Q)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(Q.device)
+    st = _lib.attn_fwd(p, Q.data_ptr(), K.data_ptr(), V.data_ptr(), W.data_ptr(), out.data_ptr(),
+                       workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                       stream.cuda_stream)
+    if st != _lib.FAVOR_OK:
+        raise _lib.FavorError(st, "favor_attn_fwd")
+    return out
+
+
+def features(X, W, side, heads_q, heads_kv, stream=None):
+    """The feature map phi of the queries (side 0) or keys (side 1) of X (B, H, L, d).
+
+    Returns (phi (rows, m) float32, c) with c the natural-log stabiliser per row (side 0)
+    or per (batch, kv head) (side 1).
+    """
+    B, H, L, d = X.shape
+    m = W.shape[1]
+    dtype = _DTYPES[X.dtype]
+    p = _lib.problem(B, heads_q, heads_kv, W.shape[0], L, d, m, dtype, _lib.FAVOR_BIDIRECTIONAL)
+    rows = B * H * L
+    phi = torch.empty((rows, m), dtype=torch.float32, device=X.device)
+    c = torch.empty((rows if side == 0 else B * heads_kv,), dtype=torch.float32, device=X.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
+    st = _lib.features(p, side, X.data_ptr(), W.data_ptr(), phi.data_ptr(), c.data_ptr(),
+                       stream.cuda_stream)
+    if st != _lib.FAVOR_OK:
+        raise _lib.FavorError(st, "favor_features")
+    return phi, c

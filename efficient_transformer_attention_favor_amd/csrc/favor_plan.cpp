@@ -1,0 +1,76 @@
+// Host-side problem validation, launch geometry and workspace layout.  No HIP calls, so
+// the argument checks of every entry point run (and are tested) without a GPU.
+#include "favor_plan.hpp"
+
+namespace favor {
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+}  // namespace
+
+favor_status make_plan(const favor_problem* p, Plan* s) {
+  if (p == nullptr || s == nullptr) return FAVOR_ERR_INVALID_ARG;
+  if (p->batch < 1 || p->heads_q < 1 || p->heads_kv < 1 || p->heads_w < 1 || p->seq_len < 1 ||
+      p->head_dim < 1 || p->num_features < 1)
+    return FAVOR_ERR_INVALID_ARG;
+  if (p->heads_q % p->heads_kv != 0) return FAVOR_ERR_INVALID_ARG;
+  if (p->heads_w != 1 && p->heads_w != p->heads_kv) return FAVOR_ERR_INVALID_ARG;
+  if (p->dtype != FAVOR_F32 && p->dtype != FAVOR_BF16) return FAVOR_ERR_UNSUPPORTED;
+  if (p->mode != FAVOR_BIDIRECTIONAL && p->mode != FAVOR_CAUSAL) return FAVOR_ERR_UNSUPPORTED;
+  if (p->head_dim != 64 && p->head_dim != 128) return FAVOR_ERR_UNSUPPORTED;
+  if (p->num_features % 64 != 0 || p->num_features > 512) return FAVOR_ERR_UNSUPPORTED;
+  if (p->chunk != 0 && p->chunk != 32 && p->chunk != 64 && p->chunk != 128)
+    return FAVOR_ERR_UNSUPPORTED;
+  const long long elems_q = (long long)p->batch * p->heads_q * p->seq_len * p->head_dim;
+  const long long elems_kv = (long long)p->batch * p->heads_kv * p->seq_len * p->head_dim;
+  if (elems_q >= (1LL << 31) || elems_kv >= (1LL << 31)) return FAVOR_ERR_UNSUPPORTED;
+
+  Plan& q = *s;
+  q.B = p->batch;
+  q.Hq = p->heads_q;
+  q.Hkv = p->heads_kv;
+  q.Hw = p->heads_w;
+  q.L = p->seq_len;
+  q.d = p->head_dim;
+  q.m = p->num_features;
+  q.dtype = p->dtype;
+  q.mode = p->mode;
+  q.chunk = p->mode == FAVOR_CAUSAL ? (p->chunk == 0 ? 32 : p->chunk) : 0;
+  q.G = q.Hq / q.Hkv;
+  q.BH = q.B * q.Hkv;
+  q.NFT = q.m / kTile;
+  q.NDT = q.d / kTile + 1;
+
+  // Split each kv head's positions into T ranges of R positions so that the key-side
+  // pass has about kRangeTarget workgroups; R is a multiple of the chunk (causal) or of
+  // a 32-position block.  The split depends on the problem only, which keeps the
+  // reduction order -- and so the result bits -- independent of the device.
+  const int unit = q.mode == FAVOR_CAUSAL ? q.chunk : kTile;
+  const int max_t = ceil_div(q.L, unit);
+  int T = ceil_div(kRangeTarget, q.BH);
+  if (T > max_t) T = max_t;
+  if (T < 1) T = 1;
+  q.R = ceil_div(ceil_div(q.L, T), unit) * unit;
+  q.T = ceil_div(q.L, q.R);
+
+  q.tile_elems = (size_t)q.m * (size_t)(q.d + kTile);
+  size_t off = 0;
+  q.off_part_s = off;
+  off = align256(off + sizeof(float) * q.tile_elems * q.BH * q.T);
+  q.off_part_c = off;
+  off = align256(off + sizeof(float) * (size_t)q.m * q.BH * q.T);
+  q.off_s = off;
+  if (q.mode == FAVOR_BIDIRECTIONAL) off = align256(off + sizeof(float) * q.tile_elems * q.BH);
+  q.off_c = off;
+  off = align256(off + sizeof(float) * (size_t)q.m * q.BH);
+  q.off_p = off;
+  if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * q.tile_elems * q.BH * q.T);
+  q.bytes = off;
+  return FAVOR_OK;
+}
+
+}  // namespace favor

@@ -1,0 +1,108 @@
+/*
+ * favor.h -- C ABI of the MI355X (gfx950) FAVOR+ attention library (libfavor.so).
+ *
+ * FAVOR+ ("Rethinking Attention with Performers", sections "요약", "ABSTRACT" and
+ * "제안 방법") estimates softmax attention softmax(Q K^T) V in linear time and space with
+ * positive orthogonal random features:
+ *
+ *     phi(x) = exp(W x - |x|^2 / 2 - c) / sqrt(m)                 W: m x d feature matrix
+ *     out_i  = phi(q_i)^T S_v / phi(q_i)^T S_1,   S = phi(K)^T [V, 1]   (bidirectional)
+ *     out_i  = the same with S summed over positions j <= i only            (causal)
+ *
+ * i.e. the row-normalised D^-1 A_hat V of the implied attention matrix
+ * A_hat = phi(Q) phi(K)^T (notation of the KDEformer review, section "提出的方法").
+ * The stabiliser c cancels between numerator and denominator: the library picks it per
+ * query row (row maximum) and per kv head (global maximum).  No 1/sqrt(d) temperature is
+ * applied: callers who want one fold d^-1/4 into Q and K.
+ *
+ * Head layout ("Fast Transformer Decoding: One Write-Head is All You Need", section
+ * "提出的方法"): heads_q query heads share heads_kv key/value heads; query head hq reads
+ * kv head hq / (heads_q / heads_kv).  W is per kv head (heads_w == heads_kv) or shared
+ * (heads_w == 1).
+ *
+ * Conventions for every entry point
+ *  - All tensor pointers are DEVICE pointers, contiguous, row-major, innermost dimension
+ *    last:  Q [batch][heads_q][seq_len][head_dim],  K and V [batch][heads_kv][seq_len][head_dim],
+ *    W [heads_w][num_features][head_dim] (float32, host-generated),
+ *    out [batch][heads_q][seq_len][head_dim].  Q, K, V and out share `dtype`.
+ *  - The caller owns every buffer; the library allocates and frees no device memory and
+ *    keeps no global state.  Scratch space is the caller's `workspace`, at least
+ *    favor_workspace_bytes() bytes, 256-byte aligned.
+ *  - `stream` is a hipStream_t (NULL = default stream).  Work is queued asynchronously;
+ *    no entry point synchronises the host.
+ *  - Arguments are checked before any HIP call.  On an error status nothing has been
+ *    queued and `out` is untouched.  FAVOR_ERR_HIP reports a failed kernel launch.
+ *  - Results are deterministic: the same inputs and problem give bitwise-identical
+ *    output (fixed-order reductions, no floating-point atomics).
+ *  - Accumulation is float32.  For bf16 problems W is split into two bf16 parts so the
+ *    feature exponent keeps float32 accuracy.
+ *  - `out` must not alias Q, K, V, W or the workspace.
+ */
+#ifndef FAVOR_H
+#define FAVOR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define FAVOR_ABI_VERSION 1
+
+typedef enum {
+  FAVOR_OK = 0,
+  FAVOR_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, bad head layout       */
+  FAVOR_ERR_UNSUPPORTED = 2,  /* head_dim, num_features, dtype, mode or chunk not built  */
+  FAVOR_ERR_WORKSPACE = 3,    /* workspace smaller than favor_workspace_bytes(), or NULL */
+  FAVOR_ERR_HIP = 4           /* a kernel launch failed                                  */
+} favor_status;
+
+typedef enum { FAVOR_F32 = 0, FAVOR_BF16 = 1 } favor_dtype;
+typedef enum { FAVOR_BIDIRECTIONAL = 0, FAVOR_CAUSAL = 1 } favor_mode;
+
+/* Problem description.  Supported: head_dim in {64, 128}; num_features a multiple of 64
+ * in [64, 512]; heads_q % heads_kv == 0; heads_w in {1, heads_kv}; seq_len >= 1;
+ * batch * heads_q * seq_len * head_dim < 2^31.  chunk (causal only) is the number of
+ * positions between carry updates: 0 (library default) or one of 32, 64, 128; ignored
+ * for bidirectional problems. */
+typedef struct {
+  int32_t batch, heads_q, heads_kv, heads_w;
+  int32_t seq_len, head_dim, num_features;
+  int32_t dtype; /* favor_dtype */
+  int32_t mode;  /* favor_mode  */
+  int32_t chunk;
+} favor_problem;
+
+/* Bytes of workspace favor_attn_fwd needs for *p (0 if *p is invalid). */
+size_t favor_workspace_bytes(const favor_problem* p);
+
+/* FAVOR+ forward (Performer page, "제안 방법"): out = D^-1 A_hat V in linear order,
+ * bidirectional or causal (inclusive mask j <= i) per p->mode.  Queues 3 (bidirectional)
+ * or 3 (causal) kernels on `stream`. */
+favor_status favor_attn_fwd(const favor_problem* p, const void* Q, const void* K, const void* V,
+                            const float* W, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* The positive feature map alone (Performer page, "제안 방법"), as a float32 tensor:
+ *   side 0 (queries): X = Q, rows = batch*heads_q*seq_len, c per row (the row maximum of
+ *                     the exponent), c_out [rows];
+ *   side 1 (keys):    X = K, rows = batch*heads_kv*seq_len, one c per (batch, kv head)
+ *                     (the maximum over that head), c_out [batch*heads_kv].
+ * phi_out [rows][num_features] = exp(W x - |x|^2/2 - c) / sqrt(m), with the natural-log
+ * stabiliser c written to c_out.  W of row x is the one its kv head uses.  Diagnostic
+ * entry point: it is not on the attention path and does not use a workspace. */
+favor_status favor_features(const favor_problem* p, int32_t side, const void* X, const float* W,
+                            float* phi_out, float* c_out, void* stream);
+
+/* Static description of a status code; never NULL. */
+const char* favor_status_string(favor_status s);
+
+/* FAVOR_ABI_VERSION of the built library. */
+int32_t favor_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAVOR_H */

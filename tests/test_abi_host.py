@@ -1,0 +1,87 @@
+"""C ABI: the library loads, exports what include/favor.h declares, and rejects bad
+arguments before touching the GPU (these calls never reach a HIP API)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from efficient_transformer_attention_favor_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    text = open(os.path.join(ROOT, "include", "favor.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(favor_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared_symbols() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in _declared_symbols():
+        assert hasattr(L, name), name
+    assert _lib.abi_version() == 1
+
+
+def _p(**kw):
+    base = dict(batch=2, heads_q=4, heads_kv=2, heads_w=2, seq_len=100, head_dim=64,
+                num_features=128, dtype=_lib.FAVOR_BF16, mode=_lib.FAVOR_BIDIRECTIONAL, chunk=0)
+    base.update(kw)
+    return _lib.problem(**base)
+
+
+BAD = [
+    (dict(batch=0), _lib.FAVOR_ERR_INVALID_ARG),
+    (dict(seq_len=0), _lib.FAVOR_ERR_INVALID_ARG),
+    (dict(heads_q=3), _lib.FAVOR_ERR_INVALID_ARG),          # not a multiple of heads_kv
+    (dict(heads_w=3), _lib.FAVOR_ERR_INVALID_ARG),          # neither 1 nor heads_kv
+    (dict(head_dim=32), _lib.FAVOR_ERR_UNSUPPORTED),
+    (dict(head_dim=96), _lib.FAVOR_ERR_UNSUPPORTED),
+    (dict(num_features=96), _lib.FAVOR_ERR_UNSUPPORTED),
+    (dict(num_features=576), _lib.FAVOR_ERR_UNSUPPORTED),
+    (dict(dtype=7), _lib.FAVOR_ERR_UNSUPPORTED),
+    (dict(mode=2), _lib.FAVOR_ERR_UNSUPPORTED),
+    (dict(mode=_lib.FAVOR_CAUSAL, chunk=48), _lib.FAVOR_ERR_UNSUPPORTED),
+    (dict(batch=1 << 12, heads_q=1 << 8, heads_kv=1 << 8, heads_w=1, seq_len=1 << 14),
+     _lib.FAVOR_ERR_UNSUPPORTED),                           # more than 2^31 elements
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD)
+def test_invalid_problems_rejected(kw, status):
+    p = _p(**kw)
+    assert _lib.workspace_bytes(p) == 0
+    assert _lib.attn_fwd(p, 8, 8, 8, 8, 8, 256, 1 << 30, None) == status
+    assert _lib.features(p, 0, 8, 8, 8, 8, None) == status
+
+
+def test_null_pointers_and_workspace():
+    p = _p()
+    need = _lib.workspace_bytes(p)
+    assert need > 0 and need % 256 == 0
+    assert _lib.attn_fwd(p, None, 8, 8, 8, 8, 256, need, None) == _lib.FAVOR_ERR_INVALID_ARG
+    assert _lib.attn_fwd(p, 8, 8, 8, 8, None, 256, need, None) == _lib.FAVOR_ERR_INVALID_ARG
+    assert _lib.attn_fwd(p, 8, 8, 8, 8, 8, None, need, None) == _lib.FAVOR_ERR_WORKSPACE
+    assert _lib.attn_fwd(p, 8, 8, 8, 8, 8, 256, need - 1, None) == _lib.FAVOR_ERR_WORKSPACE
+    assert _lib.attn_fwd(p, 8, 8, 8, 8, 8, 260, need, None) == _lib.FAVOR_ERR_WORKSPACE  # misaligned
+    assert _lib.features(p, 2, 8, 8, 8, 8, None) == _lib.FAVOR_ERR_INVALID_ARG
+    assert _lib.features(p, 0, None, 8, 8, 8, None) == _lib.FAVOR_ERR_INVALID_ARG
+    assert _lib.attn_fwd(None, 8, 8, 8, 8, 8, 256, need, None) == _lib.FAVOR_ERR_INVALID_ARG
+
+
+def test_workspace_grows_with_problem():
+    small = _lib.workspace_bytes(_p(seq_len=64))
+    big = _lib.workspace_bytes(_p(seq_len=8192))
+    causal = _lib.workspace_bytes(_p(mode=_lib.FAVOR_CAUSAL, seq_len=8192, chunk=64))
+    assert 0 < small <= big and causal > 0
+
+
+def test_status_strings():
+    for s in range(5):
+        assert isinstance(_lib.status_string(s), str) and _lib.status_string(s)
+    assert _lib.status_string(99) == "unknown status"

@@ -1,0 +1,100 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Metric: row-wise relative error max_i |y_i - r_i|_inf / |r_i|_inf, the bar being 1e-4 for
+float32 problems and 2e-2 for bf16 problems (bf16 inputs, float32 accumulation).  Small
+shapes are compared in full (several tiles plus a ragged tail); the full-size workloads
+on sampled rows that the oracle computes one by one.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.favor_oracle as O
+from efficient_transformer_attention_favor_amd import api
+from efficient_transformer_attention_favor_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda").to(dtype)
+
+
+def _run(w, Q, K, V, W, chunk=0):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v = _dev(Q, dt), _dev(K, dt), _dev(V, dt)
+    out = api.attn_fwd(q, k, v, _dev(W, torch.float32), causal=w.causal, chunk=chunk)
+    torch.cuda.synchronize()
+    return out
+
+
+def _small(name, **kw):
+    return I.workload(name).replace(name=f"{name}_small", **kw)
+
+
+SMALL = [
+    _small("c2_bidir_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1000),
+    _small("c2_bidir_bf16", batch=2, heads_q=1, heads_kv=1, heads_w=1, seq_len=1, num_features=64),
+    _small("c2_bidir_bf16", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=31, num_features=64),
+    _small("c2_bidir_bf16", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=64, num_features=192),
+    _small("c2_bidir_bf16", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=300, num_features=512),
+    _small("c2_bidir_bf16", batch=2, heads_q=6, heads_kv=2, heads_w=2, seq_len=129),
+    _small("c4_mqa_bidir_bf16", batch=2, heads_q=4, heads_kv=1, heads_w=1, seq_len=777),
+    I.workload("c1_bidir_f32"),
+    _small("c1_bidir_f32", batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=333, head_dim=128,
+           num_features=192),
+    _small("c1_bidir_f32", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=70, num_features=320),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}-L{w.seq_len}-d{w.head_dim}-m{w.num_features}")
+def test_small_full_parity(w):
+    _say(f"case {w}")
+    Q, K, V, W = I.make_inputs(w, seed=0)
+    y = _run(w, Q, K, V, W).float().cpu().numpy()
+    ref = O.favor_attention(Q, K, V, W, causal=w.causal)
+    err = O.rowwise_rel_err(y, ref)
+    _say(f"  rowwise rel err {err:.3e}")
+    assert np.isfinite(y).all()
+    assert err < TOL[w.dtype]
+
+
+def test_ones_values_give_ones():
+    w = _small("c2_bidir_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=200)
+    _say(f"case {w} V=1")
+    Q, K, V, W = I.make_inputs(w, seed=3)
+    y = _run(w, Q, K, np.ones_like(V), W).float().cpu().numpy()
+    assert np.max(np.abs(y - 1.0)) < 1e-6
+
+
+def test_deterministic_bits():
+    w = _small("c2_bidir_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1500)
+    _say(f"case {w} determinism")
+    Q, K, V, W = I.make_inputs(w, seed=5)
+    a = _run(w, Q, K, V, W)
+    b = _run(w, Q, K, V, W)
+    assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("name", ["c2_bidir_bf16", "c4_mqa_bidir_bf16"])
+def test_full_size_sampled_rows(name):
+    w = I.workload(name)
+    _say(f"case {name} full size")
+    Q, K, V, W = I.make_inputs(w, seed=0)
+    y = _run(w, Q, K, V, W)
+    rows = I.sample_rows(w, 256)
+    got = torch.stack([y[b, h, i] for b, h, i in rows]).float().cpu().numpy()
+    del y
+    ref = O.favor_rows(Q, K, V, W, rows, causal=w.causal)
+    err = O.rowwise_rel_err(got, ref)
+    _say(f"  rowwise rel err over {len(rows)} rows {err:.3e}")
+    assert err < TOL[w.dtype]
