@@ -452,6 +452,291 @@ __global__ void __launch_bounds__(256) readout_kernel(const T* __restrict__ Q, c
   }
 }
 
+
+// ======================================================================================
+// causal_scan: per kv head, c* = max over segments and features of the segment
+// stabilisers, and the exclusive prefix P_t = sum_{t' < t} 2^(c_t',f - c*) S_t' of the
+// segment summaries (fragment-native, same layout as kv_summary).  Grid (m/32 * (d/32+1)
+// tiles, B*Hkv); fixed order t = 0, 1, ...
+// ======================================================================================
+__global__ void __launch_bounds__(256) causal_scan_kernel(const float* __restrict__ part_s,
+                                                          const float* __restrict__ part_c, int T_ranges,
+                                                          int m, int NDT, float* __restrict__ prefix,
+                                                          float* __restrict__ cstar_out) {
+  __shared__ float red[256];
+  const int tile = blockIdx.x, bh = blockIdx.y;
+  const size_t tile_elems = (size_t)m * NDT * 32;
+  const float* pc = part_c + (size_t)bh * T_ranges * m;
+  float cm = -INFINITY;
+  for (int i = threadIdx.x; i < T_ranges * m; i += blockDim.x) cm = fmaxf(cm, pc[i]);
+  red[threadIdx.x] = cm;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  const float cstar = red[0];
+  if (tile == 0 && threadIdx.x == 0) cstar_out[bh] = cstar;
+  const int ft = tile / NDT;
+  for (int e = threadIdx.x; e < 1024; e += blockDim.x) {
+    const int r = e >> 6, l = e & 63;
+    const int f = 32 * ft + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+    const size_t off = (size_t)bh * T_ranges * tile_elems + (size_t)tile * 1024 + e;
+    float acc = 0.f;
+    for (int t = 0; t < T_ranges; ++t) {
+      prefix[off + (size_t)t * tile_elems] = acc;
+      acc += fast_exp2(pc[(size_t)t * m + f] - cstar) * part_s[off + (size_t)t * tile_elems];
+    }
+  }
+}
+
+// ======================================================================================
+// causal_chunk: grid (segments, B*Hq), m/64 waves; wave w owns features [64w, 64w+64).
+// Per 32-position block p0 of the segment, in order:
+//   phi_Q,w  = 2^(W_w Q^T - M_w)             (M_w: this wave's row maximum)
+//   phi_K,w  = 2^(K W_w^T - |k|^2 log2e/2 - c*) (c*: global per kv head, from the scan)
+//   num_w^T  = carry_w^T phi_Q,w^T + [V,1]^T tril(phi_K,w phi_Q,w^T)
+//   carry_w += phi_K,w^T [V, 1]
+// then out = sum_w 2^(M_w - M) num_w / sum_w 2^(M_w - M) den_w across the waves (LDS).
+// The carry of a segment starts at the scan's exclusive prefix.
+// ======================================================================================
+template <class T> struct CausalLd;
+template <> struct CausalLd<bf16> { static constexpr int PK = 48; };  // phi_K rows: 32 keys + pad
+template <> struct CausalLd<float> { static constexpr int PK = 33; };
+
+template <class T, int D, int NWMAX>
+__global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ W,
+    const float* __restrict__ prefix, const float* __restrict__ cstar_in, T* __restrict__ out, int L, int Hq,
+    int Hkv, int Hw, int m, int R, int T_ranges) {
+  using P = Prec<T>;
+  using frag = typename P::frag;
+  constexpr int NKC = D / P::KS;
+  constexpr int NDT = D / 32 + 1;
+  constexpr int LDK = Ld<T>::template K<D>;
+  constexpr int LDV = Ld<T>::template V<D>;
+  constexpr int LDP = CausalLd<T>::PK;
+  constexpr int LDR = D + 4;  // reduction rows: D partial values, den, row max
+  // The cross-wave reduction handles 32 / QSPLIT query rows at a time so that the LDS
+  // footprint stays within 160 KB for wide heads and many waves.
+  constexpr int BASE_LDS = (2 * 32 * LDK + 32 * LDV + NWMAX * 64 * LDP) * (int)sizeof(T);
+  constexpr int QSPLIT = BASE_LDS + NWMAX * 32 * LDR * 4 <= 160 * 1024       ? 1
+                         : BASE_LDS + NWMAX * 16 * LDR * 4 <= 160 * 1024 ? 2
+                                                                         : 4;
+  constexpr int QR = 32 / QSPLIT;
+  __shared__ __attribute__((aligned(16))) T Ql[32 * LDK];
+  __shared__ __attribute__((aligned(16))) T Kl[32 * LDK];
+  __shared__ __attribute__((aligned(16))) T Vl[32 * LDV];
+  __shared__ __attribute__((aligned(16))) T Pk[NWMAX][64 * LDP];
+  __shared__ __attribute__((aligned(16))) float Red[NWMAX][QR * LDR];
+
+  const int seg = blockIdx.x, bhq = blockIdx.y;
+  const int b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv), bh = b * Hkv + hkv;
+  const int nw = blockDim.x >> 6;
+  const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
+  const int f0 = wave * 64;
+  const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
+  const T* Qh = Q + (size_t)bhq * L * D;
+  T* Oh = out + (size_t)bhq * L * D;
+  const T* Kh = K + (size_t)bh * L * D;
+  const T* Vh = V + (size_t)bh * L * D;
+
+  frag wf[2][P::NSPLIT][NKC];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) {
+      frag tmp[P::NSPLIT];
+      load_w_frag(Wh + (size_t)(f0 + 32 * nt + col) * D, kc, g, tmp);
+#pragma unroll
+      for (int s = 0; s < P::NSPLIT; ++s) wf[nt][s][kc] = tmp[s];
+    }
+  const float cstar = cstar_in[bh];
+  const frag biasB = bias_cols(cstar, g, frag{});
+
+  // carry of this wave's features, from the exclusive prefix of the segment
+  f32x16 carry[2][NDT];
+  {
+    const size_t tile_elems = (size_t)m * NDT * 32;
+    const float* pf = prefix + ((size_t)bh * T_ranges + seg) * tile_elems;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        const float* src = pf + (size_t)((f0 / 32 + nt) * NDT + dt) * 1024;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) carry[nt][dt][r] = src[r * 64 + l];
+      }
+  }
+  frag ones = zero_frag(frag{});
+  if (col == 0) {
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ones[j] = (bf16)1.f;
+    } else {
+      ones = 1.f;
+    }
+  }
+  T* pk = Pk[wave];
+  float* red = Red[wave];
+
+  const int p_begin = seg * R;
+  const int p_end = min(p_begin + R, L);
+  for (int p0 = p_begin; p0 < p_end; p0 += 32) {
+    __syncthreads();
+    stage_rows<T, D, false>(Ql, LDK, Qh, p0, L);
+    stage_rows<T, D, false>(Kl, LDK, Kh, p0, L);
+    stage_rows<T, D, true>(Vl, LDV, Vh, p0, L);
+    __syncthreads();
+
+    // phi_Q of this wave's features: C = W_w Q^T (features x queries), lane = query.
+    frag qf[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) qf[kc] = load_frag_k(Ql + col * LDK, kc, g);
+    f32x16 cq[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      cq[nt] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int s = 0; s < P::NSPLIT; ++s) cq[nt] = mma(wf[nt][s][kc], qf[kc], cq[nt]);
+    }
+    float Mw = cq[0][0];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Mw = fmaxf(Mw, cq[nt][r]);
+    Mw = fmaxf(Mw, partner32(Mw));
+    frag qb[2][P::NF32];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x16 e;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(cq[nt][r] - Mw);
+      acc_to_frags(e, qb[nt]);
+    }
+
+    // phi_K of this wave's features: C = K W_w^T (keys x features), lane = feature.
+    frag kf[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) kf[kc] = load_frag_k(Kl + col * LDK, kc, g);
+    float nrm = sumsq(kf);
+    nrm += partner32(nrm);
+    const frag biasA = bias_rows(0.5f * kLog2e * nrm, g, frag{});
+    frag ka[2][P::NF32];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x16 ck = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+#pragma unroll
+        for (int s = 0; s < P::NSPLIT; ++s) ck = mma(kf[kc], wf[nt][s][kc], ck);
+      ck = mma(biasA, biasB, ck);
+      f32x16 e;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = p0 + 8 * (r >> 2) + 4 * g + (r & 3);
+        e[r] = key < L ? fast_exp2(ck[r]) : 0.f;
+      }
+      acc_to_frags(e, ka[nt]);
+      // phi_K to LDS as [feature][key] for the transposed read below
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        T* dst = pk + (32 * nt + col) * LDP + 8 * r4 + 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = (T)e[4 * r4 + i];
+      }
+    }
+
+    // num^T = carry^T phi_Q^T  (rows: value columns, lanes: queries)
+    f32x16 num[NDT];
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      num[dt] = zero16();
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        frag ca[P::NF32];
+        acc_to_frags(carry[nt][dt], ca);
+#pragma unroll
+        for (int h = 0; h < P::NF32; ++h) num[dt] = mma(ca[h], qb[nt][h], num[dt]);
+      }
+    }
+    // intra-block triangle: A^T = phi_K phi_Q^T (keys x queries), keep key <= query
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    f32x16 at = zero16();
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int h = 0; h < P::NF32; ++h) at = mma(lds_frag_rows(pk, LDP, 32 * nt, 0, h), qb[nt][h], at);
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + 4 * g + (r & 3) > col) at[r] = 0.f;
+    frag ab[P::NF32];
+    acc_to_frags(at, ab);
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int h = 0; h < P::NF32; ++h) {
+        const frag va = dt < NDT - 1 ? lds_frag_rows(Vl, LDV, 0, 32 * dt, h) : ones;
+        num[dt] = mma(va, ab[h], num[dt]);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) carry[nt][dt] = mma(ka[nt][h], va, carry[nt][dt]);
+      }
+
+    // this wave's partial to LDS (D values, den, row maximum per query), then the
+    // cross-wave sum; one reduction item = (query, 8 value columns).
+#pragma unroll
+    for (int qh = 0; qh < QSPLIT; ++qh) {
+      const int qrow = col - qh * QR;
+      if (qrow >= 0 && qrow < QR) {
+#pragma unroll
+        for (int dt = 0; dt < NDT - 1; ++dt)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 v = {num[dt][4 * q4], num[dt][4 * q4 + 1], num[dt][4 * q4 + 2], num[dt][4 * q4 + 3]};
+            *reinterpret_cast<f32x4*>(red + qrow * LDR + 32 * dt + 16 * g + 4 * q4) = v;
+          }
+        if (g == 0) {
+          red[qrow * LDR + D] = num[NDT - 1][0];
+          red[qrow * LDR + D + 1] = Mw;
+        }
+      }
+      __syncthreads();
+      for (int it = threadIdx.x; it < QR * (D / 8); it += blockDim.x) {
+        const int q = it / (D / 8), c0 = (it % (D / 8)) * 8;
+        const int pos = p0 + qh * QR + q;
+        if (pos >= L) continue;
+        float M = -INFINITY;
+        for (int w = 0; w < nw; ++w) M = fmaxf(M, Red[w][q * LDR + D + 1]);
+        float den = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int w = 0; w < nw; ++w) {
+          const float* rw = Red[w] + q * LDR;
+          const float sc = fast_exp2(rw[D + 1] - M);
+          den += sc * rw[D];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] += sc * rw[c0 + i];
+        }
+        const float inv = 1.f / den;
+        T* orow = Oh + (size_t)pos * D + c0;
+        if constexpr (sizeof(T) == 2) {
+          bf16x8 o;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) o[i] = (bf16)(acc[i] * inv);
+          *reinterpret_cast<bf16x8*>(orow) = o;
+        } else {
+          f32x4 o0 = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+          f32x4 o1 = {acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
+          *reinterpret_cast<f32x4*>(orow) = o0;
+          *reinterpret_cast<f32x4*>(orow + 4) = o1;
+        }
+      }
+      if (QSPLIT > 1) __syncthreads();
+    }
+  }
+}
+
 }  // namespace favor
 
 // ======================================================================================
@@ -488,8 +773,27 @@ favor_status run_bidirectional(const Plan& s, const T* Q, const T* K, const T* V
 }
 
 template <class T, int D>
-favor_status run_causal(const Plan&, const T*, const T*, const T*, const float*, T*, char*, hipStream_t) {
-  return FAVOR_ERR_UNSUPPORTED;
+favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const float* W, T* out, char* ws,
+                        hipStream_t st) {
+  float* part_s = reinterpret_cast<float*>(ws + s.off_part_s);
+  float* part_c = reinterpret_cast<float*>(ws + s.off_part_c);
+  float* cstar = reinterpret_cast<float*>(ws + s.off_c);
+  float* prefix = reinterpret_cast<float*>(ws + s.off_p);
+  const int nw = s.m / kFeatPerWave;
+  hipLaunchKernelGGL((kv_summary_kernel<T, D>), dim3(s.T, s.BH, ceil_div_i(nw, 4)), dim3(kWave * (nw < 4 ? nw : 4)),
+                     0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, part_s, part_c);
+  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  hipLaunchKernelGGL(causal_scan_kernel, dim3(s.NFT * s.NDT, s.BH), dim3(256), 0, st, part_s, part_c, s.T, s.m,
+                     s.NDT, prefix, cstar);
+  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  if (nw <= 4)
+    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 4>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
+                       prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
+  else
+    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 8>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
+                       prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
+  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  return FAVOR_OK;
 }
 
 template <class T>

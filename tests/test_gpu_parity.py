@@ -56,6 +56,21 @@ SMALL = [
 ]
 
 
+SMALL_CAUSAL = [
+    _small("c3_causal_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1000),
+    _small("c3_causal_bf16", batch=2, heads_q=1, heads_kv=1, heads_w=1, seq_len=1, num_features=64),
+    _small("c3_causal_bf16", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=33, num_features=128),
+    _small("c3_causal_bf16", batch=2, heads_q=4, heads_kv=2, heads_w=2, seq_len=200),
+    _small("c3_causal_bf16", batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=300, head_dim=128),
+    _small("c5_causal_long_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=700),
+    _small("c3_causal_bf16", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=257, num_features=192),
+    _small("c1_bidir_f32", causal=True, seq_len=257),
+    _small("c1_bidir_f32", causal=True, batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=100,
+           head_dim=128, num_features=256),
+]
+SMALL = SMALL + SMALL_CAUSAL
+
+
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: f"{w.name}-L{w.seq_len}-d{w.head_dim}-m{w.num_features}")
 def test_small_full_parity(w):
     _say(f"case {w}")
@@ -66,6 +81,16 @@ def test_small_full_parity(w):
     _say(f"  rowwise rel err {err:.3e}")
     assert np.isfinite(y).all()
     assert err < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("chunk", [0, 32, 64, 128])
+def test_causal_chunk_sizes(chunk):
+    w = _small("c3_causal_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1111)
+    _say(f"case {w} chunk={chunk}")
+    Q, K, V, W = I.make_inputs(w, seed=1)
+    y = _run(w, Q, K, V, W, chunk=chunk).float().cpu().numpy()
+    ref = O.favor_attention(Q, K, V, W, causal=True)
+    assert O.rowwise_rel_err(y, ref) < TOL[w.dtype]
 
 
 def test_ones_values_give_ones():
@@ -85,7 +110,8 @@ def test_deterministic_bits():
     assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("name", ["c2_bidir_bf16", "c4_mqa_bidir_bf16"])
+@pytest.mark.parametrize("name", ["c2_bidir_bf16", "c4_mqa_bidir_bf16", "c3_causal_bf16",
+                                  "c5_causal_long_bf16"])
 def test_full_size_sampled_rows(name):
     w = I.workload(name)
     _say(f"case {name} full size")
