@@ -1,0 +1,270 @@
+#!/usr/bin/env python3
+"""Throughput of the FAVOR+ forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one favor_attn_fwd call (every kernel of the path) over one batch of seeded
+synthetic input already resident in HBM.  W untimed warm-up steps, then exactly K timed
+steps between a synchronize on each side.  Prints one JSON line:
+  value          tokens/s = batch * heads_q * seq_len / step time
+  roofline       for the kernel with the longest average duration: algorithmic bytes or
+                 flops per launch over its average duration, from HIP events recorded by
+                 the library around each kernel on the stream it launches on
+  cpu_baseline   the float64 CPU oracle timed on this host on a bounded sample of the same
+                 workload (whole (batch, head) slices), scaled to tokens/s
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "FAVOR+ attention fwd tokens/s (B*H*L/s) and % MFMA/HBM roofline, 1 GPU"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA
+KERNELS = {
+    False: ("kv_summary", "kv_combine", "readout"),
+    True: ("kv_summary", "causal_scan", "causal_chunk"),
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime (the library records them on its stream)."""
+
+    def __init__(self):
+        self.rt = ctypes.CDLL("libamdhip64.so")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        out = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            out.append(e.value)
+        return out
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.rt.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def algorithmic_work(w):
+    """Per-kernel algorithmic bytes and flops of one call (what FAVOR+ itself must move and do).
+
+    Bytes: Q, K, V read once and out written once, plus W (and S where a kernel reads the
+    finished summary).  Flops: 2 L d m for a feature map plus 2 L m (d+1) for the summary
+    (keys) or the readout (queries), per head.  The combine and scan kernels do only
+    implementation work (merging position-range partials) and get none.
+    """
+    e = 2 if w.dtype == "bf16" else 4
+    B, Hq, Hkv, Hw, L, d, m = (w.batch, w.heads_q, w.heads_kv, w.heads_w, w.seq_len, w.head_dim,
+                               w.num_features)
+    side = 2 * L * d * m + 2 * L * m * (d + 1)
+    w_bytes = 4 * Hw * m * d
+    s_bytes = 4 * B * Hkv * m * (d + 1)
+    k_bytes = 2 * e * B * Hkv * L * d
+    q_bytes = 2 * e * B * Hq * L * d
+    names = KERNELS[w.causal]
+    if not w.causal:
+        return {names[0]: (k_bytes + w_bytes, B * Hkv * side), names[1]: (0, 0),
+                names[2]: (q_bytes + w_bytes + s_bytes, B * Hq * side)}
+    return {names[0]: (k_bytes + w_bytes, B * Hkv * side), names[1]: (0, 0),
+            names[2]: (q_bytes + k_bytes + w_bytes, B * Hq * side + B * Hkv * side)}
+
+
+def cpu_baseline(w, Q, K, V, W, budget_s=15.0):
+    """The float64 oracle on whole (batch, head) slices until about budget_s of CPU time."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle.favor_oracle as O
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    G = w.heads_q // w.heads_kv
+    t0 = time.perf_counter()
+    heads = 0
+    for b in range(w.batch):
+        for hq in range(w.heads_q):
+            hk = hq // G
+            Wh = W[0 if w.heads_w == 1 else hk]
+            O.favor_head(Q[b, hq], K[b, hk], V[b, hk], Wh, causal=w.causal)
+            heads += 1
+            if time.perf_counter() - t0 > budget_s:
+                break
+        else:
+            continue
+        break
+    secs = time.perf_counter() - t0
+    return {"value": heads * w.seq_len / secs, "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{heads} of {w.batch * w.heads_q} (batch, head) slices, L={w.seq_len}, "
+                      f"float64 NumPy, {secs:.1f} s on the host CPU",
+            "cpu": _cpu_model()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2_bidir_bf16")
+    ap.add_argument("--chunk", type=int, default=0, help="causal chunk (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--copy-probe-mb", type=int, default=0,
+                    help="after the timed steps, one device copy of this many MiB (counter calibration)")
+    ap.add_argument("--out", default="", help="also append the JSON line to this file")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from efficient_transformer_attention_favor_amd import _lib, api
+    from efficient_transformer_attention_favor_amd import inputs as I
+
+    w = I.workload(args.workload)
+    log(f"workload {w}")
+    Q, K, V, W = I.make_inputs(w, seed=0)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev).to(dt) for x in (Q, K, V))
+    wd = torch.from_numpy(W).to(dev)
+    out = torch.empty_like(q)
+    p = api._problem(q, k, wd, w.causal, args.chunk)
+    nbytes = _lib.workspace_bytes(p)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), wd.data_ptr(), out.data_ptr(), ws.data_ptr())
+
+    def step():
+        st = _lib.attn_fwd(p, *ptrs, nbytes, stream.cuda_stream)
+        if st != _lib.FAVOR_OK:
+            raise _lib.FavorError(st, "favor_attn_fwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    hev = HipEvents()
+    nk = _lib.FAVOR_FWD_KERNELS
+    evs = [hev.create(nk + 1) for _ in range(args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        st = _lib.attn_fwd_timed(p, *ptrs, nbytes, stream.cuda_stream, evs[i])
+        if st != _lib.FAVOR_OK:
+            raise _lib.FavorError(st, "favor_attn_fwd_timed")
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    ms_step = start.elapsed_time(end) / args.steps
+    names = KERNELS[w.causal]
+    kms = {n: float(np.mean([hev.elapsed_ms(e[j], e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    for e in evs:
+        hev.destroy(e)
+
+    if args.copy_probe_mb > 0:
+        n = args.copy_probe_mb * (1 << 20)
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: {n} bytes device-to-device")
+
+    work = algorithmic_work(w)
+    kernels = {}
+    for n in names:
+        b, f = work[n]
+        t = kms[n] * 1e-3
+        kernels[n] = {"ms": round(kms[n], 5), "alg_bytes": b, "alg_flops": f,
+                      "GB/s": round(b / t / 1e9, 1) if b else None,
+                      "TFLOP/s": round(f / t / 1e12, 2) if f else None}
+    dom = max(names, key=lambda n: kms[n])
+    b, f = work[dom]
+    t_dom = kms[dom] * 1e-3
+    peak_tf = PEAK_TFLOPS[w.dtype]
+    if b / (PEAK_HBM_GBS * 1e9) >= f / (peak_tf * 1e12):
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(b / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    else:
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(f / t_dom / 1e12, 2), "peak": peak_tf,
+                "unit": "TFLOP/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["traffic"] = None
+    roof["per_launch"] = {"alg_bytes": b, "alg_flops": f, "avg_ms": round(kms[dom], 5)}
+
+    tokens = w.batch * w.heads_q * w.seq_len
+    res = {
+        "metric": METRIC,
+        "value": round(tokens / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian Q, K, V; orthogonal random features W)",
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "heads_w": w.heads_w, "seq_len": w.seq_len, "head_dim": w.head_dim,
+                   "num_features": w.num_features, "mode": "causal" if w.causal else "bidirectional",
+                   "chunk": args.chunk, "parallelism": "single GPU"},
+        "roofline": roof,
+        "kernels": kernels,
+        "host_wall_s": round(t_host, 4),
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline(w, Q, K, V, W, args.cpu_budget)
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

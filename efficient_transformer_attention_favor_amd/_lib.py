@@ -21,8 +21,10 @@ FAVOR_BF16 = 1
 FAVOR_BIDIRECTIONAL = 0
 FAVOR_CAUSAL = 1
 
-EXPORTED = ("favor_workspace_bytes", "favor_attn_fwd", "favor_features", "favor_status_string",
-            "favor_abi_version")
+FAVOR_FWD_KERNELS = 3
+
+EXPORTED = ("favor_workspace_bytes", "favor_attn_fwd", "favor_attn_fwd_timed", "favor_features",
+            "favor_status_string", "favor_abi_version")
 
 
 class FavorProblem(ctypes.Structure):
@@ -54,6 +56,9 @@ def lib() -> ctypes.CDLL:
         L.favor_workspace_bytes.restype = ctypes.c_size_t
         L.favor_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.favor_attn_fwd.restype = ctypes.c_int
+        L.favor_attn_fwd_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
+                                           ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
+        L.favor_attn_fwd_timed.restype = ctypes.c_int
         L.favor_features.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp]
         L.favor_features.restype = ctypes.c_int
         L.favor_status_string.argtypes = [ctypes.c_int]
@@ -85,6 +90,14 @@ def workspace_bytes(p: FavorProblem) -> int:
 def attn_fwd(p: FavorProblem, q, k, v, w, out, workspace, workspace_nbytes, stream) -> int:
     return int(lib().favor_attn_fwd(_ref(p), q, k, v, w, out, workspace,
                                     ctypes.c_size_t(workspace_nbytes), stream))
+
+
+def attn_fwd_timed(p: FavorProblem, q, k, v, w, out, workspace, workspace_nbytes, stream,
+                   events) -> int:
+    arr = (ctypes.c_void_p * len(events))(*events) if events is not None else None
+    return int(lib().favor_attn_fwd_timed(_ref(p), q, k, v, w, out, workspace,
+                                          ctypes.c_size_t(workspace_nbytes), stream, arr,
+                                          0 if events is None else len(events)))
 
 
 def features(p: FavorProblem, side, x, w, phi_out, c_out, stream) -> int:

@@ -747,20 +747,30 @@ namespace {
 
 inline int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+// Records ev[i] (if given) before the i-th kernel of a call and after the last one.
+struct Marks {
+  hipEvent_t* ev;
+  int n;
+  bool mark(int i, hipStream_t st) const {
+    return ev == nullptr || i >= n || hipEventRecord(ev[i], st) == hipSuccess;
+  }
+};
+
 template <class T, int D>
 favor_status run_bidirectional(const Plan& s, const T* Q, const T* K, const T* V, const float* W, T* out,
-                               char* ws, hipStream_t st) {
+                               char* ws, hipStream_t st, const Marks& mk) {
   float* part_s = reinterpret_cast<float*>(ws + s.off_part_s);
   float* part_c = reinterpret_cast<float*>(ws + s.off_part_c);
   float* S = reinterpret_cast<float*>(ws + s.off_s);
   float* c = reinterpret_cast<float*>(ws + s.off_c);
   const int nw = s.m / kFeatPerWave;
+  if (!mk.mark(0, st)) return FAVOR_ERR_HIP;
   hipLaunchKernelGGL((kv_summary_kernel<T, D>), dim3(s.T, s.BH, ceil_div_i(nw, 4)), dim3(kWave * (nw < 4 ? nw : 4)), 0, st, K, V, W, s.L,
                      s.Hkv, s.Hw, s.m, s.R, s.T, part_s, part_c);
-  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  if (hipGetLastError() != hipSuccess || !mk.mark(1, st)) return FAVOR_ERR_HIP;
   hipLaunchKernelGGL(kv_combine_kernel, dim3(s.NFT, s.BH), dim3(256), 0, st, part_s, part_c, s.T, s.m, s.NDT,
                      S, c);
-  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  if (hipGetLastError() != hipSuccess || !mk.mark(2, st)) return FAVOR_ERR_HIP;
   const long long rows = (long long)s.G * s.L;
   const int tiles = ceil_div_i(rows, 4 * kQueriesPerWave);
   int per_head = ceil_div_i(kRangeTarget, s.BH);
@@ -768,45 +778,47 @@ favor_status run_bidirectional(const Plan& s, const T* Q, const T* K, const T* V
   if (per_head < 1) per_head = 1;
   hipLaunchKernelGGL((readout_kernel<T, D>), dim3(per_head, s.BH), dim3(256), 0, st, Q, W, S, c, out, s.L,
                      s.Hq, s.Hkv, s.Hw, s.m);
-  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  if (hipGetLastError() != hipSuccess || !mk.mark(3, st)) return FAVOR_ERR_HIP;
   return FAVOR_OK;
 }
 
 template <class T, int D>
 favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const float* W, T* out, char* ws,
-                        hipStream_t st) {
+                        hipStream_t st, const Marks& mk) {
   float* part_s = reinterpret_cast<float*>(ws + s.off_part_s);
   float* part_c = reinterpret_cast<float*>(ws + s.off_part_c);
   float* cstar = reinterpret_cast<float*>(ws + s.off_c);
   float* prefix = reinterpret_cast<float*>(ws + s.off_p);
   const int nw = s.m / kFeatPerWave;
+  if (!mk.mark(0, st)) return FAVOR_ERR_HIP;
   hipLaunchKernelGGL((kv_summary_kernel<T, D>), dim3(s.T, s.BH, ceil_div_i(nw, 4)), dim3(kWave * (nw < 4 ? nw : 4)),
                      0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, part_s, part_c);
-  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  if (hipGetLastError() != hipSuccess || !mk.mark(1, st)) return FAVOR_ERR_HIP;
   hipLaunchKernelGGL(causal_scan_kernel, dim3(s.NFT * s.NDT, s.BH), dim3(256), 0, st, part_s, part_c, s.T, s.m,
                      s.NDT, prefix, cstar);
-  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  if (hipGetLastError() != hipSuccess || !mk.mark(2, st)) return FAVOR_ERR_HIP;
   if (nw <= 4)
     hipLaunchKernelGGL((causal_chunk_kernel<T, D, 4>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
                        prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
   else
     hipLaunchKernelGGL((causal_chunk_kernel<T, D, 8>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
                        prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
-  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  if (hipGetLastError() != hipSuccess || !mk.mark(3, st)) return FAVOR_ERR_HIP;
   return FAVOR_OK;
 }
 
 template <class T>
 favor_status run_typed(const Plan& s, const void* Q, const void* K, const void* V, const float* W, void* out,
-                       char* ws, hipStream_t st) {
+                       char* ws, hipStream_t st, const Marks& mk) {
   const T* q = static_cast<const T*>(Q);
   const T* k = static_cast<const T*>(K);
   const T* v = static_cast<const T*>(V);
   T* o = static_cast<T*>(out);
   if (s.mode == FAVOR_BIDIRECTIONAL)
-    return s.d == 64 ? run_bidirectional<T, 64>(s, q, k, v, W, o, ws, st)
-                     : run_bidirectional<T, 128>(s, q, k, v, W, o, ws, st);
-  return s.d == 64 ? run_causal<T, 64>(s, q, k, v, W, o, ws, st) : run_causal<T, 128>(s, q, k, v, W, o, ws, st);
+    return s.d == 64 ? run_bidirectional<T, 64>(s, q, k, v, W, o, ws, st, mk)
+                     : run_bidirectional<T, 128>(s, q, k, v, W, o, ws, st, mk);
+  return s.d == 64 ? run_causal<T, 64>(s, q, k, v, W, o, ws, st, mk)
+                   : run_causal<T, 128>(s, q, k, v, W, o, ws, st, mk);
 }
 
 }  // namespace
@@ -832,8 +844,9 @@ const char* favor_status_string(favor_status s) {
 
 int32_t favor_abi_version(void) { return FAVOR_ABI_VERSION; }
 
-favor_status favor_attn_fwd(const favor_problem* p, const void* Q, const void* K, const void* V, const float* W,
-                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+static favor_status attn_fwd_impl(const favor_problem* p, const void* Q, const void* K, const void* V,
+                                  const float* W, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                                  const favor::Marks& mk) {
   favor::Plan s;
   const favor_status st = favor::make_plan(p, &s);
   if (st != FAVOR_OK) return st;
@@ -842,8 +855,23 @@ favor_status favor_attn_fwd(const favor_problem* p, const void* Q, const void* K
     return FAVOR_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (s.dtype == FAVOR_BF16) return favor::run_typed<favor::bf16>(s, Q, K, V, W, out, ws, hs);
-  return favor::run_typed<float>(s, Q, K, V, W, out, ws, hs);
+  if (s.dtype == FAVOR_BF16) return favor::run_typed<favor::bf16>(s, Q, K, V, W, out, ws, hs, mk);
+  return favor::run_typed<float>(s, Q, K, V, W, out, ws, hs, mk);
+}
+
+favor_status favor_attn_fwd(const favor_problem* p, const void* Q, const void* K, const void* V, const float* W,
+                            void* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_fwd_impl(p, Q, K, V, W, out, workspace, workspace_bytes, stream, favor::Marks{nullptr, 0});
+}
+
+favor_status favor_attn_fwd_timed(const favor_problem* p, const void* Q, const void* K, const void* V,
+                                  const float* W, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                                  void* const* events, int32_t n_events) {
+  if (events == nullptr || n_events < FAVOR_FWD_KERNELS + 1) return FAVOR_ERR_INVALID_ARG;
+  for (int i = 0; i < FAVOR_FWD_KERNELS + 1; ++i)
+    if (events[i] == nullptr) return FAVOR_ERR_INVALID_ARG;
+  return attn_fwd_impl(p, Q, K, V, W, out, workspace, workspace_bytes, stream,
+                       favor::Marks{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events});
 }
 
 favor_status favor_features(const favor_problem* p, int32_t side, const void* X, const float* W, float* phi_out,

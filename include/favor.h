@@ -77,12 +77,27 @@ typedef struct {
 /* Bytes of workspace favor_attn_fwd needs for *p (0 if *p is invalid). */
 size_t favor_workspace_bytes(const favor_problem* p);
 
+/* Kernels one favor_attn_fwd call queues: the key/value summary per position range (or
+ * segment), the combine (bidirectional) or prefix scan (causal), and the query readout
+ * (bidirectional) or chunked causal pass. */
+#define FAVOR_FWD_KERNELS 3
+
 /* FAVOR+ forward (Performer page, "제안 방법"): out = D^-1 A_hat V in linear order,
- * bidirectional or causal (inclusive mask j <= i) per p->mode.  Queues 3 (bidirectional)
- * or 3 (causal) kernels on `stream`. */
+ * bidirectional or causal (inclusive mask j <= i) per p->mode.  Queues FAVOR_FWD_KERNELS
+ * kernels on `stream`. */
 favor_status favor_attn_fwd(const favor_problem* p, const void* Q, const void* K, const void* V,
                             const float* W, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
+
+/* favor_attn_fwd with timing marks: events[i] (hipEvent_t, created by the caller) is
+ * recorded on `stream` before the i-th kernel and events[FAVOR_FWD_KERNELS] after the
+ * last, so hipEventElapsedTime(events[i], events[i+1]) is the i-th kernel's duration.
+ * n_events must be at least FAVOR_FWD_KERNELS + 1 (else FAVOR_ERR_INVALID_ARG); a failed
+ * event record returns FAVOR_ERR_HIP.  The kernels are the same as favor_attn_fwd's. */
+favor_status favor_attn_fwd_timed(const favor_problem* p, const void* Q, const void* K,
+                                  const void* V, const float* W, void* out, void* workspace,
+                                  size_t workspace_bytes, void* stream, void* const* events,
+                                  int32_t n_events);
 
 /* The positive feature map alone (Performer page, "제안 방법"), as a float32 tensor:
  *   side 0 (queries): X = Q, rows = batch*heads_q*seq_len, c per row (the row maximum of
