@@ -28,8 +28,9 @@ sys.path.insert(0, ROOT)
 METRIC = "FAVOR+ attention fwd tokens/s (B*H*L/s) and % MFMA/HBM roofline, 1 GPU"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA
+# Kernel slots of one call (the bidirectional path has no middle kernel).
 KERNELS = {
-    False: ("kv_summary", "kv_combine", "readout"),
+    False: ("kv_summary", None, "readout"),
     True: ("kv_summary", "causal_scan", "causal_chunk"),
 }
 
@@ -86,7 +87,7 @@ def algorithmic_work(w):
     q_bytes = 2 * e * B * Hq * L * d
     names = KERNELS[w.causal]
     if not w.causal:
-        return {names[0]: (k_bytes + w_bytes, B * Hkv * side), names[1]: (0, 0),
+        return {names[0]: (k_bytes + w_bytes, B * Hkv * side),
                 names[2]: (q_bytes + w_bytes + s_bytes, B * Hq * side)}
     return {names[0]: (k_bytes + w_bytes, B * Hkv * side), names[1]: (0, 0),
             names[2]: (q_bytes + k_bytes + w_bytes, B * Hq * side + B * Hkv * side)}
@@ -199,7 +200,8 @@ def main():
     t_host = time.perf_counter() - t_host
     ms_step = start.elapsed_time(end) / args.steps
     names = KERNELS[w.causal]
-    kms = {n: float(np.mean([hev.elapsed_ms(e[j], e[j + 1]) for e in evs])) for j, n in enumerate(names)}
+    kms = {n: float(np.mean([hev.elapsed_ms(e[j], e[j + 1]) for e in evs]))
+           for j, n in enumerate(names) if n is not None}
     for e in evs:
         hev.destroy(e)
 
@@ -214,6 +216,7 @@ def main():
 
     work = algorithmic_work(w)
     kernels = {}
+    names = [n for n in names if n is not None]
     for n in names:
         b, f = work[n]
         t = kms[n] * 1e-3

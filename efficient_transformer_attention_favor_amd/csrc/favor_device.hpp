@@ -177,6 +177,13 @@ __device__ __forceinline__ bf16x8 bias_cols(float c, int g, bf16x8) {
   return f;
 }
 __device__ __forceinline__ float bias_rows(float r, int g, float) { return g == 0 ? r : 1.f; }
+// A-side operand that picks up only the stabiliser part of bias_cols: rows get -c_col.
+__device__ __forceinline__ bf16x8 bias_unit_rows(int g, bf16x8) {
+  bf16x8 f = zero_frag(bf16x8{});
+  if (g == 0) f[3] = f[4] = f[5] = (bf16)1.f;
+  return f;
+}
+__device__ __forceinline__ float bias_unit_rows(int g, float) { return g == 0 ? 0.f : 1.f; }
 __device__ __forceinline__ float bias_cols(float c, int g, float) { return g == 0 ? -1.f : -c; }
 
 // Sum of squares of the contraction values a lane holds in its row operands.

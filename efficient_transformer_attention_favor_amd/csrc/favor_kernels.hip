@@ -12,7 +12,7 @@
 //                slice of 64 features; phi(K_blk) = exp2(K_blk W^T - |k|^2 log2e / 2 - c_f)
 //                on the MFMA (the bias enters as one extra MFMA), then S += phi^T [V, 1].
 //                c_f is a per-feature running maximum, moved lazily (kTau).
-//   kv_combine   bidirectional: S = sum_t 2^(c_t,f - c_f) S_t over the position ranges.
+//   (the readout sums the position-range partials while staging them)
 //   readout      bidirectional: per query tile, phi(Q) W-contraction on the MFMA with a
 //                running row maximum, then out^T = S^T phi(Q)^T and the division.
 //   causal_scan  causal: exclusive prefix of the per-segment summaries, all rescaled to a
@@ -23,6 +23,8 @@
 #include <hip/hip_runtime.h>
 
 #include <math.h>
+
+#include <type_traits>
 
 #include "favor_device.hpp"
 #include "favor_plan.hpp"
@@ -79,44 +81,57 @@ __device__ __forceinline__ void stage_rows(T* dst, int ld, const T* src, int p0,
 }
 
 // ======================================================================================
-// kv_summary: per (position range t, kv head bh) the partial summary
-//   S_t[f][c] = sum_{p in range} 2^(E_pf - c_f) [V, 1][p][c],
-//   E_pf = log2e (w_f . k_p - |k_p|^2 / 2),
-// stored fragment-native: tile (ft, ct) of 32 features x 32 value columns as
-// [16 registers][64 lanes] floats; register r / lane l holds feature 32 ft + 8(r/4) +
-// 4(l/32) + r%4 and value column 32 ct + vperm(l%32) (the ones column is ct = d/32, lane 0).
+// kv_summary: per (kv head bh, position range t, 64-feature slice) the partial summary
+//   S[f][c] = sum_{p in range} 2^(E_pf - c_f) [V, 1][p][c],   E_pf = log2e (w_f.k_p - |k_p|^2/2)
+// KW waves split the slice's features into NTW-tile groups and the range into position
+// groups; each wave streams 32-position blocks with its features' W in registers:
+// E = K_blk W^T (+ one bias MFMA carrying -|k|^2 log2e/2 - c_f), phi = 2^E,
+// S += phi^T [V, 1] (V transposed through wave-private LDS).  The wave partials of a
+// feature group are merged in LDS after rescaling to the largest c_f.  Output (float32):
+//   gs[bh][t][row][f], row = 32 ct + rho holds value column 32 ct + vperm(rho) (ct < d/32),
+//   row d holds the ones column (S_1);  gc[bh][t][f] = c_f (log2 units).
+// Workgroup ids are laid out so the feature slices of one (bh, t) share an XCD (and its L2
+// copy of K and V): block b runs on XCD b % 8.
 // ======================================================================================
+template <class T, int D> struct KvCfg;
+template <> struct KvCfg<bf16, 64> { static constexpr int KW = 8, NTW = 1; };   // 2 waves / SIMD
+template <> struct KvCfg<bf16, 128> { static constexpr int KW = 4, NTW = 1; };
+template <> struct KvCfg<float, 64> { static constexpr int KW = 4, NTW = 2; };
+template <> struct KvCfg<float, 128> { static constexpr int KW = 4, NTW = 1; };
+
 template <class T, int D>
-__global__ void __launch_bounds__(256) kv_summary_kernel(const T* __restrict__ K,
-                                                         const T* __restrict__ V,
-                                                         const float* __restrict__ W, int L,
-                                                         int Hkv, int Hw, int m, int R, int T_ranges,
-                                                         float* __restrict__ part_s,
-                                                         float* __restrict__ part_c) {
+__global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
+    const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ W, int L, int Hkv, int Hw, int m,
+    int R, int T_ranges, int n_units, float* __restrict__ gs, float* __restrict__ gc) {
   using P = Prec<T>;
   using frag = typename P::frag;
+  constexpr int KW = KvCfg<T, D>::KW, NTW = KvCfg<T, D>::NTW;
+  constexpr int FG = 2 / NTW;   // feature groups per workgroup (64 features)
+  constexpr int PG = KW / FG;   // position groups
   constexpr int NKC = D / P::KS;
   constexpr int NDT = D / 32 + 1;
-  constexpr int LDK = Ld<T>::template K<D>;
   constexpr int LDV = Ld<T>::template V<D>;
-  __shared__ __attribute__((aligned(16))) T Kl[32 * LDK];
-  __shared__ __attribute__((aligned(16))) T Vl[32 * LDV];
+  constexpr int ACC = NTW * NDT * 1024;  // floats of one wave's partial (fragment order)
+  __shared__ __attribute__((aligned(16))) T Vl[KW][32 * LDV];
+  __shared__ __attribute__((aligned(16))) float Red[(PG / 2) * FG][ACC];
+  __shared__ float Cs[KW][32 * NTW];
 
-  const int t = blockIdx.x, bh = blockIdx.y, hkv = bh % Hkv;
+  const int NFS = m / 64;
+  const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3;
+  const int slice = kq % NFS, unit = (kq / NFS) * 8 + xcd;
+  if (unit >= n_units) return;
+  const int bh = unit / T_ranges, t = unit % T_ranges, hkv = bh % Hkv;
   const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
-  // Up to 4 waves (256 features) per workgroup.  A wave past num_features (m not a
-  // multiple of 256) mirrors the first slice so the workgroup barriers stay uniform, and
-  // stores nothing.
-  const bool active = (int)(blockIdx.z * 4 + wave) * 64 < m;
-  const int f0 = active ? (blockIdx.z * 4 + wave) * 64 : 0;
+  const int fgi = wave % FG, pgi = wave / FG;
+  const int f0 = slice * 64 + fgi * 32 * NTW;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
   const T* Kh = K + (size_t)bh * L * D;
   const T* Vh = V + (size_t)bh * L * D;
+  T* vl = Vl[wave];
 
-  // W^T as the B operand: column = feature f0 + 32 nt + col.
-  frag wf[2][P::NSPLIT][NKC];
+  frag wf[NTW][P::NSPLIT][NKC];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       frag tmp[P::NSPLIT];
@@ -125,14 +140,9 @@ __global__ void __launch_bounds__(256) kv_summary_kernel(const T* __restrict__ K
       for (int s = 0; s < P::NSPLIT; ++s) wf[nt][s][kc] = tmp[s];
     }
 
-  float cst[2] = {0.f, 0.f};  // stabiliser of this lane's feature (log2 units)
-  frag biasB[2] = {bias_cols(0.f, g, frag{}), bias_cols(0.f, g, frag{})};
-  f32x16 S[2][NDT];
-#pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) S[nt][dt] = zero16();
-
+  float cst[NTW];  // stabiliser of this lane's feature (log2 units)
+  frag biasB[NTW];
+  f32x16 S[NTW][NDT];
   frag ones = zero_frag(frag{});
   if (col == 0) {
     if constexpr (sizeof(T) == 2) {
@@ -143,26 +153,57 @@ __global__ void __launch_bounds__(256) kv_summary_kernel(const T* __restrict__ K
     }
   }
 
-  const int p_begin = t * R;
-  const int p_end = min(p_begin + R, L);
-  bool first = true;
-  for (int p0 = p_begin; p0 < p_end; p0 += 32) {
-    __syncthreads();
-    stage_rows<T, D, false>(Kl, LDK, Kh, p0, L);
-    stage_rows<T, D, true>(Vl, LDV, Vh, p0, L);
-    __syncthreads();
+  const int pb = t * R, pe = min(pb + R, L);
+  const int Rw = ((R + 32 * PG - 1) / (32 * PG)) * 32;
+  const int wb = pb + pgi * Rw, we = min(wb + Rw, pe);
+  constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;          // chunks per row
+  constexpr int CPL = 32 * CPR / 64;    // chunks per lane per block
+  // Block loads are software-pipelined: block p0 + 32 is fetched into registers while
+  // block p0 is computed.  Loads are clamped into the range (rows past its end are real
+  // data whose features get a +huge row bias, i.e. phi = 0).
+  f32x4 vn[CPL];
+  frag kn[NKC];
+  auto fetch = [&](int q0) {
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = l + 64 * i, row = min(q0 + c / CPR, we - 1), c0 = (c % CPR) * EPC;
+      vn[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)row * D + c0);
+    }
+    const int krow = min(q0 + col, we - 1);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) kn[kc] = load_frag_k(Kh + (size_t)krow * D, kc, g);
+  };
 
-    // K block as the A operand (row = key col), |k|^2 -> bias operand.
+  // One 32-position block.  Stabiliser modes: 0 = first block of the fast pass (c_f :=
+  // this block's maximum), 1 = fast pass (c_f fixed: no VALU work on the accumulators),
+  // 2 = fallback pass (running maximum, moved lazily, accumulators rescaled).
+  auto block = [&](int p0, auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = l + 64 * i, row = c / CPR, c0 = (c % CPR) * EPC;
+      const f32x4 v = vn[i];
+      T* drow = vl + row * LDV + (c0 & ~31);
+      if constexpr (sizeof(T) == 2) {
+        *reinterpret_cast<float2*>(drow + vperm_inv(c0 & 31)) = float2{v[0], v[1]};
+        *reinterpret_cast<float2*>(drow + vperm_inv((c0 & 31) + 4)) = float2{v[2], v[3]};
+      } else {
+        *reinterpret_cast<f32x4*>(drow + vperm_inv(c0 & 31)) = v;
+      }
+    }
     frag kf[NKC];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) kf[kc] = load_frag_k(Kl + col * LDK, kc, g);
+    for (int kc = 0; kc < NKC; ++kc) kf[kc] = kn[kc];
+    fetch(min(p0 + 32, we - 1));
     float nrm = sumsq(kf);
     nrm += partner32(nrm);
-    const frag biasA = bias_rows(0.5f * kLog2e * nrm, g, frag{});
+    const float rb = p0 + col < we ? 0.5f * kLog2e * nrm : 1e30f;
+    const frag biasA = bias_rows(rb, g, frag{});
 
-    f32x16 c1[2];
+    f32x16 c1[NTW];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NTW; ++nt) {
       c1[nt] = zero16();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
@@ -170,45 +211,53 @@ __global__ void __launch_bounds__(256) kv_summary_kernel(const T* __restrict__ K
         for (int s = 0; s < P::NSPLIT; ++s) c1[nt] = mma(kf[kc], wf[nt][s][kc], c1[nt]);
       c1[nt] = mma(biasA, biasB[nt], c1[nt]);
     }
-    if (p0 + 32 > L) {
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (p0 + 8 * (r >> 2) + 4 * g + (r & 3) >= L) c1[nt][r] = -INFINITY;
-    }
 
-    // Running per-feature maximum, moved when a block exceeds it by more than kTau.
+    if constexpr (MODE == 0) {
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      float mx = c1[nt][0];
+      for (int nt = 0; nt < NTW; ++nt) {
+        float mx = c1[nt][0];
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, c1[nt][r]);
-      mx = fmaxf(mx, partner32(mx));
-      float shift = 0.f;
-      if (mx != -INFINITY && (first || mx > kTau)) shift = mx;
-      if (wave_any(shift != 0.f)) {
-        cst[nt] += shift;
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, c1[nt][r]);
+        mx = fmaxf(mx, partner32(mx));
+        cst[nt] = mx;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) c1[nt][r] -= shift;
-        biasB[nt] = bias_cols(cst[nt], g, frag{});
-        if (!first) {
-          const float fct = fast_exp2(-shift);
+        for (int r = 0; r < 16; ++r) c1[nt][r] -= mx;
+        biasB[nt] = bias_cols(mx, g, frag{});
+      }
+    } else if constexpr (MODE == 2) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float fr = __shfl(fct, 8 * (r >> 2) + 4 * g + (r & 3));
+      for (int nt = 0; nt < NTW; ++nt) {
+        float mx = c1[nt][0];
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) S[nt][dt][r] *= fr;
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, c1[nt][r]);
+        mx = fmaxf(mx, partner32(mx));
+        const bool first = cst[nt] == -INFINITY;
+        float shift = 0.f;
+        if (first || mx > kTau) shift = mx;
+        if (wave_any(shift != 0.f)) {
+          const float base = first ? 0.f : cst[nt];
+          cst[nt] = base + shift;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c1[nt][r] -= shift;
+          biasB[nt] = bias_cols(cst[nt], g, frag{});
+          if (!first) {
+            const float fct = fast_exp2(-shift);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float fr = __shfl(fct, 8 * (r >> 2) + 4 * g + (r & 3));
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) S[nt][dt][r] *= fr;
+            }
           }
+        } else if (first) {
+          cst[nt] = 0.f;  // block maximum is exactly 0
         }
       }
     }
-    first = false;
 
-    // phi^T as the A operand (row = feature, contraction = key), then S += phi^T [V, 1].
-    frag pa[2][P::NF32];
+    frag pa[NTW][P::NF32];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NTW; ++nt) {
       f32x16 e;
 #pragma unroll
       for (int r = 0; r < 16; ++r) e[r] = fast_exp2(c1[nt][r]);
@@ -218,69 +267,139 @@ __global__ void __launch_bounds__(256) kv_summary_kernel(const T* __restrict__ K
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int h = 0; h < P::NF32; ++h) {
-        const frag vb = dt < NDT - 1 ? lds_frag_rows(Vl, LDV, 0, 32 * dt, h) : ones;
+        const frag vb = dt < NDT - 1 ? lds_frag_rows(vl, LDV, 0, 32 * dt, h) : ones;
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) S[nt][dt] = mma(pa[nt][h], vb, S[nt][dt]);
+        for (int nt = 0; nt < NTW; ++nt) S[nt][dt] = mma(pa[nt][h], vb, S[nt][dt]);
       }
-  }
-
-  if (!active) return;
-  const size_t base = ((size_t)bh * T_ranges + t) * (size_t)m * (D + 32);
+    asm volatile("" ::: "memory");  // this block's LDS reads before the next block's writes
+  };
+  auto reset = [&]() {
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt) {
-    const int ft = f0 / 32 + nt;
+    for (int nt = 0; nt < NTW; ++nt) {
+      cst[nt] = -INFINITY;
+      biasB[nt] = bias_cols(0.f, g, frag{});
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      float* dst = part_s + base + (size_t)(ft * NDT + dt) * 1024;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) dst[r * 64 + l] = S[nt][dt][r];
+      for (int dt = 0; dt < NDT; ++dt) S[nt][dt] = zero16();
     }
-    if (g == 0) part_c[((size_t)bh * T_ranges + t) * m + f0 + 32 * nt + col] = cst[nt];
+  };
+
+  // Fast pass: stabiliser fixed at the first block's maximum.  Only an overflow (a later
+  // block more than ~2^100 above the first) makes it non-finite; then the range is redone
+  // with the running maximum.
+  reset();
+  if (wb < we) {
+    fetch(wb);
+    block(wb, std::integral_constant<int, 0>{});
+    for (int p0 = wb + 32; p0 < we; p0 += 32) block(p0, std::integral_constant<int, 1>{});
+  }
+  float chk = 0.f;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) chk += S[nt][dt][r];
+  if (wave_any(!(chk - chk == 0.f))) {
+    reset();
+    fetch(wb);
+    for (int p0 = wb; p0 < we; p0 += 32) block(p0, std::integral_constant<int, 2>{});
+  }
+
+  // ---- merge the position-group partials of each feature group --------------------
+  if (g == 0) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) Cs[wave][32 * nt + col] = cst[nt];
+  }
+  __syncthreads();
+  float cmax[NTW];  // merged stabiliser of this lane's C1 feature (column col)
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+    cmax[nt] = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < PG; ++q) cmax[nt] = fmaxf(cmax[nt], Cs[q * FG + fgi][32 * nt + col]);
+  }
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int fl = 32 * nt + 8 * (r >> 2) + 4 * g + (r & 3);
+      float cm = -INFINITY;
+#pragma unroll
+      for (int q = 0; q < PG; ++q) cm = fmaxf(cm, Cs[q * FG + fgi][fl]);
+      const float sc = cm == -INFINITY ? 0.f : fast_exp2(Cs[wave][fl] - cm);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) S[nt][dt][r] *= sc;
+    }
+  auto dump = [&](float* dst) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dst[((nt * NDT + dt) * 16 + r) * 64 + l] = S[nt][dt][r];
+  };
+  auto absorb = [&](const float* src) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) S[nt][dt][r] += src[((nt * NDT + dt) * 16 + r) * 64 + l];
+  };
+#pragma unroll
+  for (int step = PG / 2; step >= 1; step >>= 1) {
+    if (pgi >= step && pgi < 2 * step) dump(Red[(pgi - step) * FG + fgi]);
+    __syncthreads();
+    if (pgi < step) absorb(Red[pgi * FG + fgi]);
+    __syncthreads();
+  }
+  if (pgi != 0) return;
+
+  const size_t unit_off = (size_t)bh * T_ranges + t;
+  float* out_s = gs + unit_off * (size_t)(D + 1) * m;
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+    for (int dt = 0; dt < NDT - 1; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v = {S[nt][dt][4 * r4], S[nt][dt][4 * r4 + 1], S[nt][dt][4 * r4 + 2], S[nt][dt][4 * r4 + 3]};
+        *reinterpret_cast<f32x4*>(out_s + (size_t)(32 * dt + col) * m + f0 + 32 * nt + 8 * r4 + 4 * g) = v;
+      }
+    if (col == 0)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v = {S[nt][NDT - 1][4 * r4], S[nt][NDT - 1][4 * r4 + 1], S[nt][NDT - 1][4 * r4 + 2],
+                   S[nt][NDT - 1][4 * r4 + 3]};
+        *reinterpret_cast<f32x4*>(out_s + (size_t)D * m + f0 + 32 * nt + 8 * r4 + 4 * g) = v;
+      }
+    if (g == 0) gc[unit_off * m + f0 + 32 * nt + col] = cmax[nt];
   }
 }
 
 // ======================================================================================
-// kv_combine (bidirectional): S[f] = sum_t 2^(c_t,f - c_f) S_t[f], c_f = max_t c_t,f.
-// Grid (m/32 feature tiles, B*Hkv).  Fixed summation order t = 0, 1, ...
-// ======================================================================================
-__global__ void __launch_bounds__(256) kv_combine_kernel(const float* __restrict__ part_s,
-                                                         const float* __restrict__ part_c, int T_ranges,
-                                                         int m, int NDT, float* __restrict__ S_out,
-                                                         float* __restrict__ c_out) {
-  const int ft = blockIdx.x, bh = blockIdx.y;
-  const size_t tile_elems = (size_t)m * NDT * 32;
-  for (int e = threadIdx.x; e < NDT * 1024; e += blockDim.x) {
-    const int r = (e & 1023) >> 6, l = e & 63;
-    const int f = 32 * ft + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-    const float* pc = part_c + (size_t)bh * T_ranges * m + f;
-    float cm = -INFINITY;
-    for (int t = 0; t < T_ranges; ++t) cm = fmaxf(cm, pc[(size_t)t * m]);
-    const size_t off = (size_t)ft * NDT * 1024 + e;
-    const float* ps = part_s + (size_t)bh * T_ranges * tile_elems + off;
-    float acc = 0.f;
-    for (int t = 0; t < T_ranges; ++t) acc += fast_exp2(pc[(size_t)t * m] - cm) * ps[(size_t)t * tile_elems];
-    S_out[(size_t)bh * tile_elems + off] = acc;
-    if (e < 1024 && (l & 31) == 0) c_out[(size_t)bh * m + f] = cm;
-  }
-}
-
-// ======================================================================================
-// readout (bidirectional).  Grid (workgroups per kv head, B*Hkv), 4 waves; each wave owns
-// 32 query rows per step.  The G query heads of a kv head are G*L contiguous rows.
-// LDS holds W (hi/lo) and S^T (rows: value columns in vperm order, then the ones row;
-// features of each 32-tile reordered so one lane's 8 operand values are contiguous) for
-// a pass of MP features; more than one pass re-stages them per query tile.
+// readout (bidirectional).  Grid (workgroups per kv head, B*Hkv), NWAVE waves; each wave
+// owns QN x 32 query rows per step (the G query heads of a kv head are G*L contiguous
+// rows).  LDS holds W (hi/lo) and S^T for a pass of MP features: rows are value columns in
+// vperm order then the ones row; within a 32-feature tile the features are reordered so
+// one lane's 8 operand values are contiguous.  S is summed over the position ranges and
+// rescaled to the head's largest stabiliser while staged; with more than one pass W and S
+// are re-staged per query tile.
 // ======================================================================================
 template <class T, int D> struct ReadoutCfg;
 template <int D> struct ReadoutCfg<bf16, D> {
   static constexpr int MP = D == 64 ? 256 : 128;
   static constexpr int LDW = D + 8;
   static constexpr int LDS = MP + 8;
+  static constexpr int NWAVE = D == 64 ? 8 : 4;   // D = 64: 2 waves / SIMD
+  static constexpr int QN = D == 64 ? 2 : 1;
 };
 template <int D> struct ReadoutCfg<float, D> {
   static constexpr int MP = D == 64 ? 128 : 64;
   static constexpr int LDW = D + 1;
   static constexpr int LDS = MP + 1;
+  static constexpr int NWAVE = 4;
+  static constexpr int QN = D == 64 ? 2 : 1;
 };
 
 // position of feature fi (0..31 within a tile) in the S^T LDS row
@@ -300,20 +419,22 @@ __device__ __forceinline__ float s_frag(const float* Sl, int ld, int row, int ft
 }
 
 template <class T, int D>
-__global__ void __launch_bounds__(256) readout_kernel(const T* __restrict__ Q, const float* __restrict__ W,
-                                                      const float* __restrict__ S_in,
-                                                      const float* __restrict__ c_in, T* __restrict__ out,
-                                                      int L, int Hq, int Hkv, int Hw, int m) {
+__global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
+    readout_kernel(const T* __restrict__ Q, const float* __restrict__ W, const float* __restrict__ gs,
+                   const float* __restrict__ gc, T* __restrict__ out, int L, int Hq, int Hkv, int Hw, int m,
+                   int T_ranges) {
   using P = Prec<T>;
   using frag = typename P::frag;
   using Cfg = ReadoutCfg<T, D>;
   constexpr int NKC = D / P::KS;
   constexpr int NDT = D / 32 + 1;
-  constexpr int MP = Cfg::MP, LDW = Cfg::LDW, LDSS = Cfg::LDS;
-  constexpr int SROWS = (NDT - 1) * 32 + 1;
+  constexpr int MP = Cfg::MP, LDW = Cfg::LDW, LDSS = Cfg::LDS, QN = Cfg::QN;
+  constexpr int NT = 64 * Cfg::NWAVE;
+  constexpr int SROWS = D + 1;
+  constexpr int TILE = Cfg::NWAVE * QN * 32;
   __shared__ __attribute__((aligned(16))) T Wl[P::NSPLIT][MP * LDW];
   __shared__ __attribute__((aligned(16))) T Sl[SROWS * LDSS];
-  __shared__ float red[256];
+  __shared__ float red[NT];
 
   const int bh = blockIdx.y, b = bh / Hkv, hkv = bh % Hkv, G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
@@ -321,16 +442,15 @@ __global__ void __launch_bounds__(256) readout_kernel(const T* __restrict__ Q, c
   const T* Qb = Q + ((size_t)b * Hq + (size_t)hkv * G) * L * D;
   T* Ob = out + ((size_t)b * Hq + (size_t)hkv * G) * L * D;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
-  const size_t tile_elems = (size_t)m * NDT * 32;
-  const float* Sh = S_in + (size_t)bh * tile_elems;
-  const float* ch = c_in + (size_t)bh * m;
+  const float* gsh = gs + (size_t)bh * T_ranges * (D + 1) * m;
+  const float* gch = gc + (size_t)bh * T_ranges * m;
 
-  // Head-wide stabiliser c* = max_f c_f; S_f is rescaled by 2^(c_f - c*) when staged.
+  // Head-wide stabiliser c* = max over ranges and features.
   float cm = -INFINITY;
-  for (int f = threadIdx.x; f < m; f += blockDim.x) cm = fmaxf(cm, ch[f]);
+  for (int i = threadIdx.x; i < T_ranges * m; i += NT) cm = fmaxf(cm, gch[i]);
   red[threadIdx.x] = cm;
   __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
+  for (int s = NT / 2; s > 0; s >>= 1) {
     if ((int)threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
     __syncthreads();
   }
@@ -339,24 +459,63 @@ __global__ void __launch_bounds__(256) readout_kernel(const T* __restrict__ Q, c
   const int npass = (m + MP - 1) / MP;
   auto stage = [&](int pass) {
     const int fb = pass * MP, nf = min(MP, m - fb);
-    for (int e = threadIdx.x; e < nf * D; e += blockDim.x) {
-      const int fi = e / D, k = e % D;
-      const float x = Wh[(size_t)(fb + fi) * D + k] * kLog2e;
-      if constexpr (sizeof(T) == 2) {
-        const bf16 hi = (bf16)x;
-        Wl[0][fi * LDW + k] = hi;
-        Wl[P::NSPLIT - 1][fi * LDW + k] = (bf16)(x - (float)hi);
-      } else {
-        Wl[0][fi * LDW + k] = x;
+    // W rows: 4 float4 loads in flight per thread per step
+    constexpr int UW = 4;
+    for (int e0 = threadIdx.x; e0 < nf * (D / 4); e0 += UW * NT) {
+      f32x4 x[UW];
+#pragma unroll
+      for (int u = 0; u < UW; ++u) {
+        const int e = e0 + u * NT;
+        x[u] = e < nf * (D / 4) ? *reinterpret_cast<const f32x4*>(Wh + (size_t)(fb + e / (D / 4)) * D + (e % (D / 4)) * 4)
+                                : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < UW; ++u) {
+        const int e = e0 + u * NT;
+        if (e >= nf * (D / 4)) continue;
+        const int fi = e / (D / 4), k4 = (e % (D / 4)) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float xs = x[u][i] * kLog2e;
+          if constexpr (sizeof(T) == 2) {
+            const bf16 hi = (bf16)xs;
+            Wl[0][fi * LDW + k4 + i] = hi;
+            Wl[P::NSPLIT - 1][fi * LDW + k4 + i] = (bf16)(xs - (float)hi);
+          } else {
+            Wl[0][fi * LDW + k4 + i] = xs;
+          }
+        }
       }
     }
-    for (int e = threadIdx.x; e < SROWS * nf; e += blockDim.x) {
-      const int row = e / nf, fi = e % nf;
-      const int f = fb + fi, ft = f >> 5, fr = f & 31;
-      const int gg = (fr >> 2) & 1, r = 4 * (fr >> 3) + (fr & 3);
-      const int dt = row >> 5, rho = row & 31;
-      const float v = Sh[(size_t)(ft * NDT + dt) * 1024 + r * 64 + rho + 32 * gg] * fast_exp2(ch[f] - cstar);
-      Sl[row * LDSS + (fi & ~31) + s_pos<T>(fi & 31)] = (T)v;
+    // S rows: sum over the position ranges, rescaled to c*
+    constexpr int US = 4;
+    const int nsv = SROWS * (nf / 4);
+    for (int e0 = threadIdx.x; e0 < nsv; e0 += US * NT) {
+      f32x4 acc[US];
+#pragma unroll
+      for (int u = 0; u < US; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < T_ranges; ++t) {
+        f32x4 v[US], c[US];
+#pragma unroll
+        for (int u = 0; u < US; ++u) {
+          const int e = min(e0 + u * NT, nsv - 1);
+          const int row = e / (nf / 4), fi = (e % (nf / 4)) * 4;
+          v[u] = *reinterpret_cast<const f32x4*>(gsh + ((size_t)t * (D + 1) + row) * m + fb + fi);
+          c[u] = *reinterpret_cast<const f32x4*>(gch + (size_t)t * m + fb + fi);
+        }
+#pragma unroll
+        for (int u = 0; u < US; ++u)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[u][i] += v[u][i] * fast_exp2(c[u][i] - cstar);
+      }
+#pragma unroll
+      for (int u = 0; u < US; ++u) {
+        const int e = e0 + u * NT;
+        if (e >= nsv) continue;
+        const int row = e / (nf / 4), fi = (e % (nf / 4)) * 4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Sl[row * LDSS + ((fi + i) & ~31) + s_pos<T>((fi + i) & 31)] = (T)acc[u][i];
+      }
     }
   };
   if (npass == 1) {
@@ -364,86 +523,163 @@ __global__ void __launch_bounds__(256) readout_kernel(const T* __restrict__ Q, c
     __syncthreads();
   }
 
-  const size_t ntiles = (rows + 127) / 128;
+  const size_t ntiles = (rows + TILE - 1) / TILE;
   for (size_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
-    const size_t myrow = tile * 128 + wave * 32 + col;
-    const bool valid = myrow < rows;
-    frag qf[NKC];
+    size_t myrow[QN];
+    bool valid[QN];
+    frag qf[QN][NKC];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc)
-      qf[kc] = valid ? load_frag_k(Qb + myrow * D, kc, g) : zero_frag(frag{});
-
-    f32x16 acc[NDT];
+    for (int q = 0; q < QN; ++q) {
+      myrow[q] = tile * TILE + (size_t)(wave * QN + q) * 32 + col;
+      valid[q] = myrow[q] < rows;
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) acc[dt] = zero16();
-    float M = -INFINITY;
-
-    for (int pass = 0; pass < npass; ++pass) {
-      if (npass > 1) {
-        __syncthreads();
-        stage(pass);
-        __syncthreads();
-      }
-      const int nft = min(MP, m - pass * MP) / 32;
-      for (int ft = 0; ft < nft; ++ft) {
-        f32x16 c1 = zero16();
+      for (int kc = 0; kc < NKC; ++kc)
+        qf[q][kc] = valid[q] ? load_frag_k(Qb + myrow[q] * D, kc, g) : zero_frag(frag{});
+    }
+    f32x16 acc[QN][NDT];
+    float M[QN];
+    // One 32-feature tile.  Modes: 0 = first tile (M := its row maximum), 1 = M fixed (no
+    // VALU work on the accumulators), 2 = fallback (running maximum, moved lazily).
+    // Feature exponents of tile ft: C = W_ft Q^T (features x queries), lane = query; with
+    // BIAS the row stabiliser -M enters as one more MFMA.
+    auto c1_tile = [&](int ft, f32x16 (&c1)[QN], auto bias_tag) {
 #pragma unroll
-        for (int kc = 0; kc < NKC; ++kc)
+      for (int q = 0; q < QN; ++q) c1[q] = zero16();
 #pragma unroll
-          for (int s = 0; s < P::NSPLIT; ++s) {
-            const frag a = load_frag_k(&Wl[s][(32 * ft + col) * LDW], kc, g);
-            c1 = mma(a, qf[kc], c1);
-          }
-        float mx = c1[0];
+      for (int kc = 0; kc < NKC; ++kc)
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, c1[r]);
-        mx = fmaxf(mx, partner32(mx));
-        if (wave_any(mx > M + kTau)) {
-          const float nm = mx > M + kTau ? mx : M;
-          const float fct = fast_exp2(M - nm);
+        for (int s = 0; s < P::NSPLIT; ++s) {
+          const frag a = load_frag_k(&Wl[s][(32 * ft + col) * LDW], kc, g);
 #pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[dt][r] *= fct;
-          M = nm;
+          for (int q = 0; q < QN; ++q) c1[q] = mma(a, qf[q][kc], c1[q]);
         }
+      if constexpr (decltype(bias_tag)::value) {
+        const frag unitA = bias_unit_rows(g, frag{});
+#pragma unroll
+        for (int q = 0; q < QN; ++q) c1[q] = mma(unitA, bias_cols(M[q], g, frag{}), c1[q]);
+      }
+    };
+    // phi = 2^(c1 [- M]) and acc += S_ft^T phi.
+    auto readout_tile = [&](int ft, const f32x16 (&c1)[QN], auto sub_tag) {
+      frag pf[QN][P::NF32];
+#pragma unroll
+      for (int q = 0; q < QN; ++q) {
         f32x16 e;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(c1[r] - M);
-        frag pf[P::NF32];
-        acc_to_frags(e, pf);
+        for (int r = 0; r < 16; ++r)
+          e[r] = fast_exp2(decltype(sub_tag)::value ? c1[q][r] - M[q] : c1[q][r]);
+        acc_to_frags(e, pf[q]);
+      }
 #pragma unroll
-        for (int h = 0; h < P::NF32; ++h) {
+      for (int h = 0; h < P::NF32; ++h) {
 #pragma unroll
-          for (int dt = 0; dt < NDT - 1; ++dt) acc[dt] = mma(s_frag(Sl, LDSS, 32 * dt + col, ft, h, g), pf[h], acc[dt]);
-          const frag a1 = col == 0 ? s_frag(Sl, LDSS, 32 * (NDT - 1), ft, h, g) : zero_frag(frag{});
-          acc[NDT - 1] = mma(a1, pf[h], acc[NDT - 1]);
+        for (int dt = 0; dt < NDT - 1; ++dt) {
+          const frag a = s_frag(Sl, LDSS, 32 * dt + col, ft, h, g);
+#pragma unroll
+          for (int q = 0; q < QN; ++q) acc[q][dt] = mma(a, pf[q][h], acc[q][dt]);
+        }
+        const frag a1 = col == 0 ? s_frag(Sl, LDSS, D, ft, h, g) : zero_frag(frag{});
+#pragma unroll
+        for (int q = 0; q < QN; ++q) acc[q][NDT - 1] = mma(a1, pf[q][h], acc[q][NDT - 1]);
+      }
+    };
+    auto rowmax = [&](const f32x16& c) {
+      float mx = c[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, c[r]);
+      return fmaxf(mx, partner32(mx));
+    };
+    using Yes = std::integral_constant<bool, true>;
+    using No = std::integral_constant<bool, false>;
+    // Fast pass: the stabiliser is fixed at the first tile's row maximum and folded into
+    // the W-contraction (bias MFMA), so the loop does exponentials only.  Fallback: plain
+    // order with a lazily moved running maximum.
+    auto run = [&](bool fast) {
+#pragma unroll
+      for (int q = 0; q < QN; ++q) {
+        M[q] = -INFINITY;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[q][dt] = zero16();
+      }
+      for (int pass = 0; pass < npass; ++pass) {
+        if (npass > 1) {
+          __syncthreads();
+          stage(pass);
+          __syncthreads();
+        }
+        const int nft = min(MP, m - pass * MP) / 32;
+        if (fast) {
+          int ft = 0;
+          if (pass == 0) {
+            f32x16 c1[QN];
+            c1_tile(0, c1, No{});
+#pragma unroll
+            for (int q = 0; q < QN; ++q) M[q] = rowmax(c1[q]);
+            readout_tile(0, c1, Yes{});
+            ft = 1;
+          }
+          for (; ft < nft; ++ft) {
+            f32x16 c1[QN];
+            c1_tile(ft, c1, Yes{});
+            readout_tile(ft, c1, No{});
+          }
+        } else {
+          for (int ft = 0; ft < nft; ++ft) {
+            f32x16 c1[QN];
+            c1_tile(ft, c1, No{});
+#pragma unroll
+            for (int q = 0; q < QN; ++q) {
+              const float mx = rowmax(c1[q]);
+              if (wave_any(mx > M[q] + kTau)) {
+                const float nm = mx > M[q] + kTau ? mx : M[q];
+                const float fct = fast_exp2(M[q] - nm);
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                  for (int r = 0; r < 16; ++r) acc[q][dt][r] *= fct;
+                M[q] = nm;
+              }
+            }
+            readout_tile(ft, c1, Yes{});
+          }
         }
       }
+    };
+    // Fast pass with the stabiliser fixed at the first feature tile's row maximum; a
+    // non-finite denominator (an overflow) sends the whole tile to the fallback.
+    run(true);
+    bool bad = false;
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      const float dq = acc[q][NDT - 1][0];
+      bad |= !(dq - dq == 0.f);
     }
+    if (__syncthreads_or(bad)) run(false);
 
-    float den = acc[NDT - 1][0];
-    const float dp = partner32(den);
-    den = g ? dp : den;
-    const float inv = 1.f / den;
-    if (valid) {
-      T* orow = Ob + myrow * D;
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      float den = acc[q][NDT - 1][0];
+      const float dp = partner32(den);
+      den = g ? dp : den;
+      const float inv = 1.f / den;
+      if (!valid[q]) continue;
+      T* orow = Ob + myrow[q] * D;
 #pragma unroll
       for (int dt = 0; dt < NDT - 1; ++dt) {
         if constexpr (sizeof(T) == 2) {
           bf16x8 o0, o1;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            o0[j] = (bf16)(acc[dt][j] * inv);
-            o1[j] = (bf16)(acc[dt][8 + j] * inv);
+            o0[j] = (bf16)(acc[q][dt][j] * inv);
+            o1[j] = (bf16)(acc[q][dt][8 + j] * inv);
           }
           *reinterpret_cast<bf16x8*>(orow + 32 * dt + 16 * g) = o0;
           *reinterpret_cast<bf16x8*>(orow + 32 * dt + 16 * g + 8) = o1;
         } else {
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
-            f32x4 o = {acc[dt][4 * q4] * inv, acc[dt][4 * q4 + 1] * inv, acc[dt][4 * q4 + 2] * inv,
-                       acc[dt][4 * q4 + 3] * inv};
+            f32x4 o = {acc[q][dt][4 * q4] * inv, acc[q][dt][4 * q4 + 1] * inv, acc[q][dt][4 * q4 + 2] * inv,
+                       acc[q][dt][4 * q4 + 3] * inv};
             *reinterpret_cast<f32x4*>(orow + 32 * dt + 16 * g + 4 * q4) = o;
           }
         }
@@ -452,21 +688,24 @@ __global__ void __launch_bounds__(256) readout_kernel(const T* __restrict__ Q, c
   }
 }
 
-
 // ======================================================================================
 // causal_scan: per kv head, c* = max over segments and features of the segment
 // stabilisers, and the exclusive prefix P_t = sum_{t' < t} 2^(c_t',f - c*) S_t' of the
-// segment summaries (fragment-native, same layout as kv_summary).  Grid (m/32 * (d/32+1)
-// tiles, B*Hkv); fixed order t = 0, 1, ...
+// segment summaries (read in kv_summary's row layout, written fragment-native for the
+// chunk kernel's carry registers: tile (ft, ct) of 32 features x 32 value columns as
+// [16 registers][64 lanes], register r / lane l = feature 32 ft + 8(r/4) + 4(l/32) + r%4,
+// value column 32 ct + vperm(l%32); ct = d/32 is the ones column at lane%32 == 0).
+// Grid (m/32 * (d/32+1) tiles, B*Hkv); fixed order t = 0, 1, ...
 // ======================================================================================
-__global__ void __launch_bounds__(256) causal_scan_kernel(const float* __restrict__ part_s,
-                                                          const float* __restrict__ part_c, int T_ranges,
-                                                          int m, int NDT, float* __restrict__ prefix,
+__global__ void __launch_bounds__(256) causal_scan_kernel(const float* __restrict__ gs,
+                                                          const float* __restrict__ gc, int T_ranges, int m,
+                                                          int D, float* __restrict__ prefix,
                                                           float* __restrict__ cstar_out) {
   __shared__ float red[256];
+  const int NDT = D / 32 + 1;
   const int tile = blockIdx.x, bh = blockIdx.y;
   const size_t tile_elems = (size_t)m * NDT * 32;
-  const float* pc = part_c + (size_t)bh * T_ranges * m;
+  const float* pc = gc + (size_t)bh * T_ranges * m;
   float cm = -INFINITY;
   for (int i = threadIdx.x; i < T_ranges * m; i += blockDim.x) cm = fmaxf(cm, pc[i]);
   red[threadIdx.x] = cm;
@@ -477,15 +716,18 @@ __global__ void __launch_bounds__(256) causal_scan_kernel(const float* __restric
   }
   const float cstar = red[0];
   if (tile == 0 && threadIdx.x == 0) cstar_out[bh] = cstar;
-  const int ft = tile / NDT;
+  const int ft = tile / NDT, dt = tile % NDT;
   for (int e = threadIdx.x; e < 1024; e += blockDim.x) {
-    const int r = e >> 6, l = e & 63;
+    const int r = e >> 6, l = e & 63, rho = l & 31;
     const int f = 32 * ft + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-    const size_t off = (size_t)bh * T_ranges * tile_elems + (size_t)tile * 1024 + e;
+    const int row = dt < NDT - 1 ? 32 * dt + rho : (rho == 0 ? D : -1);
+    float* dst = prefix + (size_t)bh * T_ranges * tile_elems + (size_t)tile * 1024 + e;
     float acc = 0.f;
     for (int t = 0; t < T_ranges; ++t) {
-      prefix[off + (size_t)t * tile_elems] = acc;
-      acc += fast_exp2(pc[(size_t)t * m + f] - cstar) * part_s[off + (size_t)t * tile_elems];
+      dst[(size_t)t * tile_elems] = acc;
+      if (row >= 0)
+        acc += fast_exp2(pc[(size_t)t * m + f] - cstar) *
+               gs[(((size_t)bh * T_ranges + t) * (D + 1) + row) * m + f];
     }
   }
 }
@@ -757,27 +999,33 @@ struct Marks {
 };
 
 template <class T, int D>
+favor_status launch_kv_summary(const Plan& s, const T* K, const T* V, const float* W, float* gs, float* gc,
+                               hipStream_t st) {
+  const int units = s.BH * s.T;
+  const int nfs = s.m / kFeatPerWave;
+  hipLaunchKernelGGL((kv_summary_kernel<T, D>), dim3(8 * ceil_div_i(units, 8) * nfs), dim3(64 * KvCfg<T, D>::KW), 0,
+                     st, K, V, W,
+                     s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc);
+  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+template <class T, int D>
 favor_status run_bidirectional(const Plan& s, const T* Q, const T* K, const T* V, const float* W, T* out,
                                char* ws, hipStream_t st, const Marks& mk) {
-  float* part_s = reinterpret_cast<float*>(ws + s.off_part_s);
-  float* part_c = reinterpret_cast<float*>(ws + s.off_part_c);
-  float* S = reinterpret_cast<float*>(ws + s.off_s);
-  float* c = reinterpret_cast<float*>(ws + s.off_c);
-  const int nw = s.m / kFeatPerWave;
+  float* gs = reinterpret_cast<float*>(ws + s.off_gs);
+  float* gc = reinterpret_cast<float*>(ws + s.off_gc);
   if (!mk.mark(0, st)) return FAVOR_ERR_HIP;
-  hipLaunchKernelGGL((kv_summary_kernel<T, D>), dim3(s.T, s.BH, ceil_div_i(nw, 4)), dim3(kWave * (nw < 4 ? nw : 4)), 0, st, K, V, W, s.L,
-                     s.Hkv, s.Hw, s.m, s.R, s.T, part_s, part_c);
-  if (hipGetLastError() != hipSuccess || !mk.mark(1, st)) return FAVOR_ERR_HIP;
-  hipLaunchKernelGGL(kv_combine_kernel, dim3(s.NFT, s.BH), dim3(256), 0, st, part_s, part_c, s.T, s.m, s.NDT,
-                     S, c);
-  if (hipGetLastError() != hipSuccess || !mk.mark(2, st)) return FAVOR_ERR_HIP;
+  favor_status rc = launch_kv_summary<T, D>(s, K, V, W, gs, gc, st);
+  if (rc != FAVOR_OK) return rc;
+  if (!mk.mark(1, st) || !mk.mark(2, st)) return FAVOR_ERR_HIP;  // no middle kernel
+  using Cfg = ReadoutCfg<T, D>;
   const long long rows = (long long)s.G * s.L;
-  const int tiles = ceil_div_i(rows, 4 * kQueriesPerWave);
-  int per_head = ceil_div_i(kRangeTarget, s.BH);
+  const int tiles = ceil_div_i(rows, Cfg::NWAVE * Cfg::QN * 32);
+  int per_head = ceil_div_i(kReadoutTarget, s.BH);
   if (per_head > tiles) per_head = tiles;
   if (per_head < 1) per_head = 1;
-  hipLaunchKernelGGL((readout_kernel<T, D>), dim3(per_head, s.BH), dim3(256), 0, st, Q, W, S, c, out, s.L,
-                     s.Hq, s.Hkv, s.Hw, s.m);
+  hipLaunchKernelGGL((readout_kernel<T, D>), dim3(per_head, s.BH), dim3(64 * Cfg::NWAVE), 0, st, Q, W, gs, gc, out,
+                     s.L, s.Hq, s.Hkv, s.Hw, s.m, s.T);
   if (hipGetLastError() != hipSuccess || !mk.mark(3, st)) return FAVOR_ERR_HIP;
   return FAVOR_OK;
 }
@@ -785,17 +1033,16 @@ favor_status run_bidirectional(const Plan& s, const T* Q, const T* K, const T* V
 template <class T, int D>
 favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const float* W, T* out, char* ws,
                         hipStream_t st, const Marks& mk) {
-  float* part_s = reinterpret_cast<float*>(ws + s.off_part_s);
-  float* part_c = reinterpret_cast<float*>(ws + s.off_part_c);
-  float* cstar = reinterpret_cast<float*>(ws + s.off_c);
+  float* gs = reinterpret_cast<float*>(ws + s.off_gs);
+  float* gc = reinterpret_cast<float*>(ws + s.off_gc);
   float* prefix = reinterpret_cast<float*>(ws + s.off_p);
+  float* cstar = reinterpret_cast<float*>(ws + s.off_cstar);
   const int nw = s.m / kFeatPerWave;
   if (!mk.mark(0, st)) return FAVOR_ERR_HIP;
-  hipLaunchKernelGGL((kv_summary_kernel<T, D>), dim3(s.T, s.BH, ceil_div_i(nw, 4)), dim3(kWave * (nw < 4 ? nw : 4)),
-                     0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, part_s, part_c);
-  if (hipGetLastError() != hipSuccess || !mk.mark(1, st)) return FAVOR_ERR_HIP;
-  hipLaunchKernelGGL(causal_scan_kernel, dim3(s.NFT * s.NDT, s.BH), dim3(256), 0, st, part_s, part_c, s.T, s.m,
-                     s.NDT, prefix, cstar);
+  favor_status rc = launch_kv_summary<T, D>(s, K, V, W, gs, gc, st);
+  if (rc != FAVOR_OK || !mk.mark(1, st)) return rc != FAVOR_OK ? rc : FAVOR_ERR_HIP;
+  hipLaunchKernelGGL(causal_scan_kernel, dim3(s.NFT * s.NDT, s.BH), dim3(256), 0, st, gs, gc, s.T, s.m, s.d,
+                     prefix, cstar);
   if (hipGetLastError() != hipSuccess || !mk.mark(2, st)) return FAVOR_ERR_HIP;
   if (nw <= 4)
     hipLaunchKernelGGL((causal_chunk_kernel<T, D, 4>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,

@@ -45,30 +45,38 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
   q.NFT = q.m / kTile;
   q.NDT = q.d / kTile + 1;
 
-  // Split each kv head's positions into T ranges of R positions so that the key-side
-  // pass has about kRangeTarget workgroups; R is a multiple of the chunk (causal) or of
-  // a 32-position block.  The split depends on the problem only, which keeps the
-  // reduction order -- and so the result bits -- independent of the device.
-  const int unit = q.mode == FAVOR_CAUSAL ? q.chunk : kTile;
-  const int max_t = ceil_div(q.L, unit);
-  int T = ceil_div(kRangeTarget, q.BH);
-  if (T > max_t) T = max_t;
+  // Position ranges per kv head.  Bidirectional: about kKeyTarget key-side workgroups
+  // (one per range and 64-feature slice), each range at least 128 positions.  Causal:
+  // about kSegmentTarget chunk-kernel workgroups (one per segment and query head), the
+  // segment a multiple of the chunk.  The split depends on the problem only, which keeps
+  // the reduction order -- and so the result bits -- independent of the device.
+  const int nfs = q.m / kFeatPerWave;
+  int T, unit;
+  if (q.mode == FAVOR_CAUSAL) {
+    unit = q.chunk;
+    T = ceil_div(kSegmentTarget, (long long)q.B * q.Hq);
+    const int max_t = ceil_div(q.L, unit);
+    if (T > max_t) T = max_t;
+  } else {
+    unit = 4 * kTile;
+    T = (int)((kKeyTarget + (long long)q.BH * nfs / 2) / ((long long)q.BH * nfs));
+    const int max_t = ceil_div(q.L, unit);
+    if (T > max_t) T = max_t;
+  }
   if (T < 1) T = 1;
   q.R = ceil_div(ceil_div(q.L, T), unit) * unit;
   q.T = ceil_div(q.L, q.R);
 
   q.tile_elems = (size_t)q.m * (size_t)(q.d + kTile);
   size_t off = 0;
-  q.off_part_s = off;
-  off = align256(off + sizeof(float) * q.tile_elems * q.BH * q.T);
-  q.off_part_c = off;
+  q.off_gs = off;
+  off = align256(off + sizeof(float) * (size_t)(q.d + 1) * q.m * q.BH * q.T);
+  q.off_gc = off;
   off = align256(off + sizeof(float) * (size_t)q.m * q.BH * q.T);
-  q.off_s = off;
-  if (q.mode == FAVOR_BIDIRECTIONAL) off = align256(off + sizeof(float) * q.tile_elems * q.BH);
-  q.off_c = off;
-  off = align256(off + sizeof(float) * (size_t)q.m * q.BH);
   q.off_p = off;
   if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * q.tile_elems * q.BH * q.T);
+  q.off_cstar = off;
+  if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * q.BH);
   q.bytes = off;
   return FAVOR_OK;
 }

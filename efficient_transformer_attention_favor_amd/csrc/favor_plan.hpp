@@ -11,8 +11,9 @@ namespace favor {
 constexpr int kWave = 64;          // wavefront width on CDNA
 constexpr int kTile = 32;          // MFMA tile edge (32x32 accumulators)
 constexpr int kFeatPerWave = 64;   // features owned by one wave in the key-side kernels
-constexpr int kRangeTarget = 512;  // workgroups the key-side pass aims for
-constexpr int kQueriesPerWave = 32;
+constexpr int kKeyTarget = 256;     // key-side workgroups (4 waves each) a pass aims for
+constexpr int kSegmentTarget = 512; // causal chunk-kernel workgroups a pass aims for
+constexpr int kReadoutTarget = 256; // readout workgroups a pass aims for
 
 struct Plan {
   int B, Hq, Hkv, Hw, L, d, m, dtype, mode, chunk;
@@ -23,11 +24,10 @@ struct Plan {
   int NFT;  // feature tiles: m / 32
   int NDT;  // value-column tiles incl. the ones column: d / 32 + 1
   size_t tile_elems;   // m * (d + 32): floats of one fragment-native summary
-  size_t off_part_s;   // [BH][T] summaries (fragment-native float)
-  size_t off_part_c;   // [BH][T][m] per-feature stabilisers (log2 units)
-  size_t off_s;        // [BH] combined summary (bidirectional) / unused (causal)
-  size_t off_c;        // [BH][m] combined stabilisers (bidirectional) / [BH] global (causal)
-  size_t off_p;        // [BH][T] exclusive prefixes (causal)
+  size_t off_gs;       // [BH][T][d+1][m] range / segment summaries (float)
+  size_t off_gc;       // [BH][T][m] their per-feature stabilisers (log2 units)
+  size_t off_p;        // [BH][T] exclusive prefixes, fragment-native (causal)
+  size_t off_cstar;    // [BH] global stabiliser per kv head (causal)
   size_t bytes;        // total workspace bytes
 };
 

@@ -77,21 +77,22 @@ typedef struct {
 /* Bytes of workspace favor_attn_fwd needs for *p (0 if *p is invalid). */
 size_t favor_workspace_bytes(const favor_problem* p);
 
-/* Kernels one favor_attn_fwd call queues: the key/value summary per position range (or
- * segment), the combine (bidirectional) or prefix scan (causal), and the query readout
- * (bidirectional) or chunked causal pass. */
+/* Kernel slots of one favor_attn_fwd call: the key/value summary per position range (or
+ * segment); the prefix scan of the segment summaries (causal; empty for bidirectional
+ * problems); the query readout (bidirectional) or chunked causal pass. */
 #define FAVOR_FWD_KERNELS 3
 
 /* FAVOR+ forward (Performer page, "제안 방법"): out = D^-1 A_hat V in linear order,
- * bidirectional or causal (inclusive mask j <= i) per p->mode.  Queues FAVOR_FWD_KERNELS
- * kernels on `stream`. */
+ * bidirectional or causal (inclusive mask j <= i) per p->mode.  Queues 2 (bidirectional)
+ * or 3 (causal) kernels on `stream`. */
 favor_status favor_attn_fwd(const favor_problem* p, const void* Q, const void* K, const void* V,
                             const float* W, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
 /* favor_attn_fwd with timing marks: events[i] (hipEvent_t, created by the caller) is
  * recorded on `stream` before the i-th kernel and events[FAVOR_FWD_KERNELS] after the
- * last, so hipEventElapsedTime(events[i], events[i+1]) is the i-th kernel's duration.
+ * last, so hipEventElapsedTime(events[i], events[i+1]) is the duration of kernel slot i
+ * (an empty slot's two events are recorded back to back).
  * n_events must be at least FAVOR_FWD_KERNELS + 1 (else FAVOR_ERR_INVALID_ARG); a failed
  * event record returns FAVOR_ERR_HIP.  The kernels are the same as favor_attn_fwd's. */
 favor_status favor_attn_fwd_timed(const favor_problem* p, const void* Q, const void* K,
