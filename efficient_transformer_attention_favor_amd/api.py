@@ -74,7 +74,13 @@ def features(X, W, side, heads_q, heads_kv, stream=None):
     Returns (phi (rows, m) float32, c) with c the natural-log stabiliser per row (side 0)
     or per (batch, kv head) (side 1).
     """
+    if X.dim() != 4 or W.dim() != 3 or X.dtype not in _DTYPES or W.dtype != torch.float32:
+        raise ValueError("expected X (B, H, L, d) in float32/bfloat16 and W (Hw, m, d) float32")
+    if X.device.type != "cuda" or W.device != X.device or not (X.is_contiguous() and W.is_contiguous()):
+        raise ValueError("X and W must be contiguous tensors on one GPU")
     B, H, L, d = X.shape
+    if side not in (0, 1) or H != (heads_q if side == 0 else heads_kv):
+        raise ValueError("side 0 takes X with heads_q heads, side 1 with heads_kv heads")
     m = W.shape[1]
     dtype = _DTYPES[X.dtype]
     p = _lib.problem(B, heads_q, heads_kv, W.shape[0], L, d, m, dtype, _lib.FAVOR_BIDIRECTIONAL)

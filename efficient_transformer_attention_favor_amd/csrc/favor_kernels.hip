@@ -1121,15 +1121,4 @@ favor_status favor_attn_fwd_timed(const favor_problem* p, const void* Q, const v
                        favor::Marks{reinterpret_cast<hipEvent_t*>(const_cast<void**>(events)), n_events});
 }
 
-favor_status favor_features(const favor_problem* p, int32_t side, const void* X, const float* W, float* phi_out,
-                            float* c_out, void* stream) {
-  favor::Plan s;
-  const favor_status st = favor::make_plan(p, &s);
-  if (st != FAVOR_OK) return st;
-  if (side != 0 && side != 1) return FAVOR_ERR_INVALID_ARG;
-  if (X == nullptr || W == nullptr || phi_out == nullptr || c_out == nullptr) return FAVOR_ERR_INVALID_ARG;
-  (void)stream;
-  return FAVOR_ERR_UNSUPPORTED;
-}
-
 }  // extern "C"

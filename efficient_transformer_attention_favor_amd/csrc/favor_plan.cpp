@@ -23,7 +23,7 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
   if (p->mode != FAVOR_BIDIRECTIONAL && p->mode != FAVOR_CAUSAL) return FAVOR_ERR_UNSUPPORTED;
   if (p->head_dim != 64 && p->head_dim != 128) return FAVOR_ERR_UNSUPPORTED;
   if (p->num_features % 64 != 0 || p->num_features > 512) return FAVOR_ERR_UNSUPPORTED;
-  if (p->chunk != 0 && p->chunk != 32 && p->chunk != 64 && p->chunk != 128)
+  if (p->chunk != 0 && p->chunk != 32 && p->chunk != 64 && p->chunk != 128 && p->chunk != 256)
     return FAVOR_ERR_UNSUPPORTED;
   const long long elems_q = (long long)p->batch * p->heads_q * p->seq_len * p->head_dim;
   const long long elems_kv = (long long)p->batch * p->heads_kv * p->seq_len * p->head_dim;

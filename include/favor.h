@@ -63,9 +63,10 @@ typedef enum { FAVOR_BIDIRECTIONAL = 0, FAVOR_CAUSAL = 1 } favor_mode;
 
 /* Problem description.  Supported: head_dim in {64, 128}; num_features a multiple of 64
  * in [64, 512]; heads_q % heads_kv == 0; heads_w in {1, heads_kv}; seq_len >= 1;
- * batch * heads_q * seq_len * head_dim < 2^31.  chunk (causal only) is the number of
- * positions between carry updates: 0 (library default) or one of 32, 64, 128; ignored
- * for bidirectional problems. */
+ * batch * heads_q * seq_len * head_dim < 2^31.  chunk (causal only) is the granularity
+ * of the sequence segments that run in parallel (each segment a multiple of it): 0
+ * (library default, 32) or one of 32, 64, 128, 256; the result does not depend on it
+ * beyond rounding.  Ignored for bidirectional problems. */
 typedef struct {
   int32_t batch, heads_q, heads_kv, heads_w;
   int32_t seq_len, head_dim, num_features;
@@ -106,8 +107,11 @@ favor_status favor_attn_fwd_timed(const favor_problem* p, const void* Q, const v
  *   side 1 (keys):    X = K, rows = batch*heads_kv*seq_len, one c per (batch, kv head)
  *                     (the maximum over that head), c_out [batch*heads_kv].
  * phi_out [rows][num_features] = exp(W x - |x|^2/2 - c) / sqrt(m), with the natural-log
- * stabiliser c written to c_out.  W of row x is the one its kv head uses.  Diagnostic
- * entry point: it is not on the attention path and does not use a workspace. */
+ * stabiliser c written to c_out.  W of row x is the one its kv head uses; p->mode and
+ * p->chunk are ignored.  phi_out and c_out are device pointers owned by the caller
+ * (float32, sizes as above).  Queues 1 kernel (side 0) or 4 (side 1) on `stream`;
+ * side 1 uses c_out as scratch until its last kernel.  Diagnostic entry point: the
+ * attention kernels compute the same features on chip and never write them out. */
 favor_status favor_features(const favor_problem* p, int32_t side, const void* X, const float* W,
                             float* phi_out, float* c_out, void* stream);
 

@@ -83,7 +83,7 @@ def test_small_full_parity(w):
     assert err < TOL[w.dtype]
 
 
-@pytest.mark.parametrize("chunk", [0, 32, 64, 128])
+@pytest.mark.parametrize("chunk", [0, 32, 64, 128, 256])
 def test_causal_chunk_sizes(chunk):
     w = _small("c3_causal_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1111)
     _say(f"case {w} chunk={chunk}")
