@@ -20,7 +20,9 @@
 namespace favor {
 
 typedef __bf16 bf16;
+typedef _Float16 f16;
 typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef f16 f16x8 __attribute__((ext_vector_type(8)));
 typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -48,6 +50,9 @@ __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x16 mma(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ f32x16 mma(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -60,19 +65,26 @@ __device__ __forceinline__ f32x16 zero16() {
 }
 
 // Per-precision traits.  T is the element type of Q, K, V and out.
+//   frag   operand of the feature-side contractions (phi with S or with [V, 1])
+//   wfrag  operand of the W contraction.  bf16 problems contract in fp16: bf16 Q and K
+//          values convert to fp16 exactly (|x| < 65504; below 2^-14 they lose low bits,
+//          an absolute error under 2^-25), and W * log2(e) rounds to fp16's 11-bit
+//          significand, so the exponent is 8x more accurate than with bf16 W.
 template <class T> struct Prec;
 
 template <> struct Prec<bf16> {
   using frag = bf16x8;
+  using wfrag = f16x8;
+  using welem = f16;
   static constexpr int KS = 16;     // contraction length of one MFMA
-  static constexpr int NSPLIT = 2;  // W = W_hi + W_lo, both bf16
   static constexpr int NF32 = 2;    // operands per 32-deep contraction
 };
 
 template <> struct Prec<float> {
   using frag = float;
+  using wfrag = float;
+  using welem = float;
   static constexpr int KS = 2;
-  static constexpr int NSPLIT = 1;
   static constexpr int NF32 = 16;
 };
 
@@ -82,7 +94,22 @@ __device__ __forceinline__ bf16x8 zero_frag(bf16x8) {
   for (int j = 0; j < 8; ++j) z[j] = (bf16)0.f;
   return z;
 }
+__device__ __forceinline__ f16x8 zero_frag(f16x8) {
+  f16x8 z;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) z[j] = (f16)0.f;
+  return z;
+}
 __device__ __forceinline__ float zero_frag(float) { return 0.f; }
+
+// Q / K operand of the W contraction.
+__device__ __forceinline__ f16x8 to_wfrag(bf16x8 x) {
+  f16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = (f16)(float)x[j];
+  return r;
+}
+__device__ __forceinline__ float to_wfrag(float x) { return x; }
 
 // ---- accumulator -> operand (contraction index = accumulator row) --------------------
 
@@ -103,24 +130,25 @@ __device__ __forceinline__ void acc_to_frags(const f32x16& c, float (&f)[16]) {
 __device__ __forceinline__ bf16x8 load_frag_k(const bf16* row, int kc, int g) {
   return *reinterpret_cast<const bf16x8*>(row + 16 * kc + 8 * g);
 }
+__device__ __forceinline__ f16x8 load_frag_k(const f16* row, int kc, int g) {
+  return *reinterpret_cast<const f16x8*>(row + 16 * kc + 8 * g);
+}
 __device__ __forceinline__ float load_frag_k(const float* row, int kc, int g) {
   return row[2 * kc + g];
 }
 
-// W row (float32 in global memory) scaled by log2(e) and split into the MFMA parts.
-__device__ __forceinline__ void load_w_frag(const float* wrow, int kc, int g, bf16x8 (&f)[2]) {
+// W row (float32 in global memory) scaled by log2(e), as a W-contraction operand.
+__device__ __forceinline__ void load_w_frag(const float* wrow, int kc, int g, f16x8& f) {
   const f32x4 a = *reinterpret_cast<const f32x4*>(wrow + 16 * kc + 8 * g);
   const f32x4 b = *reinterpret_cast<const f32x4*>(wrow + 16 * kc + 8 * g + 4);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const float x = (j < 4 ? a[j] : b[j - 4]) * kLog2e;
-    const bf16 hi = (bf16)x;
-    f[0][j] = hi;
-    f[1][j] = (bf16)(x - (float)hi);
+  for (int j = 0; j < 4; ++j) {
+    f[j] = (f16)(a[j] * kLog2e);
+    f[j + 4] = (f16)(b[j] * kLog2e);
   }
 }
-__device__ __forceinline__ void load_w_frag(const float* wrow, int kc, int g, float (&f)[1]) {
-  f[0] = wrow[2 * kc + g] * kLog2e;
+__device__ __forceinline__ void load_w_frag(const float* wrow, int kc, int g, float& f) {
+  f = wrow[2 * kc + g] * kLog2e;
 }
 
 // ---- operands with the contraction index along LDS rows ------------------------------
@@ -148,43 +176,46 @@ __device__ __forceinline__ float lds_frag_rows(const float* X, int ld, int row0,
 
 // ---- the bias operand: adds -(r_row + c_col) to a feature exponent in the MFMA --------
 // A side (rows): per-row value r (e.g. |k|^2/2 in log2 units); B side (cols): per-column
-// stabiliser c.  bf16: r and c are each carried as three bf16 pieces (exact to 2^-24).
+// stabiliser c.  fp16: r and c are each carried as three fp16 pieces (exact to far below
+// float32 rounding for |values| < 65504).
 
 // x = f[i0] + f[i0+1] + f[i0+2] to float32 accuracy.
-__device__ __forceinline__ void split3(float x, bf16x8& f, int i0) {
-  const bf16 a = (bf16)x;
+__device__ __forceinline__ void split3(float x, f16x8& f, int i0) {
+  const f16 a = (f16)x;
   const float r1 = x - (float)a;
-  const bf16 b = (bf16)r1;
+  const f16 b = (f16)r1;
   f[i0] = a;
   f[i0 + 1] = b;
-  f[i0 + 2] = (bf16)(r1 - (float)b);
+  f[i0 + 2] = (f16)(r1 - (float)b);
 }
 
-__device__ __forceinline__ bf16x8 bias_rows(float r, int g, bf16x8) {
-  bf16x8 f = zero_frag(bf16x8{});
+__device__ __forceinline__ f16x8 bias_rows(float r, int g, f16x8) {
+  f16x8 f = zero_frag(f16x8{});
   if (g == 0) {
     split3(r, f, 0);
-    f[3] = f[4] = f[5] = (bf16)1.f;
+    f[3] = f[4] = f[5] = (f16)1.f;
   }
   return f;
 }
-__device__ __forceinline__ bf16x8 bias_cols(float c, int g, bf16x8) {
-  bf16x8 f = zero_frag(bf16x8{});
+__device__ __forceinline__ f16x8 bias_cols(float c, int g, f16x8) {
+  f16x8 f = zero_frag(f16x8{});
   if (g == 0) {
-    f[0] = f[1] = f[2] = (bf16)-1.f;
+    f[0] = f[1] = f[2] = (f16)-1.f;
     split3(-c, f, 3);
   }
   return f;
 }
 __device__ __forceinline__ float bias_rows(float r, int g, float) { return g == 0 ? r : 1.f; }
 // A-side operand that picks up only the stabiliser part of bias_cols: rows get -c_col.
-__device__ __forceinline__ bf16x8 bias_unit_rows(int g, bf16x8) {
-  bf16x8 f = zero_frag(bf16x8{});
-  if (g == 0) f[3] = f[4] = f[5] = (bf16)1.f;
+__device__ __forceinline__ f16x8 bias_unit_rows(int g, f16x8) {
+  f16x8 f = zero_frag(f16x8{});
+  if (g == 0) f[3] = f[4] = f[5] = (f16)1.f;
   return f;
 }
 __device__ __forceinline__ float bias_unit_rows(int g, float) { return g == 0 ? 0.f : 1.f; }
 __device__ __forceinline__ float bias_cols(float c, int g, float) { return g == 0 ? -1.f : -c; }
+// Row bias that removes a row from a contraction (its features become 2^-30000 = 0).
+constexpr float kMaskedRow = 30000.0f;
 
 // Sum of squares of the contraction values a lane holds in its row operands.
 template <int N>
@@ -198,6 +229,21 @@ __device__ __forceinline__ float sumsq(const bf16x8 (&f)[N]) {
       v[0] = f[i][j];
       v[1] = f[i][j + 1];
       s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+    }
+  return s;
+}
+template <int N>
+__device__ __forceinline__ float sumsq(const f16x8 (&f)[N]) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
+      typedef f16 f16x2 __attribute__((ext_vector_type(2)));
+      f16x2 v;
+      v[0] = f[i][j];
+      v[1] = f[i][j + 1];
+      s = __builtin_amdgcn_fdot2(v, v, s, false);
     }
   return s;
 }

@@ -43,7 +43,7 @@ __global__ void __launch_bounds__(64 * kFeatWaves)
     features_kernel(const T* __restrict__ X, const float* __restrict__ W, int L, int H, int G, int Hw, int m,
                     float* __restrict__ phi, float* __restrict__ c_out) {
   using P = Prec<T>;
-  using frag = typename P::frag;
+  using wfrag = typename P::wfrag;
   constexpr int NKC = D / P::KS;
   const int bh = blockIdx.y, h = bh % H;
   const int hkv = h / G;  // G = query heads per kv head (1 on the key side)
@@ -53,9 +53,10 @@ __global__ void __launch_bounds__(64 * kFeatWaves)
   const size_t grow = (size_t)bh * L + row;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
 
-  frag xf[NKC];
+  wfrag xf[NKC];
 #pragma unroll
-  for (int kc = 0; kc < NKC; ++kc) xf[kc] = valid ? load_frag_k(X + grow * D, kc, g) : zero_frag(frag{});
+  for (int kc = 0; kc < NKC; ++kc)
+    xf[kc] = valid ? to_wfrag(load_frag_k(X + grow * D, kc, g)) : zero_frag(wfrag{});
   float nrm = sumsq(xf);
   nrm += partner32(nrm);
   const float half_norm = 0.5f * kLog2e * nrm;
@@ -65,10 +66,9 @@ __global__ void __launch_bounds__(64 * kFeatWaves)
     f32x16 c = zero16();
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
-      frag wp[P::NSPLIT];
+      wfrag wp;
       load_w_frag(Wh + (size_t)(32 * ft + col) * D, kc, g, wp);
-#pragma unroll
-      for (int s = 0; s < P::NSPLIT; ++s) c = mma(wp[s], xf[kc], c);
+      c = mma(wp, xf[kc], c);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) c[r] -= half_norm;

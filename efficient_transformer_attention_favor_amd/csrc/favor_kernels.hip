@@ -94,7 +94,7 @@ __device__ __forceinline__ void stage_rows(T* dst, int ld, const T* src, int p0,
 // copy of K and V): block b runs on XCD b % 8.
 // ======================================================================================
 template <class T, int D> struct KvCfg;
-template <> struct KvCfg<bf16, 64> { static constexpr int KW = 8, NTW = 1; };   // 2 waves / SIMD
+template <> struct KvCfg<bf16, 64> { static constexpr int KW = 4, NTW = 2; };
 template <> struct KvCfg<bf16, 128> { static constexpr int KW = 4, NTW = 1; };
 template <> struct KvCfg<float, 64> { static constexpr int KW = 4, NTW = 2; };
 template <> struct KvCfg<float, 128> { static constexpr int KW = 4, NTW = 1; };
@@ -105,6 +105,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
     int R, int T_ranges, int n_units, float* __restrict__ gs, float* __restrict__ gc) {
   using P = Prec<T>;
   using frag = typename P::frag;
+  using wfrag = typename P::wfrag;
   constexpr int KW = KvCfg<T, D>::KW, NTW = KvCfg<T, D>::NTW;
   constexpr int FG = 2 / NTW;   // feature groups per workgroup (64 features)
   constexpr int PG = KW / FG;   // position groups
@@ -129,19 +130,14 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   const T* Vh = V + (size_t)bh * L * D;
   T* vl = Vl[wave];
 
-  frag wf[NTW][P::NSPLIT][NKC];
+  wfrag wf[NTW][NKC];
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      frag tmp[P::NSPLIT];
-      load_w_frag(Wh + (size_t)(f0 + 32 * nt + col) * D, kc, g, tmp);
-#pragma unroll
-      for (int s = 0; s < P::NSPLIT; ++s) wf[nt][s][kc] = tmp[s];
-    }
+    for (int kc = 0; kc < NKC; ++kc) load_w_frag(Wh + (size_t)(f0 + 32 * nt + col) * D, kc, g, wf[nt][kc]);
 
   float cst[NTW];  // stabiliser of this lane's feature (log2 units)
-  frag biasB[NTW];
+  wfrag biasB[NTW];
   f32x16 S[NTW][NDT];
   frag ones = zero_frag(frag{});
   if (col == 0) {
@@ -161,7 +157,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   constexpr int CPL = 32 * CPR / 64;    // chunks per lane per block
   // Block loads are software-pipelined: block p0 + 32 is fetched into registers while
   // block p0 is computed.  Loads are clamped into the range (rows past its end are real
-  // data whose features get a +huge row bias, i.e. phi = 0).
+  // data whose features get the kMaskedRow bias, i.e. phi = 0).
   f32x4 vn[CPL];
   frag kn[NKC];
   auto fetch = [&](int q0) {
@@ -192,23 +188,21 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
         *reinterpret_cast<f32x4*>(drow + vperm_inv(c0 & 31)) = v;
       }
     }
-    frag kf[NKC];
+    wfrag kf[NKC];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) kf[kc] = kn[kc];
+    for (int kc = 0; kc < NKC; ++kc) kf[kc] = to_wfrag(kn[kc]);
     fetch(min(p0 + 32, we - 1));
     float nrm = sumsq(kf);
     nrm += partner32(nrm);
-    const float rb = p0 + col < we ? 0.5f * kLog2e * nrm : 1e30f;
-    const frag biasA = bias_rows(rb, g, frag{});
+    const float rb = p0 + col < we ? 0.5f * kLog2e * nrm : kMaskedRow;
+    const wfrag biasA = bias_rows(rb, g, wfrag{});
 
     f32x16 c1[NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       c1[nt] = zero16();
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-        for (int s = 0; s < P::NSPLIT; ++s) c1[nt] = mma(kf[kc], wf[nt][s][kc], c1[nt]);
+      for (int kc = 0; kc < NKC; ++kc) c1[nt] = mma(kf[kc], wf[nt][kc], c1[nt]);
       c1[nt] = mma(biasA, biasB[nt], c1[nt]);
     }
 
@@ -222,7 +216,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
         cst[nt] = mx;
 #pragma unroll
         for (int r = 0; r < 16; ++r) c1[nt][r] -= mx;
-        biasB[nt] = bias_cols(mx, g, frag{});
+        biasB[nt] = bias_cols(mx, g, wfrag{});
       }
     } else if constexpr (MODE == 2) {
 #pragma unroll
@@ -239,7 +233,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
           cst[nt] = base + shift;
 #pragma unroll
           for (int r = 0; r < 16; ++r) c1[nt][r] -= shift;
-          biasB[nt] = bias_cols(cst[nt], g, frag{});
+          biasB[nt] = bias_cols(cst[nt], g, wfrag{});
           if (!first) {
             const float fct = fast_exp2(-shift);
 #pragma unroll
@@ -277,7 +271,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       cst[nt] = -INFINITY;
-      biasB[nt] = bias_cols(0.f, g, frag{});
+      biasB[nt] = bias_cols(0.f, g, wfrag{});
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) S[nt][dt] = zero16();
     }
@@ -387,12 +381,12 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
 // are re-staged per query tile.
 // ======================================================================================
 template <class T, int D> struct ReadoutCfg;
-template <int D> struct ReadoutCfg<bf16, D> {
-  static constexpr int MP = D == 64 ? 256 : 128;
+template <int D> struct ReadoutCfg<bf16, D> {  // features beyond the fast readout's LDS
+  static constexpr int MP = 128;
   static constexpr int LDW = D + 8;
   static constexpr int LDS = MP + 8;
-  static constexpr int NWAVE = D == 64 ? 8 : 4;   // D = 64: 2 waves / SIMD
-  static constexpr int QN = D == 64 ? 2 : 1;
+  static constexpr int NWAVE = 8;
+  static constexpr int QN = 1;
 };
 template <int D> struct ReadoutCfg<float, D> {
   static constexpr int MP = D == 64 ? 128 : 64;
@@ -425,6 +419,8 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
                    int T_ranges) {
   using P = Prec<T>;
   using frag = typename P::frag;
+  using wfrag = typename P::wfrag;
+  using welem = typename P::welem;
   using Cfg = ReadoutCfg<T, D>;
   constexpr int NKC = D / P::KS;
   constexpr int NDT = D / 32 + 1;
@@ -432,7 +428,7 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
   constexpr int NT = 64 * Cfg::NWAVE;
   constexpr int SROWS = D + 1;
   constexpr int TILE = Cfg::NWAVE * QN * 32;
-  __shared__ __attribute__((aligned(16))) T Wl[P::NSPLIT][MP * LDW];
+  __shared__ __attribute__((aligned(16))) welem Wl[MP * LDW];
   __shared__ __attribute__((aligned(16))) T Sl[SROWS * LDSS];
   __shared__ float red[NT];
 
@@ -475,16 +471,7 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
         if (e >= nf * (D / 4)) continue;
         const int fi = e / (D / 4), k4 = (e % (D / 4)) * 4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float xs = x[u][i] * kLog2e;
-          if constexpr (sizeof(T) == 2) {
-            const bf16 hi = (bf16)xs;
-            Wl[0][fi * LDW + k4 + i] = hi;
-            Wl[P::NSPLIT - 1][fi * LDW + k4 + i] = (bf16)(xs - (float)hi);
-          } else {
-            Wl[0][fi * LDW + k4 + i] = xs;
-          }
-        }
+        for (int i = 0; i < 4; ++i) Wl[fi * LDW + k4 + i] = (welem)(x[u][i] * kLog2e);
       }
     }
     // S rows: sum over the position ranges, rescaled to c*
@@ -527,14 +514,14 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
   for (size_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
     size_t myrow[QN];
     bool valid[QN];
-    frag qf[QN][NKC];
+    wfrag qf[QN][NKC];
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
       myrow[q] = tile * TILE + (size_t)(wave * QN + q) * 32 + col;
       valid[q] = myrow[q] < rows;
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc)
-        qf[q][kc] = valid[q] ? load_frag_k(Qb + myrow[q] * D, kc, g) : zero_frag(frag{});
+        qf[q][kc] = valid[q] ? to_wfrag(load_frag_k(Qb + myrow[q] * D, kc, g)) : zero_frag(wfrag{});
     }
     f32x16 acc[QN][NDT];
     float M[QN];
@@ -546,17 +533,15 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
 #pragma unroll
       for (int q = 0; q < QN; ++q) c1[q] = zero16();
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
+      for (int kc = 0; kc < NKC; ++kc) {
+        const wfrag a = load_frag_k(&Wl[(32 * ft + col) * LDW], kc, g);
 #pragma unroll
-        for (int s = 0; s < P::NSPLIT; ++s) {
-          const frag a = load_frag_k(&Wl[s][(32 * ft + col) * LDW], kc, g);
-#pragma unroll
-          for (int q = 0; q < QN; ++q) c1[q] = mma(a, qf[q][kc], c1[q]);
-        }
+        for (int q = 0; q < QN; ++q) c1[q] = mma(a, qf[q][kc], c1[q]);
+      }
       if constexpr (decltype(bias_tag)::value) {
-        const frag unitA = bias_unit_rows(g, frag{});
+        const wfrag unitA = bias_unit_rows(g, wfrag{});
 #pragma unroll
-        for (int q = 0; q < QN; ++q) c1[q] = mma(unitA, bias_cols(M[q], g, frag{}), c1[q]);
+        for (int q = 0; q < QN; ++q) c1[q] = mma(unitA, bias_cols(M[q], g, wfrag{}), c1[q]);
       }
     };
     // phi = 2^(c1 [- M]) and acc += S_ft^T phi.
@@ -689,6 +674,308 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
 }
 
 // ======================================================================================
+// readout for bf16 problems (bidirectional).  1-D grid: workgroup b runs on XCD b % 8 and
+// all workgroups of a kv head share one XCD (and its L2 copy of W and S).  NWAVE waves,
+// each streaming its own 32-row query chunks (the G query heads of a kv head are G*L
+// contiguous rows) with no workgroup barrier between chunks; the next chunk's Q is loaded
+// while the current one is computed.
+// LDS: W * log2e in fp16, S'^T in bf16 (rows: value columns in vperm order, the ones row,
+// then a zero row; features reordered within 32-feature tiles so one lane's 8 operand
+// values are contiguous) and per feature the bias operand carrying its key stabiliser c_f.
+// The key side leaves S_f = 2^c_f S'_f per position range; here c_f = max over ranges and
+// S'_f = sum_t 2^(c_tf - c_f) S'_tf.  Instead of rescaling S to one head-wide constant, c_f
+// goes into the query exponent: phi_q,f = 2^(w_f.q log2e + c_f - M_q), M_q the row
+// stabiliser, so the readout uses S' directly.
+// Feature tiles are software-pipelined: while the exponentials and readout products of
+// tile ft run, the W contraction of tile ft+1 is issued between them (a dependent MFMA
+// chain would otherwise leave the matrix core idle), with the instruction mix pinned by
+// scheduling groups.
+// ======================================================================================
+template <int D> struct RoBf16 {
+  static constexpr int MP = D == 64 ? 512 : 256;  // most features (m <= MP)
+  static constexpr int LDW = D + 8;   // fp16 W rows
+  static constexpr int LDSS = MP + 8; // bf16 S'^T rows
+  static constexpr int NWAVE = D == 64 ? 8 : 4;  // waves per workgroup (registers: 2 or 1 per SIMD)
+};
+
+// B operand of the query bias MFMA: picks up c_f (A slots 0-2) and adds -M (slots 3-5).
+__device__ __forceinline__ f16x8 qbias_cols(float M, int g, bool with_m) {
+  f16x8 f = zero_frag(f16x8{});
+  if (g == 0) {
+    f[0] = f[1] = f[2] = (f16)1.f;
+    if (with_m) split3(-M, f, 3);
+  }
+  return f;
+}
+
+// Scheduling-group masks (LLVM AMDGPU sched_group_barrier)
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgTrans = 0x400, kSgDsRead = 0x100;
+
+template <int D>
+__global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
+    readout_bf16_kernel(const bf16* __restrict__ Q, const float* __restrict__ W, const float* __restrict__ gs,
+                        const float* __restrict__ gc, bf16* __restrict__ out, int L, int Hq, int Hkv, int Hw, int m,
+                        int T_ranges, int BH, int per_head) {
+  using Cfg = RoBf16<D>;
+  constexpr int MP = Cfg::MP, LDW = Cfg::LDW, LDSS = Cfg::LDSS, NW = Cfg::NWAVE;
+  constexpr int NT = 64 * NW;
+  constexpr int NKC = D / 16;
+  constexpr int NDT = D / 32 + 1;
+  constexpr int SROWS = D + 1;
+  __shared__ __attribute__((aligned(16))) f16 Wl[MP * LDW];
+  __shared__ __attribute__((aligned(16))) bf16 Sl[(SROWS + 1) * LDSS];
+  __shared__ __attribute__((aligned(16))) f16x8 Cb[2 * MP];  // [feature][lane group]
+  __shared__ float Cf[MP];
+
+  const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3;
+  const int bh = (kq / per_head) * 8 + xcd, sub = kq % per_head;
+  if (bh >= BH) return;
+  const int b = bh / Hkv, hkv = bh % Hkv, G = Hq / Hkv;
+  const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
+  const int rows = G * L;
+  const bf16* Qb = Q + ((size_t)b * Hq + (size_t)hkv * G) * L * D;
+  bf16* Ob = out + ((size_t)b * Hq + (size_t)hkv * G) * L * D;
+  const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
+  const float* gsh = gs + (size_t)bh * T_ranges * (D + 1) * m;
+  const float* gch = gc + (size_t)bh * T_ranges * m;
+
+  // Stage W, S' and the bias rows of all m <= MP features (8 loads in flight per thread).
+  {
+    constexpr int U = 8;
+    const int fb = 0, nf = m;
+    for (int f = threadIdx.x; f < nf; f += NT) {
+      float c = -INFINITY;
+      for (int t = 0; t < T_ranges; ++t) c = fmaxf(c, gch[(size_t)t * m + fb + f]);
+      f16x8 cb = zero_frag(f16x8{});
+      split3(c, cb, 0);
+      cb[3] = cb[4] = cb[5] = (f16)1.f;
+      Cb[2 * f] = cb;
+      Cb[2 * f + 1] = zero_frag(f16x8{});
+      Cf[f] = c;
+    }
+    const int nw4 = nf * (D / 4);
+    for (int e0 = threadIdx.x; e0 < nw4; e0 += U * NT) {
+      f32x4 x[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = min(e0 + u * NT, nw4 - 1);
+        x[u] = *reinterpret_cast<const f32x4*>(Wh + (size_t)(fb + e / (D / 4)) * D + (e % (D / 4)) * 4);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * NT;
+        if (e >= nw4) continue;
+        const int fi = e / (D / 4), k4 = (e % (D / 4)) * 4;
+        typedef f16 f16x4 __attribute__((ext_vector_type(4)));
+        f16x4 h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = (f16)(x[u][i] * kLog2e);
+        *reinterpret_cast<f16x4*>(&Wl[fi * LDW + k4]) = h;
+      }
+    }
+    if (T_ranges > 1) __syncthreads();  // Cf
+    const int nsv = SROWS * (nf / 4);
+    for (int e0 = threadIdx.x; e0 < nsv; e0 += U * NT) {
+      f32x4 acc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int t = 0; t < T_ranges; ++t) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int e = min(e0 + u * NT, nsv - 1);
+          const int row = e / (nf / 4), fi = (e % (nf / 4)) * 4;
+          v[u] = *reinterpret_cast<const f32x4*>(gsh + ((size_t)t * (D + 1) + row) * m + fb + fi);
+        }
+        if (T_ranges == 1) {
+#pragma unroll
+          for (int u = 0; u < U; ++u) acc[u] = v[u];
+        } else {
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const int e = min(e0 + u * NT, nsv - 1);
+            const int fi = (e % (nf / 4)) * 4;
+            const f32x4 c = *reinterpret_cast<const f32x4*>(gch + (size_t)t * m + fb + fi);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[u][i] += v[u][i] * fast_exp2(c[i] - Cf[fi + i]);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * NT;
+        if (e >= nsv) continue;
+        const int row = e / (nf / 4), fi = (e % (nf / 4)) * 4;
+        bf16x4_t h;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = (bf16)acc[u][i];
+        *reinterpret_cast<bf16x4_t*>(&Sl[row * LDSS + (fi & ~31) + s_pos<bf16>(fi & 31)]) = h;
+      }
+    }
+    for (int e = threadIdx.x; e < LDSS; e += NT) Sl[SROWS * LDSS + e] = (bf16)0.f;  // zero row
+  }
+  __syncthreads();
+
+  const int nchunks = (rows + 31) / 32;
+  const int stride = per_head * NW;
+  const int ones_row = col == 0 ? D : D + 1;  // lanes other than 0 read the zero row
+  // Q of the wave's next chunk is loaded while the current one is computed (rows past
+  // the end are clamped to the last row and never stored).
+  bf16x8 qn[NKC];
+  auto fetch_q = [&](int ch) {
+    const int row = min(ch * 32 + col, rows - 1);
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) qn[kc] = load_frag_k(Qb + (size_t)row * D, kc, g);
+  };
+  fetch_q(min(sub * NW + wave, nchunks - 1));
+  for (int r0 = sub * NW; r0 < nchunks; r0 += stride) {
+    const int ch = r0 + wave;
+    if (ch >= nchunks) break;  // nothing left for this wave
+    const int myrow = ch * 32 + col;
+    const bool valid = myrow < rows;
+    f16x8 qf[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) qf[kc] = to_wfrag(qn[kc]);
+    fetch_q(min(ch + stride, nchunks - 1));
+    f32x16 acc[NDT];
+    float M;
+
+    auto w_frag = [&](int ft, int kc) { return load_frag_k(&Wl[(32 * ft + col) * LDW], kc, g); };
+    auto cb_frag = [&](int ft) { return Cb[2 * (32 * ft + col) + g]; };
+    auto s_fr = [&](int ft, int h, int dt) {
+      return s_frag(Sl, LDSS, dt < NDT - 1 ? 32 * dt + col : ones_row, ft, h, g);
+    };
+    // Feature exponents of tile ft, features x queries, lane = query: W_ft Q^T + c_f [- M].
+    auto c1_tile = [&](int ft, bool with_m) {
+      f32x16 c = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) c = mma(w_frag(ft, kc), qf[kc], c);
+      return mma(cb_frag(ft), qbias_cols(M, g, with_m), c);
+    };
+    auto exps = [&](const f32x16& c, float sub_by, bf16x8 (&pf)[2]) {
+      f32x16 e;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(c[r] - sub_by);
+      acc_to_frags(e, pf);
+    };
+    auto readout = [&](int ft, const bf16x8 (&pf)[2]) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mma(s_fr(ft, h, dt), pf[h], acc[dt]);
+    };
+    // One pipeline stage: exponentials and readout of tile ft (exponents in cur), W
+    // contraction of tile ft+1 into nxt.
+    auto pipe_stage = [&](int ft, const f32x16& cur, f32x16& nxt, float sub_by) {
+      f16x8 wa[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) wa[kc] = w_frag(ft + 1, kc);
+      const f16x8 ba = cb_frag(ft + 1);
+      bf16x8 pf[2];
+      exps(cur, sub_by, pf);
+      f32x16 c = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) c = mma(wa[kc], qf[kc], c);
+      nxt = mma(ba, qbias_cols(M, g, true), c);
+      readout(ft, pf);
+      // instruction mix: W / bias reads; four chain MFMAs each followed by four
+      // exponentials; the conversions; the S reads; the remaining MFMAs (chain and readout)
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, NKC + 1, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSgTrans, 4, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSgValu, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * NDT, 0);
+      __builtin_amdgcn_sched_group_barrier(kSgMfma, NKC + 1 - 4 + 2 * NDT, 0);
+    };
+    auto rowmax = [&](const f32x16& c) {
+      float mx = c[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, c[r]);
+      return fmaxf(mx, partner32(mx));
+    };
+    const int nft = m / 32;
+    auto run = [&](bool fast) {
+      M = -INFINITY;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) acc[dt] = zero16();
+      {
+        if (fast) {
+          // Stabiliser fixed at the first tile's row maximum, then folded into the bias.
+          f32x16 ca, cb;
+          ca = c1_tile(0, false);
+          M = rowmax(ca);
+          float sub_by = M;
+          int ft = 0;
+          for (;;) {
+            if (ft + 1 == nft) {
+              bf16x8 pf[2];
+              exps(ca, sub_by, pf);
+              readout(ft, pf);
+              break;
+            }
+            pipe_stage(ft, ca, cb, sub_by);
+            sub_by = 0.f;
+            ++ft;
+            if (ft + 1 == nft) {
+              bf16x8 pf[2];
+              exps(cb, 0.f, pf);
+              readout(ft, pf);
+              break;
+            }
+            pipe_stage(ft, cb, ca, 0.f);
+            ++ft;
+          }
+        } else {
+          for (int ft = 0; ft < nft; ++ft) {
+            const f32x16 c1 = c1_tile(ft, false);
+            const float mx = rowmax(c1);
+            if (wave_any(mx > M + kTau)) {
+              const float nm = mx > M + kTau ? mx : M;
+              const float fct = fast_exp2(M - nm);
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[dt][r] *= fct;
+              M = nm;
+            }
+            bf16x8 pf[2];
+            exps(c1, M, pf);
+            readout(ft, pf);
+          }
+        }
+      }
+    };
+    // Only an overflow (a later feature tile ~2^100 above the first) makes the fast pass
+    // non-finite; then this wave's rows are redone with the running maximum.
+    run(true);
+    const float dq = acc[NDT - 1][0];
+    const bool bad = valid && !(dq - dq == 0.f);
+    if (wave_any(bad)) run(false);
+
+    float den = acc[NDT - 1][0];
+    const float dp = partner32(den);
+    den = g ? dp : den;
+    const float inv = 1.f / den;
+    if (!valid) continue;
+    bf16* orow = Ob + (size_t)myrow * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT - 1; ++dt) {
+      bf16x8 o0, o1;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        o0[j] = (bf16)(acc[dt][j] * inv);
+        o1[j] = (bf16)(acc[dt][8 + j] * inv);
+      }
+      *reinterpret_cast<bf16x8*>(orow + 32 * dt + 16 * g) = o0;
+      *reinterpret_cast<bf16x8*>(orow + 32 * dt + 16 * g + 8) = o1;
+    }
+  }
+}
+
+// ======================================================================================
 // causal_scan: per kv head, c* = max over segments and features of the segment
 // stabilisers, and the exclusive prefix P_t = sum_{t' < t} 2^(c_t',f - c*) S_t' of the
 // segment summaries (read in kv_summary's row layout, written fragment-native for the
@@ -753,6 +1040,7 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     int Hkv, int Hw, int m, int R, int T_ranges) {
   using P = Prec<T>;
   using frag = typename P::frag;
+  using wfrag = typename P::wfrag;
   constexpr int NKC = D / P::KS;
   constexpr int NDT = D / 32 + 1;
   constexpr int LDK = Ld<T>::template K<D>;
@@ -783,18 +1071,13 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
   const T* Kh = K + (size_t)bh * L * D;
   const T* Vh = V + (size_t)bh * L * D;
 
-  frag wf[2][P::NSPLIT][NKC];
+  wfrag wf[2][NKC];
 #pragma unroll
   for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) {
-      frag tmp[P::NSPLIT];
-      load_w_frag(Wh + (size_t)(f0 + 32 * nt + col) * D, kc, g, tmp);
-#pragma unroll
-      for (int s = 0; s < P::NSPLIT; ++s) wf[nt][s][kc] = tmp[s];
-    }
+    for (int kc = 0; kc < NKC; ++kc) load_w_frag(Wh + (size_t)(f0 + 32 * nt + col) * D, kc, g, wf[nt][kc]);
   const float cstar = cstar_in[bh];
-  const frag biasB = bias_cols(cstar, g, frag{});
+  const wfrag biasB = bias_cols(cstar, g, wfrag{});
 
   // carry of this wave's features, from the exclusive prefix of the segment
   f32x16 carry[2][NDT];
@@ -832,17 +1115,15 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     __syncthreads();
 
     // phi_Q of this wave's features: C = W_w Q^T (features x queries), lane = query.
-    frag qf[NKC];
+    wfrag qf[NKC];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) qf[kc] = load_frag_k(Ql + col * LDK, kc, g);
+    for (int kc = 0; kc < NKC; ++kc) qf[kc] = to_wfrag(load_frag_k(Ql + col * LDK, kc, g));
     f32x16 cq[2];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       cq[nt] = zero16();
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-        for (int s = 0; s < P::NSPLIT; ++s) cq[nt] = mma(wf[nt][s][kc], qf[kc], cq[nt]);
+      for (int kc = 0; kc < NKC; ++kc) cq[nt] = mma(wf[nt][kc], qf[kc], cq[nt]);
     }
     float Mw = cq[0][0];
 #pragma unroll
@@ -860,20 +1141,18 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     }
 
     // phi_K of this wave's features: C = K W_w^T (keys x features), lane = feature.
-    frag kf[NKC];
+    wfrag kf[NKC];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) kf[kc] = load_frag_k(Kl + col * LDK, kc, g);
+    for (int kc = 0; kc < NKC; ++kc) kf[kc] = to_wfrag(load_frag_k(Kl + col * LDK, kc, g));
     float nrm = sumsq(kf);
     nrm += partner32(nrm);
-    const frag biasA = bias_rows(0.5f * kLog2e * nrm, g, frag{});
+    const wfrag biasA = bias_rows(0.5f * kLog2e * nrm, g, wfrag{});
     frag ka[2][P::NF32];
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt) {
       f32x16 ck = zero16();
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc)
-#pragma unroll
-        for (int s = 0; s < P::NSPLIT; ++s) ck = mma(kf[kc], wf[nt][s][kc], ck);
+      for (int kc = 0; kc < NKC; ++kc) ck = mma(kf[kc], wf[nt][kc], ck);
       ck = mma(biasA, biasB, ck);
       f32x16 e;
 #pragma unroll
@@ -1018,14 +1297,34 @@ favor_status run_bidirectional(const Plan& s, const T* Q, const T* K, const T* V
   favor_status rc = launch_kv_summary<T, D>(s, K, V, W, gs, gc, st);
   if (rc != FAVOR_OK) return rc;
   if (!mk.mark(1, st) || !mk.mark(2, st)) return FAVOR_ERR_HIP;  // no middle kernel
-  using Cfg = ReadoutCfg<T, D>;
   const long long rows = (long long)s.G * s.L;
-  const int tiles = ceil_div_i(rows, Cfg::NWAVE * Cfg::QN * 32);
-  int per_head = ceil_div_i(kReadoutTarget, s.BH);
-  if (per_head > tiles) per_head = tiles;
-  if (per_head < 1) per_head = 1;
-  hipLaunchKernelGGL((readout_kernel<T, D>), dim3(per_head, s.BH), dim3(64 * Cfg::NWAVE), 0, st, Q, W, gs, gc, out,
-                     s.L, s.Hq, s.Hkv, s.Hw, s.m, s.T);
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (s.m <= RoBf16<D>::MP) {
+    using Cfg = RoBf16<D>;
+    const int rounds = ceil_div_i(rows, Cfg::NWAVE * 32);
+    int per_head = ceil_div_i(kReadoutTarget, s.BH);
+    if (per_head > rounds) per_head = rounds;
+    if (per_head < 1) per_head = 1;
+    hipLaunchKernelGGL((readout_bf16_kernel<D>), dim3(8 * per_head * ceil_div_i(s.BH, 8)), dim3(64 * Cfg::NWAVE),
+                       0, st, Q, W, gs, gc, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.T, s.BH, per_head);
+    } else {
+      using Cfg = ReadoutCfg<T, D>;
+      const int tiles = ceil_div_i(rows, Cfg::NWAVE * Cfg::QN * 32);
+      int per_head = ceil_div_i(kReadoutTarget, s.BH);
+      if (per_head > tiles) per_head = tiles;
+      if (per_head < 1) per_head = 1;
+      hipLaunchKernelGGL((readout_kernel<T, D>), dim3(per_head, s.BH), dim3(64 * Cfg::NWAVE), 0, st, Q, W, gs, gc,
+                         out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.T);
+    }
+  } else {
+    using Cfg = ReadoutCfg<T, D>;
+    const int tiles = ceil_div_i(rows, Cfg::NWAVE * Cfg::QN * 32);
+    int per_head = ceil_div_i(kReadoutTarget, s.BH);
+    if (per_head > tiles) per_head = tiles;
+    if (per_head < 1) per_head = 1;
+    hipLaunchKernelGGL((readout_kernel<T, D>), dim3(per_head, s.BH), dim3(64 * Cfg::NWAVE), 0, st, Q, W, gs, gc,
+                       out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.T);
+  }
   if (hipGetLastError() != hipSuccess || !mk.mark(3, st)) return FAVOR_ERR_HIP;
   return FAVOR_OK;
 }
