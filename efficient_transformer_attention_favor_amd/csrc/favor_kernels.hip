@@ -99,10 +99,14 @@ template <> struct KvCfg<bf16, 128> { static constexpr int KW = 4, NTW = 1; };
 template <> struct KvCfg<float, 64> { static constexpr int KW = 4, NTW = 2; };
 template <> struct KvCfg<float, 128> { static constexpr int KW = 4, NTW = 1; };
 
+// With one range per kv head and bf16 data (img_s != nullptr) the workgroup writes, instead
+// of gs / gc, the readout's LDS images of its 64 features: S'^T rows in readout order, the
+// bias operands of c_f, and (one head of each W) the fp16 W rows.
 template <class T, int D>
 __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
     const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ W, int L, int Hkv, int Hw, int m,
-    int R, int T_ranges, int n_units, float* __restrict__ gs, float* __restrict__ gc) {
+    int R, int T_ranges, int n_units, float* __restrict__ gs, float* __restrict__ gc, char* __restrict__ img_w,
+    char* __restrict__ img_s, char* __restrict__ img_cb) {
   using P = Prec<T>;
   using frag = typename P::frag;
   using wfrag = typename P::wfrag;
@@ -350,6 +354,46 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   if (pgi != 0) return;
 
   const size_t unit_off = (size_t)bh * T_ranges + t;
+  if constexpr (sizeof(T) == 2) {
+    if (img_s != nullptr) {
+      // S rows are already in vperm order (V was staged permuted): lane col is row 32 dt + col
+      constexpr int LDSS = kImgMP + 8, LDW = D + 8;
+      bf16* is = reinterpret_cast<bf16*>(img_s + (size_t)bh * img_s_bytes(D));
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int ftile = (f0 + 32 * nt) >> 5;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+          if (dt == NDT - 1 && col != 0) continue;
+          const int row = dt < NDT - 1 ? 32 * dt + col : D;
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            bf16x4_t v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = (bf16)S[nt][dt][4 * a + j];
+            *reinterpret_cast<bf16x4_t*>(is + (size_t)row * LDSS + 32 * ftile + 16 * (a >> 1) + 8 * g + 4 * (a & 1)) =
+                v;
+          }
+        }
+        const int f = f0 + 32 * nt + col;
+        f16x8* icb = reinterpret_cast<f16x8*>(img_cb + (size_t)bh * img_cb_bytes(m));
+        if (g == 0) {
+          f16x8 cb = zero_frag(f16x8{});
+          split3(cmax[nt], cb, 0);
+          cb[3] = cb[4] = cb[5] = (f16)1.f;
+          icb[2 * f] = cb;
+          icb[2 * f + 1] = zero_frag(f16x8{});
+        }
+        // one writer per W head: batch 0 (kv head 0 when W is shared)
+        if (bh < Hkv && (Hw != 1 || bh == 0)) {
+          f16* iw = reinterpret_cast<f16*>(img_w + (size_t)(Hw == 1 ? 0 : hkv) * img_w_bytes(D, m));
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) *reinterpret_cast<f16x8*>(iw + (size_t)f * LDW + 16 * kc + 8 * g) = wf[nt][kc];
+        }
+      }
+      return;
+    }
+  }
   float* out_s = gs + unit_off * (size_t)(D + 1) * m;
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt) {
@@ -370,6 +414,11 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
     if (g == 0) gc[unit_off * m + f0 + 32 * nt + col] = cmax[nt];
   }
 }
+
+// s_waitcnt immediate (gfx9 encoding) that waits for vector memory only: vmcnt <= n.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // ======================================================================================
 // readout (bidirectional).  Grid (workgroups per kv head, B*Hkv), NWAVE waves; each wave
@@ -676,7 +725,7 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
 // ======================================================================================
 // readout for bf16 problems (bidirectional).  1-D grid: workgroup b runs on XCD b % 8 and
 // all workgroups of a kv head share one XCD (and its L2 copy of W and S).  NWAVE waves,
-// each streaming its own 32-row query chunks (the G query heads of a kv head are G*L
+// each streaming its own chunks of 32 QN query rows (the G query heads of a kv head are G*L
 // contiguous rows) with no workgroup barrier between chunks; the next chunk's Q is loaded
 // while the current one is computed.
 // LDS: W * log2e in fp16, S'^T in bf16 (rows: value columns in vperm order, the ones row,
@@ -686,16 +735,15 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
 // S'_f = sum_t 2^(c_tf - c_f) S'_tf.  Instead of rescaling S to one head-wide constant, c_f
 // goes into the query exponent: phi_q,f = 2^(w_f.q log2e + c_f - M_q), M_q the row
 // stabiliser, so the readout uses S' directly.
-// Feature tiles are software-pipelined: while the exponentials and readout products of
-// tile ft run, the W contraction of tile ft+1 is issued between them (a dependent MFMA
-// chain would otherwise leave the matrix core idle), with the instruction mix pinned by
-// scheduling groups.
+// Each wave handles QN 32-row query tiles per chunk, so every W and S' fragment read
+// from LDS feeds QN MFMAs and the W contractions of the tiles form independent chains.
 // ======================================================================================
 template <int D> struct RoBf16 {
-  static constexpr int MP = D == 64 ? 512 : 256;  // most features (m <= MP)
-  static constexpr int LDW = D + 8;   // fp16 W rows
-  static constexpr int LDSS = MP + 8; // bf16 S'^T rows
-  static constexpr int NWAVE = D == 64 ? 8 : 4;  // waves per workgroup (registers: 2 or 1 per SIMD)
+  static constexpr int MP = kImgMP;               // most features (m <= MP)
+  static constexpr int LDW = D + 8;               // fp16 W rows
+  static constexpr int LDSS = MP + 8;             // bf16 S'^T rows
+  static constexpr int NWAVE = 8;                 // waves per workgroup
+  static constexpr int QN = D == 64 ? 2 : 1;      // 32-row query tiles per wave and chunk
 };
 
 // B operand of the query bias MFMA: picks up c_f (A slots 0-2) and adds -M (slots 3-5).
@@ -708,22 +756,22 @@ __device__ __forceinline__ f16x8 qbias_cols(float M, int g, bool with_m) {
   return f;
 }
 
-// Scheduling-group masks (LLVM AMDGPU sched_group_barrier)
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgTrans = 0x400, kSgDsRead = 0x100;
 
 template <int D>
 __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
     readout_bf16_kernel(const bf16* __restrict__ Q, const float* __restrict__ W, const float* __restrict__ gs,
-                        const float* __restrict__ gc, bf16* __restrict__ out, int L, int Hq, int Hkv, int Hw, int m,
-                        int T_ranges, int BH, int per_head) {
+                        const float* __restrict__ gc, const char* __restrict__ img_w,
+                        const char* __restrict__ img_s, const char* __restrict__ img_cb, bf16* __restrict__ out, int L,
+                        int Hq, int Hkv, int Hw, int m, int T_ranges, int BH, int per_head) {
   using Cfg = RoBf16<D>;
-  constexpr int MP = Cfg::MP, LDW = Cfg::LDW, LDSS = Cfg::LDSS, NW = Cfg::NWAVE;
+  constexpr int MP = Cfg::MP, LDW = Cfg::LDW, LDSS = Cfg::LDSS, NW = Cfg::NWAVE, QN = Cfg::QN;
   constexpr int NT = 64 * NW;
   constexpr int NKC = D / 16;
   constexpr int NDT = D / 32 + 1;
   constexpr int SROWS = D + 1;
+  static_assert(LDSS == kImgMP + 8 && MP == kImgMP, "image layout");
   __shared__ __attribute__((aligned(16))) f16 Wl[MP * LDW];
-  __shared__ __attribute__((aligned(16))) bf16 Sl[(SROWS + 1) * LDSS];
+  __shared__ __attribute__((aligned(16))) bf16 Sl[img_s_bytes(D) / 2];  // (D+2) rows of LDSS
   __shared__ __attribute__((aligned(16))) f16x8 Cb[2 * MP];  // [feature][lane group]
   __shared__ float Cf[MP];
 
@@ -739,8 +787,39 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
   const float* gsh = gs + (size_t)bh * T_ranges * (D + 1) * m;
   const float* gch = gc + (size_t)bh * T_ranges * m;
 
-  // Stage W, S' and the bias rows of all m <= MP features (8 loads in flight per thread).
-  {
+  const int nchunks = (rows + 32 * QN - 1) / (32 * QN);
+  const int stride = per_head * NW;
+  const int ones_row = col == 0 ? D : D + 1;  // lanes other than 0 read the zero row
+  // Q of the wave's next chunk is loaded while the current one is computed (rows past
+  // the end are clamped to the last row and never stored).
+  bf16x8 qn[QN][NKC];
+  auto fetch_q = [&](int ch) {
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      const int row = min((ch * QN + q) * 32 + col, rows - 1);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) qn[q][kc] = load_frag_k(Qb + (size_t)row * D, kc, g);
+    }
+  };
+
+  if (img_s != nullptr) {
+    // One position range per head: W, S' and bias rows arrive as ready LDS images, copied
+    // by LDS DMA in 1 KB blocks spread over the waves.
+    auto copy = [&](void* dst, const char* src, int nbytes) {
+      for (int k = wave; k < nbytes / 1024; k += NW)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 1024 * k + 16 * l),
+                                         (lds_void_t*)((char*)dst + 1024 * k), 16, 0, 0);
+    };
+    copy(Wl, img_w + (size_t)(Hw == 1 ? 0 : hkv) * img_w_bytes(D, m), (int)img_w_bytes(D, m));
+    copy(Sl, img_s + (size_t)bh * img_s_bytes(D), (int)img_s_bytes(D));
+    copy(Cb, img_cb + (size_t)bh * img_cb_bytes(m), (int)img_cb_bytes(m));
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    fetch_q(min(sub * NW + wave, nchunks - 1));
+    for (int e = threadIdx.x; e < LDSS; e += NT) Sl[SROWS * LDSS + e] = (bf16)0.f;  // zero row
+  } else {
+    fetch_q(min(sub * NW + wave, nchunks - 1));
+    // Stage W, S' and the bias rows of all m <= MP features (8 loads in flight per thread).
+
     constexpr int U = 8;
     const int fb = 0, nf = m;
     for (int f = threadIdx.x; f < nf; f += NT) {
@@ -816,79 +895,64 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
   }
   __syncthreads();
 
-  const int nchunks = (rows + 31) / 32;
-  const int stride = per_head * NW;
-  const int ones_row = col == 0 ? D : D + 1;  // lanes other than 0 read the zero row
-  // Q of the wave's next chunk is loaded while the current one is computed (rows past
-  // the end are clamped to the last row and never stored).
-  bf16x8 qn[NKC];
-  auto fetch_q = [&](int ch) {
-    const int row = min(ch * 32 + col, rows - 1);
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) qn[kc] = load_frag_k(Qb + (size_t)row * D, kc, g);
-  };
-  fetch_q(min(sub * NW + wave, nchunks - 1));
   for (int r0 = sub * NW; r0 < nchunks; r0 += stride) {
     const int ch = r0 + wave;
     if (ch >= nchunks) break;  // nothing left for this wave
-    const int myrow = ch * 32 + col;
-    const bool valid = myrow < rows;
-    f16x8 qf[NKC];
+    int myrow[QN];
+    bool valid[QN];
+    f16x8 qf[QN][NKC];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) qf[kc] = to_wfrag(qn[kc]);
+    for (int q = 0; q < QN; ++q) {
+      myrow[q] = (ch * QN + q) * 32 + col;
+      valid[q] = myrow[q] < rows;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) qf[q][kc] = to_wfrag(qn[q][kc]);
+    }
     fetch_q(min(ch + stride, nchunks - 1));
-    f32x16 acc[NDT];
-    float M;
+    f32x16 acc[QN][NDT];
+    float M[QN];
 
-    auto w_frag = [&](int ft, int kc) { return load_frag_k(&Wl[(32 * ft + col) * LDW], kc, g); };
-    auto cb_frag = [&](int ft) { return Cb[2 * (32 * ft + col) + g]; };
-    auto s_fr = [&](int ft, int h, int dt) {
-      return s_frag(Sl, LDSS, dt < NDT - 1 ? 32 * dt + col : ones_row, ft, h, g);
-    };
     // Feature exponents of tile ft, features x queries, lane = query: W_ft Q^T + c_f [- M].
-    auto c1_tile = [&](int ft, bool with_m) {
-      f32x16 c = zero16();
+    // Two accumulators per query tile (even and odd contraction chunks) halve the
+    // dependent MFMA chain.
+    auto c1_tile = [&](int ft, f32x16 (&c1)[QN], bool with_m) {
+      f32x16 c2[QN];
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) c = mma(w_frag(ft, kc), qf[kc], c);
-      return mma(cb_frag(ft), qbias_cols(M, g, with_m), c);
-    };
-    auto exps = [&](const f32x16& c, float sub_by, bf16x8 (&pf)[2]) {
-      f32x16 e;
+      for (int q = 0; q < QN; ++q) c1[q] = c2[q] = zero16();
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(c[r] - sub_by);
-      acc_to_frags(e, pf);
+      for (int kc = 0; kc < NKC; ++kc) {
+        const f16x8 a = load_frag_k(&Wl[(32 * ft + col) * LDW], kc, g);
+#pragma unroll
+        for (int q = 0; q < QN; ++q) {
+          if (kc & 1) c2[q] = mma(a, qf[q][kc], c2[q]);
+          else c1[q] = mma(a, qf[q][kc], c1[q]);
+        }
+      }
+      const f16x8 ba = Cb[2 * (32 * ft + col) + g];
+#pragma unroll
+      for (int q = 0; q < QN; ++q) {
+        c2[q] = mma(ba, qbias_cols(M[q], g, with_m), c2[q]);
+        c1[q] += c2[q];
+      }
     };
-    auto readout = [&](int ft, const bf16x8 (&pf)[2]) {
+    // phi = 2^(c1 - sub) and acc += S'_ft^T phi.
+    auto readout_tile = [&](int ft, const f32x16 (&c1)[QN], bool sub_m) {
+      bf16x8 pf[QN][2];
+#pragma unroll
+      for (int q = 0; q < QN; ++q) {
+        f32x16 e;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(sub_m ? c1[q][r] - M[q] : c1[q][r]);
+        acc_to_frags(e, pf[q]);
+      }
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[dt] = mma(s_fr(ft, h, dt), pf[h], acc[dt]);
-    };
-    // One pipeline stage: exponentials and readout of tile ft (exponents in cur), W
-    // contraction of tile ft+1 into nxt.
-    auto pipe_stage = [&](int ft, const f32x16& cur, f32x16& nxt, float sub_by) {
-      f16x8 wa[NKC];
+        for (int dt = 0; dt < NDT; ++dt) {
+          const bf16x8 a = s_frag(Sl, LDSS, dt < NDT - 1 ? 32 * dt + col : ones_row, ft, h, g);
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) wa[kc] = w_frag(ft + 1, kc);
-      const f16x8 ba = cb_frag(ft + 1);
-      bf16x8 pf[2];
-      exps(cur, sub_by, pf);
-      f32x16 c = zero16();
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) c = mma(wa[kc], qf[kc], c);
-      nxt = mma(ba, qbias_cols(M, g, true), c);
-      readout(ft, pf);
-      // instruction mix: W / bias reads; four chain MFMAs each followed by four
-      // exponentials; the conversions; the S reads; the remaining MFMAs (chain and readout)
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, NKC + 1, 0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSgTrans, 4, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(kSgValu, 8, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2 * NDT, 0);
-      __builtin_amdgcn_sched_group_barrier(kSgMfma, NKC + 1 - 4 + 2 * NDT, 0);
+          for (int q = 0; q < QN; ++q) acc[q][dt] = mma(a, pf[q][h], acc[q][dt]);
+        }
     };
     auto rowmax = [&](const f32x16& c) {
       float mx = c[0];
@@ -898,79 +962,77 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
     };
     const int nft = m / 32;
     auto run = [&](bool fast) {
-      M = -INFINITY;
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) acc[dt] = zero16();
-      {
-        if (fast) {
-          // Stabiliser fixed at the first tile's row maximum, then folded into the bias.
-          f32x16 ca, cb;
-          ca = c1_tile(0, false);
-          M = rowmax(ca);
-          float sub_by = M;
-          int ft = 0;
-          for (;;) {
-            if (ft + 1 == nft) {
-              bf16x8 pf[2];
-              exps(ca, sub_by, pf);
-              readout(ft, pf);
-              break;
-            }
-            pipe_stage(ft, ca, cb, sub_by);
-            sub_by = 0.f;
-            ++ft;
-            if (ft + 1 == nft) {
-              bf16x8 pf[2];
-              exps(cb, 0.f, pf);
-              readout(ft, pf);
-              break;
-            }
-            pipe_stage(ft, cb, ca, 0.f);
-            ++ft;
-          }
-        } else {
-          for (int ft = 0; ft < nft; ++ft) {
-            const f32x16 c1 = c1_tile(ft, false);
-            const float mx = rowmax(c1);
-            if (wave_any(mx > M + kTau)) {
-              const float nm = mx > M + kTau ? mx : M;
-              const float fct = fast_exp2(M - nm);
+      for (int q = 0; q < QN; ++q) {
+        M[q] = -INFINITY;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) acc[q][dt] = zero16();
+      }
+      if (fast) {
+        // Stabiliser fixed at the first tile's row maximum, then folded into the bias.
+        {
+          f32x16 c1[QN];
+          c1_tile(0, c1, false);
+#pragma unroll
+          for (int q = 0; q < QN; ++q) M[q] = rowmax(c1[q]);
+          readout_tile(0, c1, true);
+        }
+        for (int ft = 1; ft < nft; ++ft) {
+          f32x16 c1[QN];
+          c1_tile(ft, c1, true);
+          readout_tile(ft, c1, false);
+        }
+      } else {
+        for (int ft = 0; ft < nft; ++ft) {
+          f32x16 c1[QN];
+          c1_tile(ft, c1, false);
+#pragma unroll
+          for (int q = 0; q < QN; ++q) {
+            const float mx = rowmax(c1[q]);
+            if (wave_any(mx > M[q] + kTau)) {
+              const float nm = mx > M[q] + kTau ? mx : M[q];
+              const float fct = fast_exp2(M[q] - nm);
 #pragma unroll
               for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) acc[dt][r] *= fct;
-              M = nm;
+                for (int r = 0; r < 16; ++r) acc[q][dt][r] *= fct;
+              M[q] = nm;
             }
-            bf16x8 pf[2];
-            exps(c1, M, pf);
-            readout(ft, pf);
           }
+          readout_tile(ft, c1, true);
         }
       }
     };
     // Only an overflow (a later feature tile ~2^100 above the first) makes the fast pass
     // non-finite; then this wave's rows are redone with the running maximum.
     run(true);
-    const float dq = acc[NDT - 1][0];
-    const bool bad = valid && !(dq - dq == 0.f);
+    bool bad = false;
+#pragma unroll
+    for (int q = 0; q < QN; ++q) {
+      const float dq = acc[q][NDT - 1][0];
+      bad |= valid[q] && !(dq - dq == 0.f);
+    }
     if (wave_any(bad)) run(false);
 
-    float den = acc[NDT - 1][0];
-    const float dp = partner32(den);
-    den = g ? dp : den;
-    const float inv = 1.f / den;
-    if (!valid) continue;
-    bf16* orow = Ob + (size_t)myrow * D;
 #pragma unroll
-    for (int dt = 0; dt < NDT - 1; ++dt) {
-      bf16x8 o0, o1;
+    for (int q = 0; q < QN; ++q) {
+      float den = acc[q][NDT - 1][0];
+      const float dp = partner32(den);
+      den = g ? dp : den;
+      const float inv = 1.f / den;
+      if (!valid[q]) continue;
+      bf16* orow = Ob + (size_t)myrow[q] * D;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        o0[j] = (bf16)(acc[dt][j] * inv);
-        o1[j] = (bf16)(acc[dt][8 + j] * inv);
+      for (int dt = 0; dt < NDT - 1; ++dt) {
+        bf16x8 o0, o1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          o0[j] = (bf16)(acc[q][dt][j] * inv);
+          o1[j] = (bf16)(acc[q][dt][8 + j] * inv);
+        }
+        *reinterpret_cast<bf16x8*>(orow + 32 * dt + 16 * g) = o0;
+        *reinterpret_cast<bf16x8*>(orow + 32 * dt + 16 * g + 8) = o1;
       }
-      *reinterpret_cast<bf16x8*>(orow + 32 * dt + 16 * g) = o0;
-      *reinterpret_cast<bf16x8*>(orow + 32 * dt + 16 * g + 8) = o1;
     }
   }
 }
@@ -978,23 +1040,27 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
 // ======================================================================================
 // causal_scan: per kv head, c* = max over segments and features of the segment
 // stabilisers, and the exclusive prefix P_t = sum_{t' < t} 2^(c_t',f - c*) S_t' of the
-// segment summaries (read in kv_summary's row layout, written fragment-native for the
-// chunk kernel's carry registers: tile (ft, ct) of 32 features x 32 value columns as
-// [16 registers][64 lanes], register r / lane l = feature 32 ft + 8(r/4) + 4(l/32) + r%4,
-// value column 32 ct + vperm(l%32); ct = d/32 is the ones column at lane%32 == 0).
-// Grid (m/32 * (d/32+1) tiles, B*Hkv); fixed order t = 0, 1, ...
+// segment summaries, in the summaries' own layout [d+1][m] (rows in vperm order, row d the
+// ones column).  Grid (element groups, B*Hkv); each thread owns 4 consecutive features of
+// one row and walks the segments in order, TB segments' loads in flight at a time.
 // ======================================================================================
 __global__ void __launch_bounds__(256) causal_scan_kernel(const float* __restrict__ gs,
                                                           const float* __restrict__ gc, int T_ranges, int m,
                                                           int D, float* __restrict__ prefix,
                                                           float* __restrict__ cstar_out) {
   __shared__ float red[256];
-  const int NDT = D / 32 + 1;
-  const int tile = blockIdx.x, bh = blockIdx.y;
-  const size_t tile_elems = (size_t)m * NDT * 32;
+  const int bh = blockIdx.y;
   const float* pc = gc + (size_t)bh * T_ranges * m;
+  // c*: 8 float4 loads in flight per thread
   float cm = -INFINITY;
-  for (int i = threadIdx.x; i < T_ranges * m; i += blockDim.x) cm = fmaxf(cm, pc[i]);
+  const int n4 = T_ranges * m / 4;
+  for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * 256) {
+    f32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = reinterpret_cast<const f32x4*>(pc)[min(i0 + 256 * u, n4 - 1)];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) cm = fmaxf(cm, fmaxf(fmaxf(v[u][0], v[u][1]), fmaxf(v[u][2], v[u][3])));
+  }
   red[threadIdx.x] = cm;
   __syncthreads();
   for (int s = 128; s > 0; s >>= 1) {
@@ -1002,19 +1068,30 @@ __global__ void __launch_bounds__(256) causal_scan_kernel(const float* __restric
     __syncthreads();
   }
   const float cstar = red[0];
-  if (tile == 0 && threadIdx.x == 0) cstar_out[bh] = cstar;
-  const int ft = tile / NDT, dt = tile % NDT;
-  for (int e = threadIdx.x; e < 1024; e += blockDim.x) {
-    const int r = e >> 6, l = e & 63, rho = l & 31;
-    const int f = 32 * ft + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
-    const int row = dt < NDT - 1 ? 32 * dt + rho : (rho == 0 ? D : -1);
-    float* dst = prefix + (size_t)bh * T_ranges * tile_elems + (size_t)tile * 1024 + e;
-    float acc = 0.f;
-    for (int t = 0; t < T_ranges; ++t) {
-      dst[(size_t)t * tile_elems] = acc;
-      if (row >= 0)
-        acc += fast_exp2(pc[(size_t)t * m + f] - cstar) *
-               gs[(((size_t)bh * T_ranges + t) * (D + 1) + row) * m + f];
+  if (blockIdx.x == 0 && threadIdx.x == 0) cstar_out[bh] = cstar;
+  const int e4 = blockIdx.x * 256 + threadIdx.x;  // float4 index within the [d+1][m] plane
+  if (e4 >= (D + 1) * m / 4) return;
+  const int f = (e4 * 4) % m;
+  const size_t plane = (size_t)(D + 1) * m;
+  const f32x4* src = reinterpret_cast<const f32x4*>(gs + (size_t)bh * T_ranges * plane) + e4;
+  f32x4* dst = reinterpret_cast<f32x4*>(prefix + (size_t)bh * T_ranges * plane) + e4;
+  constexpr int TB = 8;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int t0 = 0; t0 < T_ranges; t0 += TB) {
+    f32x4 sv[TB], cv[TB];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int t = min(t0 + u, T_ranges - 1);
+      sv[u] = src[(size_t)t * (plane / 4)];
+      cv[u] = *reinterpret_cast<const f32x4*>(pc + (size_t)t * m + f);
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int t = t0 + u;
+      if (t >= T_ranges) break;
+      dst[(size_t)t * (plane / 4)] = acc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] += fast_exp2(cv[u][i] - cstar) * sv[u][i];
     }
   }
 }
@@ -1079,18 +1156,24 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
   const float cstar = cstar_in[bh];
   const wfrag biasB = bias_cols(cstar, g, wfrag{});
 
-  // carry of this wave's features, from the exclusive prefix of the segment
+  // carry of this wave's features, from the exclusive prefix of the segment ([d+1][m]:
+  // lane col takes row 32 dt + col, register r feature 8(r/4) + 4g + r%4 of the tile)
   f32x16 carry[2][NDT];
   {
-    const size_t tile_elems = (size_t)m * NDT * 32;
-    const float* pf = prefix + ((size_t)bh * T_ranges + seg) * tile_elems;
+    const float* pf = prefix + ((size_t)bh * T_ranges + seg) * (size_t)(D + 1) * m;
 #pragma unroll
     for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        const float* src = pf + (size_t)((f0 / 32 + nt) * NDT + dt) * 1024;
+        const int row = dt < NDT - 1 ? 32 * dt + col : D;
+        const bool live = dt < NDT - 1 || col == 0;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) carry[nt][dt][r] = src[r * 64 + l];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 v = {0.f, 0.f, 0.f, 0.f};
+          if (live) v = *reinterpret_cast<const f32x4*>(pf + (size_t)row * m + f0 + 32 * nt + 8 * r4 + 4 * g);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) carry[nt][dt][4 * r4 + i] = v[i];
+        }
       }
   }
   frag ones = zero_frag(frag{});
@@ -1279,12 +1362,12 @@ struct Marks {
 
 template <class T, int D>
 favor_status launch_kv_summary(const Plan& s, const T* K, const T* V, const float* W, float* gs, float* gc,
-                               hipStream_t st) {
+                               char* ws, hipStream_t st) {
   const int units = s.BH * s.T;
   const int nfs = s.m / kFeatPerWave;
   hipLaunchKernelGGL((kv_summary_kernel<T, D>), dim3(8 * ceil_div_i(units, 8) * nfs), dim3(64 * KvCfg<T, D>::KW), 0,
-                     st, K, V, W,
-                     s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc);
+                     st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc, s.img ? ws + s.off_img_w : nullptr,
+                     s.img ? ws + s.off_img_s : nullptr, s.img ? ws + s.off_img_cb : nullptr);
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
@@ -1294,19 +1377,20 @@ favor_status run_bidirectional(const Plan& s, const T* Q, const T* K, const T* V
   float* gs = reinterpret_cast<float*>(ws + s.off_gs);
   float* gc = reinterpret_cast<float*>(ws + s.off_gc);
   if (!mk.mark(0, st)) return FAVOR_ERR_HIP;
-  favor_status rc = launch_kv_summary<T, D>(s, K, V, W, gs, gc, st);
+  favor_status rc = launch_kv_summary<T, D>(s, K, V, W, gs, gc, ws, st);
   if (rc != FAVOR_OK) return rc;
   if (!mk.mark(1, st) || !mk.mark(2, st)) return FAVOR_ERR_HIP;  // no middle kernel
   const long long rows = (long long)s.G * s.L;
   if constexpr (std::is_same<T, bf16>::value) {
     if (s.m <= RoBf16<D>::MP) {
     using Cfg = RoBf16<D>;
-    const int rounds = ceil_div_i(rows, Cfg::NWAVE * 32);
+    const int rounds = ceil_div_i(rows, Cfg::NWAVE * Cfg::QN * 32);
     int per_head = ceil_div_i(kReadoutTarget, s.BH);
     if (per_head > rounds) per_head = rounds;
     if (per_head < 1) per_head = 1;
     hipLaunchKernelGGL((readout_bf16_kernel<D>), dim3(8 * per_head * ceil_div_i(s.BH, 8)), dim3(64 * Cfg::NWAVE),
-                       0, st, Q, W, gs, gc, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.T, s.BH, per_head);
+                       0, st, Q, W, gs, gc, s.img ? ws + s.off_img_w : nullptr, s.img ? ws + s.off_img_s : nullptr,
+                       s.img ? ws + s.off_img_cb : nullptr, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.T, s.BH, per_head);
     } else {
       using Cfg = ReadoutCfg<T, D>;
       const int tiles = ceil_div_i(rows, Cfg::NWAVE * Cfg::QN * 32);
@@ -1338,10 +1422,10 @@ favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const
   float* cstar = reinterpret_cast<float*>(ws + s.off_cstar);
   const int nw = s.m / kFeatPerWave;
   if (!mk.mark(0, st)) return FAVOR_ERR_HIP;
-  favor_status rc = launch_kv_summary<T, D>(s, K, V, W, gs, gc, st);
+  favor_status rc = launch_kv_summary<T, D>(s, K, V, W, gs, gc, ws, st);
   if (rc != FAVOR_OK || !mk.mark(1, st)) return rc != FAVOR_OK ? rc : FAVOR_ERR_HIP;
-  hipLaunchKernelGGL(causal_scan_kernel, dim3(s.NFT * s.NDT, s.BH), dim3(256), 0, st, gs, gc, s.T, s.m, s.d,
-                     prefix, cstar);
+  hipLaunchKernelGGL(causal_scan_kernel, dim3(ceil_div_i((long long)(s.d + 1) * s.m / 4, 256), s.BH), dim3(256), 0,
+                     st, gs, gc, s.T, s.m, s.d, prefix, cstar);
   if (hipGetLastError() != hipSuccess || !mk.mark(2, st)) return FAVOR_ERR_HIP;
   if (nw <= 4)
     hipLaunchKernelGGL((causal_chunk_kernel<T, D, 4>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,

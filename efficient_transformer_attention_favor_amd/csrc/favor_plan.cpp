@@ -67,16 +67,24 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
   q.R = ceil_div(ceil_div(q.L, T), unit) * unit;
   q.T = ceil_div(q.L, q.R);
 
-  q.tile_elems = (size_t)q.m * (size_t)(q.d + kTile);
   size_t off = 0;
   q.off_gs = off;
   off = align256(off + sizeof(float) * (size_t)(q.d + 1) * q.m * q.BH * q.T);
   q.off_gc = off;
   off = align256(off + sizeof(float) * (size_t)q.m * q.BH * q.T);
   q.off_p = off;
-  if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * q.tile_elems * q.BH * q.T);
+  if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * (size_t)(q.d + 1) * q.m * q.BH * q.T);
   q.off_cstar = off;
   if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * q.BH);
+  q.img = q.mode == FAVOR_BIDIRECTIONAL && q.dtype == FAVOR_BF16 && q.T == 1 && q.m <= kImgMP;
+  q.off_img_w = q.off_img_s = q.off_img_cb = off;
+  if (q.img) {
+    off = align256(off + img_w_bytes(q.d, q.m) * q.Hw);
+    q.off_img_s = off;
+    off = align256(off + img_s_bytes(q.d) * q.BH);
+    q.off_img_cb = off;
+    off = align256(off + img_cb_bytes(q.m) * q.BH);
+  }
   q.bytes = off;
   return FAVOR_OK;
 }

@@ -14,6 +14,18 @@ constexpr int kFeatPerWave = 64;   // features owned by one wave in the key-side
 constexpr int kKeyTarget = 256;     // key-side workgroups (4 waves each) a pass aims for
 constexpr int kSegmentTarget = 512; // causal chunk-kernel workgroups a pass aims for
 constexpr int kReadoutTarget = 256; // readout workgroups a pass aims for
+// Ready-to-copy LDS images for the bf16 bidirectional readout (one position range per kv
+// head): fp16 W rows of d+8, bf16 S'^T rows of kImgMP+8 (d+2 rows: values, ones, zeros),
+// and two 16-byte bias operands per feature.  Sizes are whole 1 KB blocks (LDS DMA unit).
+constexpr int kImgMP = 256;
+#if defined(__HIP__)
+#define FAVOR_HD __host__ __device__
+#else
+#define FAVOR_HD
+#endif
+FAVOR_HD constexpr size_t img_w_bytes(int d, int m) { return (size_t)m * (d + 8) * 2; }
+FAVOR_HD constexpr size_t img_s_bytes(int d) { return (((size_t)(d + 2) * (kImgMP + 8) * 2) + 1023) & ~size_t(1023); }
+FAVOR_HD constexpr size_t img_cb_bytes(int m) { return (size_t)m * 32; }
 
 struct Plan {
   int B, Hq, Hkv, Hw, L, d, m, dtype, mode, chunk;
@@ -23,11 +35,14 @@ struct Plan {
   int R;    // positions per range / segment (multiple of the chunk)
   int NFT;  // feature tiles: m / 32
   int NDT;  // value-column tiles incl. the ones column: d / 32 + 1
-  size_t tile_elems;   // m * (d + 32): floats of one fragment-native summary
   size_t off_gs;       // [BH][T][d+1][m] range / segment summaries (float)
   size_t off_gc;       // [BH][T][m] their per-feature stabilisers (log2 units)
-  size_t off_p;        // [BH][T] exclusive prefixes, fragment-native (causal)
+  size_t off_p;        // [BH][T][d+1][m] exclusive prefixes of the segment summaries (causal)
   size_t off_cstar;    // [BH] global stabiliser per kv head (causal)
+  bool img;            // bf16 bidirectional, one range per head, m <= kImgMP: LDS images
+  size_t off_img_w;    // [Hw] fp16 W images
+  size_t off_img_s;    // [BH] bf16 S'^T images
+  size_t off_img_cb;   // [BH] bias-operand images
   size_t bytes;        // total workspace bytes
 };
 
