@@ -356,21 +356,33 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   const size_t unit_off = (size_t)bh * T_ranges + t;
   if constexpr (sizeof(T) == 2) {
     if (img_s != nullptr) {
-      // S rows are already in vperm order (V was staged permuted): lane col is row 32 dt + col
+      // The image holds S_v / S_1 per feature (rows already in vperm order: V was staged
+      // permuted, lane col is row 32 dt + col) and c'_f = c_f + log2 S_1,f, so the readout's
+      // denominator is the plain sum of its features.  S_1 (ones column, lane col 0) is
+      // spread to the other lanes by shuffles.
       constexpr int LDSS = kImgMP + 8, LDW = D + 8;
       bf16* is = reinterpret_cast<bf16*>(img_s + (size_t)bh * img_s_bytes(D));
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         const int ftile = (f0 + 32 * nt) >> 5;
+        // S_1 of this lane's register features (held by lane 32 g) and of feature col of the
+        // tile (held by lane 32 ((col >> 2) & 1), register 4 (col >> 3) + col % 4)
+        float rs1[16], s1col = 0.f;
+        const int src = 32 * ((col >> 2) & 1), rcol = 4 * (col >> 3) + (col & 3);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          if (dt == NDT - 1 && col != 0) continue;
-          const int row = dt < NDT - 1 ? 32 * dt + col : D;
+        for (int r = 0; r < 16; ++r) {
+          rs1[r] = 1.f / __shfl(S[nt][NDT - 1][r], 32 * g);
+          const float v = __shfl(S[nt][NDT - 1][r], src);
+          if (r == rcol) s1col = v;
+        }
+#pragma unroll
+        for (int dt = 0; dt < NDT - 1; ++dt) {
+          const int row = 32 * dt + col;
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
             bf16x4_t v;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = (bf16)S[nt][dt][4 * a + j];
+            for (int j = 0; j < 4; ++j) v[j] = (bf16)(S[nt][dt][4 * a + j] * rs1[4 * a + j]);
             *reinterpret_cast<bf16x4_t*>(is + (size_t)row * LDSS + 32 * ftile + 16 * (a >> 1) + 8 * g + 4 * (a & 1)) =
                 v;
           }
@@ -379,7 +391,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
         f16x8* icb = reinterpret_cast<f16x8*>(img_cb + (size_t)bh * img_cb_bytes(m));
         if (g == 0) {
           f16x8 cb = zero_frag(f16x8{});
-          split3(cmax[nt], cb, 0);
+          split3(cmax[nt] + __builtin_amdgcn_logf(s1col), cb, 0);
           cb[3] = cb[4] = cb[5] = (f16)1.f;
           icb[2 * f] = cb;
           icb[2 * f + 1] = zero_frag(f16x8{});
@@ -767,13 +779,12 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
   constexpr int MP = Cfg::MP, LDW = Cfg::LDW, LDSS = Cfg::LDSS, NW = Cfg::NWAVE, QN = Cfg::QN;
   constexpr int NT = 64 * NW;
   constexpr int NKC = D / 16;
-  constexpr int NDT = D / 32 + 1;
-  constexpr int SROWS = D + 1;
+  constexpr int NDV = D / 32;  // value-column tiles
   static_assert(LDSS == kImgMP + 8 && MP == kImgMP, "image layout");
   __shared__ __attribute__((aligned(16))) f16 Wl[MP * LDW];
-  __shared__ __attribute__((aligned(16))) bf16 Sl[img_s_bytes(D) / 2];  // (D+2) rows of LDSS
+  __shared__ __attribute__((aligned(16))) bf16 Sl[img_s_bytes(D) / 2];  // rows of LDSS (D used)
   __shared__ __attribute__((aligned(16))) f16x8 Cb[2 * MP];  // [feature][lane group]
-  __shared__ float Cf[MP];
+  __shared__ float Cf[MP], Rs[MP];
 
   const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3;
   const int bh = (kq / per_head) * 8 + xcd, sub = kq % per_head;
@@ -789,7 +800,6 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
 
   const int nchunks = (rows + 32 * QN - 1) / (32 * QN);
   const int stride = per_head * NW;
-  const int ones_row = col == 0 ? D : D + 1;  // lanes other than 0 read the zero row
   // Q of the wave's next chunk is loaded while the current one is computed (rows past
   // the end are clamped to the last row and never stored).
   bf16x8 qn[QN][NKC];
@@ -803,8 +813,8 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
   };
 
   if (img_s != nullptr) {
-    // One position range per head: W, S' and bias rows arrive as ready LDS images, copied
-    // by LDS DMA in 1 KB blocks spread over the waves.
+    // One position range per head: W, S_v / S_1 and the bias rows (c_f + log2 S_1,f)
+    // arrive as ready LDS images, copied by LDS DMA in 1 KB blocks spread over the waves.
     auto copy = [&](void* dst, const char* src, int nbytes) {
       for (int k = wave; k < nbytes / 1024; k += NW)
         __builtin_amdgcn_global_load_lds((const void*)(src + 1024 * k + 16 * l),
@@ -815,30 +825,32 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
     copy(Cb, img_cb + (size_t)bh * img_cb_bytes(m), (int)img_cb_bytes(m));
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     fetch_q(min(sub * NW + wave, nchunks - 1));
-    for (int e = threadIdx.x; e < LDSS; e += NT) Sl[SROWS * LDSS + e] = (bf16)0.f;  // zero row
   } else {
     fetch_q(min(sub * NW + wave, nchunks - 1));
-    // Stage W, S' and the bias rows of all m <= MP features (8 loads in flight per thread).
-
+    // Stage W, S_v / S_1 and the bias rows of all m <= MP features from the position-range
+    // partials: c_f = max_t c_tf, S_f = sum_t 2^(c_tf - c_f) S_tf (8 loads in flight per
+    // thread for the large tables).
     constexpr int U = 8;
-    const int fb = 0, nf = m;
-    for (int f = threadIdx.x; f < nf; f += NT) {
+    for (int f = threadIdx.x; f < m; f += NT) {
       float c = -INFINITY;
-      for (int t = 0; t < T_ranges; ++t) c = fmaxf(c, gch[(size_t)t * m + fb + f]);
+      for (int t = 0; t < T_ranges; ++t) c = fmaxf(c, gch[(size_t)t * m + f]);
+      float s1 = 0.f;
+      for (int t = 0; t < T_ranges; ++t) s1 += fast_exp2(gch[(size_t)t * m + f] - c) * gsh[((size_t)t * (D + 1) + D) * m + f];
       f16x8 cb = zero_frag(f16x8{});
-      split3(c, cb, 0);
+      split3(c + __builtin_amdgcn_logf(s1), cb, 0);
       cb[3] = cb[4] = cb[5] = (f16)1.f;
       Cb[2 * f] = cb;
       Cb[2 * f + 1] = zero_frag(f16x8{});
       Cf[f] = c;
+      Rs[f] = 1.f / s1;
     }
-    const int nw4 = nf * (D / 4);
+    const int nw4 = m * (D / 4);
     for (int e0 = threadIdx.x; e0 < nw4; e0 += U * NT) {
       f32x4 x[U];
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int e = min(e0 + u * NT, nw4 - 1);
-        x[u] = *reinterpret_cast<const f32x4*>(Wh + (size_t)(fb + e / (D / 4)) * D + (e % (D / 4)) * 4);
+        x[u] = *reinterpret_cast<const f32x4*>(Wh + (size_t)(e / (D / 4)) * D + (e % (D / 4)) * 4);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
@@ -852,8 +864,8 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
         *reinterpret_cast<f16x4*>(&Wl[fi * LDW + k4]) = h;
       }
     }
-    if (T_ranges > 1) __syncthreads();  // Cf
-    const int nsv = SROWS * (nf / 4);
+    __syncthreads();  // Cf, Rs
+    const int nsv = D * (m / 4);
     for (int e0 = threadIdx.x; e0 < nsv; e0 += U * NT) {
       f32x4 acc[U];
 #pragma unroll
@@ -863,35 +875,29 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const int e = min(e0 + u * NT, nsv - 1);
-          const int row = e / (nf / 4), fi = (e % (nf / 4)) * 4;
-          v[u] = *reinterpret_cast<const f32x4*>(gsh + ((size_t)t * (D + 1) + row) * m + fb + fi);
+          const int row = e / (m / 4), fi = (e % (m / 4)) * 4;
+          v[u] = *reinterpret_cast<const f32x4*>(gsh + ((size_t)t * (D + 1) + row) * m + fi);
         }
-        if (T_ranges == 1) {
 #pragma unroll
-          for (int u = 0; u < U; ++u) acc[u] = v[u];
-        } else {
+        for (int u = 0; u < U; ++u) {
+          const int e = min(e0 + u * NT, nsv - 1);
+          const int fi = (e % (m / 4)) * 4;
+          const f32x4 c = *reinterpret_cast<const f32x4*>(gch + (size_t)t * m + fi);
 #pragma unroll
-          for (int u = 0; u < U; ++u) {
-            const int e = min(e0 + u * NT, nsv - 1);
-            const int fi = (e % (nf / 4)) * 4;
-            const f32x4 c = *reinterpret_cast<const f32x4*>(gch + (size_t)t * m + fb + fi);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[u][i] += v[u][i] * fast_exp2(c[i] - Cf[fi + i]);
-          }
+          for (int i = 0; i < 4; ++i) acc[u][i] += v[u][i] * fast_exp2(c[i] - Cf[fi + i]);
         }
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int e = e0 + u * NT;
         if (e >= nsv) continue;
-        const int row = e / (nf / 4), fi = (e % (nf / 4)) * 4;
+        const int row = e / (m / 4), fi = (e % (m / 4)) * 4;
         bf16x4_t h;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) h[i] = (bf16)acc[u][i];
+        for (int i = 0; i < 4; ++i) h[i] = (bf16)(acc[u][i] * Rs[fi + i]);
         *reinterpret_cast<bf16x4_t*>(&Sl[row * LDSS + (fi & ~31) + s_pos<bf16>(fi & 31)]) = h;
       }
     }
-    for (int e = threadIdx.x; e < LDSS; e += NT) Sl[SROWS * LDSS + e] = (bf16)0.f;  // zero row
   }
   __syncthreads();
 
@@ -909,12 +915,12 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
       for (int kc = 0; kc < NKC; ++kc) qf[q][kc] = to_wfrag(qn[q][kc]);
     }
     fetch_q(min(ch + stride, nchunks - 1));
-    f32x16 acc[QN][NDT];
-    float M[QN];
+    f32x16 acc[QN][NDV];
+    float den[QN], M[QN];  // den: this lane's half of the features
 
-    // Feature exponents of tile ft, features x queries, lane = query: W_ft Q^T + c_f [- M].
-    // Two accumulators per query tile (even and odd contraction chunks) halve the
-    // dependent MFMA chain.
+    // Feature exponents of tile ft, features x queries, lane = query:
+    // W_ft Q^T + c'_f [- M].  Two accumulators per query tile (even and odd contraction
+    // chunks) halve the dependent MFMA chain.
     auto c1_tile = [&](int ft, f32x16 (&c1)[QN], bool with_m) {
       f32x16 c2[QN];
 #pragma unroll
@@ -935,7 +941,10 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
         c1[q] += c2[q];
       }
     };
-    // phi = 2^(c1 - sub) and acc += S'_ft^T phi.
+    // phi' = 2^(c1 - sub) rounded to bf16: den += sum of phi' (the same bf16 values the
+    // numerator uses, summed in fp32 by dot2 against (1, 1)), acc += (S_v / S_1)_ft^T phi'.
+    bf16x2 one2;
+    one2[0] = one2[1] = (bf16)1.f;
     auto readout_tile = [&](int ft, const f32x16 (&c1)[QN], bool sub_m) {
       bf16x8 pf[QN][2];
 #pragma unroll
@@ -944,12 +953,23 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
 #pragma unroll
         for (int r = 0; r < 16; ++r) e[r] = fast_exp2(sub_m ? c1[q][r] - M[q] : c1[q][r]);
         acc_to_frags(e, pf[q]);
+        float sum = den[q];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            bf16x2 v;
+            v[0] = pf[q][h][j];
+            v[1] = pf[q][h][j + 1];
+            sum = __builtin_amdgcn_fdot2_f32_bf16(v, one2, sum, false);
+          }
+        den[q] = sum;
       }
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) {
-          const bf16x8 a = s_frag(Sl, LDSS, dt < NDT - 1 ? 32 * dt + col : ones_row, ft, h, g);
+        for (int dt = 0; dt < NDV; ++dt) {
+          const bf16x8 a = s_frag(Sl, LDSS, 32 * dt + col, ft, h, g);
 #pragma unroll
           for (int q = 0; q < QN; ++q) acc[q][dt] = mma(a, pf[q][h], acc[q][dt]);
         }
@@ -965,8 +985,9 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
 #pragma unroll
       for (int q = 0; q < QN; ++q) {
         M[q] = -INFINITY;
+        den[q] = 0.f;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) acc[q][dt] = zero16();
+        for (int dt = 0; dt < NDV; ++dt) acc[q][dt] = zero16();
       }
       if (fast) {
         // Stabiliser fixed at the first tile's row maximum, then folded into the bias.
@@ -992,8 +1013,9 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
             if (wave_any(mx > M[q] + kTau)) {
               const float nm = mx > M[q] + kTau ? mx : M[q];
               const float fct = fast_exp2(M[q] - nm);
+              den[q] *= fct;
 #pragma unroll
-              for (int dt = 0; dt < NDT; ++dt)
+              for (int dt = 0; dt < NDV; ++dt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[q][dt][r] *= fct;
               M[q] = nm;
@@ -1002,28 +1024,24 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
           readout_tile(ft, c1, true);
         }
       }
+#pragma unroll
+      for (int q = 0; q < QN; ++q) den[q] += partner32(den[q]);
     };
     // Only an overflow (a later feature tile ~2^100 above the first) makes the fast pass
     // non-finite; then this wave's rows are redone with the running maximum.
     run(true);
     bool bad = false;
 #pragma unroll
-    for (int q = 0; q < QN; ++q) {
-      const float dq = acc[q][NDT - 1][0];
-      bad |= valid[q] && !(dq - dq == 0.f);
-    }
+    for (int q = 0; q < QN; ++q) bad |= valid[q] && !(den[q] - den[q] == 0.f && den[q] > 0.f);
     if (wave_any(bad)) run(false);
 
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
-      float den = acc[q][NDT - 1][0];
-      const float dp = partner32(den);
-      den = g ? dp : den;
-      const float inv = 1.f / den;
+      const float inv = 1.f / den[q];
       if (!valid[q]) continue;
       bf16* orow = Ob + (size_t)myrow[q] * D;
 #pragma unroll
-      for (int dt = 0; dt < NDT - 1; ++dt) {
+      for (int dt = 0; dt < NDV; ++dt) {
         bf16x8 o0, o1;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {

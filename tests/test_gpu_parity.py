@@ -49,6 +49,10 @@ SMALL = [
     _small("c2_bidir_bf16", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=300, num_features=512),
     _small("c2_bidir_bf16", batch=2, heads_q=6, heads_kv=2, heads_w=2, seq_len=129),
     _small("c4_mqa_bidir_bf16", batch=2, heads_q=4, heads_kv=1, heads_w=1, seq_len=777),
+    # many kv heads, so one position range per head (the readout's ready LDS images)
+    _small("c2_bidir_bf16", batch=8, heads_q=8, heads_kv=8, heads_w=8, seq_len=200),
+    _small("c4_mqa_bidir_bf16", batch=64, heads_q=2, heads_kv=1, heads_w=1, seq_len=100),
+    _small("c2_bidir_bf16", batch=32, heads_q=4, heads_kv=2, heads_w=1, seq_len=65, num_features=128),
     I.workload("c1_bidir_f32"),
     _small("c1_bidir_f32", batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=333, head_dim=128,
            num_features=192),
