@@ -1115,7 +1115,7 @@ __global__ void __launch_bounds__(256) causal_scan_kernel(const float* __restric
 }
 
 // ======================================================================================
-// causal_chunk: grid (segments, B*Hq), m/64 waves; wave w owns features [64w, 64w+64).
+// causal_chunk: grid (segments, B*Hq), m/(32 NTC) waves; wave w owns NTC 32-feature tiles.
 // Per 32-position block p0 of the segment, in order:
 //   phi_Q,w  = 2^(W_w Q^T - M_w)             (M_w: this wave's row maximum)
 //   phi_K,w  = 2^(K W_w^T - |k|^2 log2e/2 - c*) (c*: global per kv head, from the scan)
@@ -1128,7 +1128,7 @@ template <class T> struct CausalLd;
 template <> struct CausalLd<bf16> { static constexpr int PK = 48; };  // phi_K rows: 32 keys + pad
 template <> struct CausalLd<float> { static constexpr int PK = 33; };
 
-template <class T, int D, int NWMAX>
+template <class T, int D, int NTC, int NWMAX, bool PF>
 __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ W,
     const float* __restrict__ prefix, const float* __restrict__ cstar_in, T* __restrict__ out, int L, int Hq,
@@ -1144,7 +1144,8 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
   constexpr int LDR = D + 4;  // reduction rows: D partial values, den, row max
   // The cross-wave reduction handles 32 / QSPLIT query rows at a time so that the LDS
   // footprint stays within 160 KB for wide heads and many waves.
-  constexpr int BASE_LDS = (2 * 32 * LDK + 32 * LDV + NWMAX * 64 * LDP) * (int)sizeof(T);
+  constexpr int FW = 32 * NTC;  // features per wave
+  constexpr int BASE_LDS = (2 * 32 * LDK + 32 * LDV + NWMAX * FW * LDP) * (int)sizeof(T);
   constexpr int QSPLIT = BASE_LDS + NWMAX * 32 * LDR * 4 <= 160 * 1024       ? 1
                          : BASE_LDS + NWMAX * 16 * LDR * 4 <= 160 * 1024 ? 2
                                                                          : 4;
@@ -1152,23 +1153,23 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
   __shared__ __attribute__((aligned(16))) T Ql[32 * LDK];
   __shared__ __attribute__((aligned(16))) T Kl[32 * LDK];
   __shared__ __attribute__((aligned(16))) T Vl[32 * LDV];
-  __shared__ __attribute__((aligned(16))) T Pk[NWMAX][64 * LDP];
+  __shared__ __attribute__((aligned(16))) T Pk[NWMAX][FW * LDP];
   __shared__ __attribute__((aligned(16))) float Red[NWMAX][QR * LDR];
 
   const int seg = blockIdx.x, bhq = blockIdx.y;
   const int b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv), bh = b * Hkv + hkv;
   const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
-  const int f0 = wave * 64;
+  const int f0 = wave * FW;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
   const T* Qh = Q + (size_t)bhq * L * D;
   T* Oh = out + (size_t)bhq * L * D;
   const T* Kh = K + (size_t)bh * L * D;
   const T* Vh = V + (size_t)bh * L * D;
 
-  wfrag wf[2][NKC];
+  wfrag wf[NTC][NKC];
 #pragma unroll
-  for (int nt = 0; nt < 2; ++nt)
+  for (int nt = 0; nt < NTC; ++nt)
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) load_w_frag(Wh + (size_t)(f0 + 32 * nt + col) * D, kc, g, wf[nt][kc]);
   const float cstar = cstar_in[bh];
@@ -1176,11 +1177,11 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
 
   // carry of this wave's features, from the exclusive prefix of the segment ([d+1][m]:
   // lane col takes row 32 dt + col, register r feature 8(r/4) + 4g + r%4 of the tile)
-  f32x16 carry[2][NDT];
+  f32x16 carry[NTC][NDT];
   {
     const float* pf = prefix + ((size_t)bh * T_ranges + seg) * (size_t)(D + 1) * m;
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NTC; ++nt)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
         const int row = dt < NDT - 1 ? 32 * dt + col : D;
@@ -1208,33 +1209,95 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
 
   const int p_begin = seg * R;
   const int p_end = min(p_begin + R, L);
+  // The next block's Q, K, V rows are loaded into registers while the current block is
+  // computed, and written to LDS at the top of the next iteration (zeros past L).
+  constexpr int EPC = 16 / (int)sizeof(T), CPR = D / EPC, NCH = 32 * CPR;
+  constexpr int MINT = NTC == 1 ? 128 : 64;  // fewest threads a block has (m >= 64)
+  constexpr int PER = PF ? (NCH + MINT - 1) / MINT : 1;
+  f32x4 pq[PER], pkk[PER], pv[PER];
+  auto prefetch = [&](int q0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * blockDim.x;
+      const int row = c / CPR, c0 = (c % CPR) * EPC;
+      pq[i] = pkk[i] = pv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (c < NCH && q0 + row < L) {
+        const size_t off = (size_t)(q0 + row) * D + c0;
+        pq[i] = *reinterpret_cast<const f32x4*>(Qh + off);
+        pkk[i] = *reinterpret_cast<const f32x4*>(Kh + off);
+        pv[i] = *reinterpret_cast<const f32x4*>(Vh + off);
+      }
+    }
+  };
+  auto put = [&](T* dst, int ld, const f32x4& v, int row, int c0) {
+    T* drow = dst + row * ld;
+    if (sizeof(T) == 2) {
+      *reinterpret_cast<float2*>(drow + c0) = float2{v[0], v[1]};
+      *reinterpret_cast<float2*>(drow + c0 + EPC / 2) = float2{v[2], v[3]};
+    } else {
+      float* d = reinterpret_cast<float*>(drow + c0);
+      d[0] = v[0];
+      d[1] = v[1];
+      d[2] = v[2];
+      d[3] = v[3];
+    }
+  };
+  auto put_v = [&](const f32x4& v, int row, int c0) {  // value columns permuted by vperm_inv
+    const int tile = c0 & ~31;
+    T* drow = Vl + row * LDV;
+    if (sizeof(T) == 2) {
+      *reinterpret_cast<float2*>(drow + tile + vperm_inv(c0 & 31)) = float2{v[0], v[1]};
+      *reinterpret_cast<float2*>(drow + tile + vperm_inv((c0 & 31) + 4)) = float2{v[2], v[3]};
+    } else {
+      float* d = reinterpret_cast<float*>(drow + tile + vperm_inv(c0 & 31));
+      d[0] = v[0];
+      d[1] = v[1];
+      d[2] = v[2];
+      d[3] = v[3];
+    }
+  };
+  if constexpr (PF) prefetch(p_begin);
   for (int p0 = p_begin; p0 < p_end; p0 += 32) {
     __syncthreads();
-    stage_rows<T, D, false>(Ql, LDK, Qh, p0, L);
-    stage_rows<T, D, false>(Kl, LDK, Kh, p0, L);
-    stage_rows<T, D, true>(Vl, LDV, Vh, p0, L);
+    if constexpr (PF) {
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int c = threadIdx.x + i * blockDim.x;
+        if (c < NCH) {
+          const int row = c / CPR, c0 = (c % CPR) * EPC;
+          put(Ql, LDK, pq[i], row, c0);
+          put(Kl, LDK, pkk[i], row, c0);
+          put_v(pv[i], row, c0);
+        }
+      }
+      if (p0 + 32 < p_end) prefetch(p0 + 32);
+    } else {
+      stage_rows<T, D, false>(Ql, LDK, Qh, p0, L);
+      stage_rows<T, D, false>(Kl, LDK, Kh, p0, L);
+      stage_rows<T, D, true>(Vl, LDV, Vh, p0, L);
+    }
     __syncthreads();
 
     // phi_Q of this wave's features: C = W_w Q^T (features x queries), lane = query.
     wfrag qf[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) qf[kc] = to_wfrag(load_frag_k(Ql + col * LDK, kc, g));
-    f32x16 cq[2];
+    f32x16 cq[NTC];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NTC; ++nt) {
       cq[nt] = zero16();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) cq[nt] = mma(wf[nt][kc], qf[kc], cq[nt]);
     }
     float Mw = cq[0][0];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NTC; ++nt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) Mw = fmaxf(Mw, cq[nt][r]);
     Mw = fmaxf(Mw, partner32(Mw));
-    frag qb[2][P::NF32];
+    frag qb[NTC][P::NF32];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NTC; ++nt) {
       f32x16 e;
 #pragma unroll
       for (int r = 0; r < 16; ++r) e[r] = fast_exp2(cq[nt][r] - Mw);
@@ -1248,9 +1311,9 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     float nrm = sumsq(kf);
     nrm += partner32(nrm);
     const wfrag biasA = bias_rows(0.5f * kLog2e * nrm, g, wfrag{});
-    frag ka[2][P::NF32];
+    frag ka[NTC][P::NF32];
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+    for (int nt = 0; nt < NTC; ++nt) {
       f32x16 ck = zero16();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) ck = mma(kf[kc], wf[nt][kc], ck);
@@ -1277,7 +1340,7 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     for (int dt = 0; dt < NDT; ++dt) {
       num[dt] = zero16();
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
+      for (int nt = 0; nt < NTC; ++nt) {
         frag ca[P::NF32];
         acc_to_frags(carry[nt][dt], ca);
 #pragma unroll
@@ -1285,11 +1348,11 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
       }
     }
     // intra-block triangle: A^T = phi_K phi_Q^T (keys x queries), keep key <= query
-    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only: the prefetch stays in flight
     __builtin_amdgcn_wave_barrier();
     f32x16 at = zero16();
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+    for (int nt = 0; nt < NTC; ++nt)
 #pragma unroll
       for (int h = 0; h < P::NF32; ++h) at = mma(lds_frag_rows(pk, LDP, 32 * nt, 0, h), qb[nt][h], at);
 #pragma unroll
@@ -1304,7 +1367,7 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
         const frag va = dt < NDT - 1 ? lds_frag_rows(Vl, LDV, 0, 32 * dt, h) : ones;
         num[dt] = mma(va, ab[h], num[dt]);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) carry[nt][dt] = mma(ka[nt][h], va, carry[nt][dt]);
+        for (int nt = 0; nt < NTC; ++nt) carry[nt][dt] = mma(ka[nt][h], va, carry[nt][dt]);
       }
 
     // this wave's partial to LDS (D values, den, row maximum per query), then the
@@ -1445,11 +1508,17 @@ favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const
   hipLaunchKernelGGL(causal_scan_kernel, dim3(ceil_div_i((long long)(s.d + 1) * s.m / 4, 256), s.BH), dim3(256), 0,
                      st, gs, gc, s.T, s.m, s.d, prefix, cstar);
   if (hipGetLastError() != hipSuccess || !mk.mark(2, st)) return FAVOR_ERR_HIP;
-  if (nw <= 4)
-    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 4>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
+  // bf16, d = 64: one 32-feature tile per wave up to m = 256 (two waves per SIMD), else two
+  constexpr bool one_tile = std::is_same<T, bf16>::value && D == 64;
+  if (one_tile && s.m <= 256) {
+    if constexpr (one_tile)
+      hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, true>), dim3(s.T, s.B * s.Hq), dim3(kWave * (s.m / 32)), 0,
+                         st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
+  } else if (nw <= 4)
+    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 2, 4, false>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
                        prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
   else
-    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 8>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
+    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 2, 8, false>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
                        prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
   if (hipGetLastError() != hipSuccess || !mk.mark(3, st)) return FAVOR_ERR_HIP;
   return FAVOR_OK;
