@@ -8,13 +8,15 @@
 // cancel between numerator and denominator and are chosen for range only.
 //
 // Kernels (exponents are kept in log2 units: W is scaled by log2(e) on load):
-//   kv_summary   keys/values of one kv head, one position range per workgroup: per wave a
-//                slice of 64 features; phi(K_blk) = exp2(K_blk W^T - |k|^2 log2e / 2 - c_f)
-//                on the MFMA (the bias enters as one extra MFMA), then S += phi^T [V, 1].
-//                c_f is a per-feature running maximum, moved lazily (kTau).
-//   (the readout sums the position-range partials while staging them)
-//   readout      bidirectional: per query tile, phi(Q) W-contraction on the MFMA with a
-//                running row maximum, then out^T = S^T phi(Q)^T and the division.
+//   kv_summary   keys/values of one kv head, one position range and 64 features per
+//                workgroup: phi(K_blk) = exp2(K_blk W^T - |k|^2 log2e / 2 - c_f) on the MFMA
+//                (the bias enters as one extra MFMA), then S += phi^T [V, 1].  c_f is the
+//                per-feature maximum of the range's first block (running maximum only on
+//                overflow).  With one range per head (bf16) it writes the readout's LDS
+//                images directly: S_v / S_1 in bf16 and c_f + log2 S_1,f per feature.
+//   readout      bidirectional: per 32-row query tile, the W contraction on the MFMA, the
+//                key stabiliser c_f and the row stabiliser entering through one bias MFMA,
+//                then out^T = S^T phi(Q)^T and the division.
 //   causal_scan  causal: exclusive prefix of the per-segment summaries, all rescaled to a
 //                global per-head stabiliser.
 //   causal_chunk causal: per segment, 32-position blocks in order with the carried summary
@@ -435,7 +437,7 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 // ======================================================================================
 // readout (bidirectional).  Grid (workgroups per kv head, B*Hkv), NWAVE waves; each wave
 // owns QN x 32 query rows per step (the G query heads of a kv head are G*L contiguous
-// rows).  LDS holds W (hi/lo) and S^T for a pass of MP features: rows are value columns in
+// rows).  LDS holds W (fp16 for bf16 problems) and S^T for a pass of MP features: rows are value columns in
 // vperm order then the ones row; within a 32-feature tile the features are reordered so
 // one lane's 8 operand values are contiguous.  S is summed over the position ranges and
 // rescaled to the head's largest stabiliser while staged; with more than one pass W and S

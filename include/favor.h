@@ -34,8 +34,9 @@
  *    queued and `out` is untouched.  FAVOR_ERR_HIP reports a failed kernel launch.
  *  - Results are deterministic: the same inputs and problem give bitwise-identical
  *    output (fixed-order reductions, no floating-point atomics).
- *  - Accumulation is float32.  For bf16 problems W is split into two bf16 parts so the
- *    feature exponent keeps float32 accuracy.
+ *  - Accumulation is float32.  For bf16 problems the exponent W x is contracted in fp16
+ *    (W * log2(e) rounded to fp16, the bf16 inputs converted exactly), the features and
+ *    the summary in bf16; float32 problems use float32 throughout.
  *  - `out` must not alias Q, K, V, W or the workspace.
  */
 #ifndef FAVOR_H
