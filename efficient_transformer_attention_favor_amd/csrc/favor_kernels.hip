@@ -104,7 +104,10 @@ template <> struct KvCfg<float, 128> { static constexpr int KW = 4, NTW = 1; };
 // With one range per kv head and bf16 data (img_s != nullptr) the workgroup writes, instead
 // of gs / gc, the readout's LDS images of its 64 features: S'^T rows in readout order, the
 // bias operands of c_f, and (one head of each W) the fp16 W rows.
-template <class T, int D>
+// SEG (causal segments): each wave owns one whole segment instead of a share of a range,
+// so the position groups of a workgroup are PG consecutive segments and every wave writes
+// its own partial with its own stabilisers (no merge, no workgroup barrier).
+template <class T, int D, bool SEG>
 __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
     const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ W, int L, int Hkv, int Hw, int m,
     int R, int T_ranges, int n_units, float* __restrict__ gs, float* __restrict__ gc, char* __restrict__ img_w,
@@ -127,9 +130,12 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3;
   const int slice = kq % NFS, unit = (kq / NFS) * 8 + xcd;
   if (unit >= n_units) return;
-  const int bh = unit / T_ranges, t = unit % T_ranges, hkv = bh % Hkv;
   const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
   const int fgi = wave % FG, pgi = wave / FG;
+  const int TG = SEG ? (T_ranges + PG - 1) / PG : T_ranges;  // units per kv head
+  const int bh = unit / TG, hkv = bh % Hkv;
+  const int t = SEG ? (unit % TG) * PG + pgi : unit % TG;
+  if (SEG && t >= T_ranges) return;
   const int f0 = slice * 64 + fgi * 32 * NTW;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
   const T* Kh = K + (size_t)bh * L * D;
@@ -156,8 +162,8 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   }
 
   const int pb = t * R, pe = min(pb + R, L);
-  const int Rw = ((R + 32 * PG - 1) / (32 * PG)) * 32;
-  const int wb = pb + pgi * Rw, we = min(wb + Rw, pe);
+  const int Rw = SEG ? R : ((R + 32 * PG - 1) / (32 * PG)) * 32;
+  const int wb = SEG ? pb : pb + pgi * Rw, we = min(wb + Rw, pe);
   constexpr int EPC = 16 / sizeof(T);   // elements per 16-byte chunk
   constexpr int CPR = D / EPC;          // chunks per row
   constexpr int CPL = 32 * CPR / 64;    // chunks per lane per block
@@ -305,6 +311,34 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
     for (int p0 = wb; p0 < we; p0 += 32) block(p0, std::integral_constant<int, 2>{});
   }
 
+  // The partial of unit_off (float32 gs rows in vperm order, row D the ones column, and
+  // gc) relative to the stabilisers cmx of this lane's C1 features.
+  auto store_partial = [&](size_t unit_off, const float (&cmx)[NTW]) {
+    float* out_s = gs + unit_off * (size_t)(D + 1) * m;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) {
+#pragma unroll
+      for (int dt = 0; dt < NDT - 1; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 v = {S[nt][dt][4 * r4], S[nt][dt][4 * r4 + 1], S[nt][dt][4 * r4 + 2], S[nt][dt][4 * r4 + 3]};
+          *reinterpret_cast<f32x4*>(out_s + (size_t)(32 * dt + col) * m + f0 + 32 * nt + 8 * r4 + 4 * g) = v;
+        }
+      if (col == 0)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          f32x4 v = {S[nt][NDT - 1][4 * r4], S[nt][NDT - 1][4 * r4 + 1], S[nt][NDT - 1][4 * r4 + 2],
+                     S[nt][NDT - 1][4 * r4 + 3]};
+          *reinterpret_cast<f32x4*>(out_s + (size_t)D * m + f0 + 32 * nt + 8 * r4 + 4 * g) = v;
+        }
+      if (g == 0) gc[unit_off * m + f0 + 32 * nt + col] = cmx[nt];
+    }
+  };
+  if constexpr (SEG) {
+    store_partial((size_t)bh * T_ranges + t, cst);
+    return;
+  }
+
   // ---- merge the position-group partials of each feature group --------------------
   if (g == 0) {
 #pragma unroll
@@ -408,25 +442,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
       return;
     }
   }
-  float* out_s = gs + unit_off * (size_t)(D + 1) * m;
-#pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-#pragma unroll
-    for (int dt = 0; dt < NDT - 1; ++dt)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 v = {S[nt][dt][4 * r4], S[nt][dt][4 * r4 + 1], S[nt][dt][4 * r4 + 2], S[nt][dt][4 * r4 + 3]};
-        *reinterpret_cast<f32x4*>(out_s + (size_t)(32 * dt + col) * m + f0 + 32 * nt + 8 * r4 + 4 * g) = v;
-      }
-    if (col == 0)
-#pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        f32x4 v = {S[nt][NDT - 1][4 * r4], S[nt][NDT - 1][4 * r4 + 1], S[nt][NDT - 1][4 * r4 + 2],
-                   S[nt][NDT - 1][4 * r4 + 3]};
-        *reinterpret_cast<f32x4*>(out_s + (size_t)D * m + f0 + 32 * nt + 8 * r4 + 4 * g) = v;
-      }
-    if (g == 0) gc[unit_off * m + f0 + 32 * nt + col] = cmax[nt];
-  }
+  store_partial(unit_off, cmax);
 }
 
 // s_waitcnt immediate (gfx9 encoding) that waits for vector memory only: vmcnt <= n.
@@ -1446,9 +1462,17 @@ struct Marks {
 template <class T, int D>
 favor_status launch_kv_summary(const Plan& s, const T* K, const T* V, const float* W, float* gs, float* gc,
                                char* ws, hipStream_t st) {
-  const int units = s.BH * s.T;
   const int nfs = s.m / kFeatPerWave;
-  hipLaunchKernelGGL((kv_summary_kernel<T, D>), dim3(8 * ceil_div_i(units, 8) * nfs), dim3(64 * KvCfg<T, D>::KW), 0,
+  if (s.mode == FAVOR_CAUSAL) {
+    constexpr int PG = KvCfg<T, D>::KW * KvCfg<T, D>::NTW / 2;  // segments per workgroup
+    const int units = s.BH * ceil_div_i(s.T, PG);
+    hipLaunchKernelGGL((kv_summary_kernel<T, D, true>), dim3(8 * ceil_div_i(units, 8) * nfs),
+                       dim3(64 * KvCfg<T, D>::KW), 0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc,
+                       nullptr, nullptr, nullptr);
+    return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  }
+  const int units = s.BH * s.T;
+  hipLaunchKernelGGL((kv_summary_kernel<T, D, false>), dim3(8 * ceil_div_i(units, 8) * nfs), dim3(64 * KvCfg<T, D>::KW), 0,
                      st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc, s.img ? ws + s.off_img_w : nullptr,
                      s.img ? ws + s.off_img_s : nullptr, s.img ? ws + s.off_img_cb : nullptr);
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;

@@ -47,16 +47,33 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
 
   // Position ranges per kv head.  Bidirectional: about kKeyTarget key-side workgroups
   // (one per range and 64-feature slice), each range at least 128 positions.  Causal:
-  // about kSegmentTarget chunk-kernel workgroups (one per segment and query head), the
-  // segment a multiple of the chunk.  The split depends on the problem only, which keeps
-  // the reduction order -- and so the result bits -- independent of the device.
+  // segments (a multiple of the chunk) chosen by the cost model below.  The split depends
+  // on the problem only, which keeps the reduction order -- and so the result bits --
+  // independent of the device.
   const int nfs = q.m / kFeatPerWave;
   int T, unit;
   if (q.mode == FAVOR_CAUSAL) {
+    // Segment count by a cost model in units of one 32-position block step: the chunk
+    // kernel runs one workgroup per CU (about twice the time per step of the key side),
+    // the key side one wave per segment and 64-feature slice, one wave per SIMD, segments
+    // in groups of kSegGroup per workgroup.  Ties go to fewer segments.
     unit = q.chunk;
-    T = ceil_div(kSegmentTarget, (long long)q.B * q.Hq);
     const int max_t = ceil_div(q.L, unit);
-    if (T > max_t) T = max_t;
+    long long best = -1;
+    T = 1;
+    for (int t = 1; t <= max_t; ++t) {
+      const int r = ceil_div(ceil_div(q.L, t), unit) * unit;
+      if (ceil_div(q.L, r) != t) continue;  // the same split as a smaller t
+      const long long steps = r / kTile;
+      const long long chunk_rounds = ceil_div((long long)q.B * q.Hq * t, kCUs);
+      const long long key_waves = (long long)q.BH * ceil_div(t, kSegGroup) * kSegGroup * nfs;
+      const long long key_rounds = ceil_div(key_waves, 4LL * kCUs);
+      const long long cost = (2 * chunk_rounds + key_rounds) * steps;
+      if (best < 0 || cost < best) {
+        best = cost;
+        T = t;
+      }
+    }
   } else {
     unit = 4 * kTile;
     T = (int)((kKeyTarget + (long long)q.BH * nfs / 2) / ((long long)q.BH * nfs));
