@@ -216,11 +216,13 @@ __device__ __forceinline__ float bias_unit_rows(int g, float) { return g == 0 ? 
 __device__ __forceinline__ float bias_cols(float c, int g, float) { return g == 0 ? -1.f : -c; }
 // Row bias that removes a row from a contraction (its features become 2^-30000 = 0).
 constexpr float kMaskedRow = 30000.0f;
+// Word 3 of a raw buffer descriptor for untyped loads (data format 32, no swizzle).
+constexpr int kBufWord3 = 0x00020000;
 
 // Sum of squares of the contraction values a lane holds in its row operands.
 template <int N>
 __device__ __forceinline__ float sumsq(const bf16x8 (&f)[N]) {
-  float s = 0.f;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};  // four independent accumulation chains
 #pragma unroll
   for (int i = 0; i < N; ++i)
 #pragma unroll
@@ -228,13 +230,13 @@ __device__ __forceinline__ float sumsq(const bf16x8 (&f)[N]) {
       bf16x2 v;
       v[0] = f[i][j];
       v[1] = f[i][j + 1];
-      s = __builtin_amdgcn_fdot2_f32_bf16(v, v, s, false);
+      s[j / 2] = __builtin_amdgcn_fdot2_f32_bf16(v, v, s[j / 2], false);
     }
-  return s;
+  return (s[0] + s[1]) + (s[2] + s[3]);
 }
 template <int N>
 __device__ __forceinline__ float sumsq(const f16x8 (&f)[N]) {
-  float s = 0.f;
+  float s[4] = {0.f, 0.f, 0.f, 0.f};  // four independent accumulation chains
 #pragma unroll
   for (int i = 0; i < N; ++i)
 #pragma unroll
@@ -243,9 +245,9 @@ __device__ __forceinline__ float sumsq(const f16x8 (&f)[N]) {
       f16x2 v;
       v[0] = f[i][j];
       v[1] = f[i][j + 1];
-      s = __builtin_amdgcn_fdot2(v, v, s, false);
+      s[j / 2] = __builtin_amdgcn_fdot2(v, v, s[j / 2], false);
     }
-  return s;
+  return (s[0] + s[1]) + (s[2] + s[3]);
 }
 template <int N>
 __device__ __forceinline__ float sumsq(const float (&f)[N]) {

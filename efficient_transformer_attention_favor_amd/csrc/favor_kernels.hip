@@ -124,7 +124,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   constexpr int ACC = NTW * NDT * 1024;  // floats of one wave's partial (fragment order)
   __shared__ __attribute__((aligned(16))) T Vl[KW][32 * LDV];
   __shared__ __attribute__((aligned(16))) float Red[(PG / 2) * FG][ACC];
-  __shared__ float Cs[KW][32 * NTW];
+  __shared__ __attribute__((aligned(16))) float Cs[KW][32 * NTW];
 
   const int NFS = m / 64;
   const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3;
@@ -172,15 +172,32 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   // data whose features get the kMaskedRow bias, i.e. phi = 0).
   f32x4 vn[CPL];
   frag kn[NKC];
+  // bf16: raw buffer loads range-checked against the head (rows past L read as zero; the
+  // block offset is in the vector offset, which the check covers), so the per-lane offsets
+  // are fixed and a block costs one add per tensor.
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, L * D * (int)sizeof(T), kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, L * D * (int)sizeof(T), kBufWord3);
   auto fetch = [&](int q0) {
+    if constexpr (sizeof(T) == 2) {
+      const int vo = q0 * D * 2 + 16 * l, ko = (q0 + col) * D * 2 + 16 * g;
 #pragma unroll
-    for (int i = 0; i < CPL; ++i) {
-      const int c = l + 64 * i, row = min(q0 + c / CPR, we - 1), c0 = (c % CPR) * EPC;
-      vn[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)row * D + c0);
+      for (int i = 0; i < CPL; ++i)
+        vn[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vo + 1024 * i, 0, 0));
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc)
+        kn[kc] = __builtin_bit_cast(frag, __builtin_amdgcn_raw_buffer_load_b128(krs, ko + 32 * kc, 0, 0));
+    } else {
+#pragma unroll
+      for (int i = 0; i < CPL; ++i) {
+        const int c = l + 64 * i, row = min(q0 + c / CPR, we - 1), c0 = (c % CPR) * EPC;
+        vn[i] = *reinterpret_cast<const f32x4*>(Vh + (size_t)row * D + c0);
+      }
+      const int krow = min(q0 + col, we - 1);
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) kn[kc] = load_frag_k(Kh + (size_t)krow * D, kc, g);
     }
-    const int krow = min(q0 + col, we - 1);
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) kn[kc] = load_frag_k(Kh + (size_t)krow * D, kc, g);
   };
 
   // One 32-position block.  Stabiliser modes: 0 = first block of the fast pass (c_f :=
@@ -204,19 +221,20 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) kf[kc] = to_wfrag(kn[kc]);
     fetch(min(p0 + 32, we - 1));
-    float nrm = sumsq(kf);
-    nrm += partner32(nrm);
-    const float rb = p0 + col < we ? 0.5f * kLog2e * nrm : kMaskedRow;
-    const wfrag biasA = bias_rows(rb, g, wfrag{});
-
+    // the W contraction first: the norm and the bias operand are built while it runs
     f32x16 c1[NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       c1[nt] = zero16();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) c1[nt] = mma(kf[kc], wf[nt][kc], c1[nt]);
-      c1[nt] = mma(biasA, biasB[nt], c1[nt]);
     }
+    float nrm = sumsq(kf);
+    nrm += partner32(nrm);
+    const float rb = p0 + col < we ? 0.5f * kLog2e * nrm : kMaskedRow;
+    const wfrag biasA = bias_rows(rb, g, wfrag{});
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) c1[nt] = mma(biasA, biasB[nt], c1[nt]);
 
     if constexpr (MODE == 0) {
 #pragma unroll
@@ -352,25 +370,37 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
 #pragma unroll
     for (int q = 0; q < PG; ++q) cmax[nt] = fmaxf(cmax[nt], Cs[q * FG + fgi][32 * nt + col]);
   }
+  // registers 4 r4 .. 4 r4 + 3 hold features 32 nt + 8 r4 + 4 g + (0..3): one 16-byte read
 #pragma unroll
   for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int fl = 32 * nt + 8 * (r >> 2) + 4 * g + (r & 3);
-      float cm = -INFINITY;
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int fb = 32 * nt + 8 * r4 + 4 * g;
+      const f32x4 own = *reinterpret_cast<const f32x4*>(&Cs[wave][fb]);
+      f32x4 cm = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
 #pragma unroll
-      for (int q = 0; q < PG; ++q) cm = fmaxf(cm, Cs[q * FG + fgi][fl]);
-      const float sc = cm == -INFINITY ? 0.f : fast_exp2(Cs[wave][fl] - cm);
+      for (int q = 0; q < PG; ++q) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(&Cs[q * FG + fgi][fb]);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) S[nt][dt][r] *= sc;
+        for (int i = 0; i < 4; ++i) cm[i] = fmaxf(cm[i], o[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = cm[i] == -INFINITY ? 0.f : fast_exp2(own[i] - cm[i]);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) S[nt][dt][4 * r4 + i] *= sc;
+      }
     }
+  // partial exchange in 16-byte pieces: piece (nt, dt, r4) of lane l at ((nt NDT + dt) 4 + r4) 256 + 4 l
   auto dump = [&](float* dst) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) dst[((nt * NDT + dt) * 16 + r) * 64 + l] = S[nt][dt][r];
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<f32x4*>(dst + ((nt * NDT + dt) * 4 + r4) * 256 + 4 * l) =
+              f32x4{S[nt][dt][4 * r4], S[nt][dt][4 * r4 + 1], S[nt][dt][4 * r4 + 2], S[nt][dt][4 * r4 + 3]};
   };
   auto absorb = [&](const float* src) {
 #pragma unroll
@@ -378,7 +408,11 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) S[nt][dt][r] += src[((nt * NDT + dt) * 16 + r) * 64 + l];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(src + ((nt * NDT + dt) * 4 + r4) * 256 + 4 * l);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[nt][dt][4 * r4 + i] += v[i];
+        }
   };
 #pragma unroll
   for (int step = PG / 2; step >= 1; step >>= 1) {
@@ -407,7 +441,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
         const int src = 32 * ((col >> 2) & 1), rcol = 4 * (col >> 3) + (col & 3);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          rs1[r] = 1.f / __shfl(S[nt][NDT - 1][r], 32 * g);
+          rs1[r] = __builtin_amdgcn_rcpf(__shfl(S[nt][NDT - 1][r], 32 * g));
           const float v = __shfl(S[nt][NDT - 1][r], src);
           if (r == rcol) s1col = v;
         }
