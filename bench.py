@@ -119,33 +119,29 @@ def measured_traffic(workload, kernel):
     return None
 
 
-def cpu_baseline(w, Q, K, V, W, budget_s=15.0):
-    """The float64 oracle on whole (batch, head) slices until about budget_s of CPU time."""
-    import numpy as np
+def cpu_baseline(w, Q, K, V, W, min_s=10.0):
+    """The float64 oracle on whole (batch, head) slices, cycling over the workload's slices
+    until at least min_s seconds have passed (a bounded sample; at most one extra slice)."""
     from threadpoolctl import threadpool_info
 
     import oracle.favor_oracle as O
 
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     G = w.heads_q // w.heads_kv
+    total = w.batch * w.heads_q
     t0 = time.perf_counter()
     heads = 0
-    for b in range(w.batch):
-        for hq in range(w.heads_q):
-            hk = hq // G
-            Wh = W[0 if w.heads_w == 1 else hk]
-            O.favor_head(Q[b, hq], K[b, hk], V[b, hk], Wh, causal=w.causal)
-            heads += 1
-            if time.perf_counter() - t0 > budget_s:
-                break
-        else:
-            continue
-        break
+    while time.perf_counter() - t0 < min_s:
+        b, hq = divmod(heads % total, w.heads_q)
+        hk = hq // G
+        Wh = W[0 if w.heads_w == 1 else hk]
+        O.favor_head(Q[b, hq], K[b, hk], V[b, hk], Wh, causal=w.causal)
+        heads += 1
     secs = time.perf_counter() - t0
     return {"value": heads * w.seq_len / secs, "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{heads} of {w.batch * w.heads_q} (batch, head) slices, L={w.seq_len}, "
-                      f"float64 NumPy, {secs:.1f} s on the host CPU",
+            "sample": f"{heads} (batch, head) slices of L={w.seq_len} ({heads / total:.2f} passes over the "
+                      f"workload's {total}), float64 NumPy, {secs:.1f} s on the host CPU",
             "cpu": _cpu_model()}
 
 
@@ -168,7 +164,7 @@ def main():
     ap.add_argument("--workload", default="c2_bidir_bf16")
     ap.add_argument("--chunk", type=int, default=0, help="causal chunk (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle time")
+    ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (at least)")
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the timed steps, one device copy of this many MiB (counter calibration)")
     ap.add_argument("--out", default="", help="also append the JSON line to this file")
