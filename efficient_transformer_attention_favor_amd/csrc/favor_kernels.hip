@@ -971,27 +971,20 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
     float den[QN], M[QN];  // den: this lane's half of the features
 
     // Feature exponents of tile ft, features x queries, lane = query:
-    // W_ft Q^T + c'_f [- M].  Two accumulators per query tile (even and odd contraction
-    // chunks) halve the dependent MFMA chain.
+    // W_ft Q^T + c'_f [- M] (one accumulator chain; the other wave on the SIMD and the
+    // readout products of the previous tile fill the MFMA pipe meanwhile).
     auto c1_tile = [&](int ft, f32x16 (&c1)[QN], bool with_m) {
-      f32x16 c2[QN];
 #pragma unroll
-      for (int q = 0; q < QN; ++q) c1[q] = c2[q] = zero16();
+      for (int q = 0; q < QN; ++q) c1[q] = zero16();
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) {
         const f16x8 a = load_frag_k(&Wl[(32 * ft + col) * LDW], kc, g);
 #pragma unroll
-        for (int q = 0; q < QN; ++q) {
-          if (kc & 1) c2[q] = mma(a, qf[q][kc], c2[q]);
-          else c1[q] = mma(a, qf[q][kc], c1[q]);
-        }
+        for (int q = 0; q < QN; ++q) c1[q] = mma(a, qf[q][kc], c1[q]);
       }
       const f16x8 ba = Cb[2 * (32 * ft + col) + g];
 #pragma unroll
-      for (int q = 0; q < QN; ++q) {
-        c2[q] = mma(ba, qbias_cols(M[q], g, with_m), c2[q]);
-        c1[q] += c2[q];
-      }
+      for (int q = 0; q < QN; ++q) c1[q] = mma(ba, qbias_cols(M[q], g, with_m), c1[q]);
     };
     // phi' = 2^(c1 - sub) rounded to bf16: den += sum of phi' (the same bf16 values the
     // numerator uses, summed in fp32 by dot2 against (1, 1)), acc += (S_v / S_1)_ft^T phi'.

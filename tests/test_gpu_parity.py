@@ -66,6 +66,7 @@ SMALL_CAUSAL = [
     _small("c3_causal_bf16", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=33, num_features=128),
     _small("c3_causal_bf16", batch=2, heads_q=4, heads_kv=2, heads_w=2, seq_len=200),
     _small("c3_causal_bf16", batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=300, head_dim=128),
+    _small("c3_causal_bf16", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=270, head_dim=128),
     _small("c5_causal_long_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=700),
     _small("c3_causal_bf16", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=257, num_features=192),
     _small("c1_bidir_f32", causal=True, seq_len=257),
