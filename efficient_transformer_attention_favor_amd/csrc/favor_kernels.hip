@@ -1416,7 +1416,7 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
       }
 
     // this wave's partial to LDS (D values, den, row maximum per query), then the
-    // cross-wave sum; one reduction item = (query, 8 value columns).
+    // cross-wave sum; one reduction item = (query, 4 value columns), spread over all threads.
 #pragma unroll
     for (int qh = 0; qh < QSPLIT; ++qh) {
       const int qrow = col - qh * QR;
@@ -1434,32 +1434,32 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
         }
       }
       __syncthreads();
-      for (int it = threadIdx.x; it < QR * (D / 8); it += blockDim.x) {
-        const int q = it / (D / 8), c0 = (it % (D / 8)) * 8;
+      for (int it = threadIdx.x; it < QR * (D / 4); it += blockDim.x) {
+        const int q = it / (D / 4), c0 = (it % (D / 4)) * 4;
         const int pos = p0 + qh * QR + q;
         if (pos >= L) continue;
         float M = -INFINITY;
         for (int w = 0; w < nw; ++w) M = fmaxf(M, Red[w][q * LDR + D + 1]);
-        float den = 0.f, acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float den = 0.f;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int w = 0; w < nw; ++w) {
           const float* rw = Red[w] + q * LDR;
-          const float sc = fast_exp2(rw[D + 1] - M);
-          den += sc * rw[D];
+          const float2 dm = *reinterpret_cast<const float2*>(rw + D);  // den, row maximum
+          const f32x4 v = *reinterpret_cast<const f32x4*>(rw + c0);
+          const float sc = fast_exp2(dm.y - M);
+          den += sc * dm.x;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) acc[i] += sc * rw[c0 + i];
+          for (int i = 0; i < 4; ++i) acc[i] += sc * v[i];
         }
-        const float inv = 1.f / den;
+        const float inv = __builtin_amdgcn_rcpf(den);
         T* orow = Oh + (size_t)pos * D + c0;
         if constexpr (sizeof(T) == 2) {
-          bf16x8 o;
+          bf16x4_t o;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) o[i] = (bf16)(acc[i] * inv);
-          *reinterpret_cast<bf16x8*>(orow) = o;
+          for (int i = 0; i < 4; ++i) o[i] = (bf16)(acc[i] * inv);
+          *reinterpret_cast<bf16x4_t*>(orow) = o;
         } else {
-          f32x4 o0 = {acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
-          f32x4 o1 = {acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv};
-          *reinterpret_cast<f32x4*>(orow) = o0;
-          *reinterpret_cast<f32x4*>(orow + 4) = o1;
+          *reinterpret_cast<f32x4*>(orow) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
         }
       }
       if (QSPLIT > 1) __syncthreads();
