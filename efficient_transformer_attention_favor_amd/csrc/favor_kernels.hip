@@ -1302,6 +1302,9 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     }
   };
   if constexpr (PF) prefetch(p_begin);
+  // The carry (and first block) loads complete here: otherwise the compiler's wait for the
+  // carry registers, merged over the loop back edge, also waits for every later prefetch.
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   for (int p0 = p_begin; p0 < p_end; p0 += 32) {
     __syncthreads();
     if constexpr (PF) {
