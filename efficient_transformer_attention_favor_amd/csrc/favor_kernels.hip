@@ -1195,8 +1195,11 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
                          : BASE_LDS + NWMAX * 16 * LDR * 4 <= 160 * 1024 ? 2
                                                                          : 4;
   constexpr int QR = 32 / QSPLIT;
-  __shared__ __attribute__((aligned(16))) T Ql[32 * LDK];
-  __shared__ __attribute__((aligned(16))) T Kl[32 * LDK];
+  // Q and K are staged already in the W-contraction type (fp16 for bf16 problems), once
+  // per workgroup instead of once per wave.
+  using WE = typename P::welem;
+  __shared__ __attribute__((aligned(16))) WE Ql[32 * LDK];
+  __shared__ __attribute__((aligned(16))) WE Kl[32 * LDK];
   __shared__ __attribute__((aligned(16))) T Vl[32 * LDV];
   __shared__ __attribute__((aligned(16))) T Pk[NWMAX][FW * LDP];
   __shared__ __attribute__((aligned(16))) float Red[NWMAX][QR * LDR];
@@ -1274,11 +1277,10 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
       }
     }
   };
-  auto put = [&](T* dst, int ld, const f32x4& v, int row, int c0) {
-    T* drow = dst + row * ld;
-    if (sizeof(T) == 2) {
-      *reinterpret_cast<float2*>(drow + c0) = float2{v[0], v[1]};
-      *reinterpret_cast<float2*>(drow + c0 + EPC / 2) = float2{v[2], v[3]};
+  auto put = [&](WE* dst, int ld, const f32x4& v, int row, int c0) {
+    WE* drow = dst + row * ld;
+    if constexpr (sizeof(T) == 2) {
+      *reinterpret_cast<wfrag*>(drow + c0) = to_wfrag(__builtin_bit_cast(frag, v));
     } else {
       float* d = reinterpret_cast<float*>(drow + c0);
       d[0] = v[0];
@@ -1320,8 +1322,16 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
       }
       if (p0 + 32 < p_end) prefetch(p0 + 32);
     } else {
-      stage_rows<T, D, false>(Ql, LDK, Qh, p0, L);
-      stage_rows<T, D, false>(Kl, LDK, Kh, p0, L);
+      for (int c = threadIdx.x; c < NCH; c += blockDim.x) {
+        const int row = c / CPR, c0 = (c % CPR) * EPC;
+        f32x4 q = {0.f, 0.f, 0.f, 0.f}, kk = {0.f, 0.f, 0.f, 0.f};
+        if (p0 + row < L) {
+          q = *reinterpret_cast<const f32x4*>(Qh + (size_t)(p0 + row) * D + c0);
+          kk = *reinterpret_cast<const f32x4*>(Kh + (size_t)(p0 + row) * D + c0);
+        }
+        put(Ql, LDK, q, row, c0);
+        put(Kl, LDK, kk, row, c0);
+      }
       stage_rows<T, D, true>(Vl, LDV, Vh, p0, L);
     }
     __syncthreads();
@@ -1329,7 +1339,7 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     // phi_Q of this wave's features: C = W_w Q^T (features x queries), lane = query.
     wfrag qf[NKC];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) qf[kc] = to_wfrag(load_frag_k(Ql + col * LDK, kc, g));
+    for (int kc = 0; kc < NKC; ++kc) qf[kc] = load_frag_k(Ql + col * LDK, kc, g);
     f32x16 cq[NTC];
 #pragma unroll
     for (int nt = 0; nt < NTC; ++nt) {
@@ -1355,7 +1365,7 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     // phi_K of this wave's features: C = K W_w^T (keys x features), lane = feature.
     wfrag kf[NKC];
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) kf[kc] = to_wfrag(load_frag_k(Kl + col * LDK, kc, g));
+    for (int kc = 0; kc < NKC; ++kc) kf[kc] = load_frag_k(Kl + col * LDK, kc, g);
     float nrm = sumsq(kf);
     nrm += partner32(nrm);
     const wfrag biasA = bias_rows(0.5f * kLog2e * nrm, g, wfrag{});
