@@ -1368,7 +1368,8 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     for (int kc = 0; kc < NKC; ++kc) kf[kc] = load_frag_k(Kl + col * LDK, kc, g);
     float nrm = sumsq(kf);
     nrm += partner32(nrm);
-    const wfrag biasA = bias_rows(0.5f * kLog2e * nrm, g, wfrag{});
+    // keys past L (zero rows in LDS) get the masking row bias: their features are exactly 0
+    const wfrag biasA = bias_rows(p0 + col < L ? 0.5f * kLog2e * nrm : kMaskedRow, g, wfrag{});
     frag ka[NTC][P::NF32];
 #pragma unroll
     for (int nt = 0; nt < NTC; ++nt) {
@@ -1378,17 +1379,27 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
       ck = mma(biasA, biasB, ck);
       f32x16 e;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = p0 + 8 * (r >> 2) + 4 * g + (r & 3);
-        e[r] = key < L ? fast_exp2(ck[r]) : 0.f;
-      }
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(ck[r]);
       acc_to_frags(e, ka[nt]);
-      // phi_K to LDS as [feature][key] for the transposed read below
+      // phi_K to LDS as [feature][key] for the transposed read below (the operand values:
+      // register r holds key 8(r/4) + 4g + r%4)
+      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        T* dst = pk + (32 * nt + col) * LDP + 8 * r4 + 4 * g;
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dst[i] = (T)e[4 * r4 + i];
+          for (int hh = 0; hh < 2; ++hh) {
+            bf16x4_t v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = ka[nt][h][4 * hh + i];
+            *reinterpret_cast<bf16x4_t*>(pk + (32 * nt + col) * LDP + 8 * (2 * h + hh) + 4 * g) = v;
+          }
+      } else {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          T* dst = pk + (32 * nt + col) * LDP + 8 * r4 + 4 * g;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) dst[i] = e[4 * r4 + i];
+        }
       }
     }
 
