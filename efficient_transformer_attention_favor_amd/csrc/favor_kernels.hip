@@ -98,7 +98,7 @@ __device__ __forceinline__ void stage_rows(T* dst, int ld, const T* src, int p0,
 template <class T, int D> struct KvCfg;
 template <> struct KvCfg<bf16, 64> { static constexpr int KW = 4, NTW = 2; };
 template <> struct KvCfg<bf16, 128> { static constexpr int KW = 4, NTW = 1; };
-template <> struct KvCfg<float, 64> { static constexpr int KW = 4, NTW = 2; };
+template <> struct KvCfg<float, 64> { static constexpr int KW = 4, NTW = 1; };
 template <> struct KvCfg<float, 128> { static constexpr int KW = 4, NTW = 1; };
 
 // With one range per kv head and bf16 data (img_s != nullptr) the workgroup writes, instead
@@ -506,7 +506,7 @@ template <int D> struct ReadoutCfg<float, D> {
   static constexpr int LDW = D + 1;
   static constexpr int LDS = MP + 1;
   static constexpr int NWAVE = 4;
-  static constexpr int QN = D == 64 ? 2 : 1;
+  static constexpr int QN = 1;  // f32 MFMAs are slow: more waves, shorter chains
 };
 
 // position of feature fi (0..31 within a tile) in the S^T LDS row
