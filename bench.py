@@ -168,6 +168,10 @@ def main():
     ap.add_argument("--copy-probe-mb", type=int, default=0,
                     help="after the timed steps, one device copy of this many MiB (counter calibration)")
     ap.add_argument("--out", default="", help="also append the JSON line to this file")
+    ap.add_argument("--decode", action="store_true",
+                    help="time favor_attn_decode (one new position per head per step) on the workload's "
+                         "head layout instead of the forward pass")
+    ap.add_argument("--prefill", type=int, default=256, help="positions decoded before timing (--decode)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -184,6 +188,8 @@ def main():
 
     w = I.workload(args.workload)
     log(f"workload {w}")
+    if args.decode:
+        return decode_main(args, w)
     Q, K, V, W = I.make_inputs(w, seed=0)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
@@ -297,6 +303,111 @@ def main():
     if args.out:
         with open(args.out, "a") as f:
             f.write(line + "\n")
+
+
+def decode_main(args, w0):
+    """Decoding: the state holds --prefill positions, then each step adds one position per
+    (batch, kv head) and answers every query head.  Algorithmic bytes per step: the state
+    read and written once (float32 [B*Hkv][m][d+1]), W, and the new q, k, v and out rows."""
+    import numpy as np
+    import torch
+
+    from efficient_transformer_attention_favor_amd import _lib, api
+    from efficient_transformer_attention_favor_amd import inputs as I
+
+    n_pos = args.prefill + args.warmup + args.steps
+    w = w0.replace(seq_len=n_pos, causal=True)
+    Q, K, V, W = I.make_inputs(w, seed=0)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    # position-major copies so that one position's rows are contiguous
+    qs, ks, vs = (torch.from_numpy(np.ascontiguousarray(x.transpose(2, 0, 1, 3))).to(dev).to(dt) for x in (Q, K, V))
+    wd = torch.from_numpy(W).to(dev)
+    state = api.decode_state(qs[0], ks[0], wd)
+    out = torch.empty_like(qs[0])
+    p = api._decode_problem(qs[0], ks[0], wd)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(t):
+        st = _lib.attn_decode(p, qs[t].data_ptr(), ks[t].data_ptr(), vs[t].data_ptr(), wd.data_ptr(),
+                              state.data_ptr(), out.data_ptr(), stream.cuda_stream)
+        if st != _lib.FAVOR_OK:
+            raise _lib.FavorError(st, "favor_attn_decode")
+
+    for t in range(args.prefill + args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    t0 = args.prefill + args.warmup
+    start.record(stream)
+    for t in range(t0, t0 + args.steps):
+        step(t)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+
+    e = 2 if w.dtype == "bf16" else 4
+    B, Hq, Hkv, d, m = w.batch, w.heads_q, w.heads_kv, w.head_dim, w.num_features
+    alg_bytes = 2 * 4 * B * Hkv * m * (d + 1) + 4 * w.heads_w * m * d + e * d * (2 * B * Hq + 2 * B * Hkv)
+    achieved = alg_bytes / (ms_step * 1e-3) / 1e9
+    res = {
+        "metric": "FAVOR+ causal decode step tokens/s (B*Hq new positions per step), 1 GPU",
+        "value": round(B * Hq / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian q, k, v; orthogonal random features W)",
+        "config": {"workload": f"{w0.name} head layout, decode after {args.prefill} positions", "batch": B,
+                   "heads_q": Hq, "heads_kv": Hkv, "heads_w": w.heads_w, "head_dim": d, "num_features": m,
+                   "mode": "causal decode", "parallelism": "single GPU"},
+        "roofline": {"kernel": "decode_update+decode_readout", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "per_launch": {"alg_bytes": alg_bytes, "avg_ms": round(ms_step, 5)}},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_decode_baseline(w, Q, K, V, W, args)
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+def cpu_decode_baseline(w, Q, K, V, W, args, min_s=5.0):
+    """The oracle's feature map and summary update, one position at a time on the host."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle.favor_oracle as O
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    G = w.heads_q // w.heads_kv
+    B, Hkv, d, m = w.batch, w.heads_kv, w.head_dim, w.num_features
+    S = np.zeros((B, Hkv, m, d + 1))
+    t0 = time.perf_counter()
+    steps = 0
+    for t in range(w.seq_len):
+        for b in range(B):
+            for h in range(Hkv):
+                Wh = W[0 if w.heads_w == 1 else h]
+                pk = O.feature_map(K[b, h, t:t + 1], Wh)[0]
+                S[b, h] += np.outer(pk, np.append(V[b, h, t].astype(np.float64), 1.0))
+                pq = O.feature_map(Q[b, h * G:(h + 1) * G, t], Wh)
+                _ = (pq @ S[b, h, :, :d]) / (pq @ S[b, h, :, d])[:, None]
+        steps += 1
+        if time.perf_counter() - t0 >= min_s:
+            break
+    secs = time.perf_counter() - t0
+    return {"value": steps * w.batch * w.heads_q / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{steps} decode steps of {w.batch * w.heads_q} heads, float64 NumPy, {secs:.1f} s",
+            "cpu": _cpu_model()}
 
 
 if __name__ == "__main__":

@@ -24,7 +24,7 @@ FAVOR_CAUSAL = 1
 FAVOR_FWD_KERNELS = 3
 
 EXPORTED = ("favor_workspace_bytes", "favor_attn_fwd", "favor_attn_fwd_timed", "favor_features",
-            "favor_status_string", "favor_abi_version")
+            "favor_decode_state_bytes", "favor_attn_decode", "favor_status_string", "favor_abi_version")
 
 
 class FavorProblem(ctypes.Structure):
@@ -61,6 +61,10 @@ def lib() -> ctypes.CDLL:
         L.favor_attn_fwd_timed.restype = ctypes.c_int
         L.favor_features.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp]
         L.favor_features.restype = ctypes.c_int
+        L.favor_decode_state_bytes.argtypes = [P]
+        L.favor_decode_state_bytes.restype = ctypes.c_size_t
+        L.favor_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
+        L.favor_attn_decode.restype = ctypes.c_int
         L.favor_status_string.argtypes = [ctypes.c_int]
         L.favor_status_string.restype = ctypes.c_char_p
         L.favor_abi_version.argtypes = []
@@ -102,6 +106,14 @@ def attn_fwd_timed(p: FavorProblem, q, k, v, w, out, workspace, workspace_nbytes
 
 def features(p: FavorProblem, side, x, w, phi_out, c_out, stream) -> int:
     return int(lib().favor_features(_ref(p), int(side), x, w, phi_out, c_out, stream))
+
+
+def decode_state_bytes(p: FavorProblem) -> int:
+    return int(lib().favor_decode_state_bytes(_ref(p)))
+
+
+def attn_decode(p: FavorProblem, q, k, v, w, state, out, stream) -> int:
+    return int(lib().favor_attn_decode(_ref(p), q, k, v, w, state, out, stream))
 
 
 def abi_version() -> int:

@@ -94,3 +94,45 @@ def features(X, W, side, heads_q, heads_kv, stream=None):
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_features")
     return phi, c
+
+
+def _decode_problem(q, k, W):
+    if q.dim() != 3 or k.dim() != 3 or W.dim() != 3 or q.dtype not in _DTYPES:
+        raise ValueError("expected q (B, Hq, d), k and v (B, Hkv, d) in float32/bfloat16, W (Hw, m, d)")
+    B, Hq, d = q.shape
+    return _lib.problem(B, Hq, k.shape[1], W.shape[0], 1, d, W.shape[1], _DTYPES[q.dtype],
+                        _lib.FAVOR_CAUSAL, 0)
+
+
+def decode_state(q, k, W):
+    """A zero (empty) decoding state for queries like q (B, Hq, d) and keys like k (B, Hkv, d)."""
+    nbytes = _lib.decode_state_bytes(_decode_problem(q, k, W))
+    if nbytes == 0:
+        raise ValueError("unsupported decoding problem")
+    return torch.zeros(nbytes // 4, dtype=torch.float32, device=q.device)
+
+
+def attn_decode(q, k, v, W, state, out=None, stream=None):
+    """One causal decoding step: adds position (k, v) to `state` (from decode_state, updated
+    in place) and returns out (B, Hq, d) = the new position's attention output."""
+    if q.device.type != "cuda" or any(t.device != q.device for t in (k, v, W, state)):
+        raise ValueError("tensors must be on one GPU")
+    if k.dtype != q.dtype or v.dtype != q.dtype or W.dtype != torch.float32 or state.dtype != torch.float32:
+        raise ValueError("q, k, v share one dtype; W and the state are float32")
+    if k.shape != v.shape or k.shape[0] != q.shape[0] or k.shape[2] != q.shape[2] or W.shape[2] != q.shape[2]:
+        raise ValueError("k and v must be (B, Hkv, d) matching q, W (Hw, m, d)")
+    for name, t in (("q", q), ("k", k), ("v", v), ("W", W), ("state", state)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    p = _decode_problem(q, k, W)
+    if state.numel() * 4 < _lib.decode_state_bytes(p):
+        raise ValueError("state is smaller than favor_decode_state_bytes()")
+    if out is None:
+        out = torch.empty_like(q)
+    if stream is None:
+        stream = torch.cuda.current_stream(q.device)
+    st = _lib.attn_decode(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), state.data_ptr(),
+                          out.data_ptr(), stream.cuda_stream)
+    if st != _lib.FAVOR_OK:
+        raise _lib.FavorError(st, "favor_attn_decode")
+    return out

@@ -1,0 +1,223 @@
+// Causal decoding, one position per call (the favor_attn_decode entry point).
+//
+// "Rethinking Attention with Performers" (review page), section "제안 방법": attention in
+// linear order through positive random features, phi(x) = exp(W x - |x|^2/2 - c)/sqrt(m).
+// With the inclusive causal mask the summary of the positions seen so far,
+// S = sum_j phi(k_j) [v_j, 1]^T, is all a new query needs; "Fast Transformer Decoding: One
+// Write-Head is All You Need" (review page), "ABSTRACT": incremental decoding is bound by
+// reloading the key/value history, which this m x (d+1) summary per kv head replaces.
+//
+// Two small kernels per step:
+//   decode_update   kDecSplit workgroups per (batch, kv head), each updating one slice of
+//                   its summary (each recomputes the exponents and keeps its own copy of
+//                   c, which all slices advance identically): the new key's exponents
+//                   e_f = log2e (w_f.k - |k|^2/2), c' = max(c, max_f e_f),
+//                   S <- 2^(c - c') S + 2^(e - c') [v, 1]   (float32, VALU).
+//   decode_readout  one workgroup per (batch, query head): p_f = 2^(log2e w_f.q - M),
+//                   M the row maximum, out = sum_f p_f S_v,f / sum_f p_f S_1,f.
+// Both are latency-bound (a few hundred KB of state per call); the arithmetic is float32 on
+// the VALU, so bf16 problems round only their inputs and outputs.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "favor_device.hpp"
+#include "favor_plan.hpp"
+
+namespace favor {
+namespace {
+
+constexpr int kDecThreads = 256;
+constexpr int kDecSplit = 8;  // summary slices per (batch, kv head), one workgroup each
+
+template <class T> __device__ __forceinline__ float to_f(T x) { return (float)x; }
+
+// Block-wide maximum / sum over kDecThreads threads: within each wave by shuffles, then
+// across the waves through LDS (red: at least kDecThreads / 64 floats).
+__device__ __forceinline__ float block_max(float x, float* red) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x = fmaxf(x, __shfl_xor(x, s));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kDecThreads / 64; ++w) r = fmaxf(r, red[w]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float block_sum(float x, float* red) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int w = 1; w < kDecThreads / 64; ++w) r += red[w];
+  __syncthreads();
+  return r;
+}
+
+// w_f . x (log2e applied by the caller); x in LDS as float.
+template <int D>
+__device__ __forceinline__ float row_dot(const float* __restrict__ wrow, const float* x) {
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int i = 0; i < D; i += 4) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(wrow + i);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[j] = fmaf(w[j], x[i + j], acc[j]);
+  }
+  return (acc[0] + acc[1]) + (acc[2] + acc[3]);
+}
+
+template <class T, int D>
+__global__ void __launch_bounds__(kDecThreads)
+    decode_update(const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ W, int Hkv, int Hw,
+                  int m, float* __restrict__ S, float* __restrict__ cst) {
+  __shared__ float kl[D], vl[D + 1], phi[512], red[kDecThreads];
+  const int bh = blockIdx.x / kDecSplit, part = blockIdx.x % kDecSplit, hkv = bh % Hkv;
+  const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
+  const int t = threadIdx.x;
+  if (t < D) {
+    kl[t] = to_f(k[(size_t)bh * D + t]);
+    vl[t] = to_f(v[(size_t)bh * D + t]);
+  }
+  if (t == 0) vl[D] = 1.f;  // the ones column carries the normaliser
+  __syncthreads();
+  float nrm = 0.f;
+  if (t < D) nrm = kl[t] * kl[t];
+  nrm = block_sum(nrm, red);
+
+  float mx = -INFINITY;
+  for (int f = t; f < m; f += kDecThreads) {
+    const float e = kLog2e * (row_dot<D>(Wh + (size_t)f * D, kl) - 0.5f * nrm);
+    phi[f] = e;
+    mx = fmaxf(mx, e);
+  }
+  mx = block_max(mx, red);
+  const float c_old = cst[bh * kDecSplit + part];
+  const float c_new = fmaxf(c_old, mx);
+  const float scale = fast_exp2(c_old - c_new);
+  for (int f = t; f < m; f += kDecThreads) phi[f] = fast_exp2(phi[f] - c_new);
+  __syncthreads();
+
+  // this workgroup's slice of S [m][D+1] (m (D+1) / kDecSplit floats, a multiple of 4):
+  // 4 consecutive elements per thread and step, two steps' loads in flight
+  const int n = m * (D + 1) / kDecSplit;
+  float* Sh = S + (size_t)bh * m * (D + 1) + (size_t)part * n;
+  const int i_base = part * n;
+  auto upd = [&](int i, f32x4 x) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = i_base + i + u, f = e / (D + 1), j = e - f * (D + 1);
+      x[u] = fmaf(x[u], scale, phi[f] * vl[j]);
+    }
+    *reinterpret_cast<f32x4*>(Sh + i) = x;
+  };
+  int i = 4 * t;
+  for (; i + 4 * kDecThreads < n; i += 8 * kDecThreads) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(Sh + i);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(Sh + i + 4 * kDecThreads);
+    upd(i, a);
+    upd(i + 4 * kDecThreads, b);
+  }
+  if (i < n) upd(i, *reinterpret_cast<const f32x4*>(Sh + i));
+  if (t == 0) cst[bh * kDecSplit + part] = c_new;
+}
+
+template <class T, int D>
+__global__ void __launch_bounds__(kDecThreads)
+    decode_readout(const T* __restrict__ q, const float* __restrict__ W, const float* __restrict__ S, int Hq,
+                   int Hkv, int Hw, int m, T* __restrict__ out) {
+  constexpr int FG = kDecThreads / D;  // feature groups (threads per value column)
+  __shared__ float ql[D], p[512], red[kDecThreads], part[FG][D];
+  const int bhq = blockIdx.x, b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv);
+  const int bh = b * Hkv + hkv;
+  const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
+  const float* Sh = S + (size_t)bh * m * (D + 1);
+  const int t = threadIdx.x;
+  if (t < D) ql[t] = to_f(q[(size_t)bhq * D + t]);
+  __syncthreads();
+
+  float mx = -INFINITY;
+  for (int f = t; f < m; f += kDecThreads) {
+    const float e = kLog2e * row_dot<D>(Wh + (size_t)f * D, ql);
+    p[f] = e;
+    mx = fmaxf(mx, e);
+  }
+  mx = block_max(mx, red);  // the row stabiliser (cancels in the ratio)
+  float den = 0.f;
+  for (int f = t; f < m; f += kDecThreads) {
+    p[f] = fast_exp2(p[f] - mx);
+    den = fmaf(p[f], Sh[(size_t)f * (D + 1) + D], den);
+  }
+  den = block_sum(den, red);  // also orders the p[] writes before the reads below
+
+  // thread (fg, j): features fg, fg + FG, ... of value column j
+  const int j = t % D, fg = t / D;
+  // m / FG is a multiple of 16: 16 independent loads in flight per step
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int f = fg; f < m; f += 16 * FG) {
+    float sv[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) sv[u] = Sh[(size_t)(f + u * FG) * (D + 1) + j];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) acc[u & 3] = fmaf(p[f + u * FG], sv[u], acc[u & 3]);
+  }
+  part[fg][j] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+  __syncthreads();
+  if (t < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int g = 0; g < FG; ++g) s += part[g][t];
+    out[(size_t)bhq * D + t] = (T)(s / den);
+  }
+}
+
+template <class T, int D>
+favor_status run_decode(const Plan& s, const void* q, const void* k, const void* v, const float* W, float* state,
+                        void* out, hipStream_t st) {
+  float* S = state;
+  float* cst = state + (size_t)s.BH * s.m * (s.d + 1);
+  hipLaunchKernelGGL((decode_update<T, D>), dim3(s.BH * kDecSplit), dim3(kDecThreads), 0, st, static_cast<const T*>(k),
+                     static_cast<const T*>(v), W, s.Hkv, s.Hw, s.m, S, cst);
+  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  hipLaunchKernelGGL((decode_readout<T, D>), dim3(s.B * s.Hq), dim3(kDecThreads), 0, st,
+                     static_cast<const T*>(q), W, S, s.Hq, s.Hkv, s.Hw, s.m, static_cast<T*>(out));
+  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+favor_status decode_plan(const favor_problem* p, Plan* s) {
+  if (p == nullptr) return FAVOR_ERR_INVALID_ARG;
+  favor_problem one = *p;
+  one.chunk = 0;  // no segments in decoding
+  const favor_status st = make_plan(&one, s);
+  if (st != FAVOR_OK) return st;
+  if (p->mode != FAVOR_CAUSAL || p->seq_len != 1) return FAVOR_ERR_INVALID_ARG;
+  return FAVOR_OK;
+}
+
+}  // namespace
+}  // namespace favor
+
+extern "C" size_t favor_decode_state_bytes(const favor_problem* p) {
+  favor::Plan s;
+  if (favor::decode_plan(p, &s) != FAVOR_OK) return 0;
+  const size_t n = (size_t)s.BH * s.m * (s.d + 1) + (size_t)s.BH * favor::kDecSplit;
+  return (n * sizeof(float) + 255) & ~size_t(255);
+}
+
+extern "C" favor_status favor_attn_decode(const favor_problem* p, const void* q, const void* k, const void* v,
+                                          const float* W, float* state, void* out, void* stream) {
+  favor::Plan s;
+  const favor_status st = favor::decode_plan(p, &s);
+  if (st != FAVOR_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || W == nullptr || state == nullptr || out == nullptr)
+    return FAVOR_ERR_INVALID_ARG;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (s.dtype == FAVOR_BF16)
+    return s.d == 64 ? favor::run_decode<favor::bf16, 64>(s, q, k, v, W, state, out, hs)
+                     : favor::run_decode<favor::bf16, 128>(s, q, k, v, W, state, out, hs);
+  return s.d == 64 ? favor::run_decode<float, 64>(s, q, k, v, W, state, out, hs)
+                   : favor::run_decode<float, 128>(s, q, k, v, W, state, out, hs);
+}

@@ -116,6 +116,32 @@ favor_status favor_attn_fwd_timed(const favor_problem* p, const void* Q, const v
 favor_status favor_features(const favor_problem* p, int32_t side, const void* X, const float* W,
                             float* phi_out, float* c_out, void* stream);
 
+/* Causal decoding, one new position per (batch, head) per call.
+ *
+ * The causal mode is a running sum over positions (FAVOR+ in linear order, Performer page,
+ * "제안 방법"; the inclusive mask j <= i), so one step of incremental decoding needs only
+ * the summary of the positions so far, an m x (d+1) matrix per kv head, instead of the
+ * whole key/value history whose reloading bounds incremental decoding (MQA page,
+ * "ABSTRACT"; under multi-query heads one summary serves all G query heads of a kv head).
+ *
+ * State (device memory, caller-owned, favor_decode_state_bytes(p) bytes, 256-byte
+ * aligned): float32 S[batch*heads_kv][m][d+1] followed by float32 c[batch*heads_kv][8]
+ * (eight equal copies, one per slice of S that is updated in parallel), with
+ *   S = sum_{j so far} 2^(e_j - c) [v_j, 1],  e_j,f = log2(e) (w_f . k_j - |k_j|^2 / 2),
+ * i.e. the summary in log2 units, scaled by 2^-c (c only ever grows; S is rescaled when it
+ * does).  A zero-filled buffer is the empty state.
+ *
+ * favor_attn_decode: q [batch][heads_q][d], k and v [batch][heads_kv][d] (the new
+ * position), W as for favor_attn_fwd, out [batch][heads_q][d] (device pointers; q, k, v,
+ * out in p->dtype).  p->mode must be FAVOR_CAUSAL and p->seq_len 1; p->chunk is ignored.
+ * Adds the new position to the state, then writes out = phi(q) S_v / phi(q) S_1 (so the
+ * new position attends to itself and to every earlier one).  Queues 2 kernels on
+ * `stream`; concurrent calls on one state race.  Errors as for favor_attn_fwd (a null
+ * pointer is FAVOR_ERR_INVALID_ARG; nothing is queued on an error). */
+size_t favor_decode_state_bytes(const favor_problem* p);
+favor_status favor_attn_decode(const favor_problem* p, const void* q, const void* k, const void* v,
+                               const float* W, float* state, void* out, void* stream);
+
 /* Static description of a status code; never NULL. */
 const char* favor_status_string(favor_status s);
 

@@ -85,3 +85,23 @@ def test_status_strings():
     for s in range(5):
         assert isinstance(_lib.status_string(s), str) and _lib.status_string(s)
     assert _lib.status_string(99) == "unknown status"
+
+
+def test_decode_validation():
+    """favor_attn_decode takes causal problems of one position; its state size is the
+    summaries [B*Hkv][m][d+1] plus one stabiliser per kv head, 256-byte aligned."""
+    p = _p(mode=_lib.FAVOR_CAUSAL, seq_len=1, chunk=48)  # the chunk is ignored when decoding
+    n = _lib.decode_state_bytes(p)
+    assert n == ((2 * 2 * 128 * 65 + 2 * 2 * 8) * 4 + 255) // 256 * 256
+    assert _lib.decode_state_bytes(_p(seq_len=1)) == 0                       # bidirectional
+    assert _lib.decode_state_bytes(_p(mode=_lib.FAVOR_CAUSAL, seq_len=2)) == 0
+    assert _lib.attn_decode(_p(seq_len=1), 8, 8, 8, 8, 256, 8, None) == _lib.FAVOR_ERR_INVALID_ARG
+    assert _lib.attn_decode(_p(mode=_lib.FAVOR_CAUSAL, seq_len=3), 8, 8, 8, 8, 256, 8, None) == \
+        _lib.FAVOR_ERR_INVALID_ARG
+    assert _lib.attn_decode(_p(mode=_lib.FAVOR_CAUSAL, seq_len=1, head_dim=32), 8, 8, 8, 8, 256, 8, None) == \
+        _lib.FAVOR_ERR_UNSUPPORTED
+    for i in range(6):
+        args = [8, 8, 8, 8, 256, 8]
+        args[i] = None
+        assert _lib.attn_decode(p, *args, None) == _lib.FAVOR_ERR_INVALID_ARG
+    assert _lib.attn_decode(None, 8, 8, 8, 8, 256, 8, None) == _lib.FAVOR_ERR_INVALID_ARG
