@@ -73,7 +73,7 @@ __device__ __forceinline__ float row_dot(const float* __restrict__ wrow, const f
 template <class T, int D>
 __global__ void __launch_bounds__(kDecThreads)
     decode_update(const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ W, int Hkv, int Hw,
-                  int m, float* __restrict__ S, float* __restrict__ cst) {
+                  int m, float* __restrict__ S, float* __restrict__ cst, unsigned* __restrict__ count) {
   __shared__ float kl[D], vl[D + 1], phi[512], red[kDecThreads];
   const int bh = blockIdx.x / kDecSplit, part = blockIdx.x % kDecSplit, hkv = bh % Hkv;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
@@ -95,7 +95,10 @@ __global__ void __launch_bounds__(kDecThreads)
     mx = fmaxf(mx, e);
   }
   mx = block_max(mx, red);
-  const float c_old = cst[bh * kDecSplit + part];
+  // an empty state (no position yet) takes the new key's maximum as its constant; after
+  // that c only grows, so S never overflows and never has to be scaled up
+  const unsigned seen = count[bh * kDecSplit + part];
+  const float c_old = seen ? cst[bh * kDecSplit + part] : mx;
   const float c_new = fmaxf(c_old, mx);
   const float scale = fast_exp2(c_old - c_new);
   for (int f = t; f < m; f += kDecThreads) phi[f] = fast_exp2(phi[f] - c_new);
@@ -122,7 +125,10 @@ __global__ void __launch_bounds__(kDecThreads)
     upd(i + 4 * kDecThreads, b);
   }
   if (i < n) upd(i, *reinterpret_cast<const f32x4*>(Sh + i));
-  if (t == 0) cst[bh * kDecSplit + part] = c_new;
+  if (t == 0) {
+    cst[bh * kDecSplit + part] = c_new;
+    count[bh * kDecSplit + part] = seen + 1u;
+  }
 }
 
 template <class T, int D>
@@ -179,8 +185,9 @@ favor_status run_decode(const Plan& s, const void* q, const void* k, const void*
                         void* out, hipStream_t st) {
   float* S = state;
   float* cst = state + (size_t)s.BH * s.m * (s.d + 1);
+  unsigned* count = reinterpret_cast<unsigned*>(cst + (size_t)s.BH * kDecSplit);
   hipLaunchKernelGGL((decode_update<T, D>), dim3(s.BH * kDecSplit), dim3(kDecThreads), 0, st, static_cast<const T*>(k),
-                     static_cast<const T*>(v), W, s.Hkv, s.Hw, s.m, S, cst);
+                     static_cast<const T*>(v), W, s.Hkv, s.Hw, s.m, S, cst, count);
   if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
   hipLaunchKernelGGL((decode_readout<T, D>), dim3(s.B * s.Hq), dim3(kDecThreads), 0, st,
                      static_cast<const T*>(q), W, S, s.Hq, s.Hkv, s.Hw, s.m, static_cast<T*>(out));
@@ -203,7 +210,7 @@ favor_status decode_plan(const favor_problem* p, Plan* s) {
 extern "C" size_t favor_decode_state_bytes(const favor_problem* p) {
   favor::Plan s;
   if (favor::decode_plan(p, &s) != FAVOR_OK) return 0;
-  const size_t n = (size_t)s.BH * s.m * (s.d + 1) + (size_t)s.BH * favor::kDecSplit;
+  const size_t n = (size_t)s.BH * s.m * (s.d + 1) + 2 * (size_t)s.BH * favor::kDecSplit;
   return (n * sizeof(float) + 255) & ~size_t(255);
 }
 

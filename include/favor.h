@@ -125,11 +125,12 @@ favor_status favor_features(const favor_problem* p, int32_t side, const void* X,
  * "ABSTRACT"; under multi-query heads one summary serves all G query heads of a kv head).
  *
  * State (device memory, caller-owned, favor_decode_state_bytes(p) bytes, 256-byte
- * aligned): float32 S[batch*heads_kv][m][d+1] followed by float32 c[batch*heads_kv][8]
- * (eight equal copies, one per slice of S that is updated in parallel), with
+ * aligned): float32 S[batch*heads_kv][m][d+1], float32 c[batch*heads_kv][8] and uint32
+ * n[batch*heads_kv][8] (eight equal copies, one per slice of S updated in parallel), with
  *   S = sum_{j so far} 2^(e_j - c) [v_j, 1],  e_j,f = log2(e) (w_f . k_j - |k_j|^2 / 2),
- * i.e. the summary in log2 units, scaled by 2^-c (c only ever grows; S is rescaled when it
- * does).  A zero-filled buffer is the empty state.
+ * i.e. the summary in log2 units scaled by 2^-c, and n the number of positions added.  c
+ * starts at the first key's largest exponent and only grows (S is rescaled when it does).
+ * A zero-filled buffer is the empty state.
  *
  * favor_attn_decode: q [batch][heads_q][d], k and v [batch][heads_kv][d] (the new
  * position), W as for favor_attn_fwd, out [batch][heads_q][d] (device pointers; q, k, v,

@@ -92,7 +92,7 @@ def test_decode_validation():
     summaries [B*Hkv][m][d+1] plus one stabiliser per kv head, 256-byte aligned."""
     p = _p(mode=_lib.FAVOR_CAUSAL, seq_len=1, chunk=48)  # the chunk is ignored when decoding
     n = _lib.decode_state_bytes(p)
-    assert n == ((2 * 2 * 128 * 65 + 2 * 2 * 8) * 4 + 255) // 256 * 256
+    assert n == ((2 * 2 * 128 * 65 + 2 * 2 * 8 * 2) * 4 + 255) // 256 * 256
     assert _lib.decode_state_bytes(_p(seq_len=1)) == 0                       # bidirectional
     assert _lib.decode_state_bytes(_p(mode=_lib.FAVOR_CAUSAL, seq_len=2)) == 0
     assert _lib.attn_decode(_p(seq_len=1), 8, 8, 8, 8, 256, 8, None) == _lib.FAVOR_ERR_INVALID_ARG

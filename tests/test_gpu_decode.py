@@ -88,9 +88,12 @@ def test_decode_state_is_the_summary():
     st = state.cpu().numpy().astype(np.float64)
     BH, m, d = w.batch * w.heads_kv, w.num_features, w.head_dim
     S = st[:BH * m * (d + 1)].reshape(BH, m, d + 1)
-    cs = st[BH * m * (d + 1):BH * m * (d + 1) + 8 * BH].reshape(BH, 8)
+    off = BH * m * (d + 1)
+    cs = st[off:off + 8 * BH].reshape(BH, 8)
     assert (cs == cs[:, :1]).all()  # one copy per summary slice, all advanced alike
     c = cs[:, 0]
+    n = state.cpu()[off + 8 * BH:off + 16 * BH].view(torch.int32).numpy()
+    assert (n == w.seq_len).all()
     for bh in range(BH):
         b, h = divmod(bh, w.heads_kv)
         Wh = W[0 if w.heads_w == 1 else h]
@@ -121,3 +124,17 @@ def test_decode_full_width_sampled():
     err = O.rowwise_rel_err(got, ref)
     _say(f"  c3 layout, 64 positions: rowwise rel err {err:.3e}")
     assert err <= TOL["bf16"]
+
+
+def test_decode_keys_far_below_zero():
+    """Keys of large norm (x 8, exact in bf16): every feature exponent is far below 0 (below
+    the float32 range as a power of 2), so the state's constant must come from the first key."""
+    w = CASES[0]
+    Q, K, V, W = I.make_inputs(w, seed=4)
+    K = K * np.float32(8)
+    got, _ = _decode_all(w, Q, K, V, W)
+    ref = O.favor_attention(Q, K, V, W, causal=True)
+    err = O.rowwise_rel_err(got, ref)
+    _say(f"  large keys: rowwise rel err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL[w.dtype]
