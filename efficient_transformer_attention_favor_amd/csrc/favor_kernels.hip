@@ -807,7 +807,7 @@ template <int D> struct RoBf16 {
   static constexpr int LDW = D + 8;               // fp16 W rows
   static constexpr int LDSS = MP + 8;             // bf16 S'^T rows
   static constexpr int NWAVE = 8;                 // waves per workgroup
-  static constexpr int QN = D == 64 ? 2 : 1;      // 32-row query tiles per wave and chunk
+  static constexpr int QN = 1;  // 32-row query tiles per wave and chunk (more, shorter chunks)
 };
 
 // B operand of the query bias MFMA: picks up c_f (A slots 0-2) and adds -M (slots 3-5).
