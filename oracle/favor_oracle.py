@@ -162,6 +162,70 @@ def favor_rows(Q, K, V, W, rows, causal=False):
     return out
 
 
+def favor_head_grads(q, k, v, W, dout):
+    """Gradients of sum(dout * out) for bidirectional FAVOR+ on one head, out = favor_head(q, k, v, W).
+
+    Written out from the linear-order definition by the chain rule (the pages give no
+    backward pass; W is a fixed input).  With phi = feature_map, S_v = phi(K)^T V,
+    S_1 = phi(K)^T 1, D_i = phi(q_i) . S_1 and out_i = phi(q_i) S_v / D_i:
+        g_i = dout_i / D_i,   h_i = -(dout_i . out_i) / D_i
+        dphi(q_i) = S_v g_i + S_1 h_i
+        dS_v = sum_i phi(q_i) g_i^T,   dS_1 = sum_i phi(q_i) h_i
+        dphi(k_j) = dS_v v_j + dS_1,   dv_j = dS_v^T phi(k_j)
+    and, since d phi(x)_f / dx = phi(x)_f (w_f - x),
+        dx = W^T (dphi * phi) - x sum_f (dphi * phi)_f.
+    Returns (dq (Lq, d), dk (L, d), dv (L, d)) in float64.
+    """
+    q = np.asarray(q, dtype=_F)
+    k = np.asarray(k, dtype=_F)
+    v = np.asarray(v, dtype=_F)
+    W = np.asarray(W, dtype=_F)
+    dout = np.asarray(dout, dtype=_F)
+    pq = feature_map(q, W)
+    pk = feature_map(k, W)
+    Sv, S1 = kv_summary(pk, v)
+    D = pq @ S1
+    out = (pq @ Sv) / D[:, None]
+    g = dout / D[:, None]
+    h = -np.sum(dout * out, axis=1) / D
+    dpq = g @ Sv.T + np.outer(h, S1)
+    dSv = pq.T @ g
+    dS1 = pq.T @ h
+    dpk = v @ dSv.T + dS1[None, :]
+    dv = pk @ dSv
+
+    def through_features(x, dphi, phi):
+        t = dphi * phi
+        return t @ W - x * t.sum(axis=1)[:, None]
+
+    return through_features(q, dpq, pq), through_features(k, dpk, pk), dv
+
+
+def favor_grads(Q, K, V, W, dOut):
+    """Gradients (dQ, dK, dV) of sum(dOut * favor_attention(Q, K, V, W)), bidirectional, with
+    the MQA head map: a kv head's dK and dV sum over the query heads that read it."""
+    B, Hq, L, d = Q.shape
+    Hkv, Hw = K.shape[1], W.shape[0]
+    kv_of, w_of = head_maps(Hq, Hkv, Hw)
+    G = Hq // Hkv
+    dQ = np.empty(Q.shape)
+    dK = np.zeros(K.shape)
+    dV = np.zeros(V.shape)
+    for b in range(B):
+        for hk in range(Hkv):
+            heads = [hq for hq in range(Hq) if kv_of[hq] == hk]
+            # the G query heads of a kv head form one longer query sequence over the same S
+            q = np.concatenate([Q[b, hq] for hq in heads])
+            do = np.concatenate([dOut[b, hq] for hq in heads])
+            dq, dk, dv = favor_head_grads(q, K[b, hk], V[b, hk], W[w_of[hk]], do)
+            for n, hq in enumerate(heads):
+                dQ[b, hq] = dq[n * L:(n + 1) * L]
+            dK[b, hk] += dk
+            dV[b, hk] += dv
+    assert G == len(heads)
+    return dQ, dK, dV
+
+
 def softmax_head(q, k, v, causal=False):
     """Exact softmax attention softmax(q k^T) v on one head (no 1/sqrt(d): the data carry it)."""
     q, k, v = (np.asarray(t, dtype=_F) for t in (q, k, v))

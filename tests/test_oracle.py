@@ -319,3 +319,61 @@ def test_planted_mistakes_fail():
     weights = a.sum(axis=1)
     assert np.allclose(good[0], weights / weights.sum(), atol=1e-14)
     assert not np.allclose(bad[0], weights / weights.sum(), atol=1e-6)
+
+
+# ---- backward (gradients of sum(dout * out), bidirectional) --------------------------
+
+def _loss(Q, K, V, W, dOut):
+    return float(np.sum(dOut * O.favor_attention(Q, K, V, W)))
+
+
+@pytest.mark.parametrize("Hq,Hkv,Hw", [(1, 1, 1), (4, 2, 2), (4, 1, 1)])
+def test_grads_match_central_differences(Hq, Hkv, Hw):
+    """Pin: the written-out gradients agree with central differences of the forward oracle
+    along random directions (float64, step 1e-5: truncation error ~1e-10)."""
+    rng = np.random.default_rng(11)
+    B, L, d, m = 2, 7, 4, 12
+    Q = rng.standard_normal((B, Hq, L, d)) * d ** -0.25
+    K = rng.standard_normal((B, Hkv, L, d)) * d ** -0.25
+    V = rng.standard_normal((B, Hkv, L, d))
+    W = np.stack([orf_matrix(m, d, rng) for _ in range(Hw)])
+    dOut = rng.standard_normal((B, Hq, L, d))
+    dQ, dK, dV = O.favor_grads(Q, K, V, W, dOut)
+    eps = 1e-5
+    for _ in range(3):
+        uq, uk, uv = (rng.standard_normal(x.shape) for x in (Q, K, V))
+        fd = (_loss(Q + eps * uq, K + eps * uk, V + eps * uv, W, dOut)
+              - _loss(Q - eps * uq, K - eps * uk, V - eps * uv, W, dOut)) / (2 * eps)
+        an = np.sum(dQ * uq) + np.sum(dK * uk) + np.sum(dV * uv)
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+    # each input separately, so a mistake in one gradient cannot hide behind another
+    for which in range(3):
+        u = [np.zeros_like(x) for x in (Q, K, V)]
+        u[which] = rng.standard_normal(u[which].shape)
+        fd = (_loss(Q + eps * u[0], K + eps * u[1], V + eps * u[2], W, dOut)
+              - _loss(Q - eps * u[0], K - eps * u[1], V - eps * u[2], W, dOut)) / (2 * eps)
+        an = np.sum((dQ, dK, dV)[which] * u[which])
+        assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
+
+
+def test_grad_of_values_is_the_attention_transpose():
+    """dV = A_hat_norm^T dout, with A_hat_norm = D^-1 phi(Q) phi(K)^T (the output is linear in V)."""
+    rng = np.random.default_rng(12)
+    L, d, m = 9, 4, 16
+    q, k, v = rng.standard_normal((3, L, d)) * 0.7
+    W = orf_matrix(m, d, rng)
+    dout = rng.standard_normal((L, d))
+    A = O.implied_attention(q, k, W)
+    A = A / A.sum(axis=1, keepdims=True)
+    _, _, dv = O.favor_head_grads(q, k, v, W, dout)
+    assert np.max(np.abs(dv - A.T @ dout)) < 1e-12
+
+
+def test_grads_vanish_for_constant_values():
+    """V = 1: the output is identically 1 whatever Q and K are, so dQ = dK = 0."""
+    rng = np.random.default_rng(13)
+    L, d, m = 6, 4, 8
+    q, k = rng.standard_normal((2, L, d)) * 0.7
+    W = orf_matrix(m, d, rng)
+    dq, dk, _ = O.favor_head_grads(q, k, np.ones((L, d)), W, rng.standard_normal((L, d)))
+    assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
