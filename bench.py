@@ -172,6 +172,8 @@ def main():
                     help="time favor_attn_decode (one new position per head per step) on the workload's "
                          "head layout instead of the forward pass")
     ap.add_argument("--prefill", type=int, default=256, help="positions decoded before timing (--decode)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time favor_attn_bwd (gradients of Q, K, V; bidirectional workloads) instead of the forward")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -190,6 +192,8 @@ def main():
     log(f"workload {w}")
     if args.decode:
         return decode_main(args, w)
+    if args.backward:
+        return backward_main(args, w)
     Q, K, V, W = I.make_inputs(w, seed=0)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
@@ -373,6 +377,85 @@ def decode_main(args, w0):
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_decode_baseline(w, Q, K, V, W, args)
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+def backward_main(args, w):
+    """Gradients of the bidirectional forward: one step = one favor_attn_bwd call on an
+    upstream gradient of the output's shape (inputs resident).  Algorithmic flops: the
+    feature maps of Q and K, S, phi(Q) S, dphi(Q), dS, dphi(K), and the three products with W
+    and dS that give dQ, dK, dV; they run as float32 FMAs, so the roofline is float32."""
+    import numpy as np
+    import torch
+
+    from efficient_transformer_attention_favor_amd import _lib, api
+    from efficient_transformer_attention_favor_amd import inputs as I
+
+    if w.causal:
+        print("favor_attn_bwd covers bidirectional problems only", file=sys.stderr)
+        sys.exit(2)
+    Q, K, V, W = I.make_inputs(w, seed=0)
+    dO = np.random.default_rng(0).standard_normal(Q.shape).astype(np.float32)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    q, k, v, do = (torch.from_numpy(x).to(dev).to(dt) for x in (Q, K, V, dO))
+    wd = torch.from_numpy(W).to(dev)
+    p = api._problem(q, k, wd, False, 0)
+    nbytes = _lib.bwd_workspace_bytes(p)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), wd.data_ptr(), do.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+            dv.data_ptr(), ws.data_ptr())
+
+    def step():
+        st = _lib.attn_bwd(p, *ptrs, nbytes, stream.cuda_stream)
+        if st != _lib.FAVOR_OK:
+            raise _lib.FavorError(st, "favor_attn_bwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+
+    e = 2 if w.dtype == "bf16" else 4
+    B, Hq, Hkv, L, d, m = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.num_features
+    Rq, Rk = B * Hq * L, B * Hkv * L
+    flops = 2 * m * ((Rq + Rk) * d + Rk * (d + 1) + 3 * Rq * (d + 1) + Rq * d + Rk * (d + 1) + 2 * Rk * d)
+    alg_bytes = e * d * (3 * Rq + 4 * Rk) + 4 * w.heads_w * m * d
+    achieved = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "FAVOR+ attention bwd (dQ, dK, dV) tokens/s (B*H*L/s), 1 GPU",
+        "value": round(Rq / (ms_step * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic (seeded Gaussian Q, K, V and upstream gradient; orthogonal random features W)",
+        "config": {"workload": f"{w.name} backward", "batch": B, "heads_q": Hq, "heads_kv": Hkv,
+                   "heads_w": w.heads_w, "seq_len": L, "head_dim": d, "num_features": m,
+                   "input_dtype": w.dtype, "mode": "bidirectional backward", "parallelism": "single GPU"},
+        "roofline": {"kernel": "favor_attn_bwd (all kernels)", "bound": "alu", "achieved": round(achieved, 2),
+                     "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["f32"], 4),
+                     "traffic": None, "per_launch": {"alg_flops": flops, "alg_bytes": alg_bytes,
+                                                     "avg_ms": round(ms_step, 5)}},
+    }
     line = json.dumps(res)
     print(line, flush=True)
     if args.out:

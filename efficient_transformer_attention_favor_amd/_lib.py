@@ -24,7 +24,8 @@ FAVOR_CAUSAL = 1
 FAVOR_FWD_KERNELS = 3
 
 EXPORTED = ("favor_workspace_bytes", "favor_attn_fwd", "favor_attn_fwd_timed", "favor_features",
-            "favor_decode_state_bytes", "favor_attn_decode", "favor_status_string", "favor_abi_version")
+            "favor_decode_state_bytes", "favor_attn_decode", "favor_bwd_workspace_bytes", "favor_attn_bwd",
+            "favor_status_string", "favor_abi_version")
 
 
 class FavorProblem(ctypes.Structure):
@@ -65,6 +66,10 @@ def lib() -> ctypes.CDLL:
         L.favor_decode_state_bytes.restype = ctypes.c_size_t
         L.favor_attn_decode.argtypes = [P, vp, vp, vp, vp, vp, vp, vp]
         L.favor_attn_decode.restype = ctypes.c_int
+        L.favor_bwd_workspace_bytes.argtypes = [P]
+        L.favor_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.favor_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.favor_attn_bwd.restype = ctypes.c_int
         L.favor_status_string.argtypes = [ctypes.c_int]
         L.favor_status_string.restype = ctypes.c_char_p
         L.favor_abi_version.argtypes = []
@@ -114,6 +119,15 @@ def decode_state_bytes(p: FavorProblem) -> int:
 
 def attn_decode(p: FavorProblem, q, k, v, w, state, out, stream) -> int:
     return int(lib().favor_attn_decode(_ref(p), q, k, v, w, state, out, stream))
+
+
+def bwd_workspace_bytes(p: FavorProblem) -> int:
+    return int(lib().favor_bwd_workspace_bytes(_ref(p)))
+
+
+def attn_bwd(p: FavorProblem, q, k, v, w, dout, dq, dk, dv, workspace, workspace_nbytes, stream) -> int:
+    return int(lib().favor_attn_bwd(_ref(p), q, k, v, w, dout, dq, dk, dv, workspace,
+                                    ctypes.c_size_t(workspace_nbytes), stream))
 
 
 def abi_version() -> int:

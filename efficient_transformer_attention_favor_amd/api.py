@@ -136,3 +136,26 @@ def attn_decode(q, k, v, W, state, out=None, stream=None):
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_attn_decode")
     return out
+
+
+def attn_bwd(Q, K, V, W, dout, workspace=None, stream=None):
+    """Gradients (dQ, dK, dV) of sum(dout * attn_fwd(Q, K, V, W)), bidirectional; W fixed."""
+    _check(Q, K, V, W)
+    if dout.shape != Q.shape or dout.dtype != Q.dtype or dout.device != Q.device or not dout.is_contiguous():
+        raise ValueError("dout must be a contiguous tensor like Q")
+    p = _problem(Q, K, W, False, 0)
+    nbytes = _lib.bwd_workspace_bytes(p)
+    if nbytes == 0:
+        st = _lib.attn_bwd(p, None, None, None, None, None, None, None, None, None, 0, None)
+        raise _lib.FavorError(st, "favor_attn_bwd")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(Q.device)
+    dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+    st = _lib.attn_bwd(p, Q.data_ptr(), K.data_ptr(), V.data_ptr(), W.data_ptr(), dout.data_ptr(), dQ.data_ptr(),
+                       dK.data_ptr(), dV.data_ptr(), workspace.data_ptr(),
+                       workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if st != _lib.FAVOR_OK:
+        raise _lib.FavorError(st, "favor_attn_bwd")
+    return dQ, dK, dV

@@ -1,0 +1,365 @@
+// Gradients of bidirectional FAVOR+ (the favor_attn_bwd entry point).
+//
+// "Rethinking Attention with Performers" (review page), section "제안 방법": out = D^-1 A_hat V
+// in linear order with positive random features phi.  The pages give no backward pass; the
+// gradients below follow from that definition by the chain rule (W is a fixed input).  Per kv
+// head, with the G query heads of that head taken as one sequence of G*L query rows,
+// S = phi(K)^T [V, 1] = [S_v, S_1] and, per query row i, D_i = phi(q_i) . S_1:
+//   g_i  = dout_i / D_i,   h_i = -(dout_i . out_i) / D_i,          G1 = [g, h]   (rows x (d+1))
+//   dphi(Q) = G1 S^T,      dS = phi(Q)^T G1,
+//   dphi(K) = [V, 1] dS^T, dV = phi(K) dS_v,
+//   dX = (dphi(X) * phi(X)) W - X * rowsum(dphi(X) * phi(X))   for X = Q, K
+// (d phi(x)_f / dx = phi(x)_f (w_f - x)); for X = Q the row sums are exactly 0 (out_i does not
+// change when phi(q_i) is scaled), so that term is left out.  The feature matrices are scaled by any per-row
+// (queries) or per-head (keys) constant, as the feature kernels leave them: every product
+// above is invariant under those scalings.
+//
+// Implementation: the feature kernels write phi(Q) and phi(K) as float32 matrices, then seven
+// batched float32 GEMMs (one batch entry per (batch, kv head)) and four row kernels.  All
+// arithmetic is float32; bf16 problems round only their inputs and the gradients they return.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include "favor_device.hpp"
+#include "favor_ops.hpp"
+#include "favor_plan.hpp"
+
+namespace favor {
+namespace {
+
+// ---- batched float32 GEMM: C = op(A) op(B), 64 x 64 tiles, 16-deep k steps ----------
+// op(A) is M x K: A stored [M][K] (TA false) or [K][M] (TA true), leading dimension lda;
+// op(B) is K x N: B stored [K][N] (TB false) or [N][K] (TB true).  Batch entry z uses
+// A + (z % modA) sA, B + (z % modB) sB, C + z sC.  256 threads, 4 x 4 outputs each.
+// With ksplit > 1 (long contractions with few output tiles) grid.z enumerates (split,
+// batch entry); split s covers contraction indices [s kc, (s+1) kc) and writes its partial
+// to C + (s batch + z) sC, summed afterwards in split order by sum_splits.
+constexpr int GT = 64, GK = 16, GLD = GT + 4;
+
+template <bool TA, bool TB>
+__global__ void __launch_bounds__(256)
+    gemm_f32(const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N, int K,
+             int lda, int ldb, int ldc, long long sA, long long sB, long long sC, int modA, int modB, int batch,
+             int kc) {
+  __shared__ __attribute__((aligned(16))) float As[GK][GLD];
+  __shared__ __attribute__((aligned(16))) float Bs[GK][GLD];
+  const int z = blockIdx.z % batch, split = blockIdx.z / batch;
+  A += (long long)(z % modA) * sA;
+  B += (long long)(z % modB) * sB;
+  C += (long long)blockIdx.z * sC;
+  const int kbeg = split * kc, kend = min(K, kbeg + kc);
+  const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  const int t = threadIdx.x, tx = t % 16, ty = t / 16;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = kbeg; k0 < kend; k0 += GK) {
+#pragma unroll
+    for (int e = t; e < GT * GK; e += 256) {
+      // consecutive threads walk the operand's contiguous dimension
+      const int mm = TA ? e % GT : e / GK, kk = TA ? e / GT : e % GK;
+      const int gm = m0 + mm, gk = k0 + kk;
+      float x = 0.f;
+      if (gm < M && gk < kend) x = TA ? A[(long long)gk * lda + gm] : A[(long long)gm * lda + gk];
+      As[kk][mm] = x;
+    }
+#pragma unroll
+    for (int e = t; e < GT * GK; e += 256) {
+      const int nn = TB ? e / GK : e % GT, kk = TB ? e % GK : e / GT;
+      const int gn = n0 + nn, gk = k0 + kk;
+      float x = 0.f;
+      if (gn < N && gk < kend) x = TB ? B[(long long)gn * ldb + gk] : B[(long long)gk * ldb + gn];
+      Bs[kk][nn] = x;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < GK; ++kk) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&As[kk][ty * 4]);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(&Bs[kk][tx * 4]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int gm = m0 + ty * 4 + i;
+    if (gm >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int gn = n0 + tx * 4 + j;
+      if (gn < N) C[(long long)gm * ldc + gn] = acc[i][j];
+    }
+  }
+}
+
+template <bool TA, bool TB>
+favor_status gemm(const float* A, const float* B, float* C, int M, int N, int K, int lda, int ldb, int ldc,
+                  long long sA, long long sB, long long sC, int modA, int modB, int batch, hipStream_t st) {
+  const dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch);
+  hipLaunchKernelGGL((gemm_f32<TA, TB>), grid, dim3(256), 0, st, A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC,
+                     modA, modB, batch, K);
+  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+// C[z] = sum over s of P[s][z] (in split order), each [M][N] dense.
+__global__ void __launch_bounds__(256) sum_splits(const float* __restrict__ P, float* __restrict__ C, long long n,
+                                                  int splits) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  float s = 0.f;
+  for (int k = 0; k < splits; ++k) s += P[(long long)k * n + i];
+  C[i] = s;
+}
+
+// Splits of a long contraction so that the launch has about 4096 workgroups, each split at
+// least 256 deep (a multiple of the 16-deep step).
+int ksplit_for(int M, int N, int K, int batch) {
+  const long long tiles = (long long)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * batch;
+  long long s = (4096 + tiles - 1) / tiles;
+  const long long smax = (K + 255) / 256;
+  if (s > smax) s = smax;
+  return s < 1 ? 1 : (int)s;
+}
+
+// C (dense [M][N] per batch entry) = op(A) op(B) with a split contraction; P holds
+// splits * batch * M * N floats of partials.
+template <bool TA, bool TB>
+favor_status gemm_split(const float* A, const float* B, float* C, float* P, int M, int N, int K, int lda, int ldb,
+                        long long sA, long long sB, int modA, int modB, int batch, int splits, hipStream_t st) {
+  const int kc = ((K + splits - 1) / splits + GK - 1) / GK * GK;
+  const dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch * splits);
+  hipLaunchKernelGGL((gemm_f32<TA, TB>), grid, dim3(256), 0, st, A, B, P, M, N, K, lda, ldb, N, sA, sB,
+                     (long long)M * N, modA, modB, batch, kc);
+  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  const long long n = (long long)batch * M * N;
+  hipLaunchKernelGGL(sum_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P, C, n, splits);
+  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+// ---- row kernels: one wave per row, 4 rows per workgroup -----------------------------
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) x += __shfl_xor(x, s);
+  return x;
+}
+
+// V1 = [V, 1] as float32 [rows][D+1].
+template <class T, int D>
+__global__ void __launch_bounds__(256) ones_column(const T* __restrict__ V, float* __restrict__ V1, long long rows) {
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int l = threadIdx.x & 63;
+  for (int c = l; c <= D; c += 64) V1[r * (D + 1) + c] = c < D ? (float)V[r * D + c] : 1.f;
+}
+
+// From ND = phi(Q) S ([rows][D+1], numerators then D_i): G1 = [dout/D, -(dout . out)/D].
+template <class T, int D>
+__global__ void __launch_bounds__(256)
+    output_grads(const float* __restrict__ ND, const T* __restrict__ dout, float* __restrict__ G1, long long rows) {
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int l = threadIdx.x & 63;
+  const float* nd = ND + r * (D + 1);
+  const float inv = 1.f / nd[D];
+  float dot = 0.f;
+  for (int c = l; c < D; c += 64) dot = fmaf((float)dout[r * D + c], nd[c] * inv, dot);
+  dot = wave_sum(dot);
+  float* g = G1 + r * (D + 1);
+  for (int c = l; c < D; c += 64) g[c] = (float)dout[r * D + c] * inv;
+  if (l == 0) g[D] = -dot * inv;
+}
+
+// T = dphi * phi in place and its row sums.
+__global__ void __launch_bounds__(256)
+    feature_product(float* __restrict__ dphi, const float* __restrict__ phi, float* __restrict__ rowsum, int m,
+                    long long rows) {
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int l = threadIdx.x & 63;
+  float s = 0.f;
+  for (int f = l; f < m; f += 64) {
+    const float x = dphi[r * m + f] * phi[r * m + f];
+    dphi[r * m + f] = x;
+    s += x;
+  }
+  s = wave_sum(s);
+  if (l == 0) rowsum[r] = s;
+}
+
+// dX = P - X * rowsum, in the input dtype.
+template <class T, int D>
+__global__ void __launch_bounds__(256)
+    input_grads(const float* __restrict__ P, const T* __restrict__ X, const float* __restrict__ rowsum,
+                T* __restrict__ dX, long long rows) {
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int l = threadIdx.x & 63;
+  const float t = rowsum[r];
+  for (int c = l; c < D; c += 64) dX[r * D + c] = (T)(P[r * D + c] - (float)X[r * D + c] * t);
+}
+
+template <class T, int D>
+__global__ void __launch_bounds__(256) to_dtype(const float* __restrict__ P, T* __restrict__ dX, long long rows) {
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int l = threadIdx.x & 63;
+  for (int c = l; c < D; c += 64) dX[r * D + c] = (T)P[r * D + c];
+}
+
+// ---- workspace -----------------------------------------------------------------------
+
+struct BwdLayout {
+  size_t phq, cq, phk, ck, v1, S, ND, G1, dphq, tq, Pq, dS, dphk, tk, Pk, dVf, part, bytes;
+  int split_k, split_q;  // contraction splits of S = phi(K)^T [V, 1] and dS = phi(Q)^T G1
+};
+
+size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+
+BwdLayout bwd_layout(const Plan& s) {
+  const size_t Rq = (size_t)s.B * s.Hq * s.L, Rk = (size_t)s.B * s.Hkv * s.L;
+  const size_t m = s.m, d1 = s.d + 1, f = sizeof(float);
+  BwdLayout w;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = a256(off + n * f);
+    return o;
+  };
+  w.phq = take(Rq * m);
+  w.cq = take(Rq);
+  w.phk = take(Rk * m);
+  w.ck = take(s.BH);
+  w.v1 = take(Rk * d1);
+  w.S = take((size_t)s.BH * m * d1);
+  w.ND = take(Rq * d1);
+  w.G1 = take(Rq * d1);
+  w.dphq = take(Rq * m);
+  w.tq = take(Rq);
+  w.Pq = take(Rq * s.d);
+  w.dS = take((size_t)s.BH * m * d1);
+  w.dphk = take(Rk * m);
+  w.tk = take(Rk);
+  w.Pk = take(Rk * s.d);
+  w.dVf = take(Rk * s.d);
+  w.split_k = ksplit_for(s.m, s.d + 1, s.L, s.BH);
+  w.split_q = ksplit_for(s.m, s.d + 1, s.G * s.L, s.BH);
+  w.part = take((size_t)(w.split_k > w.split_q ? w.split_k : w.split_q) * s.BH * m * d1);
+  w.bytes = off;
+  return w;
+}
+
+int row_blocks(long long rows) { return (int)((rows + 3) / 4); }
+
+template <class T, int D>
+favor_status run_bwd(const Plan& s, const void* Qv, const void* Kv, const void* Vv, const float* W, const void* dOv,
+                     void* dQv, void* dKv, void* dVv, char* ws, hipStream_t st) {
+  const T* Q = static_cast<const T*>(Qv);
+  const T* K = static_cast<const T*>(Kv);
+  const T* V = static_cast<const T*>(Vv);
+  const T* dO = static_cast<const T*>(dOv);
+  const BwdLayout w = bwd_layout(s);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  float *phq = F(w.phq), *phk = F(w.phk), *v1 = F(w.v1), *S = F(w.S), *ND = F(w.ND), *G1 = F(w.G1);
+  float *dphq = F(w.dphq), *tq = F(w.tq), *Pq = F(w.Pq), *dS = F(w.dS), *dphk = F(w.dphk), *tk = F(w.tk);
+  float *Pk = F(w.Pk), *dVf = F(w.dVf);
+  const long long Rq = (long long)s.B * s.Hq * s.L, Rk = (long long)s.B * s.Hkv * s.L;
+  const int m = s.m, D1 = D + 1, GL = s.G * s.L, L = s.L, BH = s.BH;
+  // W of batch entry z (= b * Hkv + hkv): head hkv, or the shared one
+  const int wmod = s.Hw == 1 ? 1 : s.Hkv;
+  const long long wstride = s.Hw == 1 ? 0 : (long long)m * D;
+  favor_status rc;
+#define FAVOR_TRY(x)        \
+  if ((rc = (x)) != FAVOR_OK) return rc
+#define FAVOR_LAUNCHED() \
+  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP
+
+  FAVOR_TRY(launch_features(s, 0, Q, W, phq, F(w.cq), st));
+  FAVOR_TRY(launch_features(s, 1, K, W, phk, F(w.ck), st));
+  hipLaunchKernelGGL((ones_column<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, V, v1, Rk);
+  FAVOR_LAUNCHED();
+  // S = phi(K)^T [V, 1]                                    (m x D+1, contraction over L)
+  FAVOR_TRY((gemm_split<true, false>(phk, v1, S, F(w.part), m, D1, L, m, D1, (long long)L * m, (long long)L * D1,
+                                     BH, BH, BH, w.split_k, st)));
+  // ND = phi(Q) S                                          (G L x D+1)
+  FAVOR_TRY((gemm<false, false>(phq, S, ND, GL, D1, m, m, D1, D1, (long long)GL * m, (long long)m * D1,
+                                (long long)GL * D1, BH, BH, BH, st)));
+  hipLaunchKernelGGL((output_grads<T, D>), dim3(row_blocks(Rq)), dim3(256), 0, st, ND, dO, G1, Rq);
+  FAVOR_LAUNCHED();
+  // dphi(Q) = G1 S^T                                       (G L x m)
+  FAVOR_TRY((gemm<false, true>(G1, S, dphq, GL, m, D1, D1, D1, m, (long long)GL * D1, (long long)m * D1,
+                               (long long)GL * m, BH, BH, BH, st)));
+  hipLaunchKernelGGL(feature_product, dim3(row_blocks(Rq)), dim3(256), 0, st, dphq, phq, tq, m, Rq);
+  FAVOR_LAUNCHED();
+  // dQ = T W: the term -Q * rowsum(T) vanishes for queries (rowsum(T)_i = g_i . N_i +
+  // h_i D_i = 0, since scaling phi(q_i) leaves out_i unchanged), and dropping it avoids
+  // subtracting the rounding noise of that cancellation
+  FAVOR_TRY((gemm<false, false>(dphq, W, Pq, GL, D, m, m, D, D, (long long)GL * m, wstride, (long long)GL * D, BH,
+                                wmod, BH, st)));
+  hipLaunchKernelGGL((to_dtype<T, D>), dim3(row_blocks(Rq)), dim3(256), 0, st, Pq, static_cast<T*>(dQv), Rq);
+  FAVOR_LAUNCHED();
+  // dS = phi(Q)^T G1                                       (m x D+1, contraction over G L)
+  FAVOR_TRY((gemm_split<true, false>(phq, G1, dS, F(w.part), m, D1, GL, m, D1, (long long)GL * m,
+                                     (long long)GL * D1, BH, BH, BH, w.split_q, st)));
+  // dphi(K) = [V, 1] dS^T                                  (L x m)
+  FAVOR_TRY((gemm<false, true>(v1, dS, dphk, L, m, D1, D1, D1, m, (long long)L * D1, (long long)m * D1,
+                               (long long)L * m, BH, BH, BH, st)));
+  hipLaunchKernelGGL(feature_product, dim3(row_blocks(Rk)), dim3(256), 0, st, dphk, phk, tk, m, Rk);
+  FAVOR_LAUNCHED();
+  FAVOR_TRY((gemm<false, false>(dphk, W, Pk, L, D, m, m, D, D, (long long)L * m, wstride, (long long)L * D, BH,
+                                wmod, BH, st)));
+  hipLaunchKernelGGL((input_grads<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, Pk, K, tk, static_cast<T*>(dKv),
+                     Rk);
+  FAVOR_LAUNCHED();
+  // dV = phi(K) dS_v                                       (L x D; dS rows have stride D+1)
+  FAVOR_TRY((gemm<false, false>(phk, dS, dVf, L, D, m, m, D1, D, (long long)L * m, (long long)m * D1,
+                                (long long)L * D, BH, BH, BH, st)));
+  hipLaunchKernelGGL((to_dtype<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, dVf, static_cast<T*>(dVv), Rk);
+  FAVOR_LAUNCHED();
+#undef FAVOR_TRY
+#undef FAVOR_LAUNCHED
+  return FAVOR_OK;
+}
+
+favor_status bwd_plan(const favor_problem* p, Plan* s) {
+  const favor_status st = make_plan(p, s);
+  if (st != FAVOR_OK) return st;
+  if (p->mode != FAVOR_BIDIRECTIONAL) return FAVOR_ERR_UNSUPPORTED;
+  return FAVOR_OK;
+}
+
+}  // namespace
+}  // namespace favor
+
+extern "C" size_t favor_bwd_workspace_bytes(const favor_problem* p) {
+  favor::Plan s;
+  if (favor::bwd_plan(p, &s) != FAVOR_OK) return 0;
+  return favor::bwd_layout(s).bytes;
+}
+
+extern "C" favor_status favor_attn_bwd(const favor_problem* p, const void* Q, const void* K, const void* V,
+                                       const float* W, const void* dout, void* dQ, void* dK, void* dV,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  favor::Plan s;
+  const favor_status st = favor::bwd_plan(p, &s);
+  if (st != FAVOR_OK) return st;
+  if (Q == nullptr || K == nullptr || V == nullptr || W == nullptr || dout == nullptr || dQ == nullptr ||
+      dK == nullptr || dV == nullptr)
+    return FAVOR_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < favor::bwd_layout(s).bytes ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return FAVOR_ERR_WORKSPACE;
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (s.dtype == FAVOR_BF16)
+    return s.d == 64 ? favor::run_bwd<favor::bf16, 64>(s, Q, K, V, W, dout, dQ, dK, dV, ws, hs)
+                     : favor::run_bwd<favor::bf16, 128>(s, Q, K, V, W, dout, dQ, dK, dV, ws, hs);
+  return s.d == 64 ? favor::run_bwd<float, 64>(s, Q, K, V, W, dout, dQ, dK, dV, ws, hs)
+                   : favor::run_bwd<float, 128>(s, Q, K, V, W, dout, dQ, dK, dV, ws, hs);
+}

@@ -20,6 +20,7 @@
 #include <math.h>
 
 #include "favor_device.hpp"
+#include "favor_ops.hpp"
 #include "favor_plan.hpp"
 
 namespace favor {
@@ -148,6 +149,16 @@ favor_status run_features(const Plan& s, int side, const void* Xv, const float* 
 }
 
 }  // namespace
+
+favor_status launch_features(const Plan& s, int side, const void* X, const float* W, float* phi, float* c,
+                             hipStream_t st) {
+  if (s.dtype == FAVOR_BF16)
+    return s.d == 64 ? run_features<bf16, 64>(s, side, X, W, phi, c, st)
+                     : run_features<bf16, 128>(s, side, X, W, phi, c, st);
+  return s.d == 64 ? run_features<float, 64>(s, side, X, W, phi, c, st)
+                   : run_features<float, 128>(s, side, X, W, phi, c, st);
+}
+
 }  // namespace favor
 
 extern "C" favor_status favor_features(const favor_problem* p, int32_t side, const void* X, const float* W,
@@ -157,10 +168,5 @@ extern "C" favor_status favor_features(const favor_problem* p, int32_t side, con
   if (st != FAVOR_OK) return st;
   if (side != 0 && side != 1) return FAVOR_ERR_INVALID_ARG;
   if (X == nullptr || W == nullptr || phi_out == nullptr || c_out == nullptr) return FAVOR_ERR_INVALID_ARG;
-  hipStream_t hs = static_cast<hipStream_t>(stream);
-  if (s.dtype == FAVOR_BF16)
-    return s.d == 64 ? favor::run_features<favor::bf16, 64>(s, side, X, W, phi_out, c_out, hs)
-                     : favor::run_features<favor::bf16, 128>(s, side, X, W, phi_out, c_out, hs);
-  return s.d == 64 ? favor::run_features<float, 64>(s, side, X, W, phi_out, c_out, hs)
-                   : favor::run_features<float, 128>(s, side, X, W, phi_out, c_out, hs);
+  return favor::launch_features(s, side, X, W, phi_out, c_out, static_cast<hipStream_t>(stream));
 }

@@ -1,0 +1,15 @@
+// Launchers shared between the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "favor_plan.hpp"
+
+namespace favor {
+
+// The feature map of the queries (side 0, row stabilisers) or keys (side 1, one stabiliser
+// per (batch, kv head)) as float32 [rows][m], stabilisers in natural-log units in c.
+favor_status launch_features(const Plan& s, int side, const void* X, const float* W, float* phi, float* c,
+                             hipStream_t st);
+
+}  // namespace favor

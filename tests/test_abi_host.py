@@ -105,3 +105,20 @@ def test_decode_validation():
         args[i] = None
         assert _lib.attn_decode(p, *args, None) == _lib.FAVOR_ERR_INVALID_ARG
     assert _lib.attn_decode(None, 8, 8, 8, 8, 256, 8, None) == _lib.FAVOR_ERR_INVALID_ARG
+
+
+def test_backward_validation():
+    p = _p()
+    need = _lib.bwd_workspace_bytes(p)
+    assert need > 0 and need % 256 == 0
+    causal = _p(mode=_lib.FAVOR_CAUSAL)
+    assert _lib.bwd_workspace_bytes(causal) == 0
+    assert _lib.attn_bwd(causal, 8, 8, 8, 8, 8, 8, 8, 8, 256, need, None) == _lib.FAVOR_ERR_UNSUPPORTED
+    for i in range(8):
+        args = [8] * 8
+        args[i] = None
+        assert _lib.attn_bwd(p, *args, 256, need, None) == _lib.FAVOR_ERR_INVALID_ARG
+    assert _lib.attn_bwd(p, *([8] * 8), None, need, None) == _lib.FAVOR_ERR_WORKSPACE
+    assert _lib.attn_bwd(p, *([8] * 8), 256, need - 1, None) == _lib.FAVOR_ERR_WORKSPACE
+    assert _lib.attn_bwd(p, *([8] * 8), 260, need, None) == _lib.FAVOR_ERR_WORKSPACE
+    assert _lib.bwd_workspace_bytes(_p(seq_len=4096)) > need

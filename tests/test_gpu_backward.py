@@ -1,0 +1,96 @@
+"""Gradients of bidirectional FAVOR+ (favor_attn_bwd) against the float64 oracle.
+
+The oracle's gradients (``favor_grads``) are the chain rule written out from the linear-order
+definition and pinned by central differences in tests/test_oracle.py.  Metric: the largest
+error of a gradient tensor relative to its largest entry, max|g - r| / max|r|, with the
+forward's bars (1e-4 float32, 2e-2 bf16).  A row-wise metric does not fit gradients: a row
+of dQ is a sum over the m features of terms (dphi * phi)_f w_f that nearly cancel for some
+rows (the terms are ~1e6 times the result in these cases), so any float32 evaluation has a
+large error relative to such a row but not relative to the gradient as a whole.  The
+row-wise figure is printed alongside.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle.favor_oracle as O
+from efficient_transformer_attention_favor_amd import api
+from efficient_transformer_attention_favor_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _tensor_rel_err(g, r):
+    return float(np.max(np.abs(np.asarray(g, np.float64) - r)) / np.max(np.abs(r)))
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dev(x, dtype):
+    return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda").to(dtype)
+
+
+def _small(name, **kw):
+    return I.workload(name).replace(name=f"{name}_bwd", causal=False, **kw)
+
+
+CASES = [
+    _small("c2_bidir_bf16", batch=2, heads_q=4, heads_kv=2, heads_w=2, seq_len=200, num_features=128),
+    _small("c2_bidir_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=333),
+    _small("c4_mqa_bidir_bf16", batch=2, heads_q=4, heads_kv=1, heads_w=1, seq_len=150),
+    _small("c5_causal_long_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=100),  # m = 512, heavy rows
+    _small("c1_bidir_f32", seq_len=300),
+    _small("c1_bidir_f32", batch=2, heads_q=2, heads_kv=1, heads_w=1, seq_len=97, head_dim=128, num_features=192),
+]
+
+
+def _grads(w, Q, K, V, W, dO):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v, do = _dev(Q, dt), _dev(K, dt), _dev(V, dt), _dev(dO, dt)
+    dq, dk, dv = api.attn_bwd(q, k, v, _dev(W, torch.float32), do)
+    torch.cuda.synchronize()
+    return [x.float().cpu().numpy() for x in (dq, dk, dv)]
+
+
+def _upstream(w, seed=0):
+    g = np.random.default_rng(seed).standard_normal((w.batch, w.heads_q, w.seq_len, w.head_dim)).astype(np.float32)
+    return I.round_to_bf16(g) if w.dtype == "bf16" else g
+
+
+@pytest.mark.parametrize("w", CASES, ids=lambda w: f"{w.dtype}_B{w.batch}H{w.heads_q}/{w.heads_kv}"
+                         f"_L{w.seq_len}_d{w.head_dim}_m{w.num_features}")
+def test_backward_matches_oracle(w):
+    _say(f"backward parity {w}")
+    Q, K, V, W = I.make_inputs(w, seed=0)
+    dO = _upstream(w)
+    got = _grads(w, Q, K, V, W, dO)
+    ref = O.favor_grads(Q, K, V, W, dO)
+    for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
+        err = _tensor_rel_err(g, r)
+        _say(f"  {name}: rel err {err:.3e} (row-wise {O.rowwise_rel_err(g, r):.3e})")
+        assert err <= TOL[w.dtype], name
+
+
+def test_backward_deterministic():
+    w = CASES[0]
+    Q, K, V, W = I.make_inputs(w, seed=3)
+    dO = _upstream(w, 3)
+    a = _grads(w, Q, K, V, W, dO)
+    b = _grads(w, Q, K, V, W, dO)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_backward_constant_values():
+    """V = 1: the output is 1 whatever Q and K are, so dQ and dK vanish (up to rounding)."""
+    w = CASES[4]
+    Q, K, V, W = I.make_inputs(w, seed=1)
+    V = np.ones_like(V)
+    dq, dk, _ = _grads(w, Q, K, V, W, _upstream(w, 1))
+    assert np.max(np.abs(dq)) < 1e-4 and np.max(np.abs(dk)) < 1e-4

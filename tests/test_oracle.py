@@ -377,3 +377,21 @@ def test_grads_vanish_for_constant_values():
     W = orf_matrix(m, d, rng)
     dq, dk, _ = O.favor_head_grads(q, k, np.ones((L, d)), W, rng.standard_normal((L, d)))
     assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
+
+
+def test_query_feature_gradient_is_orthogonal_to_the_features():
+    """Scaling phi(q_i) leaves out_i unchanged, so sum_f dphi(q_i)_f phi(q_i)_f = 0: the
+    identity that lets an implementation drop the -q * rowsum term of dq."""
+    rng = np.random.default_rng(14)
+    L, d, m = 8, 4, 16
+    q, k, v = rng.standard_normal((3, L, d)) * 0.7
+    W = orf_matrix(m, d, rng)
+    dout = rng.standard_normal((L, d))
+    pq, pk = O.feature_map(q, W), O.feature_map(k, W)
+    Sv, S1 = O.kv_summary(pk, v)
+    D = pq @ S1
+    out = (pq @ Sv) / D[:, None]
+    dpq = (dout / D[:, None]) @ Sv.T + np.outer(-np.sum(dout * out, axis=1) / D, S1)
+    assert np.max(np.abs(np.sum(dpq * pq, axis=1))) < 1e-12
+    dq, _, _ = O.favor_head_grads(q, k, v, W, dout)
+    assert np.max(np.abs(dq - (dpq * pq) @ W)) < 1e-12
