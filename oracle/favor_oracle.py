@@ -162,8 +162,8 @@ def favor_rows(Q, K, V, W, rows, causal=False):
     return out
 
 
-def favor_head_grads(q, k, v, W, dout):
-    """Gradients of sum(dout * out) for bidirectional FAVOR+ on one head, out = favor_head(q, k, v, W).
+def favor_head_grads(q, k, v, W, dout, causal=False):
+    """Gradients of sum(dout * out) for FAVOR+ on one head, out = favor_head(q, k, v, W, causal).
 
     Written out from the linear-order definition by the chain rule (the pages give no
     backward pass; W is a fixed input).  With phi = feature_map, S_v = phi(K)^T V,
@@ -174,6 +174,9 @@ def favor_head_grads(q, k, v, W, dout):
         dphi(k_j) = dS_v v_j + dS_1,   dv_j = dS_v^T phi(k_j)
     and, since d phi(x)_f / dx = phi(x)_f (w_f - x),
         dx = W^T (dphi * phi) - x sum_f (dphi * phi)_f.
+    Causal (inclusive mask): S_v, S_1 are the running sums over j <= i at query row i, and
+    key row j receives dS_v, dS_1 summed over the query rows i >= j only; the first is a
+    left-to-right sweep, the second a right-to-left one.  q has the length of k then.
     Returns (dq (Lq, d), dk (L, d), dv (L, d)) in float64.
     """
     q = np.asarray(q, dtype=_F)
@@ -183,16 +186,44 @@ def favor_head_grads(q, k, v, W, dout):
     dout = np.asarray(dout, dtype=_F)
     pq = feature_map(q, W)
     pk = feature_map(k, W)
-    Sv, S1 = kv_summary(pk, v)
-    D = pq @ S1
-    out = (pq @ Sv) / D[:, None]
-    g = dout / D[:, None]
-    h = -np.sum(dout * out, axis=1) / D
-    dpq = g @ Sv.T + np.outer(h, S1)
-    dSv = pq.T @ g
-    dS1 = pq.T @ h
-    dpk = v @ dSv.T + dS1[None, :]
-    dv = pk @ dSv
+    if not causal:
+        Sv, S1 = kv_summary(pk, v)
+        D = pq @ S1
+        out = (pq @ Sv) / D[:, None]
+        g = dout / D[:, None]
+        h = -np.sum(dout * out, axis=1) / D
+        dpq = g @ Sv.T + np.outer(h, S1)
+        dSv = pq.T @ g
+        dS1 = pq.T @ h
+        dpk = v @ dSv.T + dS1[None, :]
+        dv = pk @ dSv
+    else:
+        L, d = v.shape
+        m = pk.shape[1]
+        if len(q) != L:
+            raise ValueError("causal: queries and keys must have the same length")
+        g = np.empty((L, d))
+        h = np.empty(L)
+        dpq = np.empty((L, m))
+        Sv = np.zeros((m, d))
+        S1 = np.zeros(m)
+        for i in range(L):  # left to right: the prefix summaries each query row sees
+            Sv += np.outer(pk[i], v[i])
+            S1 += pk[i]
+            D = pq[i] @ S1
+            out_i = (pq[i] @ Sv) / D
+            g[i] = dout[i] / D
+            h[i] = -(dout[i] @ out_i) / D
+            dpq[i] = Sv @ g[i] + S1 * h[i]
+        dpk = np.empty((L, m))
+        dv = np.empty((L, d))
+        dSv = np.zeros((m, d))
+        dS1 = np.zeros(m)
+        for j in range(L - 1, -1, -1):  # right to left: the query rows i >= j
+            dSv += np.outer(pq[j], g[j])
+            dS1 += pq[j] * h[j]
+            dpk[j] = dSv @ v[j] + dS1
+            dv[j] = dSv.T @ pk[j]
 
     def through_features(x, dphi, phi):
         t = dphi * phi
@@ -201,9 +232,9 @@ def favor_head_grads(q, k, v, W, dout):
     return through_features(q, dpq, pq), through_features(k, dpk, pk), dv
 
 
-def favor_grads(Q, K, V, W, dOut):
-    """Gradients (dQ, dK, dV) of sum(dOut * favor_attention(Q, K, V, W)), bidirectional, with
-    the MQA head map: a kv head's dK and dV sum over the query heads that read it."""
+def favor_grads(Q, K, V, W, dOut, causal=False):
+    """Gradients (dQ, dK, dV) of sum(dOut * favor_attention(Q, K, V, W, causal)), with the MQA
+    head map: a kv head's dK and dV sum over the query heads that read it."""
     B, Hq, L, d = Q.shape
     Hkv, Hw = K.shape[1], W.shape[0]
     kv_of, w_of = head_maps(Hq, Hkv, Hw)
@@ -214,6 +245,15 @@ def favor_grads(Q, K, V, W, dOut):
     for b in range(B):
         for hk in range(Hkv):
             heads = [hq for hq in range(Hq) if kv_of[hq] == hk]
+            assert G == len(heads)
+            if causal:
+                # each query head is its own sequence over the positions of the kv head
+                for hq in heads:
+                    dq, dk, dv = favor_head_grads(Q[b, hq], K[b, hk], V[b, hk], W[w_of[hk]], dOut[b, hq], True)
+                    dQ[b, hq] = dq
+                    dK[b, hk] += dk
+                    dV[b, hk] += dv
+                continue
             # the G query heads of a kv head form one longer query sequence over the same S
             q = np.concatenate([Q[b, hq] for hq in heads])
             do = np.concatenate([dOut[b, hq] for hq in heads])
@@ -222,7 +262,6 @@ def favor_grads(Q, K, V, W, dOut):
                 dQ[b, hq] = dq[n * L:(n + 1) * L]
             dK[b, hk] += dk
             dV[b, hk] += dv
-    assert G == len(heads)
     return dQ, dK, dV
 
 

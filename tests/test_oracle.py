@@ -323,12 +323,13 @@ def test_planted_mistakes_fail():
 
 # ---- backward (gradients of sum(dout * out), bidirectional) --------------------------
 
-def _loss(Q, K, V, W, dOut):
-    return float(np.sum(dOut * O.favor_attention(Q, K, V, W)))
+def _loss(Q, K, V, W, dOut, causal=False):
+    return float(np.sum(dOut * O.favor_attention(Q, K, V, W, causal)))
 
 
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Hq,Hkv,Hw", [(1, 1, 1), (4, 2, 2), (4, 1, 1)])
-def test_grads_match_central_differences(Hq, Hkv, Hw):
+def test_grads_match_central_differences(Hq, Hkv, Hw, causal):
     """Pin: the written-out gradients agree with central differences of the forward oracle
     along random directions (float64, step 1e-5: truncation error ~1e-10)."""
     rng = np.random.default_rng(11)
@@ -338,20 +339,20 @@ def test_grads_match_central_differences(Hq, Hkv, Hw):
     V = rng.standard_normal((B, Hkv, L, d))
     W = np.stack([orf_matrix(m, d, rng) for _ in range(Hw)])
     dOut = rng.standard_normal((B, Hq, L, d))
-    dQ, dK, dV = O.favor_grads(Q, K, V, W, dOut)
+    dQ, dK, dV = O.favor_grads(Q, K, V, W, dOut, causal)
     eps = 1e-5
     for _ in range(3):
         uq, uk, uv = (rng.standard_normal(x.shape) for x in (Q, K, V))
-        fd = (_loss(Q + eps * uq, K + eps * uk, V + eps * uv, W, dOut)
-              - _loss(Q - eps * uq, K - eps * uk, V - eps * uv, W, dOut)) / (2 * eps)
+        fd = (_loss(Q + eps * uq, K + eps * uk, V + eps * uv, W, dOut, causal)
+              - _loss(Q - eps * uq, K - eps * uk, V - eps * uv, W, dOut, causal)) / (2 * eps)
         an = np.sum(dQ * uq) + np.sum(dK * uk) + np.sum(dV * uv)
         assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
     # each input separately, so a mistake in one gradient cannot hide behind another
     for which in range(3):
         u = [np.zeros_like(x) for x in (Q, K, V)]
         u[which] = rng.standard_normal(u[which].shape)
-        fd = (_loss(Q + eps * u[0], K + eps * u[1], V + eps * u[2], W, dOut)
-              - _loss(Q - eps * u[0], K - eps * u[1], V - eps * u[2], W, dOut)) / (2 * eps)
+        fd = (_loss(Q + eps * u[0], K + eps * u[1], V + eps * u[2], W, dOut, causal)
+              - _loss(Q - eps * u[0], K - eps * u[1], V - eps * u[2], W, dOut, causal)) / (2 * eps)
         an = np.sum((dQ, dK, dV)[which] * u[which])
         assert abs(fd - an) <= 1e-7 * max(1.0, abs(an))
 
@@ -395,3 +396,47 @@ def test_query_feature_gradient_is_orthogonal_to_the_features():
     assert np.max(np.abs(np.sum(dpq * pq, axis=1))) < 1e-12
     dq, _, _ = O.favor_head_grads(q, k, v, W, dout)
     assert np.max(np.abs(dq - (dpq * pq) @ W)) < 1e-12
+
+
+def test_causal_grads_of_values_are_the_masked_attention_transpose():
+    """Causal: dV = A_norm^T dout with A_norm the row-normalised lower-triangular A_hat."""
+    rng = np.random.default_rng(15)
+    L, d, m = 9, 4, 16
+    q, k, v = rng.standard_normal((3, L, d)) * 0.7
+    W = orf_matrix(m, d, rng)
+    dout = rng.standard_normal((L, d))
+    A = O.implied_attention(q, k, W, causal=True)
+    A = A / A.sum(axis=1, keepdims=True)
+    _, _, dv = O.favor_head_grads(q, k, v, W, dout, causal=True)
+    assert np.max(np.abs(dv - A.T @ dout)) < 1e-12
+
+
+def test_causal_grads_last_row_equal_bidirectional():
+    """The last query row sees every key, so with an upstream gradient on that row only the
+    causal gradients are the bidirectional ones; with the upstream gradient on rows < t only,
+    keys and values at positions >= t receive nothing."""
+    rng = np.random.default_rng(16)
+    L, d, m, t = 10, 4, 16, 6
+    q, k, v = rng.standard_normal((3, L, d)) * 0.7
+    W = orf_matrix(m, d, rng)
+    dout = np.zeros((L, d))
+    dout[-1] = rng.standard_normal(d)
+    a = O.favor_head_grads(q, k, v, W, dout, causal=True)
+    b = O.favor_head_grads(q, k, v, W, dout, causal=False)
+    for x, y in zip(a, b):
+        assert np.max(np.abs(x - y)) < 1e-12
+    dout = rng.standard_normal((L, d))
+    dout[t:] = 0
+    _, dk, dv = O.favor_head_grads(q, k, v, W, dout, causal=True)
+    assert np.all(dk[t:] == 0) and np.all(dv[t:] == 0)
+    assert np.max(np.abs(dk[:t])) > 1e-3 and np.max(np.abs(dv[:t])) > 1e-3
+
+
+def test_causal_grads_vanish_for_constant_values():
+    """V = 1 gives out = 1 under the mask as well, so dQ = dK = 0."""
+    rng = np.random.default_rng(17)
+    L, d, m = 7, 4, 8
+    q, k = rng.standard_normal((2, L, d)) * 0.7
+    W = orf_matrix(m, d, rng)
+    dq, dk, _ = O.favor_head_grads(q, k, np.ones((L, d)), W, rng.standard_normal((L, d)), causal=True)
+    assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
