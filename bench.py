@@ -385,26 +385,25 @@ def decode_main(args, w0):
 
 
 def backward_main(args, w):
-    """Gradients of the bidirectional forward: one step = one favor_attn_bwd call on an
-    upstream gradient of the output's shape (inputs resident).  Algorithmic flops: the
+    """Gradients of the forward in the workload's mode: one step = one favor_attn_bwd call on
+    an upstream gradient of the output's shape (inputs resident).  Algorithmic flops: the
     feature maps of Q and K, S, phi(Q) S, dphi(Q), dS, dphi(K), and the three products with W
-    and dS that give dQ, dK, dV; they run as float32 FMAs, so the roofline is float32."""
+    and dS that give dQ, dK, dV (the same count for both modes, as for the forward; the
+    causal chunk products execute more, reported as exec_flops); they run as float32 FMAs,
+    so the roofline is float32."""
     import numpy as np
     import torch
 
     from efficient_transformer_attention_favor_amd import _lib, api
     from efficient_transformer_attention_favor_amd import inputs as I
 
-    if w.causal:
-        print("favor_attn_bwd covers bidirectional problems only", file=sys.stderr)
-        sys.exit(2)
     Q, K, V, W = I.make_inputs(w, seed=0)
     dO = np.random.default_rng(0).standard_normal(Q.shape).astype(np.float32)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
     q, k, v, do = (torch.from_numpy(x).to(dev).to(dt) for x in (Q, K, V, dO))
     wd = torch.from_numpy(W).to(dev)
-    p = api._problem(q, k, wd, False, 0)
+    p = api._problem(q, k, wd, w.causal, 0)
     nbytes = _lib.bwd_workspace_bytes(p)
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -433,6 +432,15 @@ def backward_main(args, w):
     B, Hq, Hkv, L, d, m = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.num_features
     Rq, Rk = B * Hq * L, B * Hkv * L
     flops = 2 * m * ((Rq + Rk) * d + Rk * (d + 1) + 3 * Rq * (d + 1) + Rq * d + Rk * (d + 1) + 2 * Rk * d)
+    exec_flops = flops
+    if w.causal:
+        C = 64
+        Lp = (L + C - 1) // C * C
+        Qp, Kp = B * Hq * Lp, B * Hkv * Lp
+        d1 = d + 1
+        exec_flops = 2 * ((Rq + Rk) * d * m + Kp * m * d1 + Qp * C * m + Qp * C * d1 + Qp * m * d1 + Qp * C * d1
+                          + Qp * C * m + Qp * d1 * m + Qp * m * d + Qp * m * d1 + Kp * d1 * m + Qp * C * m
+                          + Kp * m * d + Kp * m * d + Qp * C * d)
     alg_bytes = e * d * (3 * Rq + 4 * Rk) + 4 * w.heads_w * m * d
     achieved = flops / (ms_step * 1e-3) / 1e12
     res = {
@@ -450,10 +458,11 @@ def backward_main(args, w):
         "data": "synthetic (seeded Gaussian Q, K, V and upstream gradient; orthogonal random features W)",
         "config": {"workload": f"{w.name} backward", "batch": B, "heads_q": Hq, "heads_kv": Hkv,
                    "heads_w": w.heads_w, "seq_len": L, "head_dim": d, "num_features": m,
-                   "input_dtype": w.dtype, "mode": "bidirectional backward", "parallelism": "single GPU"},
+                   "input_dtype": w.dtype, "mode": f"{'causal' if w.causal else 'bidirectional'} backward",
+                   "parallelism": "single GPU"},
         "roofline": {"kernel": "favor_attn_bwd (all kernels)", "bound": "alu", "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["f32"], 4),
-                     "traffic": None, "per_launch": {"alg_flops": flops, "alg_bytes": alg_bytes,
+                     "traffic": None, "per_launch": {"alg_flops": flops, "exec_flops": exec_flops, "alg_bytes": alg_bytes,
                                                      "avg_ms": round(ms_step, 5)}},
     }
     line = json.dumps(res)

@@ -138,12 +138,12 @@ def attn_decode(q, k, v, W, state, out=None, stream=None):
     return out
 
 
-def attn_bwd(Q, K, V, W, dout, workspace=None, stream=None):
-    """Gradients (dQ, dK, dV) of sum(dout * attn_fwd(Q, K, V, W)), bidirectional; W fixed."""
+def attn_bwd(Q, K, V, W, dout, causal=False, workspace=None, stream=None):
+    """Gradients (dQ, dK, dV) of sum(dout * attn_fwd(Q, K, V, W, causal)); W fixed."""
     _check(Q, K, V, W)
     if dout.shape != Q.shape or dout.dtype != Q.dtype or dout.device != Q.device or not dout.is_contiguous():
         raise ValueError("dout must be a contiguous tensor like Q")
-    p = _problem(Q, K, W, False, 0)
+    p = _problem(Q, K, W, causal, 0)
     nbytes = _lib.bwd_workspace_bytes(p)
     if nbytes == 0:
         st = _lib.attn_bwd(p, None, None, None, None, None, None, None, None, None, 0, None)

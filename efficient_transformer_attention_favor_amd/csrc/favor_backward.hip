@@ -17,6 +17,17 @@
 // Implementation: the feature kernels write phi(Q) and phi(K) as float32 matrices, then seven
 // batched float32 GEMMs (one batch entry per (batch, kv head)) and four row kernels.  All
 // arithmetic is float32; bf16 problems round only their inputs and the gradients they return.
+//
+// Causal (inclusive mask j <= i): the positions of each head are cut into chunks of C = 64
+// (the last one zero-padded), S_<c is the exclusive prefix of the chunk summaries
+// phi(K_c)^T [V_c, 1] and R_>c the exclusive suffix, over later chunks and the G query heads,
+// of phi(Q_c)^T G1_c.  Per chunk, with tril() keeping j <= i:
+//   P_c = tril(phi(Q_c) phi(K_c)^T),  A_c = tril(G1_c [V_c, 1]^T)
+//   [N, D]_c   = P_c [V_c, 1] + phi(Q_c) S_<c           (the forward, for G1)
+//   dphi(Q_c)  = A_c phi(K_c) + G1_c S_<c^T
+//   dphi(K_c)  = sum_g A_g,c^T phi(Q_g,c) + [V_c, 1] R_>c^T
+//   dV_c       = sum_g P_g,c^T g_g,c + phi(K_c) R_>c,v
+// as batched 64 x 64 chunk products, then the same feature and row steps as above.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -31,25 +42,41 @@ namespace {
 // ---- batched float32 GEMM: C = op(A) op(B), 64 x 64 tiles, 16-deep k steps ----------
 // op(A) is M x K: A stored [M][K] (TA false) or [K][M] (TA true), leading dimension lda;
 // op(B) is K x N: B stored [K][N] (TB false) or [N][K] (TB true).  Batch entry z uses
-// A + (z % modA) sA, B + (z % modB) sB, C + z sC.  256 threads, 4 x 4 outputs each.
-// With ksplit > 1 (long contractions with few output tiles) grid.z enumerates (split,
-// batch entry); split s covers contraction indices [s kc, (s+1) kc) and writes its partial
-// to C + (s batch + z) sC, summed afterwards in split order by sum_splits.
+// A + mapA(z) sA, B + mapB(z) sB, C + z sC.  256 threads, 4 x 4 outputs each; the grid is
+// one dimension (batch entries x row tiles x column tiles), so any batch count fits.
+// flags: kAccum adds to C instead of overwriting it; kTril zeroes the outputs with column >
+// row (the causal mask of a 64 x 64 chunk product).
+// With ksplit > 1 (long contractions with few output tiles) the batch index enumerates
+// (split, batch entry); split s covers contraction indices [s kc, (s+1) kc) and writes its
+// partial to C + (s batch + z) sC, summed afterwards in split order by sum_splits.
 constexpr int GT = 64, GK = 16, GLD = GT + 4;
+constexpr int kAccum = 1, kTril = 2;
+
+// Operand block read by batch entry z: ((z / div) % mod) * mul + z % inner.
+struct BMap {
+  int div, mod, mul, inner;
+};
+constexpr BMap kIdent{1, 0x7fffffff, 1, 1};
+constexpr BMap modulo(int n) { return BMap{1, n, 1, 1}; }
+__device__ __forceinline__ long long block_of(const BMap& b, int z) {
+  return (long long)((z / b.div) % b.mod) * b.mul + z % b.inner;
+}
 
 template <bool TA, bool TB>
 __global__ void __launch_bounds__(256)
     gemm_f32(const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N, int K,
-             int lda, int ldb, int ldc, long long sA, long long sB, long long sC, int modA, int modB, int batch,
-             int kc) {
+             int lda, int ldb, int ldc, long long sA, long long sB, long long sC, BMap mapA, BMap mapB, int batch,
+             int kc, int flags) {
   __shared__ __attribute__((aligned(16))) float As[GK][GLD];
   __shared__ __attribute__((aligned(16))) float Bs[GK][GLD];
-  const int z = blockIdx.z % batch, split = blockIdx.z / batch;
-  A += (long long)(z % modA) * sA;
-  B += (long long)(z % modB) * sB;
-  C += (long long)blockIdx.z * sC;
+  const int tn = (N + GT - 1) / GT, tm = (M + GT - 1) / GT;
+  const int bx = blockIdx.x % tn, by = (blockIdx.x / tn) % tm, zs = blockIdx.x / (tn * tm);
+  const int z = zs % batch, split = zs / batch;
+  A += block_of(mapA, z) * sA;
+  B += block_of(mapB, z) * sB;
+  C += (long long)zs * sC;
   const int kbeg = split * kc, kend = min(K, kbeg + kc);
-  const int m0 = blockIdx.y * GT, n0 = blockIdx.x * GT;
+  const int m0 = by * GT, n0 = bx * GT;
   const int t = threadIdx.x, tx = t % 16, ty = t / 16;
   float acc[4][4];
 #pragma unroll
@@ -93,17 +120,24 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int gn = n0 + tx * 4 + j;
-      if (gn < N) C[(long long)gm * ldc + gn] = acc[i][j];
+      if (gn >= N) continue;
+      float x = (flags & kTril) && gn > gm ? 0.f : acc[i][j];
+      if (flags & kAccum) x += C[(long long)gm * ldc + gn];
+      C[(long long)gm * ldc + gn] = x;
     }
   }
 }
 
+unsigned gemm_blocks(int M, int N, long long entries) {
+  return (unsigned)(((N + GT - 1) / GT) * (long long)((M + GT - 1) / GT) * entries);
+}
+
 template <bool TA, bool TB>
 favor_status gemm(const float* A, const float* B, float* C, int M, int N, int K, int lda, int ldb, int ldc,
-                  long long sA, long long sB, long long sC, int modA, int modB, int batch, hipStream_t st) {
-  const dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch);
-  hipLaunchKernelGGL((gemm_f32<TA, TB>), grid, dim3(256), 0, st, A, B, C, M, N, K, lda, ldb, ldc, sA, sB, sC,
-                     modA, modB, batch, K);
+                  long long sA, long long sB, long long sC, BMap mapA, BMap mapB, int batch, hipStream_t st,
+                  int flags = 0) {
+  hipLaunchKernelGGL((gemm_f32<TA, TB>), dim3(gemm_blocks(M, N, batch)), dim3(256), 0, st, A, B, C, M, N, K, lda,
+                     ldb, ldc, sA, sB, sC, mapA, mapB, batch, K, flags);
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
@@ -131,11 +165,10 @@ int ksplit_for(int M, int N, int K, int batch) {
 // splits * batch * M * N floats of partials.
 template <bool TA, bool TB>
 favor_status gemm_split(const float* A, const float* B, float* C, float* P, int M, int N, int K, int lda, int ldb,
-                        long long sA, long long sB, int modA, int modB, int batch, int splits, hipStream_t st) {
+                        long long sA, long long sB, BMap mapA, BMap mapB, int batch, int splits, hipStream_t st) {
   const int kc = ((K + splits - 1) / splits + GK - 1) / GK * GK;
-  const dim3 grid((N + GT - 1) / GT, (M + GT - 1) / GT, batch * splits);
-  hipLaunchKernelGGL((gemm_f32<TA, TB>), grid, dim3(256), 0, st, A, B, P, M, N, K, lda, ldb, N, sA, sB,
-                     (long long)M * N, modA, modB, batch, kc);
+  hipLaunchKernelGGL((gemm_f32<TA, TB>), dim3(gemm_blocks(M, N, (long long)batch * splits)), dim3(256), 0, st, A,
+                     B, P, M, N, K, lda, ldb, N, sA, sB, (long long)M * N, mapA, mapB, batch, kc, 0);
   if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
   const long long n = (long long)batch * M * N;
   hipLaunchKernelGGL(sum_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P, C, n, splits);
@@ -143,6 +176,19 @@ favor_status gemm_split(const float* A, const float* B, float* C, float* P, int 
 }
 
 // ---- row kernels: one wave per row, 4 rows per workgroup -----------------------------
+// Float32 intermediates may hold Lp >= L rows per head (zero padding up to a whole number
+// of chunks); the user's tensors hold L.  Row r of a padded matrix is position r % Lp of
+// head r / Lp.
+
+__device__ __forceinline__ long long unpadded_row(long long r, int L, int Lp, bool* real) {
+  const long long h = r / Lp, pos = r - h * Lp;
+  *real = pos < L;
+  return h * L + pos;
+}
+__device__ __forceinline__ long long padded_row(long long r, int L, int Lp) {
+  const long long h = r / L;
+  return h * Lp + (r - h * L);
+}
 
 __device__ __forceinline__ float wave_sum(float x) {
 #pragma unroll
@@ -150,29 +196,40 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
-// V1 = [V, 1] as float32 [rows][D+1].
-template <class T, int D>
-__global__ void __launch_bounds__(256) ones_column(const T* __restrict__ V, float* __restrict__ V1, long long rows) {
-  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int l = threadIdx.x & 63;
-  for (int c = l; c <= D; c += 64) V1[r * (D + 1) + c] = c < D ? (float)V[r * D + c] : 1.f;
-}
-
-// From ND = phi(Q) S ([rows][D+1], numerators then D_i): G1 = [dout/D, -(dout . out)/D].
+// V1 = [V, 1] as float32 [rows][D+1] (rows padded; padding rows all zero).
 template <class T, int D>
 __global__ void __launch_bounds__(256)
-    output_grads(const float* __restrict__ ND, const T* __restrict__ dout, float* __restrict__ G1, long long rows) {
+    ones_column(const T* __restrict__ V, float* __restrict__ V1, long long rows, int L, int Lp) {
   const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   const int l = threadIdx.x & 63;
+  bool real;
+  const long long u = unpadded_row(r, L, Lp, &real);
+  for (int c = l; c <= D; c += 64) V1[r * (D + 1) + c] = !real ? 0.f : c < D ? (float)V[u * D + c] : 1.f;
+}
+
+// From ND = phi(Q) S ([rows][D+1], numerators then D_i): G1 = [dout/D, -(dout . out)/D]
+// (rows padded; padding rows of G1 all zero).
+template <class T, int D>
+__global__ void __launch_bounds__(256)
+    output_grads(const float* __restrict__ ND, const T* __restrict__ dout, float* __restrict__ G1, long long rows,
+                 int L, int Lp) {
+  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const int l = threadIdx.x & 63;
+  float* g = G1 + r * (D + 1);
+  bool real;
+  const long long u = unpadded_row(r, L, Lp, &real);
+  if (!real) {
+    for (int c = l; c <= D; c += 64) g[c] = 0.f;
+    return;
+  }
   const float* nd = ND + r * (D + 1);
   const float inv = 1.f / nd[D];
   float dot = 0.f;
-  for (int c = l; c < D; c += 64) dot = fmaf((float)dout[r * D + c], nd[c] * inv, dot);
+  for (int c = l; c < D; c += 64) dot = fmaf((float)dout[u * D + c], nd[c] * inv, dot);
   dot = wave_sum(dot);
-  float* g = G1 + r * (D + 1);
-  for (int c = l; c < D; c += 64) g[c] = (float)dout[r * D + c] * inv;
+  for (int c = l; c < D; c += 64) g[c] = (float)dout[u * D + c] * inv;
   if (l == 0) g[D] = -dot * inv;
 }
 
@@ -193,24 +250,68 @@ __global__ void __launch_bounds__(256)
   if (l == 0) rowsum[r] = s;
 }
 
-// dX = P - X * rowsum, in the input dtype.
+// dX = P - X * rowsum, in the input dtype (rows: the user's; P and rowsum padded).
 template <class T, int D>
 __global__ void __launch_bounds__(256)
     input_grads(const float* __restrict__ P, const T* __restrict__ X, const float* __restrict__ rowsum,
-                T* __restrict__ dX, long long rows) {
+                T* __restrict__ dX, long long rows, int L, int Lp) {
   const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   const int l = threadIdx.x & 63;
-  const float t = rowsum[r];
-  for (int c = l; c < D; c += 64) dX[r * D + c] = (T)(P[r * D + c] - (float)X[r * D + c] * t);
+  const long long p = padded_row(r, L, Lp);
+  const float t = rowsum[p];
+  for (int c = l; c < D; c += 64) dX[r * D + c] = (T)(P[p * D + c] - (float)X[r * D + c] * t);
 }
 
 template <class T, int D>
-__global__ void __launch_bounds__(256) to_dtype(const float* __restrict__ P, T* __restrict__ dX, long long rows) {
+__global__ void __launch_bounds__(256)
+    to_dtype(const float* __restrict__ P, T* __restrict__ dX, long long rows, int L, int Lp) {
   const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   const int l = threadIdx.x & 63;
-  for (int c = l; c < D; c += 64) dX[r * D + c] = (T)P[r * D + c];
+  const long long p = padded_row(r, L, Lp);
+  for (int c = l; c < D; c += 64) dX[r * D + c] = (T)P[p * D + c];
+}
+
+// ---- chunk scans (causal) --------------------------------------------------------------
+// One thread per summary element e (n = m (D+1) per chunk), one head per grid row.
+
+// S[h][c] <- sum over c' < c of S[h][c'], in place, in chunk order.
+__global__ void __launch_bounds__(256) chunk_prefix(float* __restrict__ S, int NC, int n) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  float* p = S + (size_t)blockIdx.y * NC * n + e;
+  float run = 0.f;
+  int c = 0;
+  for (; c + 4 <= NC; c += 4) {
+    float x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = p[(size_t)(c + u) * n];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      p[(size_t)(c + u) * n] = run;
+      run += x[u];
+    }
+  }
+  for (; c < NC; ++c) {
+    const float x = p[(size_t)c * n];
+    p[(size_t)c * n] = run;
+    run += x;
+  }
+}
+
+// Rx[h][c] = sum over c' > c (from the last chunk down) and over the G query heads g of
+// kv head h (in order) of Rc[h G + g][c'].
+__global__ void __launch_bounds__(256)
+    chunk_suffix(const float* __restrict__ Rc, float* __restrict__ Rx, int NC, int G, int n) {
+  const int e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= n) return;
+  const size_t h = blockIdx.y;
+  float run = 0.f;
+  for (int c = NC - 1; c >= 0; --c) {
+    Rx[(h * NC + c) * n + e] = run;
+    for (int g = 0; g < G; ++g) run += Rc[((h * G + g) * NC + c) * n + e];
+  }
 }
 
 // ---- workspace -----------------------------------------------------------------------
@@ -257,6 +358,11 @@ BwdLayout bwd_layout(const Plan& s) {
 
 int row_blocks(long long rows) { return (int)((rows + 3) / 4); }
 
+#define FAVOR_TRY(x)        \
+  if ((rc = (x)) != FAVOR_OK) return rc
+#define FAVOR_LAUNCHED() \
+  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP
+
 template <class T, int D>
 favor_status run_bwd(const Plan& s, const void* Qv, const void* Kv, const void* Vv, const float* W, const void* dOv,
                      void* dQv, void* dKv, void* dVv, char* ws, hipStream_t st) {
@@ -275,88 +381,216 @@ favor_status run_bwd(const Plan& s, const void* Qv, const void* Kv, const void* 
   const int wmod = s.Hw == 1 ? 1 : s.Hkv;
   const long long wstride = s.Hw == 1 ? 0 : (long long)m * D;
   favor_status rc;
-#define FAVOR_TRY(x)        \
-  if ((rc = (x)) != FAVOR_OK) return rc
-#define FAVOR_LAUNCHED() \
-  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP
-
   FAVOR_TRY(launch_features(s, 0, Q, W, phq, F(w.cq), st));
   FAVOR_TRY(launch_features(s, 1, K, W, phk, F(w.ck), st));
-  hipLaunchKernelGGL((ones_column<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, V, v1, Rk);
+  hipLaunchKernelGGL((ones_column<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, V, v1, Rk, L, L);
   FAVOR_LAUNCHED();
   // S = phi(K)^T [V, 1]                                    (m x D+1, contraction over L)
   FAVOR_TRY((gemm_split<true, false>(phk, v1, S, F(w.part), m, D1, L, m, D1, (long long)L * m, (long long)L * D1,
-                                     BH, BH, BH, w.split_k, st)));
+                                     kIdent, kIdent, BH, w.split_k, st)));
   // ND = phi(Q) S                                          (G L x D+1)
   FAVOR_TRY((gemm<false, false>(phq, S, ND, GL, D1, m, m, D1, D1, (long long)GL * m, (long long)m * D1,
-                                (long long)GL * D1, BH, BH, BH, st)));
-  hipLaunchKernelGGL((output_grads<T, D>), dim3(row_blocks(Rq)), dim3(256), 0, st, ND, dO, G1, Rq);
+                                (long long)GL * D1, kIdent, kIdent, BH, st)));
+  hipLaunchKernelGGL((output_grads<T, D>), dim3(row_blocks(Rq)), dim3(256), 0, st, ND, dO, G1, Rq, L, L);
   FAVOR_LAUNCHED();
   // dphi(Q) = G1 S^T                                       (G L x m)
   FAVOR_TRY((gemm<false, true>(G1, S, dphq, GL, m, D1, D1, D1, m, (long long)GL * D1, (long long)m * D1,
-                               (long long)GL * m, BH, BH, BH, st)));
+                               (long long)GL * m, kIdent, kIdent, BH, st)));
   hipLaunchKernelGGL(feature_product, dim3(row_blocks(Rq)), dim3(256), 0, st, dphq, phq, tq, m, Rq);
   FAVOR_LAUNCHED();
   // dQ = T W: the term -Q * rowsum(T) vanishes for queries (rowsum(T)_i = g_i . N_i +
   // h_i D_i = 0, since scaling phi(q_i) leaves out_i unchanged), and dropping it avoids
   // subtracting the rounding noise of that cancellation
-  FAVOR_TRY((gemm<false, false>(dphq, W, Pq, GL, D, m, m, D, D, (long long)GL * m, wstride, (long long)GL * D, BH,
-                                wmod, BH, st)));
-  hipLaunchKernelGGL((to_dtype<T, D>), dim3(row_blocks(Rq)), dim3(256), 0, st, Pq, static_cast<T*>(dQv), Rq);
+  FAVOR_TRY((gemm<false, false>(dphq, W, Pq, GL, D, m, m, D, D, (long long)GL * m, wstride, (long long)GL * D,
+                                kIdent, modulo(wmod), BH, st)));
+  hipLaunchKernelGGL((to_dtype<T, D>), dim3(row_blocks(Rq)), dim3(256), 0, st, Pq, static_cast<T*>(dQv), Rq, L, L);
   FAVOR_LAUNCHED();
   // dS = phi(Q)^T G1                                       (m x D+1, contraction over G L)
   FAVOR_TRY((gemm_split<true, false>(phq, G1, dS, F(w.part), m, D1, GL, m, D1, (long long)GL * m,
-                                     (long long)GL * D1, BH, BH, BH, w.split_q, st)));
+                                     (long long)GL * D1, kIdent, kIdent, BH, w.split_q, st)));
   // dphi(K) = [V, 1] dS^T                                  (L x m)
   FAVOR_TRY((gemm<false, true>(v1, dS, dphk, L, m, D1, D1, D1, m, (long long)L * D1, (long long)m * D1,
-                               (long long)L * m, BH, BH, BH, st)));
+                               (long long)L * m, kIdent, kIdent, BH, st)));
   hipLaunchKernelGGL(feature_product, dim3(row_blocks(Rk)), dim3(256), 0, st, dphk, phk, tk, m, Rk);
   FAVOR_LAUNCHED();
-  FAVOR_TRY((gemm<false, false>(dphk, W, Pk, L, D, m, m, D, D, (long long)L * m, wstride, (long long)L * D, BH,
-                                wmod, BH, st)));
+  FAVOR_TRY((gemm<false, false>(dphk, W, Pk, L, D, m, m, D, D, (long long)L * m, wstride, (long long)L * D, kIdent,
+                                modulo(wmod), BH, st)));
   hipLaunchKernelGGL((input_grads<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, Pk, K, tk, static_cast<T*>(dKv),
-                     Rk);
+                     Rk, L, L);
   FAVOR_LAUNCHED();
   // dV = phi(K) dS_v                                       (L x D; dS rows have stride D+1)
   FAVOR_TRY((gemm<false, false>(phk, dS, dVf, L, D, m, m, D1, D, (long long)L * m, (long long)m * D1,
-                                (long long)L * D, BH, BH, BH, st)));
-  hipLaunchKernelGGL((to_dtype<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, dVf, static_cast<T*>(dVv), Rk);
+                                (long long)L * D, kIdent, kIdent, BH, st)));
+  hipLaunchKernelGGL((to_dtype<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, dVf, static_cast<T*>(dVv), Rk, L,
+                     L);
   FAVOR_LAUNCHED();
-#undef FAVOR_TRY
-#undef FAVOR_LAUNCHED
   return FAVOR_OK;
 }
 
-favor_status bwd_plan(const favor_problem* p, Plan* s) {
-  const favor_status st = make_plan(p, s);
-  if (st != FAVOR_OK) return st;
-  if (p->mode != FAVOR_BIDIRECTIONAL) return FAVOR_ERR_UNSUPPORTED;
+// ---- causal ----------------------------------------------------------------------------
+
+constexpr int kBwdChunk = GT;  // one 64 x 64 tile per chunk product
+
+struct CausalLayout {
+  size_t phq, cq, phk, ck, v1, Sx, Pm, ND, G1, A, dphq, tq, Pq, Rc, Rx, dphk, tk, Pk, dVf, bytes;
+  int NC, Lp;  // chunks per head, padded positions per head
+};
+
+CausalLayout causal_layout(const Plan& s) {
+  CausalLayout w;
+  w.NC = (s.L + kBwdChunk - 1) / kBwdChunk;
+  w.Lp = w.NC * kBwdChunk;
+  const size_t Rq = (size_t)s.B * s.Hq * w.Lp, Rk = (size_t)s.B * s.Hkv * w.Lp;
+  const size_t m = s.m, d1 = s.d + 1, C = kBwdChunk, f = sizeof(float);
+  const size_t Zq = (size_t)s.B * s.Hq * w.NC, Zk = (size_t)s.BH * w.NC;
+  size_t off = 0;
+  auto take = [&](size_t n) {
+    const size_t o = off;
+    off = a256(off + n * f);
+    return o;
+  };
+  w.phq = take(Rq * m);
+  w.cq = take(Rq);
+  w.phk = take(Rk * m);
+  w.ck = take(s.BH);
+  w.v1 = take(Rk * d1);
+  w.Sx = take(Zk * m * d1);
+  w.Pm = take(Rq * C);
+  w.ND = take(Rq * d1);
+  w.G1 = take(Rq * d1);
+  w.A = take(Rq * C);
+  w.dphq = take(Rq * m);
+  w.tq = take(Rq);
+  w.Pq = take(Rq * s.d);
+  w.Rc = take(Zq * m * d1);
+  w.Rx = take(Zk * m * d1);
+  w.dphk = take(Rk * m);
+  w.tk = take(Rk);
+  w.Pk = take(Rk * s.d);
+  w.dVf = take(Rk * s.d);
+  w.bytes = off;
+  return w;
+}
+
+template <class T, int D>
+favor_status run_bwd_causal(const Plan& s, const void* Qv, const void* Kv, const void* Vv, const float* W,
+                            const void* dOv, void* dQv, void* dKv, void* dVv, char* ws, hipStream_t st) {
+  const T* K = static_cast<const T*>(Kv);
+  const CausalLayout w = causal_layout(s);
+  auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
+  float *phq = F(w.phq), *phk = F(w.phk), *v1 = F(w.v1), *Sx = F(w.Sx), *Pm = F(w.Pm), *ND = F(w.ND);
+  float *G1 = F(w.G1), *A = F(w.A), *dphq = F(w.dphq), *tq = F(w.tq), *Pq = F(w.Pq), *Rc = F(w.Rc);
+  float *Rx = F(w.Rx), *dphk = F(w.dphk), *tk = F(w.tk), *Pk = F(w.Pk), *dVf = F(w.dVf);
+  const int C = kBwdChunk, NC = w.NC, Lp = w.Lp, L = s.L, m = s.m, D1 = D + 1, G = s.G;
+  const int BHk = s.BH, BHq = s.B * s.Hq, Zq = BHq * NC, Zk = BHk * NC;
+  const long long Rqp = (long long)BHq * Lp, Rkp = (long long)BHk * Lp;
+  const long long Rq = (long long)BHq * L, Rk = (long long)BHk * L;
+  const long long cm = (long long)C * m, cd1 = (long long)C * D1, cc = (long long)C * C, sm = (long long)m * D1;
+  const long long cd = (long long)C * D;
+  // query chunk z = (b Hq + hq) NC + c reads key chunk (b Hkv + hq / G) NC + c; key chunk
+  // z = bhk NC + c reads query chunk (bhk G + g) NC + c of group member g (base offset g NC)
+  const BMap key_of_q{G * NC, 0x7fffffff, NC, NC};
+  const BMap q_of_k{NC, 0x7fffffff, G * NC, NC};
+  const long long wstride = s.Hw == 1 ? 0 : (long long)m * D;
+  const BMap w_of_q{G, s.Hkv, 1, 1}, w_of_k = modulo(s.Hkv);
+  const dim3 scan_grid((unsigned)((sm + 255) / 256), (unsigned)BHk);
+  favor_status rc;
+
+  FAVOR_TRY(launch_features(s, 0, Qv, W, phq, F(w.cq), st, Lp));
+  FAVOR_TRY(launch_features(s, 1, Kv, W, phk, F(w.ck), st, Lp));
+  hipLaunchKernelGGL((ones_column<T, D>), dim3(row_blocks(Rkp)), dim3(256), 0, st, static_cast<const T*>(Vv), v1,
+                     Rkp, L, Lp);
+  FAVOR_LAUNCHED();
+  // S_c = phi(K_c)^T [V_c, 1] per chunk, then exclusive prefixes S_<c in place
+  FAVOR_TRY((gemm<true, false>(phk, v1, Sx, m, D1, C, m, D1, D1, cm, cd1, sm, kIdent, kIdent, Zk, st)));
+  hipLaunchKernelGGL(chunk_prefix, scan_grid, dim3(256), 0, st, Sx, NC, (int)sm);
+  FAVOR_LAUNCHED();
+  // P = tril(phi(Q_c) phi(K_c)^T);  [N, D] = P [V_c, 1] + phi(Q_c) S_<c
+  FAVOR_TRY((gemm<false, true>(phq, phk, Pm, C, C, m, m, m, C, cm, cm, cc, kIdent, key_of_q, Zq, st, kTril)));
+  FAVOR_TRY((gemm<false, false>(Pm, v1, ND, C, D1, C, C, D1, D1, cc, cd1, cd1, kIdent, key_of_q, Zq, st)));
+  FAVOR_TRY((gemm<false, false>(phq, Sx, ND, C, D1, m, m, D1, D1, cm, sm, cd1, kIdent, key_of_q, Zq, st, kAccum)));
+  hipLaunchKernelGGL((output_grads<T, D>), dim3(row_blocks(Rqp)), dim3(256), 0, st, ND, static_cast<const T*>(dOv),
+                     G1, Rqp, L, Lp);
+  FAVOR_LAUNCHED();
+  // A = tril(G1_c [V_c, 1]^T);  dphi(Q_c) = A phi(K_c) + G1_c S_<c^T
+  FAVOR_TRY((gemm<false, true>(G1, v1, A, C, C, D1, D1, D1, C, cd1, cd1, cc, kIdent, key_of_q, Zq, st, kTril)));
+  FAVOR_TRY((gemm<false, false>(A, phk, dphq, C, m, C, C, m, m, cc, cm, cm, kIdent, key_of_q, Zq, st)));
+  FAVOR_TRY((gemm<false, true>(G1, Sx, dphq, C, m, D1, D1, D1, m, cd1, sm, cm, kIdent, key_of_q, Zq, st, kAccum)));
+  hipLaunchKernelGGL(feature_product, dim3(row_blocks(Rqp)), dim3(256), 0, st, dphq, phq, tq, m, Rqp);
+  FAVOR_LAUNCHED();
+  // dQ = T W (the row-sum term is 0 for queries, as in the bidirectional case)
+  FAVOR_TRY((gemm<false, false>(dphq, W, Pq, Lp, D, m, m, D, D, (long long)Lp * m, wstride, (long long)Lp * D,
+                                kIdent, w_of_q, BHq, st)));
+  hipLaunchKernelGGL((to_dtype<T, D>), dim3(row_blocks(Rq)), dim3(256), 0, st, Pq, static_cast<T*>(dQv), Rq, L, Lp);
+  FAVOR_LAUNCHED();
+  // R_c = phi(Q_c)^T G1_c per query chunk; R_>c summed over later chunks and the G heads
+  FAVOR_TRY((gemm<true, false>(phq, G1, Rc, m, D1, C, m, D1, D1, cm, cd1, sm, kIdent, kIdent, Zq, st)));
+  hipLaunchKernelGGL(chunk_suffix, scan_grid, dim3(256), 0, st, Rc, Rx, NC, G, (int)sm);
+  FAVOR_LAUNCHED();
+  // dphi(K_c) = [V_c, 1] R_>c^T + sum_g A_g,c^T phi(Q_g,c)
+  FAVOR_TRY((gemm<false, true>(v1, Rx, dphk, C, m, D1, D1, D1, m, cd1, sm, cm, kIdent, kIdent, Zk, st)));
+  for (int g = 0; g < G; ++g)
+    FAVOR_TRY((gemm<true, false>(A + g * NC * cc, phq + g * NC * cm, dphk, C, m, C, C, m, m, cc, cm, cm, q_of_k,
+                                 q_of_k, Zk, st, kAccum)));
+  hipLaunchKernelGGL(feature_product, dim3(row_blocks(Rkp)), dim3(256), 0, st, dphk, phk, tk, m, Rkp);
+  FAVOR_LAUNCHED();
+  FAVOR_TRY((gemm<false, false>(dphk, W, Pk, Lp, D, m, m, D, D, (long long)Lp * m, wstride, (long long)Lp * D,
+                                kIdent, w_of_k, BHk, st)));
+  hipLaunchKernelGGL((input_grads<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, Pk, K, tk, static_cast<T*>(dKv),
+                     Rk, L, Lp);
+  FAVOR_LAUNCHED();
+  // dV_c = phi(K_c) R_>c,v + sum_g P_g,c^T g_g,c          (R and G1 rows have stride D+1)
+  FAVOR_TRY((gemm<false, false>(phk, Rx, dVf, C, D, m, m, D1, D, cm, sm, cd, kIdent, kIdent, Zk, st)));
+  for (int g = 0; g < G; ++g)
+    FAVOR_TRY((gemm<true, false>(Pm + g * NC * cc, G1 + g * NC * cd1, dVf, C, D, C, C, D1, D, cc, cd1, cd, q_of_k,
+                                 q_of_k, Zk, st, kAccum)));
+  hipLaunchKernelGGL((to_dtype<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, dVf, static_cast<T*>(dVv), Rk, L,
+                     Lp);
+  FAVOR_LAUNCHED();
   return FAVOR_OK;
 }
+#undef FAVOR_TRY
+#undef FAVOR_LAUNCHED
+
+size_t bwd_bytes(const Plan& s) {
+  return s.mode == FAVOR_CAUSAL ? causal_layout(s).bytes : bwd_layout(s).bytes;
+}
+
+// Validation as for the forward; the causal backward uses its own chunk of 64 whatever the
+// problem's chunk field asks of the forward.
+favor_status bwd_plan(const favor_problem* p, Plan* s) { return make_plan(p, s); }
 
 }  // namespace
 }  // namespace favor
 
 extern "C" size_t favor_bwd_workspace_bytes(const favor_problem* p) {
   favor::Plan s;
-  if (favor::bwd_plan(p, &s) != FAVOR_OK) return 0;
-  return favor::bwd_layout(s).bytes;
+  if (p == nullptr || favor::bwd_plan(p, &s) != FAVOR_OK) return 0;
+  return favor::bwd_bytes(s);
 }
 
 extern "C" favor_status favor_attn_bwd(const favor_problem* p, const void* Q, const void* K, const void* V,
                                        const float* W, const void* dout, void* dQ, void* dK, void* dV,
                                        void* workspace, size_t workspace_bytes, void* stream) {
   favor::Plan s;
+  if (p == nullptr) return FAVOR_ERR_INVALID_ARG;
   const favor_status st = favor::bwd_plan(p, &s);
   if (st != FAVOR_OK) return st;
   if (Q == nullptr || K == nullptr || V == nullptr || W == nullptr || dout == nullptr || dQ == nullptr ||
       dK == nullptr || dV == nullptr)
     return FAVOR_ERR_INVALID_ARG;
-  if (workspace == nullptr || workspace_bytes < favor::bwd_layout(s).bytes ||
+  if (workspace == nullptr || workspace_bytes < favor::bwd_bytes(s) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
     return FAVOR_ERR_WORKSPACE;
   char* ws = static_cast<char*>(workspace);
   hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (s.mode == FAVOR_CAUSAL) {
+    if (s.dtype == FAVOR_BF16)
+      return s.d == 64 ? favor::run_bwd_causal<favor::bf16, 64>(s, Q, K, V, W, dout, dQ, dK, dV, ws, hs)
+                       : favor::run_bwd_causal<favor::bf16, 128>(s, Q, K, V, W, dout, dQ, dK, dV, ws, hs);
+    return s.d == 64 ? favor::run_bwd_causal<float, 64>(s, Q, K, V, W, dout, dQ, dK, dV, ws, hs)
+                     : favor::run_bwd_causal<float, 128>(s, Q, K, V, W, dout, dQ, dK, dV, ws, hs);
+  }
   if (s.dtype == FAVOR_BF16)
     return s.d == 64 ? favor::run_bwd<favor::bf16, 64>(s, Q, K, V, W, dout, dQ, dK, dV, ws, hs)
                      : favor::run_bwd<favor::bf16, 128>(s, Q, K, V, W, dout, dQ, dK, dV, ws, hs);

@@ -14,7 +14,8 @@
 // term subtracted on the VALU).  Queries: one pass for the row maximum, a second that
 // recomputes the tile and writes phi.  Keys: a pass that folds the head maximum into an
 // order-preserving unsigned encoding with atomicMax (exact, so the result does not depend
-// on the order), then the writing pass, then a decode into c_out.
+// on the order), then the writing pass, then a decode into c_out.  Internal callers may ask
+// for Lo >= L output rows per head: rows L..Lo-1 of each head are then written as zeros.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -41,8 +42,8 @@ __device__ __forceinline__ float dec_order(unsigned k) {
 // 2: keys, writing pass with the head maximum from pass 1.
 template <class T, int D, int MODE>
 __global__ void __launch_bounds__(64 * kFeatWaves)
-    features_kernel(const T* __restrict__ X, const float* __restrict__ W, int L, int H, int G, int Hw, int m,
-                    float* __restrict__ phi, float* __restrict__ c_out) {
+    features_kernel(const T* __restrict__ X, const float* __restrict__ W, int L, int Lo, int H, int G, int Hw,
+                    int m, float* __restrict__ phi, float* __restrict__ c_out) {
   using P = Prec<T>;
   using wfrag = typename P::wfrag;
   constexpr int NKC = D / P::KS;
@@ -50,8 +51,8 @@ __global__ void __launch_bounds__(64 * kFeatWaves)
   const int hkv = h / G;  // G = query heads per kv head (1 on the key side)
   const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
   const int row = (blockIdx.x * kFeatWaves + wave) * 32 + col;
-  const bool valid = row < L;
-  const size_t grow = (size_t)bh * L + row;
+  const bool valid = row < L, out_row = row < Lo;
+  const size_t grow = (size_t)bh * L + row, orow = (size_t)bh * Lo + row;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
 
   wfrag xf[NKC];
@@ -79,13 +80,13 @@ __global__ void __launch_bounds__(64 * kFeatWaves)
   auto write = [&](float cst) {
     for (int ft = 0; ft < m / 32; ++ft) {
       const f32x16 e = tile(ft);
-      if (!valid) continue;
-      float* dst = phi + grow * m + 32 * ft + 4 * g;
+      if (!out_row) continue;
+      float* dst = phi + orow * m + 32 * ft + 4 * g;
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         f32x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = fast_exp2(e[4 * r4 + i] - cst) * inv_sqrt_m;
+        for (int i = 0; i < 4; ++i) v[i] = valid ? fast_exp2(e[4 * r4 + i] - cst) * inv_sqrt_m : 0.f;
         *reinterpret_cast<f32x4*>(dst + 8 * r4) = v;
       }
     }
@@ -104,7 +105,7 @@ __global__ void __launch_bounds__(64 * kFeatWaves)
   mx = fmaxf(mx, partner32(mx));  // the other half of this row's features
   if constexpr (MODE == 0) {
     write(mx);
-    if (valid && g == 0) c_out[grow] = mx / kLog2e;
+    if (valid && g == 0) c_out[orow] = mx / kLog2e;
   } else {
     if (!valid) mx = -INFINITY;
 #pragma unroll
@@ -124,13 +125,13 @@ __global__ void head_max_decode(float* c, int n) {
 }
 
 template <class T, int D>
-favor_status run_features(const Plan& s, int side, const void* Xv, const float* W, float* phi, float* c,
+favor_status run_features(const Plan& s, int side, const void* Xv, const float* W, float* phi, float* c, int Lo,
                           hipStream_t st) {
   const T* X = static_cast<const T*>(Xv);
   const dim3 block(64 * kFeatWaves);
-  const int row_blocks = (s.L + 32 * kFeatWaves - 1) / (32 * kFeatWaves);
+  const int row_blocks = (Lo + 32 * kFeatWaves - 1) / (32 * kFeatWaves);
   if (side == 0) {
-    hipLaunchKernelGGL((features_kernel<T, D, 0>), dim3(row_blocks, s.B * s.Hq), block, 0, st, X, W, s.L, s.Hq,
+    hipLaunchKernelGGL((features_kernel<T, D, 0>), dim3(row_blocks, s.B * s.Hq), block, 0, st, X, W, s.L, Lo, s.Hq,
                        s.G, s.Hw, s.m, phi, c);
     return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
   }
@@ -138,10 +139,10 @@ favor_status run_features(const Plan& s, int side, const void* Xv, const float* 
   const int ib = (nh + 255) / 256;
   hipLaunchKernelGGL(head_max_init, dim3(ib), dim3(256), 0, st, reinterpret_cast<unsigned*>(c), nh);
   if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
-  hipLaunchKernelGGL((features_kernel<T, D, 1>), dim3(row_blocks, nh), block, 0, st, X, W, s.L, s.Hkv, 1, s.Hw,
+  hipLaunchKernelGGL((features_kernel<T, D, 1>), dim3(row_blocks, nh), block, 0, st, X, W, s.L, Lo, s.Hkv, 1, s.Hw,
                      s.m, phi, c);
   if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
-  hipLaunchKernelGGL((features_kernel<T, D, 2>), dim3(row_blocks, nh), block, 0, st, X, W, s.L, s.Hkv, 1, s.Hw,
+  hipLaunchKernelGGL((features_kernel<T, D, 2>), dim3(row_blocks, nh), block, 0, st, X, W, s.L, Lo, s.Hkv, 1, s.Hw,
                      s.m, phi, c);
   if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
   hipLaunchKernelGGL(head_max_decode, dim3(ib), dim3(256), 0, st, c, nh);
@@ -151,12 +152,13 @@ favor_status run_features(const Plan& s, int side, const void* Xv, const float* 
 }  // namespace
 
 favor_status launch_features(const Plan& s, int side, const void* X, const float* W, float* phi, float* c,
-                             hipStream_t st) {
+                             hipStream_t st, int Lo) {
+  if (Lo < s.L) Lo = s.L;
   if (s.dtype == FAVOR_BF16)
-    return s.d == 64 ? run_features<bf16, 64>(s, side, X, W, phi, c, st)
-                     : run_features<bf16, 128>(s, side, X, W, phi, c, st);
-  return s.d == 64 ? run_features<float, 64>(s, side, X, W, phi, c, st)
-                   : run_features<float, 128>(s, side, X, W, phi, c, st);
+    return s.d == 64 ? run_features<bf16, 64>(s, side, X, W, phi, c, Lo, st)
+                     : run_features<bf16, 128>(s, side, X, W, phi, c, Lo, st);
+  return s.d == 64 ? run_features<float, 64>(s, side, X, W, phi, c, Lo, st)
+                   : run_features<float, 128>(s, side, X, W, phi, c, Lo, st);
 }
 
 }  // namespace favor

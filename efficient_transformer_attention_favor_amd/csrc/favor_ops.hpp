@@ -8,8 +8,9 @@
 namespace favor {
 
 // The feature map of the queries (side 0, row stabilisers) or keys (side 1, one stabiliser
-// per (batch, kv head)) as float32 [rows][m], stabilisers in natural-log units in c.
+// per (batch, kv head)) as float32 [rows][m], stabilisers in natural-log units in c.  With
+// Lo > L each head gets Lo rows of phi (and of c for queries), rows L..Lo-1 written as zero.
 favor_status launch_features(const Plan& s, int side, const void* X, const float* W, float* phi, float* c,
-                             hipStream_t st);
+                             hipStream_t st, int Lo = 0);
 
 }  // namespace favor

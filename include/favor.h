@@ -143,16 +143,20 @@ size_t favor_decode_state_bytes(const favor_problem* p);
 favor_status favor_attn_decode(const favor_problem* p, const void* q, const void* k, const void* v,
                                const float* W, float* state, void* out, void* stream);
 
-/* Gradients of bidirectional FAVOR+ with respect to Q, K and V (W fixed): for an upstream
- * gradient dout of out = favor_attn_fwd(Q, K, V, W), the gradients of sum(dout * out).
- * The pages give no backward pass: it follows from the linear-order definition (Performer
- * page, "제안 방법"; out = D^-1 A_hat V, KDEformer page, "提出的方法") by the chain rule,
- * with the multi-query head map (a kv head's dK and dV sum over its query heads).
+/* Gradients of FAVOR+ with respect to Q, K and V (W fixed): for an upstream gradient dout
+ * of out = favor_attn_fwd(Q, K, V, W) in the problem's mode, the gradients of
+ * sum(dout * out).  The pages give no backward pass: it follows from the linear-order
+ * definition (Performer page, "제안 방법"; out = D^-1 A_hat V, KDEformer page, "提出的方法")
+ * by the chain rule, with the multi-query head map (a kv head's dK and dV sum over its
+ * query heads).  Causal problems (inclusive mask j <= i) run over chunks of 64 positions
+ * with prefix sums of the key summaries and suffix sums of the query-side ones; p->chunk is
+ * validated as for the forward and otherwise ignored.
  * dout, dQ like Q, dK and dV like K (device pointers, p->dtype; float32 arithmetic inside).
- * p->mode must be FAVOR_BIDIRECTIONAL (FAVOR_ERR_UNSUPPORTED otherwise).  The workspace
- * (favor_bwd_workspace_bytes(p) bytes, 256-byte aligned, caller-owned) holds the float32
- * feature matrices phi(Q), phi(K) and their gradients: about 4 m (B Hq L + B Hkv L) floats.
- * Errors as for favor_attn_fwd.  Queues about 20 kernels on `stream`. */
+ * The workspace (favor_bwd_workspace_bytes(p) bytes, 256-byte aligned, caller-owned) holds
+ * the float32 feature matrices phi(Q), phi(K) and their gradients, about
+ * 4 m (B Hq L + B Hkv L) floats, and for causal problems also the per-chunk summaries,
+ * about 2 (B Hq + B Hkv) (L / 64) m (d+1) floats.  Errors as for favor_attn_fwd.  Queues
+ * about 20 kernels (causal: 25 + 2 heads_q / heads_kv) on `stream`. */
 size_t favor_bwd_workspace_bytes(const favor_problem* p);
 favor_status favor_attn_bwd(const favor_problem* p, const void* Q, const void* K, const void* V,
                             const float* W, const void* dout, void* dQ, void* dK, void* dV,

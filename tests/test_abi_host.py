@@ -112,8 +112,14 @@ def test_backward_validation():
     need = _lib.bwd_workspace_bytes(p)
     assert need > 0 and need % 256 == 0
     causal = _p(mode=_lib.FAVOR_CAUSAL)
-    assert _lib.bwd_workspace_bytes(causal) == 0
-    assert _lib.attn_bwd(causal, 8, 8, 8, 8, 8, 8, 8, 8, 256, need, None) == _lib.FAVOR_ERR_UNSUPPORTED
+    cneed = _lib.bwd_workspace_bytes(causal)
+    assert cneed > need and cneed % 256 == 0
+    assert _lib.attn_bwd(causal, *([8] * 8), 256, cneed - 1, None) == _lib.FAVOR_ERR_WORKSPACE
+    assert _lib.bwd_workspace_bytes(_p(head_dim=32)) == 0
+    assert _lib.attn_bwd(_p(head_dim=32), *([8] * 8), 256, need, None) == _lib.FAVOR_ERR_UNSUPPORTED
+    assert _lib.attn_bwd(_p(mode=_lib.FAVOR_CAUSAL, chunk=48), *([8] * 8), 256, cneed, None) == \
+        _lib.FAVOR_ERR_UNSUPPORTED
+    assert _lib.attn_bwd(None, *([8] * 8), 256, need, None) == _lib.FAVOR_ERR_INVALID_ARG
     for i in range(8):
         args = [8] * 8
         args[i] = None

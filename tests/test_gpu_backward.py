@@ -1,4 +1,4 @@
-"""Gradients of bidirectional FAVOR+ (favor_attn_bwd) against the float64 oracle.
+"""Gradients of FAVOR+ (favor_attn_bwd), bidirectional and causal, against the float64 oracle.
 
 The oracle's gradients (``favor_grads``) are the chain rule written out from the linear-order
 definition and pinned by central differences in tests/test_oracle.py.  Metric: the largest
@@ -7,7 +7,8 @@ forward's bars (1e-4 float32, 2e-2 bf16).  A row-wise metric does not fit gradie
 of dQ is a sum over the m features of terms (dphi * phi)_f w_f that nearly cancel for some
 rows (the terms are ~1e6 times the result in these cases), so any float32 evaluation has a
 large error relative to such a row but not relative to the gradient as a whole.  The
-row-wise figure is printed alongside.
+row-wise figure is printed alongside.  At the full workload sizes the oracle computes the
+gradients of one kv head (and its query heads), which depend on nothing else.
 """
 import sys
 
@@ -37,8 +38,8 @@ def _dev(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x)).to(device="cuda").to(dtype)
 
 
-def _small(name, **kw):
-    return I.workload(name).replace(name=f"{name}_bwd", causal=False, **kw)
+def _small(name, causal=False, **kw):
+    return I.workload(name).replace(name=f"{name}_bwd", causal=causal, **kw)
 
 
 CASES = [
@@ -50,11 +51,23 @@ CASES = [
     _small("c1_bidir_f32", batch=2, heads_q=2, heads_kv=1, heads_w=1, seq_len=97, head_dim=128, num_features=192),
 ]
 
+# causal: ragged tails (L not a multiple of the 64-position chunk), one chunk, MQA groups
+CAUSAL_CASES = [
+    _small("c3_causal_bf16", True, batch=2, heads_q=4, heads_kv=2, heads_w=2, seq_len=200, num_features=128),
+    _small("c3_causal_bf16", True, batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=64),
+    _small("c3_causal_bf16", True, batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=31, num_features=64),
+    _small("c4_mqa_bidir_bf16", True, batch=2, heads_q=4, heads_kv=1, heads_w=1, seq_len=150),
+    _small("c5_causal_long_bf16", True, batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=300),  # m = 512, heavy rows
+    _small("c1_bidir_f32", True, seq_len=300),
+    _small("c1_bidir_f32", True, batch=2, heads_q=2, heads_kv=1, heads_w=1, seq_len=97, head_dim=128,
+           num_features=192),
+]
+
 
 def _grads(w, Q, K, V, W, dO):
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     q, k, v, do = _dev(Q, dt), _dev(K, dt), _dev(V, dt), _dev(dO, dt)
-    dq, dk, dv = api.attn_bwd(q, k, v, _dev(W, torch.float32), do)
+    dq, dk, dv = api.attn_bwd(q, k, v, _dev(W, torch.float32), do, causal=w.causal)
     torch.cuda.synchronize()
     return [x.float().cpu().numpy() for x in (dq, dk, dv)]
 
@@ -64,14 +77,14 @@ def _upstream(w, seed=0):
     return I.round_to_bf16(g) if w.dtype == "bf16" else g
 
 
-@pytest.mark.parametrize("w", CASES, ids=lambda w: f"{w.dtype}_B{w.batch}H{w.heads_q}/{w.heads_kv}"
-                         f"_L{w.seq_len}_d{w.head_dim}_m{w.num_features}")
+@pytest.mark.parametrize("w", CASES + CAUSAL_CASES, ids=lambda w: f"{'causal' if w.causal else 'bidir'}_{w.dtype}"
+                         f"_B{w.batch}H{w.heads_q}/{w.heads_kv}_L{w.seq_len}_d{w.head_dim}_m{w.num_features}")
 def test_backward_matches_oracle(w):
     _say(f"backward parity {w}")
     Q, K, V, W = I.make_inputs(w, seed=0)
     dO = _upstream(w)
     got = _grads(w, Q, K, V, W, dO)
-    ref = O.favor_grads(Q, K, V, W, dO)
+    ref = O.favor_grads(Q, K, V, W, dO, causal=w.causal)
     for name, g, r in zip(("dQ", "dK", "dV"), got, ref):
         err = _tensor_rel_err(g, r)
         _say(f"  {name}: rel err {err:.3e} (row-wise {O.rowwise_rel_err(g, r):.3e})")
@@ -94,3 +107,56 @@ def test_backward_constant_values():
     V = np.ones_like(V)
     dq, dk, _ = _grads(w, Q, K, V, W, _upstream(w, 1))
     assert np.max(np.abs(dq)) < 1e-4 and np.max(np.abs(dk)) < 1e-4
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_deterministic_modes(causal):
+    w = (CASES if not causal else CAUSAL_CASES)[3]
+    Q, K, V, W = I.make_inputs(w, seed=4)
+    dO = _upstream(w, 4)
+    a = _grads(w, Q, K, V, W, dO)
+    b = _grads(w, Q, K, V, W, dO)
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_causal_backward_single_position():
+    """L = 1: out = v_0 whatever Q and K are, so dQ = dK = 0 and dV_0 = the sum of dout over
+    the query heads of the kv head."""
+    w = _small("c3_causal_bf16", True, batch=2, heads_q=4, heads_kv=2, heads_w=2, seq_len=1, num_features=64)
+    Q, K, V, W = I.make_inputs(w, seed=2)
+    dO = _upstream(w, 2)
+    dq, dk, dv = _grads(w, Q, K, V, W, dO)
+    assert np.max(np.abs(dq)) < 1e-5 and np.max(np.abs(dk)) < 1e-5
+    ref = dO.reshape(w.batch, w.heads_kv, 2, 1, w.head_dim).astype(np.float64).sum(axis=2)
+    assert np.max(np.abs(dv - ref)) <= 2e-2 * np.max(np.abs(ref))
+
+
+def test_causal_backward_last_row_matches_bidirectional():
+    """An upstream gradient on the last position only: the causal gradients are the
+    bidirectional ones (the last query row sees every key)."""
+    w = CAUSAL_CASES[5]
+    Q, K, V, W = I.make_inputs(w, seed=6)
+    dO = np.zeros((w.batch, w.heads_q, w.seq_len, w.head_dim), np.float32)
+    dO[:, :, -1] = np.random.default_rng(6).standard_normal((w.batch, w.heads_q, w.head_dim))
+    c = _grads(w, Q, K, V, W, dO)
+    b = _grads(w.replace(causal=False), Q, K, V, W, dO)
+    for x, y in zip(c, b):
+        assert np.max(np.abs(x - y)) <= 1e-5 * np.max(np.abs(y))
+
+
+@pytest.mark.parametrize("name", ["c2_bidir_bf16", "c3_causal_bf16", "c4_mqa_bidir_bf16", "c5_causal_long_bf16"])
+def test_backward_full_size_one_head(name):
+    """Full workload sizes on the GPU; the oracle's gradients of kv head (b, hkv) = (0, 0) and
+    its query heads, which no other head influences."""
+    w = I.workload(name)
+    _say(f"backward full size {name}")
+    Q, K, V, W = I.make_inputs(w, seed=0)
+    dO = _upstream(w)
+    got = _grads(w, Q, K, V, W, dO)
+    G = w.heads_q // w.heads_kv
+    sl = (slice(0, 1), slice(0, G))
+    ref = O.favor_grads(Q[sl], K[:1, :1], V[:1, :1], W[:1], dO[sl], causal=w.causal)
+    for name_, g, r in zip(("dQ", "dK", "dV"), (got[0][sl], got[1][:1, :1], got[2][:1, :1]), ref):
+        err = _tensor_rel_err(g, r)
+        _say(f"  {name_}: rel err {err:.3e}")
+        assert err <= TOL[w.dtype], name_
