@@ -173,7 +173,13 @@ def main():
                          "head layout instead of the forward pass")
     ap.add_argument("--prefill", type=int, default=256, help="positions decoded before timing (--decode)")
     ap.add_argument("--backward", action="store_true",
-                    help="time favor_attn_bwd (gradients of Q, K, V; bidirectional workloads) instead of the forward")
+                    help="time favor_attn_bwd (gradients of Q, K, V) instead of the forward")
+    ap.add_argument("--approx-study", action="store_true",
+                    help="error of FAVOR+ against exact softmax over feature counts and seeds, orthogonal vs "
+                         "i.i.d. features drawn on the device (favor_draw_features); no timing")
+    ap.add_argument("--seeds", type=int, default=8, help="feature draws per setting (--approx-study)")
+    ap.add_argument("--qk-scale", type=float, default=1.0,
+                    help="multiply the workload's Q and K by this factor (--approx-study; 1 = the workload)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -194,6 +200,8 @@ def main():
         return decode_main(args, w)
     if args.backward:
         return backward_main(args, w)
+    if args.approx_study:
+        return approx_study(args, w)
     Q, K, V, W = I.make_inputs(w, seed=0)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
@@ -464,6 +472,67 @@ def backward_main(args, w):
                      "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["f32"], 4),
                      "traffic": None, "per_launch": {"alg_flops": flops, "exec_flops": exec_flops, "alg_bytes": alg_bytes,
                                                      "avg_ms": round(ms_step, 5)}},
+    }
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+def approx_study(args, w):
+    """Error of FAVOR+ against exact softmax attention over the feature count m and args.seeds
+    draws of W, orthogonal vs i.i.d. rows, both drawn on the device from consecutive seeds
+    (Performer page, "제안 방법" and "주요 결과": orthogonal features lower the estimator's
+    error).  Inputs: the workload's Q, K, V (Q and K times --qk-scale, which sets the kernel's
+    temperature and so the features' variance); 256 sampled query rows; exact softmax on those
+    rows in float32 on the GPU.  Metric per setting: RMS over the sampled rows' entries of
+    (FAVOR+ - softmax), mean and standard deviation over the draws.  One JSON line."""
+    import numpy as np
+    import torch
+
+    from efficient_transformer_attention_favor_amd import api
+    from efficient_transformer_attention_favor_amd import inputs as I
+
+    Q, K, V, _ = I.make_inputs(w, seed=0)
+    Q, K = Q * args.qk_scale, K * args.qk_scale
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev).to(dt) for x in (Q, K, V))
+    rows = I.sample_rows(w, 256)
+    G = w.heads_q // w.heads_kv
+    exact = []
+    for b, h, i in rows:  # softmax(q_i K^T) V on the (masked) keys, float32
+        n = int(i) + 1 if w.causal else w.seq_len
+        kk = k[b, h // G, :n].float()
+        s = kk @ q[b, h, i].float()
+        exact.append(torch.softmax(s, dim=0) @ v[b, h // G, :n].float())
+    exact = torch.stack(exact)
+    bi, hi, ii = (torch.as_tensor(rows[:, j], device=dev) for j in range(3))
+    table = []
+    for m in (64, 128, 256, 512):
+        entry = {"m": m}
+        for kind, orth in (("orf", True), ("iid", False)):
+            errs = []
+            for sd in range(args.seeds):
+                Wd = api.draw_features(w.heads_w, m, w.head_dim, 1000 * m + sd, orth)
+                y = api.attn_fwd(q, k, v, Wd, causal=w.causal)
+                got = y[bi, hi, ii].float()
+                errs.append(float(torch.sqrt(torch.mean((got - exact) ** 2))))
+                del y
+            entry[f"{kind}_rms"] = round(float(np.mean(errs)), 6)
+            entry[f"{kind}_std"] = round(float(np.std(errs)), 6)
+        entry["orf_over_iid"] = round(entry["orf_rms"] / entry["iid_rms"], 4)
+        log(f"m={m}: {entry}")
+        table.append(entry)
+    res = {
+        "metric": "FAVOR+ RMS error vs exact softmax attention (256 sampled rows)",
+        "unit": "RMS", "higher_is_better": False, "seeds": args.seeds, "dtype": w.dtype,
+        "data": "synthetic (seeded Gaussian Q, K, V; W drawn on the device by favor_draw_features)",
+        "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
+                   "heads_w": w.heads_w, "seq_len": w.seq_len, "head_dim": w.head_dim,
+                   "mode": "causal" if w.causal else "bidirectional", "qk_scale": args.qk_scale},
+        "table": table,
     }
     line = json.dumps(res)
     print(line, flush=True)

@@ -25,7 +25,7 @@ FAVOR_FWD_KERNELS = 3
 
 EXPORTED = ("favor_workspace_bytes", "favor_attn_fwd", "favor_attn_fwd_timed", "favor_features",
             "favor_decode_state_bytes", "favor_attn_decode", "favor_bwd_workspace_bytes", "favor_attn_bwd",
-            "favor_status_string", "favor_abi_version")
+            "favor_draw_features", "favor_status_string", "favor_abi_version")
 
 
 class FavorProblem(ctypes.Structure):
@@ -70,6 +70,9 @@ def lib() -> ctypes.CDLL:
         L.favor_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.favor_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.favor_attn_bwd.restype = ctypes.c_int
+        L.favor_draw_features.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64,
+                                          ctypes.c_int32, vp, vp]
+        L.favor_draw_features.restype = ctypes.c_int
         L.favor_status_string.argtypes = [ctypes.c_int]
         L.favor_status_string.restype = ctypes.c_char_p
         L.favor_abi_version.argtypes = []
@@ -128,6 +131,10 @@ def bwd_workspace_bytes(p: FavorProblem) -> int:
 def attn_bwd(p: FavorProblem, q, k, v, w, dout, dq, dk, dv, workspace, workspace_nbytes, stream) -> int:
     return int(lib().favor_attn_bwd(_ref(p), q, k, v, w, dout, dq, dk, dv, workspace,
                                     ctypes.c_size_t(workspace_nbytes), stream))
+
+
+def draw_features(heads_w, num_features, head_dim, seed, orthogonal, w, stream) -> int:
+    return lib().favor_draw_features(heads_w, num_features, head_dim, seed, int(orthogonal), w, stream)
 
 
 def abi_version() -> int:

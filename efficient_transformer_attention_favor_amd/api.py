@@ -159,3 +159,15 @@ def attn_bwd(Q, K, V, W, dout, causal=False, workspace=None, stream=None):
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_attn_bwd")
     return dQ, dK, dV
+
+
+def draw_features(heads_w, num_features, head_dim, seed, orthogonal=True, device="cuda", stream=None):
+    """W [heads_w][num_features][head_dim] float32 drawn on the device from `seed`
+    (orthogonal random features, or i.i.d. Gaussian rows with orthogonal=False)."""
+    W = torch.empty((heads_w, num_features, head_dim), dtype=torch.float32, device=device)
+    if stream is None:
+        stream = torch.cuda.current_stream(W.device)
+    st = _lib.draw_features(heads_w, num_features, head_dim, int(seed), orthogonal, W.data_ptr(), stream.cuda_stream)
+    if st != _lib.FAVOR_OK:
+        raise _lib.FavorError(st, "favor_draw_features")
+    return W

@@ -116,6 +116,24 @@ favor_status favor_attn_fwd_timed(const favor_problem* p, const void* Q, const v
 favor_status favor_features(const favor_problem* p, int32_t side, const void* X, const float* W,
                             float* phi_out, float* c_out, void* stream);
 
+/* Random feature matrix drawn on the device from a seed: W [heads_w][num_features][head_dim]
+ * float32 (device pointer, caller-owned).  Orthogonal random features (Performer page,
+ * "제안 방법": random features with orthogonal rows lower the estimator's variance) when
+ * orthogonal = 1: per block of head_dim rows, a standard Gaussian head_dim x head_dim
+ * matrix whose rows are orthonormalised by modified Gram-Schmidt in row order (float64)
+ * and rescaled by the lengths of the Gaussian rows; rows past num_features in the last
+ * block are dropped.  orthogonal = 0: the Gaussian rows themselves (i.i.d. features).
+ * The Gaussians come from a counter-based stream that depends on the seed only:
+ * Philox4x32-10 (Salmon et al., SC 2011) with key (seed mod 2^32, seed div 2^32) on
+ * counter (p mod 2^32, p div 2^32, 0, 0) for the p-th pair, Box-Muller on two 53-bit
+ * uniforms taken from the output's 64-bit halves; number e = ((h nblocks + b) d + i) d + j
+ * fills head h, block b, row i, column j.  The same seed gives the same W on every device.
+ * 1 <= head_dim <= 128 (else FAVOR_ERR_UNSUPPORTED), 1 <= num_features, heads_w <= 65536,
+ * orthogonal in {0, 1}, W not null (else FAVOR_ERR_INVALID_ARG).  Queues 1 kernel
+ * (heads_w * ceil(num_features / head_dim) workgroups) on `stream`. */
+favor_status favor_draw_features(int32_t heads_w, int32_t num_features, int32_t head_dim, uint64_t seed,
+                                 int32_t orthogonal, float* W, void* stream);
+
 /* Causal decoding, one new position per (batch, head) per call.
  *
  * The causal mode is a running sum over positions (FAVOR+ in linear order, Performer page,

@@ -128,3 +128,14 @@ def test_backward_validation():
     assert _lib.attn_bwd(p, *([8] * 8), 256, need - 1, None) == _lib.FAVOR_ERR_WORKSPACE
     assert _lib.attn_bwd(p, *([8] * 8), 260, need, None) == _lib.FAVOR_ERR_WORKSPACE
     assert _lib.bwd_workspace_bytes(_p(seq_len=4096)) > need
+
+
+def test_draw_features_validation():
+    L = _lib
+    assert L.draw_features(1, 64, 64, 0, True, None, None) == L.FAVOR_ERR_INVALID_ARG
+    assert L.draw_features(0, 64, 64, 0, True, 256, None) == L.FAVOR_ERR_INVALID_ARG
+    assert L.draw_features(1, 0, 64, 0, True, 256, None) == L.FAVOR_ERR_INVALID_ARG
+    assert L.draw_features(1, 64, 0, 0, True, 256, None) == L.FAVOR_ERR_INVALID_ARG
+    assert L.draw_features(1, 64, 64, 0, 2, 256, None) == L.FAVOR_ERR_INVALID_ARG
+    assert L.draw_features(1, 64, 129, 0, True, 256, None) == L.FAVOR_ERR_UNSUPPORTED
+    assert L.draw_features(65537, 64, 64, 0, True, 256, None) == L.FAVOR_ERR_INVALID_ARG
