@@ -51,6 +51,9 @@ __all__ = [
     "softmax_rows",
     "head_maps",
     "rowwise_rel_err",
+    "relu_feature_map",
+    "generalized_attention",
+    "generalized_rows",
 ]
 
 _F = np.float64
@@ -263,6 +266,71 @@ def favor_grads(Q, K, V, W, dOut, causal=False):
             dK[b, hk] += dk
             dV[b, hk] += dv
     return dQ, dK, dV
+
+
+def relu_feature_map(X, W):
+    """phi(x) = ReLU(W x) / sqrt(m): a non-negative random feature map for a kernel other than
+    softmax (Performer page, "ABSTRACT": FAVOR+ also models kernelisable attention beyond
+    softmax).  For w ~ N(0, I_d), m E[phi(x) . phi(y)] = E[ReLU(w.x) ReLU(w.y)], the
+    first-order arc-cosine kernel |x||y| (sin t + (pi - t) cos t) / (2 pi), t the angle
+    between x and y (pinned in tests/test_oracle.py)."""
+    X = np.asarray(X, dtype=_F)
+    W = np.asarray(W, dtype=_F)
+    return np.maximum(X @ W.T, 0.0) / np.sqrt(W.shape[0])
+
+
+def _ratio(num, den):
+    # a row whose weights are all zero (possible with ReLU features) gets a zero output
+    out = np.zeros_like(num)
+    ok = den > 0
+    out[ok] = num[ok] / den[ok, None]
+    return out
+
+
+def generalized_attention(Q, K, V, W, causal=False, fn="relu"):
+    """D^-1 A V with A = phi(Q) phi(K)^T for the feature map `fn` (KDEformer page, "提出的方法":
+    attention as D^-1 A V), evaluated in linear order phi(Q) (phi(K)^T [V, 1]) per head, the
+    causal mask j <= i as a running sum.  (B, Hq, L, d) float64."""
+    if fn != "relu":
+        raise ValueError(fn)
+    B, Hq, L, d = Q.shape
+    Hkv, Hw = K.shape[1], W.shape[0]
+    kv_of, w_of = head_maps(Hq, Hkv, Hw)
+    out = np.empty((B, Hq, L, d))
+    for b in range(B):
+        for hq in range(Hq):
+            hk = kv_of[hq]
+            pq = relu_feature_map(Q[b, hq], W[w_of[hk]])
+            pk = relu_feature_map(K[b, hk], W[w_of[hk]])
+            v = np.asarray(V[b, hk], dtype=_F)
+            if causal:
+                Sv = np.cumsum(pk[:, :, None] * v[:, None, :], axis=0)   # (L, m, d) prefixes
+                S1 = np.cumsum(pk, axis=0)
+                num = np.einsum("lf,lfd->ld", pq, Sv)
+                den = np.einsum("lf,lf->l", pq, S1)
+            else:
+                num = pq @ (pk.T @ v)
+                den = pq @ pk.sum(axis=0)
+            out[b, hq] = _ratio(num, den)
+    return out
+
+
+def generalized_rows(Q, K, V, W, rows, causal=False, fn="relu"):
+    """The same at the listed (b, hq, i) rows, by the row definition sum_j a_ij v_j / sum_j a_ij."""
+    if fn != "relu":
+        raise ValueError(fn)
+    B, Hq, L, d = Q.shape
+    Hkv, Hw = K.shape[1], W.shape[0]
+    kv_of, w_of = head_maps(Hq, Hkv, Hw)
+    out = np.empty((len(rows), d))
+    for n, (b, hq, i) in enumerate(np.asarray(rows)):
+        hk = kv_of[int(hq)]
+        n_keys = int(i) + 1 if causal else L
+        pk = relu_feature_map(K[b, hk, :n_keys], W[w_of[hk]])
+        a = pk @ relu_feature_map(Q[b, hq, i][None, :], W[w_of[hk]])[0]
+        s = a.sum()
+        out[n] = (a @ np.asarray(V[b, hk, :n_keys], dtype=_F)) / s if s > 0 else 0.0
+    return out
 
 
 def softmax_head(q, k, v, causal=False):

@@ -440,3 +440,52 @@ def test_causal_grads_vanish_for_constant_values():
     W = orf_matrix(m, d, rng)
     dq, dk, _ = O.favor_head_grads(q, k, np.ones((L, d)), W, rng.standard_normal((L, d)), causal=True)
     assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
+
+
+# ---- generalised attention: ReLU random features ----------------------------------------
+
+def test_relu_features_estimate_the_arc_cosine_kernel():
+    """Pin: with many i.i.d. Gaussian features, phi(x) . phi(y) tends to the first-order
+    arc-cosine kernel |x||y| (sin t + (pi - t) cos t) / (2 pi) (closed form of
+    E[ReLU(w.x) ReLU(w.y)] for w ~ N(0, I))."""
+    rng = np.random.default_rng(21)
+    d, m = 3, 400_000
+    W = rng.standard_normal((m, d))
+    for _ in range(3):
+        x, y = rng.standard_normal((2, d))
+        est = float(O.relu_feature_map(x[None], W)[0] @ O.relu_feature_map(y[None], W)[0])
+        t = np.arccos(np.clip(x @ y / np.linalg.norm(x) / np.linalg.norm(y), -1, 1))
+        exact = np.linalg.norm(x) * np.linalg.norm(y) * (np.sin(t) + (np.pi - t) * np.cos(t)) / (2 * np.pi)
+        # Monte Carlo error: std <= sqrt(3) |x||y| / sqrt(m) = 0.0027 |x||y|
+        assert abs(est - exact) < 0.01 * np.linalg.norm(x) * np.linalg.norm(y)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_generalized_linear_order_equals_row_definition(causal):
+    rng = np.random.default_rng(22)
+    B, Hq, Hkv, L, d, m = 2, 4, 2, 33, 8, 32
+    Q, K, V = rng.standard_normal((B, Hq, L, d)), rng.standard_normal((B, Hkv, L, d)), rng.standard_normal((B, Hkv, L, d))
+    W = rng.standard_normal((Hkv, m, d))
+    full = O.generalized_attention(Q, K, V, W, causal)
+    rows = np.array([(b, h, i) for b in range(B) for h in range(Hq) for i in range(L)])
+    by_row = O.generalized_rows(Q, K, V, W, rows, causal).reshape(full.shape)
+    assert np.max(np.abs(full - by_row)) < 1e-12
+    ones = O.generalized_attention(Q, K, np.ones_like(V), W, causal)
+    assert np.max(np.abs(ones - 1)) < 1e-12
+
+
+def test_generalized_zero_weights_give_zero_rows():
+    """A query whose ReLU features are all zero has no weight on any key: its row is 0 (the
+    reading for 0/0); a single position otherwise returns its value."""
+    d, m = 4, 16
+    rng = np.random.default_rng(23)
+    W = np.abs(rng.standard_normal((1, m, d)))          # every row has positive entries
+    Q = np.zeros((1, 1, 3, d))
+    Q[0, 0, 0] = -1.0                                    # W q < 0 for every feature
+    Q[0, 0, 1:] = np.abs(rng.standard_normal((2, d)))
+    K = np.abs(rng.standard_normal((1, 1, 3, d)))
+    V = rng.standard_normal((1, 1, 3, d))
+    out = O.generalized_attention(Q, K, V, W)
+    assert np.all(out[0, 0, 0] == 0) and np.all(np.abs(out[0, 0, 1:]) > 0)
+    one = O.generalized_attention(Q[:, :, 1:2], K[:, :, :1], V[:, :, :1], W)
+    assert np.max(np.abs(one[0, 0, 0] - V[0, 0, 0])) < 1e-12
