@@ -174,6 +174,8 @@ def main():
     ap.add_argument("--prefill", type=int, default=256, help="positions decoded before timing (--decode)")
     ap.add_argument("--backward", action="store_true",
                     help="time favor_attn_bwd (gradients of Q, K, V) instead of the forward")
+    ap.add_argument("--generalized", default="", choices=["", "relu"],
+                    help="time favor_attn_fwd_generalized with this feature map instead of the softmax forward")
     ap.add_argument("--approx-study", action="store_true",
                     help="error of FAVOR+ against exact softmax over feature counts and seeds, orthogonal vs "
                          "i.i.d. features drawn on the device (favor_draw_features); no timing")
@@ -202,6 +204,8 @@ def main():
         return backward_main(args, w)
     if args.approx_study:
         return approx_study(args, w)
+    if args.generalized:
+        return generalized_main(args, w)
     Q, K, V, W = I.make_inputs(w, seed=0)
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
@@ -472,6 +476,71 @@ def backward_main(args, w):
                      "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["f32"], 4),
                      "traffic": None, "per_launch": {"alg_flops": flops, "exec_flops": exec_flops, "alg_bytes": alg_bytes,
                                                      "avg_ms": round(ms_step, 5)}},
+    }
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+def generalized_main(args, w):
+    """Kernelised attention with the ReLU feature map (favor_attn_fwd_generalized): one step =
+    one call on the workload (inputs resident).  Algorithmic flops as for the softmax forward
+    (features of Q and K, S, phi(Q) S); float32 products, so the roofline is float32."""
+    import numpy as np
+    import torch
+
+    from efficient_transformer_attention_favor_amd import _lib, api
+    from efficient_transformer_attention_favor_amd import inputs as I
+
+    Q, K, V, W = I.make_inputs(w, seed=0)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(x).to(dev).to(dt) for x in (Q, K, V))
+    wd = torch.from_numpy(W).to(dev)
+    p = api._problem(q, k, wd, w.causal, 0)
+    fn = _lib.FAVOR_FEATURE_RELU
+    nbytes = _lib.generalized_workspace_bytes(p, fn)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), wd.data_ptr(), out.data_ptr(), ws.data_ptr())
+
+    def step():
+        st = _lib.attn_fwd_generalized(p, fn, *ptrs, nbytes, stream.cuda_stream)
+        if st != _lib.FAVOR_OK:
+            raise _lib.FavorError(st, "favor_attn_fwd_generalized")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = start.elapsed_time(end) / args.steps
+    B, Hq, Hkv, L, d, m = w.batch, w.heads_q, w.heads_kv, w.seq_len, w.head_dim, w.num_features
+    Rq, Rk = B * Hq * L, B * Hkv * L
+    flops = 2 * m * ((Rq + Rk) * d + (Rq + Rk) * (d + 1))
+    achieved = flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "kernelised attention (ReLU random features) fwd tokens/s (B*H*L/s), 1 GPU",
+        "value": round(Rq / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded Gaussian Q, K, V; orthogonal random features W)",
+        "config": {"workload": f"{w.name} relu features", "batch": B, "heads_q": Hq, "heads_kv": Hkv,
+                   "heads_w": w.heads_w, "seq_len": L, "head_dim": d, "num_features": m,
+                   "input_dtype": w.dtype, "mode": "causal" if w.causal else "bidirectional",
+                   "parallelism": "single GPU"},
+        "roofline": {"kernel": "favor_attn_fwd_generalized (all kernels)", "bound": "alu",
+                     "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS["f32"], 4), "traffic": None,
+                     "per_launch": {"alg_flops": flops, "avg_ms": round(ms_step, 5)}},
     }
     line = json.dumps(res)
     print(line, flush=True)

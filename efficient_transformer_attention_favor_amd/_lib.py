@@ -22,10 +22,12 @@ FAVOR_BIDIRECTIONAL = 0
 FAVOR_CAUSAL = 1
 
 FAVOR_FWD_KERNELS = 3
+FAVOR_FEATURE_RELU = 1
 
 EXPORTED = ("favor_workspace_bytes", "favor_attn_fwd", "favor_attn_fwd_timed", "favor_features",
             "favor_decode_state_bytes", "favor_attn_decode", "favor_bwd_workspace_bytes", "favor_attn_bwd",
-            "favor_draw_features", "favor_status_string", "favor_abi_version")
+            "favor_draw_features", "favor_generalized_workspace_bytes", "favor_attn_fwd_generalized",
+            "favor_status_string", "favor_abi_version")
 
 
 class FavorProblem(ctypes.Structure):
@@ -70,6 +72,10 @@ def lib() -> ctypes.CDLL:
         L.favor_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.favor_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.favor_attn_bwd.restype = ctypes.c_int
+        L.favor_generalized_workspace_bytes.argtypes = [P, ctypes.c_int32]
+        L.favor_generalized_workspace_bytes.restype = ctypes.c_size_t
+        L.favor_attn_fwd_generalized.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.favor_attn_fwd_generalized.restype = ctypes.c_int
         L.favor_draw_features.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_uint64,
                                           ctypes.c_int32, vp, vp]
         L.favor_draw_features.restype = ctypes.c_int
@@ -131,6 +137,14 @@ def bwd_workspace_bytes(p: FavorProblem) -> int:
 def attn_bwd(p: FavorProblem, q, k, v, w, dout, dq, dk, dv, workspace, workspace_nbytes, stream) -> int:
     return int(lib().favor_attn_bwd(_ref(p), q, k, v, w, dout, dq, dk, dv, workspace,
                                     ctypes.c_size_t(workspace_nbytes), stream))
+
+
+def generalized_workspace_bytes(p: FavorProblem, fn) -> int:
+    return lib().favor_generalized_workspace_bytes(_ref(p), fn)
+
+
+def attn_fwd_generalized(p: FavorProblem, fn, q, k, v, w, out, workspace, workspace_nbytes, stream) -> int:
+    return lib().favor_attn_fwd_generalized(_ref(p), fn, q, k, v, w, out, workspace, workspace_nbytes, stream)
 
 
 def draw_features(heads_w, num_features, head_dim, seed, orthogonal, w, stream) -> int:

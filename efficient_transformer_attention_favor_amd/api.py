@@ -68,6 +68,32 @@ def attn_fwd(Q, K, V, W, causal=False, chunk=0, out=None, workspace=None, stream
     return out
 
 
+def attn_fwd_generalized(Q, K, V, W, fn="relu", causal=False, out=None, workspace=None, stream=None):
+    """Kernelised attention D^-1 A V with A = phi(Q) phi(K)^T for the feature map `fn`
+    ("relu": phi(x) = ReLU(W x) / sqrt(m)); returns out (B, Hq, L, d) in Q's dtype."""
+    fns = {"relu": _lib.FAVOR_FEATURE_RELU}
+    if fn not in fns:
+        raise ValueError(f"unknown feature map {fn!r}")
+    _check(Q, K, V, W)
+    p = _problem(Q, K, W, causal, 0)
+    nbytes = _lib.generalized_workspace_bytes(p, fns[fn])
+    if nbytes == 0:
+        st = _lib.attn_fwd_generalized(p, fns[fn], None, None, None, None, None, None, 0, None)
+        raise _lib.FavorError(st, "favor_attn_fwd_generalized")
+    if out is None:
+        out = torch.empty_like(Q)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(Q.device)
+    st = _lib.attn_fwd_generalized(p, fns[fn], Q.data_ptr(), K.data_ptr(), V.data_ptr(), W.data_ptr(),
+                                   out.data_ptr(), workspace.data_ptr(),
+                                   workspace.numel() * workspace.element_size(), stream.cuda_stream)
+    if st != _lib.FAVOR_OK:
+        raise _lib.FavorError(st, "favor_attn_fwd_generalized")
+    return out
+
+
 def features(X, W, side, heads_q, heads_kv, stream=None):
     """The feature map phi of the queries (side 0) or keys (side 1) of X (B, H, L, d).
 

@@ -11,7 +11,8 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 SOURCES = [os.path.join(PKG, "csrc", f) for f in ("favor_kernels.hip", "favor_features.hip", "favor_decode.hip",
-                                                  "favor_backward.hip", "favor_draw.hip", "favor_plan.cpp")]
+                                                  "favor_backward.hip", "favor_draw.hip", "favor_generalized.hip",
+                                                  "favor_plan.cpp")]
 OUTPUT = os.path.join(PKG, "libfavor.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

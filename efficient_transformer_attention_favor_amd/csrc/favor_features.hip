@@ -39,7 +39,8 @@ __device__ __forceinline__ float dec_order(unsigned k) {
 }
 
 // MODE 0: queries (row stabiliser, two passes in the kernel); 1: keys, head-maximum pass;
-// 2: keys, writing pass with the head maximum from pass 1.
+// 2: keys, writing pass with the head maximum from pass 1; 3: the ReLU feature map
+// ReLU(W x) / sqrt(m) of queries or keys (no norm term, no stabiliser; c_out unused).
 template <class T, int D, int MODE>
 __global__ void __launch_bounds__(64 * kFeatWaves)
     features_kernel(const T* __restrict__ X, const float* __restrict__ W, int L, int Lo, int H, int G, int Hw,
@@ -72,8 +73,10 @@ __global__ void __launch_bounds__(64 * kFeatWaves)
       load_w_frag(Wh + (size_t)(32 * ft + col) * D, kc, g, wp);
       c = mma(wp, xf[kc], c);
     }
+    if constexpr (MODE != 3) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) c[r] -= half_norm;
+      for (int r = 0; r < 16; ++r) c[r] -= half_norm;
+    }
     return c;
   };
   const float inv_sqrt_m = 1.0f / sqrtf((float)m);
@@ -86,7 +89,14 @@ __global__ void __launch_bounds__(64 * kFeatWaves)
       for (int r4 = 0; r4 < 4; ++r4) {
         f32x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = valid ? fast_exp2(e[4 * r4 + i] - cst) * inv_sqrt_m : 0.f;
+        for (int i = 0; i < 4; ++i) {
+          float x;
+          if constexpr (MODE == 3)
+            x = fmaxf(e[4 * r4 + i], 0.f) * (inv_sqrt_m / kLog2e);  // the W operand carries log2 e
+          else
+            x = fast_exp2(e[4 * r4 + i] - cst) * inv_sqrt_m;
+          v[i] = valid ? x : 0.f;
+        }
         *reinterpret_cast<f32x4*>(dst + 8 * r4) = v;
       }
     }
@@ -94,6 +104,10 @@ __global__ void __launch_bounds__(64 * kFeatWaves)
 
   if constexpr (MODE == 2) {
     write(dec_order(reinterpret_cast<const unsigned*>(c_out)[bh]));
+    return;
+  }
+  if constexpr (MODE == 3) {
+    write(0.f);
     return;
   }
   float mx = -INFINITY;
@@ -149,7 +163,27 @@ favor_status run_features(const Plan& s, int side, const void* Xv, const float* 
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
+template <class T, int D>
+favor_status run_relu_features(const Plan& s, int side, const void* Xv, const float* W, float* phi, int Lo,
+                               hipStream_t st) {
+  const int row_blocks = (Lo + 32 * kFeatWaves - 1) / (32 * kFeatWaves);
+  const int H = side == 0 ? s.Hq : s.Hkv, G = side == 0 ? s.G : 1;
+  hipLaunchKernelGGL((features_kernel<T, D, 3>), dim3(row_blocks, s.B * H), dim3(64 * kFeatWaves), 0, st,
+                     static_cast<const T*>(Xv), W, s.L, Lo, H, G, s.Hw, s.m, phi, nullptr);
+  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
 }  // namespace
+
+favor_status launch_relu_features(const Plan& s, int side, const void* X, const float* W, float* phi,
+                                  hipStream_t st, int Lo) {
+  if (Lo < s.L) Lo = s.L;
+  if (s.dtype == FAVOR_BF16)
+    return s.d == 64 ? run_relu_features<bf16, 64>(s, side, X, W, phi, Lo, st)
+                     : run_relu_features<bf16, 128>(s, side, X, W, phi, Lo, st);
+  return s.d == 64 ? run_relu_features<float, 64>(s, side, X, W, phi, Lo, st)
+                   : run_relu_features<float, 128>(s, side, X, W, phi, Lo, st);
+}
 
 favor_status launch_features(const Plan& s, int side, const void* X, const float* W, float* phi, float* c,
                              hipStream_t st, int Lo) {

@@ -13,4 +13,9 @@ namespace favor {
 favor_status launch_features(const Plan& s, int side, const void* X, const float* W, float* phi, float* c,
                              hipStream_t st, int Lo = 0);
 
+// The ReLU feature map ReLU(W x) / sqrt(m) of the queries (side 0) or keys (side 1) as
+// float32 [rows][m], Lo rows per head as above.
+favor_status launch_relu_features(const Plan& s, int side, const void* X, const float* W, float* phi,
+                                  hipStream_t st, int Lo = 0);
+
 }  // namespace favor

@@ -116,6 +116,22 @@ favor_status favor_attn_fwd_timed(const favor_problem* p, const void* Q, const v
 favor_status favor_features(const favor_problem* p, int32_t side, const void* X, const float* W,
                             float* phi_out, float* c_out, void* stream);
 
+/* Kernelised attention with another non-negative feature map (Performer page, "ABSTRACT":
+ * FAVOR+ also models kernelisable attention beyond softmax): out = D^-1 A V with
+ * A = phi(Q) phi(K)^T, the inclusive causal mask in FAVOR_CAUSAL mode, evaluated in linear
+ * order like favor_attn_fwd.  fn selects phi:
+ *   FAVOR_FEATURE_RELU  phi(x) = ReLU(W x) / sqrt(m)  (the first-order arc-cosine kernel).
+ * A row whose weights are all zero gets a zero output.  Arguments, layouts and errors as
+ * for favor_attn_fwd (an unknown fn is FAVOR_ERR_UNSUPPORTED); the workspace
+ * (favor_generalized_workspace_bytes(p, fn) bytes, 256-byte aligned) holds the float32
+ * feature matrices, about m (B Hq + B Hkv) L floats.  The features are materialised and
+ * the products run in float32 (about 8 kernels on `stream`). */
+typedef enum { FAVOR_FEATURE_RELU = 1 } favor_feature_fn;
+size_t favor_generalized_workspace_bytes(const favor_problem* p, int32_t fn);
+favor_status favor_attn_fwd_generalized(const favor_problem* p, int32_t fn, const void* Q, const void* K,
+                                        const void* V, const float* W, void* out, void* workspace,
+                                        size_t workspace_bytes, void* stream);
+
 /* Random feature matrix drawn on the device from a seed: W [heads_w][num_features][head_dim]
  * float32 (device pointer, caller-owned).  Orthogonal random features (Performer page,
  * "제안 방법": random features with orthogonal rows lower the estimator's variance) when

@@ -139,3 +139,22 @@ def test_draw_features_validation():
     assert L.draw_features(1, 64, 64, 0, 2, 256, None) == L.FAVOR_ERR_INVALID_ARG
     assert L.draw_features(1, 64, 129, 0, True, 256, None) == L.FAVOR_ERR_UNSUPPORTED
     assert L.draw_features(65537, 64, 64, 0, True, 256, None) == L.FAVOR_ERR_INVALID_ARG
+
+
+def test_generalized_validation():
+    L = _lib
+    p = _p()
+    need = L.generalized_workspace_bytes(p, L.FAVOR_FEATURE_RELU)
+    assert need > 0 and need % 256 == 0
+    assert L.generalized_workspace_bytes(p, 0) == 0 and L.generalized_workspace_bytes(p, 7) == 0
+    causal = _p(mode=L.FAVOR_CAUSAL)
+    assert L.generalized_workspace_bytes(causal, L.FAVOR_FEATURE_RELU) > 0
+    assert L.attn_fwd_generalized(p, 0, 8, 8, 8, 8, 8, 256, need, None) == L.FAVOR_ERR_UNSUPPORTED
+    assert L.attn_fwd_generalized(None, 1, 8, 8, 8, 8, 8, 256, need, None) == L.FAVOR_ERR_INVALID_ARG
+    for i in range(5):
+        args = [8] * 5
+        args[i] = None
+        assert L.attn_fwd_generalized(p, 1, *args, 256, need, None) == L.FAVOR_ERR_INVALID_ARG
+    assert L.attn_fwd_generalized(p, 1, *([8] * 5), 256, need - 1, None) == L.FAVOR_ERR_WORKSPACE
+    assert L.attn_fwd_generalized(p, 1, *([8] * 5), 260, need, None) == L.FAVOR_ERR_WORKSPACE
+    assert L.attn_fwd_generalized(_p(head_dim=32), 1, *([8] * 5), 256, need, None) == L.FAVOR_ERR_UNSUPPORTED
