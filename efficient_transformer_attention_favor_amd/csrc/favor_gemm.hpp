@@ -12,17 +12,23 @@
 namespace favor {
 namespace {
 
-// ---- batched float32 GEMM: C = op(A) op(B), 64 x 64 tiles, 16-deep k steps ----------
+// ---- batched float32 GEMM on the matrix cores: C = op(A) op(B) ---------------------------
 // op(A) is M x K: A stored [M][K] (TA false) or [K][M] (TA true), leading dimension lda;
 // op(B) is K x N: B stored [K][N] (TB false) or [N][K] (TB true).  Batch entry z uses
-// A + mapA(z) sA, B + mapB(z) sB, C + z sC.  256 threads, 4 x 4 outputs each; the grid is
-// one dimension (batch entries x row tiles x column tiles), so any batch count fits.
+// A + mapA(z) sA, B + mapB(z) sB, C + z sC.  The grid is one dimension (batch entries x row
+// tiles x column tiles), so any batch count fits.
+// Workgroup: a 64 x 64 tile of C, 4 waves in a 2 x 2 grid of 32 x 32 tiles, each
+// accumulated with v_mfma_f32_32x32x2_f32 (float32 in, float32 accumulate).  Contraction
+// slabs of 32 are staged through LDS as [row][k] (k contiguous), the next slab's global
+// loads in flight while the current one is multiplied.  Within a slab, lane group g
+// (lanes 32 g .. 32 g + 31) supplies k = 8 h + 4 g + j to MFMA (h, j), so one 16-byte LDS
+// read feeds four MFMAs.  Waves whose 32 x 32 tile lies wholly outside C skip the products.
 // flags: kAccum adds to C instead of overwriting it; kTril zeroes the outputs with column >
 // row (the causal mask of a 64 x 64 chunk product).
 // With ksplit > 1 (long contractions with few output tiles) the batch index enumerates
 // (split, batch entry); split s covers contraction indices [s kc, (s+1) kc) and writes its
 // partial to C + (s batch + z) sC, summed afterwards in split order by sum_splits.
-constexpr int GT = 64, GK = 16, GLD = GT + 4;
+constexpr int GT = 64, GK = 32, GLD = GK + 4;
 constexpr int kAccum = 1, kTril = 2;
 
 // Operand block read by batch entry z: ((z / div) % mod) * mul + z % inner.
@@ -40,8 +46,9 @@ __global__ void __launch_bounds__(256)
     gemm_f32(const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N, int K,
              int lda, int ldb, int ldc, long long sA, long long sB, long long sC, BMap mapA, BMap mapB, int batch,
              int kc, int flags) {
-  __shared__ __attribute__((aligned(16))) float As[GK][GLD];
-  __shared__ __attribute__((aligned(16))) float Bs[GK][GLD];
+  constexpr int PER = GT * GK / 256;  // operand elements per thread and slab
+  __shared__ __attribute__((aligned(16))) float As[GT][GLD];
+  __shared__ __attribute__((aligned(16))) float Bs[GT][GLD];
   const int tn = (N + GT - 1) / GT, tm = (M + GT - 1) / GT;
   const int bx = blockIdx.x % tn, by = (blockIdx.x / tn) % tm, zs = blockIdx.x / (tn * tm);
   const int z = zs % batch, split = zs / batch;
@@ -50,54 +57,68 @@ __global__ void __launch_bounds__(256)
   C += (long long)zs * sC;
   const int kbeg = split * kc, kend = min(K, kbeg + kc);
   const int m0 = by * GT, n0 = bx * GT;
-  const int t = threadIdx.x, tx = t % 16, ty = t / 16;
-  float acc[4][4];
+  const int t = threadIdx.x, wave = t >> 6, l = t & 63, c32 = l & 31, g = l >> 5;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool active = m0 + 32 * wm < M && n0 + 32 * wn < N;
+
+  // element e of a slab: consecutive threads walk the operand's contiguous dimension
+  auto a_rc = [&](int e, int& row, int& k) {
+    row = TA ? e % GT : e / GK;
+    k = TA ? e / GT : e % GK;
+  };
+  auto b_rc = [&](int e, int& col, int& k) {
+    col = TB ? e / GK : e % GT;
+    k = TB ? e % GK : e / GT;
+  };
+  float ra[PER], rb[PER];
+  auto fetch = [&](int k0) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+    for (int u = 0; u < PER; ++u) {
+      int row, k, col, kb;
+      a_rc(t + 256 * u, row, k);
+      const int gm = m0 + row, gk = k0 + k;
+      ra[u] = gm < M && gk < kend ? (TA ? A[(long long)gk * lda + gm] : A[(long long)gm * lda + gk]) : 0.f;
+      b_rc(t + 256 * u, col, kb);
+      const int gn = n0 + col, gkb = k0 + kb;
+      rb[u] = gn < N && gkb < kend ? (TB ? B[(long long)gn * ldb + gkb] : B[(long long)gkb * ldb + gn]) : 0.f;
+    }
+  };
+
+  f32x16 acc = zero16();
+  if (kbeg < kend) fetch(kbeg);
   for (int k0 = kbeg; k0 < kend; k0 += GK) {
 #pragma unroll
-    for (int e = t; e < GT * GK; e += 256) {
-      // consecutive threads walk the operand's contiguous dimension
-      const int mm = TA ? e % GT : e / GK, kk = TA ? e / GT : e % GK;
-      const int gm = m0 + mm, gk = k0 + kk;
-      float x = 0.f;
-      if (gm < M && gk < kend) x = TA ? A[(long long)gk * lda + gm] : A[(long long)gm * lda + gk];
-      As[kk][mm] = x;
-    }
-#pragma unroll
-    for (int e = t; e < GT * GK; e += 256) {
-      const int nn = TB ? e / GK : e % GT, kk = TB ? e % GK : e / GT;
-      const int gn = n0 + nn, gk = k0 + kk;
-      float x = 0.f;
-      if (gn < N && gk < kend) x = TB ? B[(long long)gn * ldb + gk] : B[(long long)gk * ldb + gn];
-      Bs[kk][nn] = x;
+    for (int u = 0; u < PER; ++u) {
+      int row, k, col, kb;
+      a_rc(t + 256 * u, row, k);
+      As[row][k] = ra[u];
+      b_rc(t + 256 * u, col, kb);
+      Bs[col][kb] = rb[u];
     }
     __syncthreads();
+    if (k0 + GK < kend) fetch(k0 + GK);
+    if (active) {
 #pragma unroll
-    for (int kk = 0; kk < GK; ++kk) {
-      const f32x4 a = *reinterpret_cast<const f32x4*>(&As[kk][ty * 4]);
-      const f32x4 b = *reinterpret_cast<const f32x4*>(&Bs[kk][tx * 4]);
+      for (int h = 0; h < GK / 8; ++h) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&As[32 * wm + c32][8 * h + 4 * g]);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&Bs[32 * wn + c32][8 * h + 4 * g]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc = mma(a[j], b[j], acc);
+      }
     }
     __syncthreads();
   }
+  if (!active) return;
+  // accumulator r of lane (c32, g): row 8 (r / 4) + 4 g + r % 4, column c32 of the wave's tile
+  const int gn = n0 + 32 * wn + c32;
+  if (gn >= N) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int gm = m0 + ty * 4 + i;
+  for (int r = 0; r < 16; ++r) {
+    const int gm = m0 + 32 * wm + 8 * (r >> 2) + 4 * g + (r & 3);
     if (gm >= M) continue;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int gn = n0 + tx * 4 + j;
-      if (gn >= N) continue;
-      float x = (flags & kTril) && gn > gm ? 0.f : acc[i][j];
-      if (flags & kAccum) x += C[(long long)gm * ldc + gn];
-      C[(long long)gm * ldc + gn] = x;
-    }
+    float x = (flags & kTril) && gn > gm ? 0.f : acc[r];
+    if (flags & kAccum) x += C[(long long)gm * ldc + gn];
+    C[(long long)gm * ldc + gn] = x;
   }
 }
 
@@ -125,7 +146,7 @@ __global__ void __launch_bounds__(256) sum_splits(const float* __restrict__ P, f
 }
 
 // Splits of a long contraction so that the launch has about 4096 workgroups, each split at
-// least 256 deep (a multiple of the 16-deep step).
+// least 256 deep (a multiple of the contraction slab).
 inline int ksplit_for(int M, int N, int K, int batch) {
   const long long tiles = (long long)((N + GT - 1) / GT) * ((M + GT - 1) / GT) * batch;
   long long s = (4096 + tiles - 1) / tiles;
