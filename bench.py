@@ -93,15 +93,18 @@ def algorithmic_work(w):
             names[2]: (q_bytes + k_bytes + w_bytes, B * Hq * side + B * Hkv * side)}
 
 
+# The sources the forward kernels (favor_attn_fwd) are built from.
+FORWARD_SOURCES = ("favor_device.hpp", "favor_kernels.hip", "favor_plan.cpp", "favor_plan.hpp")
+
+
 def source_digest():
-    """SHA-256 over the library's kernel sources (identifies the kernels counters were taken on)."""
+    """SHA-256 over the forward kernels' sources (identifies the kernels counters were taken on)."""
     import hashlib
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "efficient_transformer_attention_favor_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".hpp", ".cpp")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    for name in sorted(FORWARD_SOURCES):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
 
 
