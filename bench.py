@@ -148,6 +148,55 @@ def cpu_baseline(w, Q, K, V, W, min_s=10.0):
             "cpu": _cpu_model()}
 
 
+def cpu_backward_baseline(w, Q, K, V, W, dO, min_s=10.0):
+    """The oracle's gradients on whole kv-head slices (a kv head with its query heads),
+    cycling over the workload's slices until at least min_s seconds have passed."""
+    from threadpoolctl import threadpool_info
+
+    import oracle.favor_oracle as O
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    G = w.heads_q // w.heads_kv
+    total = w.batch * w.heads_kv
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < min_s:
+        b, hk = divmod(n % total, w.heads_kv)
+        sl = (slice(b, b + 1), slice(hk * G, (hk + 1) * G))
+        Wh = W[0 if w.heads_w == 1 else hk][None]
+        O.favor_grads(Q[sl], K[b:b + 1, hk:hk + 1], V[b:b + 1, hk:hk + 1], Wh, dO[sl], causal=w.causal)
+        n += 1
+    secs = time.perf_counter() - t0
+    return {"value": n * G * w.seq_len / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} kv-head slices ({G} query heads each) of L={w.seq_len}, float64 NumPy, "
+                      f"{secs:.1f} s on the host CPU", "cpu": _cpu_model()}
+
+
+def cpu_generalized_baseline(w, Q, K, V, W, min_s=10.0):
+    """The oracle's ReLU attention on whole (batch, query head) slices, cycling until at least
+    min_s seconds have passed."""
+    from threadpoolctl import threadpool_info
+
+    import oracle.favor_oracle as O
+
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    G = w.heads_q // w.heads_kv
+    total = w.batch * w.heads_q
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < min_s:
+        b, hq = divmod(n % total, w.heads_q)
+        hk = hq // G
+        Wh = W[0 if w.heads_w == 1 else hk][None]
+        O.generalized_attention(Q[b:b + 1, hq:hq + 1], K[b:b + 1, hk:hk + 1], V[b:b + 1, hk:hk + 1], Wh,
+                                causal=w.causal)
+        n += 1
+    secs = time.perf_counter() - t0
+    return {"value": n * w.seq_len / secs, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n} (batch, head) slices of L={w.seq_len}, float64 NumPy, {secs:.1f} s on the host CPU",
+            "cpu": _cpu_model()}
+
+
 def _cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -404,8 +453,8 @@ def backward_main(args, w):
     an upstream gradient of the output's shape (inputs resident).  Algorithmic flops: the
     feature maps of Q and K, S, phi(Q) S, dphi(Q), dS, dphi(K), and the three products with W
     and dS that give dQ, dK, dV (the same count for both modes, as for the forward; the
-    causal chunk products execute more, reported as exec_flops); they run as float32 FMAs,
-    so the roofline is float32."""
+    causal chunk products execute more, reported as exec_flops); they run as float32 MFMAs,
+    so the roofline is the float32 matrix peak."""
     import numpy as np
     import torch
 
@@ -475,11 +524,14 @@ def backward_main(args, w):
                    "heads_w": w.heads_w, "seq_len": L, "head_dim": d, "num_features": m,
                    "input_dtype": w.dtype, "mode": f"{'causal' if w.causal else 'bidirectional'} backward",
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": "favor_attn_bwd (all kernels)", "bound": "alu", "achieved": round(achieved, 2),
+        "roofline": {"kernel": "favor_attn_bwd (all kernels)", "bound": "mfma", "achieved": round(achieved, 2),
                      "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s", "frac": round(achieved / PEAK_TFLOPS["f32"], 4),
                      "traffic": None, "per_launch": {"alg_flops": flops, "exec_flops": exec_flops, "alg_bytes": alg_bytes,
                                                      "avg_ms": round(ms_step, 5)}},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_backward_baseline(w, Q, K, V, W, dO,
+                                                    min_s=args.cpu_budget)
     line = json.dumps(res)
     print(line, flush=True)
     if args.out:
@@ -490,7 +542,8 @@ def backward_main(args, w):
 def generalized_main(args, w):
     """Kernelised attention with the ReLU feature map (favor_attn_fwd_generalized): one step =
     one call on the workload (inputs resident).  Algorithmic flops as for the softmax forward
-    (features of Q and K, S, phi(Q) S); float32 products, so the roofline is float32."""
+    (features of Q and K, S, phi(Q) S); float32 MFMA products, so the roofline is the float32
+    matrix peak."""
     import numpy as np
     import torch
 
@@ -540,11 +593,13 @@ def generalized_main(args, w):
                    "heads_w": w.heads_w, "seq_len": L, "head_dim": d, "num_features": m,
                    "input_dtype": w.dtype, "mode": "causal" if w.causal else "bidirectional",
                    "parallelism": "single GPU"},
-        "roofline": {"kernel": "favor_attn_fwd_generalized (all kernels)", "bound": "alu",
+        "roofline": {"kernel": "favor_attn_fwd_generalized (all kernels)", "bound": "mfma",
                      "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
                      "frac": round(achieved / PEAK_TFLOPS["f32"], 4), "traffic": None,
                      "per_launch": {"alg_flops": flops, "avg_ms": round(ms_step, 5)}},
     }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_generalized_baseline(w, Q, K, V, W, min_s=args.cpu_budget)
     line = json.dumps(res)
     print(line, flush=True)
     if args.out:

@@ -15,8 +15,10 @@
 // above is invariant under those scalings.
 //
 // Implementation: the feature kernels write phi(Q) and phi(K) as float32 matrices, then seven
-// batched float32 GEMMs (one batch entry per (batch, kv head)) and four row kernels.  All
-// arithmetic is float32; bf16 problems round only their inputs and the gradients they return.
+// batched float32 GEMMs on the matrix cores (one batch entry per (batch, kv head)) and row
+// kernels.  The GEMMs that form dphi(Q) and dphi(K) multiply by phi in their epilogue, so
+// they write T = dphi * phi directly (and, for keys, T's row sums in 32-feature partials).
+// All arithmetic is float32; bf16 problems round only their inputs and returned gradients.
 //
 // Causal (inclusive mask j <= i): the positions of each head are cut into chunks of C = 64
 // (the last one zero-padded), S_<c is the exclusive prefix of the chunk summaries
@@ -65,33 +67,19 @@ __global__ void __launch_bounds__(256)
   if (l == 0) g[D] = -dot * inv;
 }
 
-// T = dphi * phi in place and its row sums.
-__global__ void __launch_bounds__(256)
-    feature_product(float* __restrict__ dphi, const float* __restrict__ phi, float* __restrict__ rowsum, int m,
-                    long long rows) {
-  const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= rows) return;
-  const int l = threadIdx.x & 63;
-  float s = 0.f;
-  for (int f = l; f < m; f += 64) {
-    const float x = dphi[r * m + f] * phi[r * m + f];
-    dphi[r * m + f] = x;
-    s += x;
-  }
-  s = wave_sum(s);
-  if (l == 0) rowsum[r] = s;
-}
-
-// dX = P - X * rowsum, in the input dtype (rows: the user's; P and rowsum padded).
+// dX = P - X * rowsum(T), in the input dtype (rows: the user's; P and the row sums padded).
+// The row sums of T = dphi * phi arrive as nt partial sums per row (one per 32 features,
+// written by the GEMM that forms T), added here in feature order.
 template <class T, int D>
 __global__ void __launch_bounds__(256)
-    input_grads(const float* __restrict__ P, const T* __restrict__ X, const float* __restrict__ rowsum,
+    input_grads(const float* __restrict__ P, const T* __restrict__ X, const float* __restrict__ rowp, int nt,
                 T* __restrict__ dX, long long rows, int L, int Lp) {
   const long long r = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   const int l = threadIdx.x & 63;
   const long long p = padded_row(r, L, Lp);
-  const float t = rowsum[p];
+  // lane j < nt holds partial j; the wave sum adds them in a fixed order
+  const float t = wave_sum(l < nt ? rowp[p * nt + l] : 0.f);
   for (int c = l; c < D; c += 64) dX[r * D + c] = (T)(P[p * D + c] - (float)X[r * D + c] * t);
 }
 
@@ -124,7 +112,7 @@ __global__ void __launch_bounds__(256)
 // ---- workspace -----------------------------------------------------------------------
 
 struct BwdLayout {
-  size_t phq, cq, phk, ck, v1, S, ND, G1, dphq, tq, Pq, dS, dphk, tk, Pk, dVf, part, bytes;
+  size_t phq, cq, phk, ck, v1, S, ND, G1, dphq, Pq, dS, dphk, tk, Pk, dVf, part, bytes;
   int split_k, split_q;  // contraction splits of S = phi(K)^T [V, 1] and dS = phi(Q)^T G1
 };
 
@@ -148,11 +136,10 @@ BwdLayout bwd_layout(const Plan& s) {
   w.ND = take(Rq * d1);
   w.G1 = take(Rq * d1);
   w.dphq = take(Rq * m);
-  w.tq = take(Rq);
   w.Pq = take(Rq * s.d);
   w.dS = take((size_t)s.BH * m * d1);
   w.dphk = take(Rk * m);
-  w.tk = take(Rk);
+  w.tk = take(Rk * (m / 32));
   w.Pk = take(Rk * s.d);
   w.dVf = take(Rk * s.d);
   w.split_k = ksplit_for(s.m, s.d + 1, s.L, s.BH);
@@ -178,7 +165,7 @@ favor_status run_bwd(const Plan& s, const void* Qv, const void* Kv, const void* 
   const BwdLayout w = bwd_layout(s);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   float *phq = F(w.phq), *phk = F(w.phk), *v1 = F(w.v1), *S = F(w.S), *ND = F(w.ND), *G1 = F(w.G1);
-  float *dphq = F(w.dphq), *tq = F(w.tq), *Pq = F(w.Pq), *dS = F(w.dS), *dphk = F(w.dphk), *tk = F(w.tk);
+  float *dphq = F(w.dphq), *Pq = F(w.Pq), *dS = F(w.dS), *dphk = F(w.dphk), *tk = F(w.tk);
   float *Pk = F(w.Pk), *dVf = F(w.dVf);
   const long long Rq = (long long)s.B * s.Hq * s.L, Rk = (long long)s.B * s.Hkv * s.L;
   const int m = s.m, D1 = D + 1, GL = s.G * s.L, L = s.L, BH = s.BH;
@@ -198,11 +185,11 @@ favor_status run_bwd(const Plan& s, const void* Qv, const void* Kv, const void* 
                                 (long long)GL * D1, kIdent, kIdent, BH, st)));
   hipLaunchKernelGGL((output_grads<T, D>), dim3(row_blocks(Rq)), dim3(256), 0, st, ND, dO, G1, Rq, L, L);
   FAVOR_LAUNCHED();
-  // dphi(Q) = G1 S^T                                       (G L x m)
+  // T = dphi(Q) * phi(Q) with dphi(Q) = G1 S^T                 (G L x m)
+  Epi eq;
+  eq.aux = phq;
   FAVOR_TRY((gemm<false, true>(G1, S, dphq, GL, m, D1, D1, D1, m, (long long)GL * D1, (long long)m * D1,
-                               (long long)GL * m, kIdent, kIdent, BH, st)));
-  hipLaunchKernelGGL(feature_product, dim3(row_blocks(Rq)), dim3(256), 0, st, dphq, phq, tq, m, Rq);
-  FAVOR_LAUNCHED();
+                               (long long)GL * m, kIdent, kIdent, BH, st, kMulAux, eq)));
   // dQ = T W: the term -Q * rowsum(T) vanishes for queries (rowsum(T)_i = g_i . N_i +
   // h_i D_i = 0, since scaling phi(q_i) leaves out_i unchanged), and dropping it avoids
   // subtracting the rounding noise of that cancellation
@@ -213,15 +200,18 @@ favor_status run_bwd(const Plan& s, const void* Qv, const void* Kv, const void* 
   // dS = phi(Q)^T G1                                       (m x D+1, contraction over G L)
   FAVOR_TRY((gemm_split<true, false>(phq, G1, dS, F(w.part), m, D1, GL, m, D1, (long long)GL * m,
                                      (long long)GL * D1, kIdent, kIdent, BH, w.split_q, st)));
-  // dphi(K) = [V, 1] dS^T                                  (L x m)
+  // T' = dphi(K) * phi(K) with dphi(K) = [V, 1] dS^T, and its row sums   (L x m)
+  Epi ek;
+  ek.aux = phk;
+  ek.rowp = tk;
+  ek.ldrp = m / 32;
+  ek.srp = (long long)L * (m / 32);
   FAVOR_TRY((gemm<false, true>(v1, dS, dphk, L, m, D1, D1, D1, m, (long long)L * D1, (long long)m * D1,
-                               (long long)L * m, kIdent, kIdent, BH, st)));
-  hipLaunchKernelGGL(feature_product, dim3(row_blocks(Rk)), dim3(256), 0, st, dphk, phk, tk, m, Rk);
-  FAVOR_LAUNCHED();
+                               (long long)L * m, kIdent, kIdent, BH, st, kMulAux | kRowSum, ek)));
   FAVOR_TRY((gemm<false, false>(dphk, W, Pk, L, D, m, m, D, D, (long long)L * m, wstride, (long long)L * D, kIdent,
                                 modulo(wmod), BH, st)));
-  hipLaunchKernelGGL((input_grads<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, Pk, K, tk, static_cast<T*>(dKv),
-                     Rk, L, L);
+  hipLaunchKernelGGL((input_grads<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, Pk, K, tk, m / 32,
+                     static_cast<T*>(dKv), Rk, L, L);
   FAVOR_LAUNCHED();
   // dV = phi(K) dS_v                                       (L x D; dS rows have stride D+1)
   FAVOR_TRY((gemm<false, false>(phk, dS, dVf, L, D, m, m, D1, D, (long long)L * m, (long long)m * D1,
@@ -237,7 +227,7 @@ favor_status run_bwd(const Plan& s, const void* Qv, const void* Kv, const void* 
 constexpr int kBwdChunk = GT;  // one 64 x 64 tile per chunk product
 
 struct CausalLayout {
-  size_t phq, cq, phk, ck, v1, Sx, Pm, ND, G1, A, dphq, tq, Pq, Rc, Rx, dphk, tk, Pk, dVf, bytes;
+  size_t phq, cq, phk, ck, v1, Sx, Pm, ND, G1, A, dphq, Pq, Rc, Rx, dphk, tk, Pk, dVf, bytes;
   int NC, Lp;  // chunks per head, padded positions per head
 };
 
@@ -265,12 +255,11 @@ CausalLayout causal_layout(const Plan& s) {
   w.G1 = take(Rq * d1);
   w.A = take(Rq * C);
   w.dphq = take(Rq * m);
-  w.tq = take(Rq);
   w.Pq = take(Rq * s.d);
   w.Rc = take(Zq * m * d1);
   w.Rx = take(Zk * m * d1);
   w.dphk = take(Rk * m);
-  w.tk = take(Rk);
+  w.tk = take(Rk * (m / 32));
   w.Pk = take(Rk * s.d);
   w.dVf = take(Rk * s.d);
   w.bytes = off;
@@ -284,7 +273,7 @@ favor_status run_bwd_causal(const Plan& s, const void* Qv, const void* Kv, const
   const CausalLayout w = causal_layout(s);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
   float *phq = F(w.phq), *phk = F(w.phk), *v1 = F(w.v1), *Sx = F(w.Sx), *Pm = F(w.Pm), *ND = F(w.ND);
-  float *G1 = F(w.G1), *A = F(w.A), *dphq = F(w.dphq), *tq = F(w.tq), *Pq = F(w.Pq), *Rc = F(w.Rc);
+  float *G1 = F(w.G1), *A = F(w.A), *dphq = F(w.dphq), *Pq = F(w.Pq), *Rc = F(w.Rc);
   float *Rx = F(w.Rx), *dphk = F(w.dphk), *tk = F(w.tk), *Pk = F(w.Pk), *dVf = F(w.dVf);
   const int C = kBwdChunk, NC = w.NC, Lp = w.Lp, L = s.L, m = s.m, D1 = D + 1, G = s.G;
   const int BHk = s.BH, BHq = s.B * s.Hq, Zq = BHq * NC, Zk = BHk * NC;
@@ -317,12 +306,13 @@ favor_status run_bwd_causal(const Plan& s, const void* Qv, const void* Kv, const
   hipLaunchKernelGGL((output_grads<T, D>), dim3(row_blocks(Rqp)), dim3(256), 0, st, ND, static_cast<const T*>(dOv),
                      G1, Rqp, L, Lp);
   FAVOR_LAUNCHED();
-  // A = tril(G1_c [V_c, 1]^T);  dphi(Q_c) = A phi(K_c) + G1_c S_<c^T
+  // A = tril(G1_c [V_c, 1]^T);  T = dphi(Q_c) * phi(Q_c), dphi(Q_c) = A phi(K_c) + G1_c S_<c^T
+  Epi eq;
+  eq.aux = phq;
   FAVOR_TRY((gemm<false, true>(G1, v1, A, C, C, D1, D1, D1, C, cd1, cd1, cc, kIdent, key_of_q, Zq, st, kTril)));
   FAVOR_TRY((gemm<false, false>(A, phk, dphq, C, m, C, C, m, m, cc, cm, cm, kIdent, key_of_q, Zq, st)));
-  FAVOR_TRY((gemm<false, true>(G1, Sx, dphq, C, m, D1, D1, D1, m, cd1, sm, cm, kIdent, key_of_q, Zq, st, kAccum)));
-  hipLaunchKernelGGL(feature_product, dim3(row_blocks(Rqp)), dim3(256), 0, st, dphq, phq, tq, m, Rqp);
-  FAVOR_LAUNCHED();
+  FAVOR_TRY((gemm<false, true>(G1, Sx, dphq, C, m, D1, D1, D1, m, cd1, sm, cm, kIdent, key_of_q, Zq, st,
+                               kAccum | kMulAux, eq)));
   // dQ = T W (the row-sum term is 0 for queries, as in the bidirectional case)
   FAVOR_TRY((gemm<false, false>(dphq, W, Pq, Lp, D, m, m, D, D, (long long)Lp * m, wstride, (long long)Lp * D,
                                 kIdent, w_of_q, BHq, st)));
@@ -332,17 +322,20 @@ favor_status run_bwd_causal(const Plan& s, const void* Qv, const void* Kv, const
   FAVOR_TRY((gemm<true, false>(phq, G1, Rc, m, D1, C, m, D1, D1, cm, cd1, sm, kIdent, kIdent, Zq, st)));
   hipLaunchKernelGGL(chunk_suffix, scan_grid, dim3(256), 0, st, Rc, Rx, NC, G, (int)sm);
   FAVOR_LAUNCHED();
-  // dphi(K_c) = [V_c, 1] R_>c^T + sum_g A_g,c^T phi(Q_g,c)
+  // T' = dphi(K_c) * phi(K_c) and its row sums, dphi(K_c) = [V_c, 1] R_>c^T + sum_g A_g,c^T phi(Q_g,c)
+  Epi ek;
+  ek.aux = phk;
+  ek.rowp = tk;
+  ek.ldrp = m / 32;
+  ek.srp = (long long)C * (m / 32);
   FAVOR_TRY((gemm<false, true>(v1, Rx, dphk, C, m, D1, D1, D1, m, cd1, sm, cm, kIdent, kIdent, Zk, st)));
   for (int g = 0; g < G; ++g)
     FAVOR_TRY((gemm<true, false>(A + g * NC * cc, phq + g * NC * cm, dphk, C, m, C, C, m, m, cc, cm, cm, q_of_k,
-                                 q_of_k, Zk, st, kAccum)));
-  hipLaunchKernelGGL(feature_product, dim3(row_blocks(Rkp)), dim3(256), 0, st, dphk, phk, tk, m, Rkp);
-  FAVOR_LAUNCHED();
+                                 q_of_k, Zk, st, g == G - 1 ? kAccum | kMulAux | kRowSum : kAccum, ek)));
   FAVOR_TRY((gemm<false, false>(dphk, W, Pk, Lp, D, m, m, D, D, (long long)Lp * m, wstride, (long long)Lp * D,
                                 kIdent, w_of_k, BHk, st)));
-  hipLaunchKernelGGL((input_grads<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, Pk, K, tk, static_cast<T*>(dKv),
-                     Rk, L, Lp);
+  hipLaunchKernelGGL((input_grads<T, D>), dim3(row_blocks(Rk)), dim3(256), 0, st, Pk, K, tk, m / 32,
+                     static_cast<T*>(dKv), Rk, L, Lp);
   FAVOR_LAUNCHED();
   // dV_c = phi(K_c) R_>c,v + sum_g P_g,c^T g_g,c          (R and G1 rows have stride D+1)
   FAVOR_TRY((gemm<false, false>(phk, Rx, dVf, C, D, m, m, D1, D, cm, sm, cd, kIdent, kIdent, Zk, st)));

@@ -24,12 +24,22 @@ namespace {
 // (lanes 32 g .. 32 g + 31) supplies k = 8 h + 4 g + j to MFMA (h, j), so one 16-byte LDS
 // read feeds four MFMAs.  Waves whose 32 x 32 tile lies wholly outside C skip the products.
 // flags: kAccum adds to C instead of overwriting it; kTril zeroes the outputs with column >
-// row (the causal mask of a 64 x 64 chunk product).
+// row (the causal mask of a 64 x 64 chunk product); kMulAux multiplies the result
+// elementwise by epi.aux (indexed like C); kRowSum also writes the row sums of the result
+// over each 32-column tile to epi.rowp[z][row][col / 32] (z stride epi.srp, row stride
+// epi.ldrp), to be added up in column order by the reader (deterministic).
 // With ksplit > 1 (long contractions with few output tiles) the batch index enumerates
 // (split, batch entry); split s covers contraction indices [s kc, (s+1) kc) and writes its
 // partial to C + (s batch + z) sC, summed afterwards in split order by sum_splits.
 constexpr int GT = 64, GK = 32, GLD = GK + 4;
-constexpr int kAccum = 1, kTril = 2;
+constexpr int kAccum = 1, kTril = 2, kMulAux = 4, kRowSum = 8;
+
+struct Epi {
+  const float* aux = nullptr;
+  float* rowp = nullptr;
+  int ldrp = 0;
+  long long srp = 0;
+};
 
 // Operand block read by batch entry z: ((z / div) % mod) * mul + z % inner.
 struct BMap {
@@ -45,7 +55,7 @@ template <bool TA, bool TB>
 __global__ void __launch_bounds__(256)
     gemm_f32(const float* __restrict__ A, const float* __restrict__ B, float* __restrict__ C, int M, int N, int K,
              int lda, int ldb, int ldc, long long sA, long long sB, long long sC, BMap mapA, BMap mapB, int batch,
-             int kc, int flags) {
+             int kc, int flags, Epi epi) {
   constexpr int PER = GT * GK / 256;  // operand elements per thread and slab
   __shared__ __attribute__((aligned(16))) float As[GT][GLD];
   __shared__ __attribute__((aligned(16))) float Bs[GT][GLD];
@@ -111,14 +121,40 @@ __global__ void __launch_bounds__(256)
   if (!active) return;
   // accumulator r of lane (c32, g): row 8 (r / 4) + 4 g + r % 4, column c32 of the wave's tile
   const int gn = n0 + 32 * wn + c32;
-  if (gn >= N) return;
+  const float* aux = epi.aux + (long long)zs * sC;
+  const int mrow = m0 + 32 * wm + 4 * g;  // + 8 (r / 4) + r % 4
+  auto ok = [&](int r) { return mrow + 8 * (r >> 2) + (r & 3) < M && gn < N; };
+  auto at = [&](int r) { return (long long)(mrow + 8 * (r >> 2) + (r & 3)) * ldc + gn; };
+  float x[16];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int gm = m0 + 32 * wm + 8 * (r >> 2) + 4 * g + (r & 3);
-    if (gm >= M) continue;
-    float x = (flags & kTril) && gn > gm ? 0.f : acc[r];
-    if (flags & kAccum) x += C[(long long)gm * ldc + gn];
-    C[(long long)gm * ldc + gn] = x;
+  for (int r = 0; r < 16; ++r) x[r] = (flags & kTril) && gn > mrow + 8 * (r >> 2) + (r & 3) ? 0.f : acc[r];
+  // all loads of the epilogue are issued before any store
+  if (flags & kAccum) {
+    float cv[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cv[r] = ok(r) ? C[at(r)] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] += cv[r];
+  }
+  if (flags & kMulAux) {
+    float av[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) av[r] = ok(r) ? aux[at(r)] : 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) x[r] *= av[r];
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (ok(r)) C[at(r)] = x[r];
+  if (flags & kRowSum) {  // wave-uniform: sums over the 32 columns of each lane group
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float y = ok(r) ? x[r] : 0.f;
+#pragma unroll
+      for (int s = 1; s < 32; s <<= 1) y += __shfl_xor(y, s);
+      const int gm = mrow + 8 * (r >> 2) + (r & 3);
+      if (c32 == (r & 31) && gm < M) epi.rowp[(long long)zs * epi.srp + (long long)gm * epi.ldrp + (n0 >> 5) + wn] = y;
+    }
   }
 }
 
@@ -129,9 +165,9 @@ inline unsigned gemm_blocks(int M, int N, long long entries) {
 template <bool TA, bool TB>
 favor_status gemm(const float* A, const float* B, float* C, int M, int N, int K, int lda, int ldb, int ldc,
                   long long sA, long long sB, long long sC, BMap mapA, BMap mapB, int batch, hipStream_t st,
-                  int flags = 0) {
+                  int flags = 0, Epi epi = Epi{}) {
   hipLaunchKernelGGL((gemm_f32<TA, TB>), dim3(gemm_blocks(M, N, batch)), dim3(256), 0, st, A, B, C, M, N, K, lda,
-                     ldb, ldc, sA, sB, sC, mapA, mapB, batch, K, flags);
+                     ldb, ldc, sA, sB, sC, mapA, mapB, batch, K, flags, epi);
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
@@ -162,7 +198,7 @@ favor_status gemm_split(const float* A, const float* B, float* C, float* P, int 
                         long long sA, long long sB, BMap mapA, BMap mapB, int batch, int splits, hipStream_t st) {
   const int kc = ((K + splits - 1) / splits + GK - 1) / GK * GK;
   hipLaunchKernelGGL((gemm_f32<TA, TB>), dim3(gemm_blocks(M, N, (long long)batch * splits)), dim3(256), 0, st, A,
-                     B, P, M, N, K, lda, ldb, N, sA, sB, (long long)M * N, mapA, mapB, batch, kc, 0);
+                     B, P, M, N, K, lda, ldb, N, sA, sB, (long long)M * N, mapA, mapB, batch, kc, 0, Epi{});
   if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
   const long long n = (long long)batch * M * N;
   hipLaunchKernelGGL(sum_splits, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, P, C, n, splits);

@@ -303,11 +303,15 @@ def generalized_attention(Q, K, V, W, causal=False, fn="relu"):
             pq = relu_feature_map(Q[b, hq], W[w_of[hk]])
             pk = relu_feature_map(K[b, hk], W[w_of[hk]])
             v = np.asarray(V[b, hk], dtype=_F)
-            if causal:
-                Sv = np.cumsum(pk[:, :, None] * v[:, None, :], axis=0)   # (L, m, d) prefixes
-                S1 = np.cumsum(pk, axis=0)
-                num = np.einsum("lf,lfd->ld", pq, Sv)
-                den = np.einsum("lf,lf->l", pq, S1)
+            if causal:  # left-to-right running sums over j <= i
+                m = pk.shape[1]
+                Sv, S1 = np.zeros((m, d)), np.zeros(m)
+                num, den = np.empty((L, d)), np.empty(L)
+                for i in range(L):
+                    Sv += np.outer(pk[i], v[i])
+                    S1 += pk[i]
+                    num[i] = pq[i] @ Sv
+                    den[i] = pq[i] @ S1
             else:
                 num = pq @ (pk.T @ v)
                 den = pq @ pk.sum(axis=0)
