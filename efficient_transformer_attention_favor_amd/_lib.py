@@ -27,6 +27,7 @@ FAVOR_FEATURE_RELU = 1
 EXPORTED = ("favor_workspace_bytes", "favor_attn_fwd", "favor_attn_fwd_timed", "favor_features",
             "favor_decode_state_bytes", "favor_attn_decode", "favor_bwd_workspace_bytes", "favor_attn_bwd",
             "favor_draw_features", "favor_generalized_workspace_bytes", "favor_attn_fwd_generalized",
+            "favor_decode_prefill_workspace_bytes", "favor_decode_prefill",
             "favor_status_string", "favor_abi_version")
 
 
@@ -72,6 +73,10 @@ def lib() -> ctypes.CDLL:
         L.favor_bwd_workspace_bytes.restype = ctypes.c_size_t
         L.favor_attn_bwd.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.favor_attn_bwd.restype = ctypes.c_int
+        L.favor_decode_prefill_workspace_bytes.argtypes = [P]
+        L.favor_decode_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.favor_decode_prefill.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.favor_decode_prefill.restype = ctypes.c_int
         L.favor_generalized_workspace_bytes.argtypes = [P, ctypes.c_int32]
         L.favor_generalized_workspace_bytes.restype = ctypes.c_size_t
         L.favor_attn_fwd_generalized.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
@@ -137,6 +142,14 @@ def bwd_workspace_bytes(p: FavorProblem) -> int:
 def attn_bwd(p: FavorProblem, q, k, v, w, dout, dq, dk, dv, workspace, workspace_nbytes, stream) -> int:
     return int(lib().favor_attn_bwd(_ref(p), q, k, v, w, dout, dq, dk, dv, workspace,
                                     ctypes.c_size_t(workspace_nbytes), stream))
+
+
+def decode_prefill_workspace_bytes(p: FavorProblem) -> int:
+    return lib().favor_decode_prefill_workspace_bytes(_ref(p))
+
+
+def decode_prefill(p: FavorProblem, k, v, w, state, workspace, workspace_nbytes, stream) -> int:
+    return lib().favor_decode_prefill(_ref(p), k, v, w, state, workspace, workspace_nbytes, stream)
 
 
 def generalized_workspace_bytes(p: FavorProblem, fn) -> int:

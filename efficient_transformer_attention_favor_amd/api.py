@@ -138,6 +138,33 @@ def decode_state(q, k, W):
     return torch.zeros(nbytes // 4, dtype=torch.float32, device=q.device)
 
 
+def decode_prefill(K, V, W, heads_q, state=None, stream=None):
+    """The decoding state after the prompt K, V (B, Hkv, L, d): favor_decode_prefill.  Returns
+    the state (float32, the layout of decode_state), ready for attn_decode."""
+    if K.dim() != 4 or V.shape != K.shape or K.dtype not in _DTYPES or V.dtype != K.dtype:
+        raise ValueError("expected K, V (B, Hkv, L, d) of one dtype (float32/bfloat16)")
+    if W.dtype != torch.float32 or W.dim() != 3 or any(not t.is_contiguous() for t in (K, V, W)):
+        raise ValueError("W must be a contiguous float32 (Hw, m, d); K, V contiguous")
+    B, Hkv, L, d = K.shape
+    p = _lib.problem(B, heads_q, Hkv, W.shape[0], L, d, W.shape[1], _DTYPES[K.dtype], _lib.FAVOR_CAUSAL, 0)
+    one = _lib.problem(B, heads_q, Hkv, W.shape[0], 1, d, W.shape[1], _DTYPES[K.dtype], _lib.FAVOR_CAUSAL, 0)
+    nbytes, sbytes = _lib.decode_prefill_workspace_bytes(p), _lib.decode_state_bytes(one)
+    if nbytes == 0 or sbytes == 0:
+        raise ValueError("unsupported prefill problem")
+    if state is None:
+        state = torch.empty(sbytes // 4, dtype=torch.float32, device=K.device)
+    elif state.dtype != torch.float32 or state.numel() * 4 < sbytes or not state.is_contiguous():
+        raise ValueError("state must be a contiguous float32 tensor of favor_decode_state_bytes()")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
+    if stream is None:
+        stream = torch.cuda.current_stream(K.device)
+    st = _lib.decode_prefill(p, K.data_ptr(), V.data_ptr(), W.data_ptr(), state.data_ptr(), ws.data_ptr(), nbytes,
+                             stream.cuda_stream)
+    if st != _lib.FAVOR_OK:
+        raise _lib.FavorError(st, "favor_decode_prefill")
+    return state
+
+
 def attn_decode(q, k, v, W, state, out=None, stream=None):
     """One causal decoding step: adds position (k, v) to `state` (from decode_state, updated
     in place) and returns out (B, Hq, d) = the new position's attention output."""

@@ -17,11 +17,17 @@
 //                   M the row maximum, out = sum_f p_f S_v,f / sum_f p_f S_1,f.
 // Both are latency-bound (a few hundred KB of state per call); the arithmetic is float32 on
 // the VALU, so bf16 problems round only their inputs and outputs.
+//
+// A prompt enters the state in one call (favor_decode_prefill): the key side of the forward
+// pass summarises the prompt's positions over ranges (float32 partials with per-feature
+// stabilisers c_tf), then prefill_state merges them into the state format:
+//   c = max over t, f of c_tf,  S[f][col] = sum_t 2^(c_tf - c) partial_t[col][f],  n = L.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
 
 #include "favor_device.hpp"
+#include "favor_ops.hpp"
 #include "favor_plan.hpp"
 
 namespace favor {
@@ -194,6 +200,39 @@ favor_status run_decode(const Plan& s, const void* q, const void* k, const void*
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
+// One workgroup per (batch, kv head): the merged state of its T range partials.
+__global__ void __launch_bounds__(kDecThreads)
+    prefill_state(const float* __restrict__ gs, const float* __restrict__ gc, int T, int d, int m, int L,
+                  float* __restrict__ S, float* __restrict__ cst, unsigned* __restrict__ count) {
+  __shared__ float red[kDecThreads];
+  __shared__ float scale[512];
+  const int bh = blockIdx.x, t0 = threadIdx.x;
+  const float* gch = gc + (size_t)bh * T * m;
+  float mx = -INFINITY;
+  for (int i = t0; i < T * m; i += kDecThreads) mx = fmaxf(mx, gch[i]);
+  mx = block_max(mx, red);
+  const int d1 = d + 1;
+  const float* gsh = gs + (size_t)bh * T * d1 * m;
+  float* Sh = S + (size_t)bh * m * d1;
+  for (int t = 0; t < T; ++t) {
+    for (int f = t0; f < m; f += kDecThreads) scale[f] = fast_exp2(gch[(size_t)t * m + f] - mx);
+    __syncthreads();
+    // element (f, col) of the state, f fastest (reads of the partial are contiguous)
+    for (int e = t0; e < m * d1; e += kDecThreads) {
+      const int col = e / m, f = e - col * m;
+      const int row = col == d ? d : 32 * (col >> 5) + vperm_inv(col & 31);
+      const float v = scale[f] * gsh[((size_t)t * d1 + row) * m + f];
+      float* dst = Sh + (size_t)f * d1 + col;
+      *dst = t == 0 ? v : *dst + v;
+    }
+    __syncthreads();
+  }
+  if (t0 < kDecSplit) {
+    cst[bh * kDecSplit + t0] = mx;
+    count[bh * kDecSplit + t0] = (unsigned)L;
+  }
+}
+
 favor_status decode_plan(const favor_problem* p, Plan* s) {
   if (p == nullptr) return FAVOR_ERR_INVALID_ARG;
   favor_problem one = *p;
@@ -204,8 +243,49 @@ favor_status decode_plan(const favor_problem* p, Plan* s) {
   return FAVOR_OK;
 }
 
+// The prompt's problem as a bidirectional key-side pass over its L positions (the chunk
+// field is validated as for the forward and otherwise ignored).
+favor_status prefill_plan(const favor_problem* p, Plan* s) {
+  if (p == nullptr) return FAVOR_ERR_INVALID_ARG;
+  const favor_status st = make_plan(p, s);  // validation of the problem as given
+  if (st != FAVOR_OK) return st;
+  if (p->mode != FAVOR_CAUSAL) return FAVOR_ERR_INVALID_ARG;
+  favor_problem q = *p;
+  q.mode = FAVOR_BIDIRECTIONAL;
+  q.chunk = 0;
+  return make_plan(&q, s);
+}
+
 }  // namespace
 }  // namespace favor
+
+extern "C" size_t favor_decode_prefill_workspace_bytes(const favor_problem* p) {
+  favor::Plan s;
+  if (favor::prefill_plan(p, &s) != FAVOR_OK) return 0;
+  return s.off_p;  // the range partials gs and their stabilisers gc
+}
+
+extern "C" favor_status favor_decode_prefill(const favor_problem* p, const void* K, const void* V, const float* W,
+                                             float* state, void* workspace, size_t workspace_bytes, void* stream) {
+  favor::Plan s;
+  const favor_status st = favor::prefill_plan(p, &s);
+  if (st != FAVOR_OK) return st;
+  if (K == nullptr || V == nullptr || W == nullptr || state == nullptr) return FAVOR_ERR_INVALID_ARG;
+  if (workspace == nullptr || workspace_bytes < s.off_p || (reinterpret_cast<uintptr_t>(workspace) & 255) != 0)
+    return FAVOR_ERR_WORKSPACE;
+  if (s.m > 512) return FAVOR_ERR_UNSUPPORTED;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  float* gs = reinterpret_cast<float*>(ws + s.off_gs);
+  float* gc = reinterpret_cast<float*>(ws + s.off_gc);
+  const favor_status rc = favor::launch_key_summaries(s, K, V, W, gs, gc, hs);
+  if (rc != FAVOR_OK) return rc;
+  float* cst = state + (size_t)s.BH * s.m * (s.d + 1);
+  unsigned* count = reinterpret_cast<unsigned*>(cst + (size_t)s.BH * favor::kDecSplit);
+  hipLaunchKernelGGL(favor::prefill_state, dim3(s.BH), dim3(favor::kDecThreads), 0, hs, gs, gc, s.T, s.d, s.m, s.L,
+                     state, cst, count);
+  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
 
 extern "C" size_t favor_decode_state_bytes(const favor_problem* p) {
   favor::Plan s;

@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "favor_device.hpp"
+#include "favor_ops.hpp"
 #include "favor_plan.hpp"
 
 namespace favor {
@@ -1616,6 +1617,23 @@ favor_status run_typed(const Plan& s, const void* Q, const void* K, const void* 
 }
 
 }  // namespace
+
+favor_status launch_key_summaries(const Plan& plan, const void* K, const void* V, const float* W, float* gs,
+                                  float* gc, hipStream_t st) {
+  if (plan.mode != FAVOR_BIDIRECTIONAL) return FAVOR_ERR_INVALID_ARG;
+  Plan s = plan;
+  s.img = false;  // float32 partials, never the readout's images
+  if (s.dtype == FAVOR_BF16)
+    return s.d == 64 ? launch_kv_summary<bf16, 64>(s, static_cast<const bf16*>(K), static_cast<const bf16*>(V), W, gs,
+                                                   gc, nullptr, st)
+                     : launch_kv_summary<bf16, 128>(s, static_cast<const bf16*>(K), static_cast<const bf16*>(V), W,
+                                                    gs, gc, nullptr, st);
+  return s.d == 64 ? launch_kv_summary<float, 64>(s, static_cast<const float*>(K), static_cast<const float*>(V), W,
+                                                  gs, gc, nullptr, st)
+                   : launch_kv_summary<float, 128>(s, static_cast<const float*>(K), static_cast<const float*>(V), W,
+                                                   gs, gc, nullptr, st);
+}
+
 }  // namespace favor
 
 extern "C" {

@@ -18,4 +18,11 @@ favor_status launch_features(const Plan& s, int side, const void* X, const float
 favor_status launch_relu_features(const Plan& s, int side, const void* X, const float* W, float* phi,
                                   hipStream_t st, int Lo = 0);
 
+// The key-side range summaries of a bidirectional plan as float32 partials:
+// gs [BH][T][d+1][m] (value rows in the permuted order vperm within each 32-column tile, row d
+// the ones column) and gc [BH][T][m], the per-feature stabilisers in log2 units, with
+// gs = sum over the range's positions of 2^(e - gc) [v, 1], e = log2(e) (w . k - |k|^2 / 2).
+favor_status launch_key_summaries(const Plan& s, const void* K, const void* V, const float* W, float* gs,
+                                  float* gc, hipStream_t st);
+
 }  // namespace favor

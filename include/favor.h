@@ -174,6 +174,19 @@ favor_status favor_draw_features(int32_t heads_w, int32_t num_features, int32_t 
  * `stream`; concurrent calls on one state race.  Errors as for favor_attn_fwd (a null
  * pointer is FAVOR_ERR_INVALID_ARG; nothing is queued on an error). */
 size_t favor_decode_state_bytes(const favor_problem* p);
+
+/* Prompt prefill for decoding: writes the state (layout above) that holds the prompt's L =
+ * p->seq_len positions, i.e. the state favor_attn_decode would reach after decoding them
+ * one by one (up to rounding), with c the largest key exponent of the prompt and n = L.
+ * p->mode must be FAVOR_CAUSAL (the state belongs to a causal sequence); the state buffer
+ * has favor_decode_state_bytes of the same problem with seq_len 1 and is overwritten
+ * whole.  K, V [batch][heads_kv][L][d] and W as for favor_attn_fwd.  The workspace
+ * (favor_decode_prefill_workspace_bytes(p) bytes, 256-byte aligned) holds the key side's
+ * float32 range partials.  Runs the forward pass's key-side kernel, then one merge kernel
+ * per call on `stream`.  Errors as for favor_attn_fwd. */
+size_t favor_decode_prefill_workspace_bytes(const favor_problem* p);
+favor_status favor_decode_prefill(const favor_problem* p, const void* K, const void* V, const float* W,
+                                  float* state, void* workspace, size_t workspace_bytes, void* stream);
 favor_status favor_attn_decode(const favor_problem* p, const void* q, const void* k, const void* v,
                                const float* W, float* state, void* out, void* stream);
 

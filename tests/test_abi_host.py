@@ -158,3 +158,21 @@ def test_generalized_validation():
     assert L.attn_fwd_generalized(p, 1, *([8] * 5), 256, need - 1, None) == L.FAVOR_ERR_WORKSPACE
     assert L.attn_fwd_generalized(p, 1, *([8] * 5), 260, need, None) == L.FAVOR_ERR_WORKSPACE
     assert L.attn_fwd_generalized(_p(head_dim=32), 1, *([8] * 5), 256, need, None) == L.FAVOR_ERR_UNSUPPORTED
+
+
+def test_decode_prefill_validation():
+    L = _lib
+    causal = _p(mode=L.FAVOR_CAUSAL, seq_len=300)
+    need = L.decode_prefill_workspace_bytes(causal)
+    assert need > 0 and need % 256 == 0
+    assert L.decode_prefill_workspace_bytes(_p(seq_len=300)) == 0            # bidirectional
+    assert L.decode_prefill(_p(seq_len=300), 8, 8, 8, 256, 256, need, None) == L.FAVOR_ERR_INVALID_ARG
+    assert L.decode_prefill(None, 8, 8, 8, 256, 256, need, None) == L.FAVOR_ERR_INVALID_ARG
+    for i in range(4):
+        args = [8, 8, 8, 256]
+        args[i] = None
+        assert L.decode_prefill(causal, *args, 256, need, None) == L.FAVOR_ERR_INVALID_ARG
+    assert L.decode_prefill(causal, 8, 8, 8, 256, 256, need - 1, None) == L.FAVOR_ERR_WORKSPACE
+    assert L.decode_prefill(causal, 8, 8, 8, 256, None, need, None) == L.FAVOR_ERR_WORKSPACE
+    assert L.decode_prefill(_p(mode=L.FAVOR_CAUSAL, head_dim=32), 8, 8, 8, 256, 256, need, None) == \
+        L.FAVOR_ERR_UNSUPPORTED

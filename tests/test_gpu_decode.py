@@ -138,3 +138,71 @@ def test_decode_keys_far_below_zero():
     _say(f"  large keys: rowwise rel err {err:.3e}")
     assert np.isfinite(got).all()
     assert err <= TOL[w.dtype]
+
+
+# ---- prompt prefill (favor_decode_prefill) ---------------------------------------------
+
+PREFILL = [
+    _small("c1_bidir_f32", batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=1000, causal=True),   # 8 ranges
+    _small("c1_bidir_f32", batch=2, heads_q=2, heads_kv=2, heads_w=2, seq_len=77, head_dim=128, num_features=192,
+           causal=True),
+    _small("c3_causal_bf16", batch=2, heads_q=4, heads_kv=2, heads_w=2, seq_len=700),
+    _small("c5_causal_long_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=300),  # m = 512, heavy rows
+]
+
+
+def _state_parts(state, w):
+    st = state.cpu().numpy().astype(np.float64)
+    BH, m, d = w.batch * w.heads_kv, w.num_features, w.head_dim
+    S = st[:BH * m * (d + 1)].reshape(BH, m, d + 1)
+    off = BH * m * (d + 1)
+    cs = st[off:off + 8 * BH].reshape(BH, 8)
+    n = state.cpu()[off + 8 * BH:off + 16 * BH].view(torch.int32).numpy()
+    return S, cs, n
+
+
+@pytest.mark.parametrize("w", PREFILL, ids=lambda w: f"{w.dtype}_B{w.batch}H{w.heads_q}/{w.heads_kv}"
+                         f"_L{w.seq_len}_d{w.head_dim}_m{w.num_features}")
+def test_prefill_state_is_the_summary(w):
+    """The prefilled state, times 2^c / sqrt(m), is phi(K)^T [V, 1] of the prompt (float32
+    problems 1e-5; bf16 problems 1e-2: the key side rounds phi to bf16 for the products)."""
+    _say(f"prefill state {w}")
+    Q, K, V, W = I.make_inputs(w, seed=1)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    state = api.decode_prefill(_dev(K, dt), _dev(V, dt), _dev(W, torch.float32), w.heads_q)
+    torch.cuda.synchronize()
+    S, cs, n = _state_parts(state, w)
+    assert (cs == cs[:, :1]).all() and (n == w.seq_len).all()
+    d, m = w.head_dim, w.num_features
+    worst = 0.0
+    for bh in range(w.batch * w.heads_kv):
+        b, h = divmod(bh, w.heads_kv)
+        Wh = W[0 if w.heads_w == 1 else h]
+        Sv, S1 = O.kv_summary(O.feature_map(K[b, h], Wh), V[b, h])
+        got = S[bh] * 2.0 ** cs[bh, 0] / np.sqrt(m)
+        want = np.concatenate([Sv, S1[:, None]], axis=1)
+        worst = max(worst, np.abs(got - want).max() / np.abs(want).max())
+    _say(f"  state rel err {worst:.2e}")
+    assert worst <= (1e-5 if w.dtype == "f32" else 1e-2)
+
+
+@pytest.mark.parametrize("w", PREFILL, ids=lambda w: f"{w.dtype}_B{w.batch}H{w.heads_q}/{w.heads_kv}"
+                         f"_L{w.seq_len}_d{w.head_dim}_m{w.num_features}")
+def test_prefill_then_decode(w):
+    """Prefill the first L - 8 positions, decode the last 8: their outputs are the causal
+    output at those positions."""
+    _say(f"prefill + decode {w}")
+    Q, K, V, W = I.make_inputs(w, seed=2)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    q, k, v, wd = _dev(Q, dt), _dev(K, dt), _dev(V, dt), _dev(W, torch.float32)
+    L0 = w.seq_len - 8
+    state = api.decode_prefill(k[:, :, :L0].contiguous(), v[:, :, :L0].contiguous(), wd, w.heads_q)
+    outs = []
+    for t in range(L0, w.seq_len):
+        outs.append(api.attn_decode(q[:, :, t].contiguous(), k[:, :, t].contiguous(), v[:, :, t].contiguous(), wd,
+                                    state).float().cpu().numpy())
+    got = np.stack(outs, axis=2)
+    ref = O.favor_attention(Q, K, V, W, causal=True)[:, :, L0:]
+    err = O.rowwise_rel_err(got, ref)
+    _say(f"  rowwise rel err {err:.3e}")
+    assert err <= TOL[w.dtype]
