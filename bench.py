@@ -374,9 +374,10 @@ def main():
 
 
 def decode_main(args, w0):
-    """Decoding: the state holds --prefill positions, then each step adds one position per
-    (batch, kv head) and answers every query head.  Algorithmic bytes per step: the state
-    read and written once (float32 [B*Hkv][m][d+1]), W, and the new q, k, v and out rows."""
+    """Decoding: the state holds --prefill positions (one favor_decode_prefill call, timed on
+    its own as prefill_ms), then each step adds one position per (batch, kv head) and answers
+    every query head.  Algorithmic bytes per step: the state read and written once (float32
+    [B*Hkv][m][d+1]), W, and the new q, k, v and out rows."""
     import numpy as np
     import torch
 
@@ -392,6 +393,18 @@ def decode_main(args, w0):
     qs, ks, vs = (torch.from_numpy(np.ascontiguousarray(x.transpose(2, 0, 1, 3))).to(dev).to(dt) for x in (Q, K, V))
     wd = torch.from_numpy(W).to(dev)
     state = api.decode_state(qs[0], ks[0], wd)
+    prefill_ms = None
+    if args.prefill > 0:
+        kp, vp = (torch.from_numpy(np.ascontiguousarray(x[:, :, :args.prefill])).to(dev).to(dt) for x in (K, V))
+        api.decode_prefill(kp, vp, wd, w.heads_q, state=state)  # untimed first call
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        api.decode_prefill(kp, vp, wd, w.heads_q, state=state)
+        e1.record()
+        torch.cuda.synchronize()
+        prefill_ms = round(e0.elapsed_time(e1), 5)
+        del kp, vp
     out = torch.empty_like(qs[0])
     p = api._decode_problem(qs[0], ks[0], wd)
     stream = torch.cuda.current_stream(dev)
@@ -402,7 +415,7 @@ def decode_main(args, w0):
         if st != _lib.FAVOR_OK:
             raise _lib.FavorError(st, "favor_attn_decode")
 
-    for t in range(args.prefill + args.warmup):
+    for t in range(args.prefill, args.prefill + args.warmup):
         step(t)
     torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
@@ -434,7 +447,7 @@ def decode_main(args, w0):
         "data": "synthetic (seeded Gaussian q, k, v; orthogonal random features W)",
         "config": {"workload": f"{w0.name} head layout, decode after {args.prefill} positions", "batch": B,
                    "heads_q": Hq, "heads_kv": Hkv, "heads_w": w.heads_w, "head_dim": d, "num_features": m,
-                   "mode": "causal decode", "parallelism": "single GPU"},
+                   "mode": "causal decode", "parallelism": "single GPU", "prefill_ms": prefill_ms},
         "roofline": {"kernel": "decode_update+decode_readout", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": None, "per_launch": {"alg_bytes": alg_bytes, "avg_ms": round(ms_step, 5)}},
