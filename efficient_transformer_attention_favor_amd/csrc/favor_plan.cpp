@@ -28,6 +28,8 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
   const long long elems_q = (long long)p->batch * p->heads_q * p->seq_len * p->head_dim;
   const long long elems_kv = (long long)p->batch * p->heads_kv * p->seq_len * p->head_dim;
   if (elems_q >= (1LL << 31) || elems_kv >= (1LL << 31)) return FAVOR_ERR_UNSUPPORTED;
+  // (batch, head) pairs index the second grid dimension of several launches
+  if ((long long)p->batch * p->heads_q > 65535) return FAVOR_ERR_UNSUPPORTED;
 
   Plan& q = *s;
   q.B = p->batch;

@@ -49,6 +49,8 @@ BAD = [
     (dict(mode=_lib.FAVOR_CAUSAL, chunk=48), _lib.FAVOR_ERR_UNSUPPORTED),
     (dict(batch=1 << 12, heads_q=1 << 8, heads_kv=1 << 8, heads_w=1, seq_len=1 << 14),
      _lib.FAVOR_ERR_UNSUPPORTED),                           # more than 2^31 elements
+    (dict(batch=1 << 12, heads_q=1 << 4, heads_kv=1 << 4, heads_w=1, seq_len=1),
+     _lib.FAVOR_ERR_UNSUPPORTED),                           # more than 65535 (batch, head) pairs
 ]
 
 
