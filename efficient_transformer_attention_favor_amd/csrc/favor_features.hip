@@ -20,6 +20,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 #include "favor_device.hpp"
 #include "favor_ops.hpp"
 #include "favor_plan.hpp"
@@ -28,6 +30,10 @@ namespace favor {
 namespace {
 
 constexpr int kFeatWaves = 4;
+// bf16 problems with m <= kFeatLdsM: the workgroup (8 waves, 256 rows) first stages the
+// fp16 W log2e rows of its head in LDS, so W is read and converted once per workgroup
+// instead of once per wave and feature tile.
+constexpr int kFeatLdsM = 256, kFeatLdsWaves = 8;
 
 // Monotone map float -> uint32 (larger float, larger code) and its inverse.
 __device__ __forceinline__ unsigned enc_order(float x) {
@@ -41,20 +47,38 @@ __device__ __forceinline__ float dec_order(unsigned k) {
 // MODE 0: queries (row stabiliser, two passes in the kernel); 1: keys, head-maximum pass;
 // 2: keys, writing pass with the head maximum from pass 1; 3: the ReLU feature map
 // ReLU(W x) / sqrt(m) of queries or keys (no norm term, no stabiliser; c_out unused).
-template <class T, int D, int MODE>
-__global__ void __launch_bounds__(64 * kFeatWaves)
+template <class T, int D, int MODE, bool LW>
+__global__ void __launch_bounds__(64 * (LW ? kFeatLdsWaves : kFeatWaves))
     features_kernel(const T* __restrict__ X, const float* __restrict__ W, int L, int Lo, int H, int G, int Hw,
                     int m, float* __restrict__ phi, float* __restrict__ c_out) {
   using P = Prec<T>;
   using wfrag = typename P::wfrag;
   constexpr int NKC = D / P::KS;
+  constexpr int NWV = LW ? kFeatLdsWaves : kFeatWaves;
+  constexpr int LDW = D + 8;  // fp16 W row stride in LDS (16-byte aligned rows)
+  __shared__ __attribute__((aligned(16))) f16 Wl[LW ? kFeatLdsM * LDW : 8];
   const int bh = blockIdx.y, h = bh % H;
   const int hkv = h / G;  // G = query heads per kv head (1 on the key side)
   const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
-  const int row = (blockIdx.x * kFeatWaves + wave) * 32 + col;
+  const int row = (blockIdx.x * NWV + wave) * 32 + col;
   const bool valid = row < L, out_row = row < Lo;
   const size_t grow = (size_t)bh * L + row, orow = (size_t)bh * Lo + row;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
+  if constexpr (LW) {
+    for (int e = threadIdx.x; e < m * (D / 8); e += 64 * NWV) {
+      const int f = e / (D / 8), c8 = (e - f * (D / 8)) * 8;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(Wh + (size_t)f * D + c8);
+      const f32x4 b = *reinterpret_cast<const f32x4*>(Wh + (size_t)f * D + c8 + 4);
+      f16x8 v;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = (f16)(a[j] * kLog2e);
+        v[j + 4] = (f16)(b[j] * kLog2e);
+      }
+      *reinterpret_cast<f16x8*>(Wl + f * LDW + c8) = v;
+    }
+    __syncthreads();
+  }
 
   wfrag xf[NKC];
 #pragma unroll
@@ -70,7 +94,10 @@ __global__ void __launch_bounds__(64 * kFeatWaves)
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) {
       wfrag wp;
-      load_w_frag(Wh + (size_t)(32 * ft + col) * D, kc, g, wp);
+      if constexpr (LW)
+        wp = *reinterpret_cast<const f16x8*>(Wl + (32 * ft + col) * LDW + 16 * kc + 8 * g);
+      else
+        load_w_frag(Wh + (size_t)(32 * ft + col) * D, kc, g, wp);
       c = mma(wp, xf[kc], c);
     }
     if constexpr (MODE != 3) {
@@ -138,27 +165,39 @@ __global__ void head_max_decode(float* c, int n) {
   if (i < n) c[i] = dec_order(reinterpret_cast<const unsigned*>(c)[i]) / kLog2e;
 }
 
+// One launch of features_kernel in mode MODE over rows of H heads (G query heads per W head).
+template <class T, int D, int MODE>
+bool launch_mode(const Plan& s, const T* X, const float* W, int Lo, int H, int G, float* phi, float* c,
+                 hipStream_t st) {
+  const int nh = s.B * H;
+  if constexpr (std::is_same<T, bf16>::value) {
+    if (s.m <= kFeatLdsM) {
+      constexpr int R = 32 * kFeatLdsWaves;
+      hipLaunchKernelGGL((features_kernel<T, D, MODE, true>), dim3((Lo + R - 1) / R, nh), dim3(64 * kFeatLdsWaves),
+                         0, st, X, W, s.L, Lo, H, G, s.Hw, s.m, phi, c);
+      return hipGetLastError() == hipSuccess;
+    }
+  }
+  {
+    constexpr int R = 32 * kFeatWaves;
+    hipLaunchKernelGGL((features_kernel<T, D, MODE, false>), dim3((Lo + R - 1) / R, nh), dim3(64 * kFeatWaves), 0,
+                       st, X, W, s.L, Lo, H, G, s.Hw, s.m, phi, c);
+  }
+  return hipGetLastError() == hipSuccess;
+}
+
 template <class T, int D>
 favor_status run_features(const Plan& s, int side, const void* Xv, const float* W, float* phi, float* c, int Lo,
                           hipStream_t st) {
   const T* X = static_cast<const T*>(Xv);
-  const dim3 block(64 * kFeatWaves);
-  const int row_blocks = (Lo + 32 * kFeatWaves - 1) / (32 * kFeatWaves);
-  if (side == 0) {
-    hipLaunchKernelGGL((features_kernel<T, D, 0>), dim3(row_blocks, s.B * s.Hq), block, 0, st, X, W, s.L, Lo, s.Hq,
-                       s.G, s.Hw, s.m, phi, c);
-    return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
-  }
+  if (side == 0)
+    return launch_mode<T, D, 0>(s, X, W, Lo, s.Hq, s.G, phi, c, st) ? FAVOR_OK : FAVOR_ERR_HIP;
   const int nh = s.B * s.Hkv;
   const int ib = (nh + 255) / 256;
   hipLaunchKernelGGL(head_max_init, dim3(ib), dim3(256), 0, st, reinterpret_cast<unsigned*>(c), nh);
   if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
-  hipLaunchKernelGGL((features_kernel<T, D, 1>), dim3(row_blocks, nh), block, 0, st, X, W, s.L, Lo, s.Hkv, 1, s.Hw,
-                     s.m, phi, c);
-  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
-  hipLaunchKernelGGL((features_kernel<T, D, 2>), dim3(row_blocks, nh), block, 0, st, X, W, s.L, Lo, s.Hkv, 1, s.Hw,
-                     s.m, phi, c);
-  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  if (!launch_mode<T, D, 1>(s, X, W, Lo, s.Hkv, 1, phi, c, st)) return FAVOR_ERR_HIP;
+  if (!launch_mode<T, D, 2>(s, X, W, Lo, s.Hkv, 1, phi, c, st)) return FAVOR_ERR_HIP;
   hipLaunchKernelGGL(head_max_decode, dim3(ib), dim3(256), 0, st, c, nh);
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
@@ -166,11 +205,9 @@ favor_status run_features(const Plan& s, int side, const void* Xv, const float* 
 template <class T, int D>
 favor_status run_relu_features(const Plan& s, int side, const void* Xv, const float* W, float* phi, int Lo,
                                hipStream_t st) {
-  const int row_blocks = (Lo + 32 * kFeatWaves - 1) / (32 * kFeatWaves);
   const int H = side == 0 ? s.Hq : s.Hkv, G = side == 0 ? s.G : 1;
-  hipLaunchKernelGGL((features_kernel<T, D, 3>), dim3(row_blocks, s.B * H), dim3(64 * kFeatWaves), 0, st,
-                     static_cast<const T*>(Xv), W, s.L, Lo, H, G, s.Hw, s.m, phi, nullptr);
-  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  return launch_mode<T, D, 3>(s, static_cast<const T*>(Xv), W, Lo, H, G, phi, nullptr, st) ? FAVOR_OK
+                                                                                            : FAVOR_ERR_HIP;
 }
 
 }  // namespace
