@@ -110,6 +110,7 @@ __global__ void __launch_bounds__(256)
     if (active) {
 #pragma unroll
       for (int h = 0; h < GK / 8; ++h) {
+        if (k0 + 8 * h >= kend) break;  // a ragged last slab (e.g. K = d + 1) skips its empty groups
         const f32x4 a = *reinterpret_cast<const f32x4*>(&As[32 * wm + c32][8 * h + 4 * g]);
         const f32x4 b = *reinterpret_cast<const f32x4*>(&Bs[32 * wn + c32][8 * h + 4 * g]);
 #pragma unroll
