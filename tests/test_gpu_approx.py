@@ -66,3 +66,29 @@ def test_report_error_vs_softmax(name):
          + "; ".join(f"{k}: row-wise rel {e:.3e}, Frobenius rel {f:.3e}, RMS {r:.3e}" for k, (e, f, r) in res.items()))
     for vals in res.values():
         assert all(np.isfinite(v) for v in vals)
+
+
+def test_error_falls_with_features_and_orthogonal_rows_help():
+    """At low temperature (Q and K scaled by 1/4, so the positive features' variance is
+    small) the error against exact softmax falls like 1/sqrt(m) and orthogonal rows beat
+    i.i.d. rows (Performer page, "제안 방법" and "주요 결과"), with W drawn on the device."""
+    w = I.workload("c2_bidir_bf16").replace(name="approx_low_temp", batch=1, heads_q=4, heads_kv=4, heads_w=4)
+    Q, K, V, _ = I.make_inputs(w, seed=0)
+    Q, K = I.round_to_bf16(Q * 0.25), I.round_to_bf16(K * 0.25)  # exact in bf16 (power of two)
+    rows = I.sample_rows(w, 256)
+    exact = O.softmax_rows(Q, K, V, rows)
+    q, k, v = (_dev(x, torch.bfloat16) for x in (Q, K, V))
+    rms = {}
+    for m in (64, 512):
+        for orth in (True, False):
+            errs = []
+            for seed in range(4):
+                Wd = api.draw_features(w.heads_w, m, w.head_dim, 100 * m + seed, orth)
+                y = api.attn_fwd(q, k, v, Wd)
+                got = torch.stack([y[b, h, i] for b, h, i in rows]).float().cpu().numpy()
+                errs.append(np.sqrt(np.mean((got - exact) ** 2)))
+            rms[(m, orth)] = float(np.mean(errs))
+    _say(f"  RMS error vs softmax: {rms}")
+    for orth in (True, False):
+        assert rms[(512, orth)] < 0.5 * rms[(64, orth)]   # sqrt(8) = 2.8 expected
+    assert rms[(64, True)] < rms[(64, False)] and rms[(512, True)] < rms[(512, False)]
