@@ -129,3 +129,22 @@ def test_full_size_sampled_rows(name):
     err = O.rowwise_rel_err(got, ref)
     _say(f"  rowwise rel err over {len(rows)} rows {err:.3e}")
     assert err < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_large_norm_inputs(causal, dtype):
+    """Q and K scaled by 4 (exact in bf16): exponents spread over a range far beyond float32
+    (|w.k| up to ~100 in log2 units), so the first block's stabilisers can be overtaken by
+    later ones and the overflow fallback runs."""
+    base = "c1_bidir_f32" if dtype == "f32" else "c2_bidir_bf16"
+    w = _small(base, batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=700, num_features=128, causal=causal)
+    _say(f"case {w} x4")
+    Q, K, V, W = I.make_inputs(w, seed=7)
+    Q, K = Q * np.float32(4), K * np.float32(4)
+    y = _run(w, Q, K, V, W).float().cpu().numpy()
+    ref = O.favor_attention(Q, K, V, W, causal=causal)
+    err = O.rowwise_rel_err(y, ref)
+    _say(f"  rowwise rel err {err:.3e}")
+    assert np.isfinite(y).all()
+    assert err < TOL[w.dtype]
