@@ -7,13 +7,14 @@
 // Write-Head is All You Need" (review page), "ABSTRACT": incremental decoding is bound by
 // reloading the key/value history, which this m x (d+1) summary per kv head replaces.
 //
-// Two small kernels per step:
-//   decode_update   kDecSplit workgroups per (batch, kv head), each updating one slice of
-//                   its summary (each recomputes the exponents and keeps its own copy of
-//                   c, which all slices advance identically): the new key's exponents
-//                   e_f = log2e (w_f.k - |k|^2/2), c' = max(c, max_f e_f),
-//                   S <- 2^(c - c') S + 2^(e - c') [v, 1]   (float32, VALU).
-//   decode_readout  one workgroup per (batch, query head): p_f = 2^(log2e w_f.q - M),
+// The state keeps one stabiliser per slice of m / kDecSplit features (any constant per
+// feature cancels once it is folded into the query exponent, as in the forward readout), so
+// the slices never need each other.  Two small kernels per step:
+//   decode_update   kDecSplit workgroups per (batch, kv head), workgroup s owning features
+//                   [s m/8, (s+1) m/8) and their rows of S: the new key's exponents
+//                   e_f = log2e (w_f.k - |k|^2/2), c_s' = max(c_s, max over its f of e_f),
+//                   S_f <- 2^(c_s - c_s') S_f + 2^(e_f - c_s') [v, 1]   (float32, VALU).
+//   decode_readout  one workgroup per (batch, query head): p_f = 2^(log2e w_f.q + c_s(f) - M),
 //                   M the row maximum, out = sum_f p_f S_v,f / sum_f p_f S_1,f.
 // Both are latency-bound (a few hundred KB of state per call); the arithmetic is float32 on
 // the VALU, so bf16 problems round only their inputs and outputs.
@@ -21,7 +22,8 @@
 // A prompt enters the state in one call (favor_decode_prefill): the key side of the forward
 // pass summarises the prompt's positions over ranges (float32 partials with per-feature
 // stabilisers c_tf), then prefill_state merges them into the state format:
-//   c = max over t, f of c_tf,  S[f][col] = sum_t 2^(c_tf - c) partial_t[col][f],  n = L.
+//   c_s = max of c_tf over t and the features f of slice s,
+//   S[f][col] = sum_t 2^(c_tf - c_s(f)) partial_t[col][f],  n = L.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
@@ -80,8 +82,9 @@ template <class T, int D>
 __global__ void __launch_bounds__(kDecThreads)
     decode_update(const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ W, int Hkv, int Hw,
                   int m, float* __restrict__ S, float* __restrict__ cst, unsigned* __restrict__ count) {
-  __shared__ float kl[D], vl[D + 1], phi[512], red[kDecThreads];
+  __shared__ float kl[D], vl[D + 1], phi[512 / kDecSplit], red[kDecThreads];
   const int bh = blockIdx.x / kDecSplit, part = blockIdx.x % kDecSplit, hkv = bh % Hkv;
+  const int mf = m / kDecSplit, fb = part * mf;  // this workgroup's features
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
   const int t = threadIdx.x;
   if (t < D) {
@@ -95,8 +98,8 @@ __global__ void __launch_bounds__(kDecThreads)
   nrm = block_sum(nrm, red);
 
   float mx = -INFINITY;
-  for (int f = t; f < m; f += kDecThreads) {
-    const float e = kLog2e * (row_dot<D>(Wh + (size_t)f * D, kl) - 0.5f * nrm);
+  for (int f = t; f < mf; f += kDecThreads) {
+    const float e = kLog2e * (row_dot<D>(Wh + (size_t)(fb + f) * D, kl) - 0.5f * nrm);
     phi[f] = e;
     mx = fmaxf(mx, e);
   }
@@ -107,18 +110,17 @@ __global__ void __launch_bounds__(kDecThreads)
   const float c_old = seen ? cst[bh * kDecSplit + part] : mx;
   const float c_new = fmaxf(c_old, mx);
   const float scale = fast_exp2(c_old - c_new);
-  for (int f = t; f < m; f += kDecThreads) phi[f] = fast_exp2(phi[f] - c_new);
+  for (int f = t; f < mf; f += kDecThreads) phi[f] = fast_exp2(phi[f] - c_new);
   __syncthreads();
 
-  // this workgroup's slice of S [m][D+1] (m (D+1) / kDecSplit floats, a multiple of 4):
-  // 4 consecutive elements per thread and step, two steps' loads in flight
-  const int n = m * (D + 1) / kDecSplit;
+  // this workgroup's rows of S [m][D+1] (mf (D+1) floats, a multiple of 4): 4 consecutive
+  // elements per thread and step, two steps' loads in flight
+  const int n = mf * (D + 1);
   float* Sh = S + (size_t)bh * m * (D + 1) + (size_t)part * n;
-  const int i_base = part * n;
   auto upd = [&](int i, f32x4 x) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int e = i_base + i + u, f = e / (D + 1), j = e - f * (D + 1);
+      const int e = i + u, f = e / (D + 1), j = e - f * (D + 1);
       x[u] = fmaf(x[u], scale, phi[f] * vl[j]);
     }
     *reinterpret_cast<f32x4*>(Sh + i) = x;
@@ -139,8 +141,8 @@ __global__ void __launch_bounds__(kDecThreads)
 
 template <class T, int D>
 __global__ void __launch_bounds__(kDecThreads)
-    decode_readout(const T* __restrict__ q, const float* __restrict__ W, const float* __restrict__ S, int Hq,
-                   int Hkv, int Hw, int m, T* __restrict__ out) {
+    decode_readout(const T* __restrict__ q, const float* __restrict__ W, const float* __restrict__ S,
+                   const float* __restrict__ cst, int Hq, int Hkv, int Hw, int m, T* __restrict__ out) {
   constexpr int FG = kDecThreads / D;  // feature groups (threads per value column)
   __shared__ float ql[D], p[512], red[kDecThreads], part[FG][D];
   const int bhq = blockIdx.x, b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv);
@@ -152,8 +154,10 @@ __global__ void __launch_bounds__(kDecThreads)
   __syncthreads();
 
   float mx = -INFINITY;
+  const int mf = m / kDecSplit;
   for (int f = t; f < m; f += kDecThreads) {
-    const float e = kLog2e * row_dot<D>(Wh + (size_t)f * D, ql);
+    // the slice's stabiliser joins the query exponent
+    const float e = kLog2e * row_dot<D>(Wh + (size_t)f * D, ql) + cst[bh * kDecSplit + f / mf];
     p[f] = e;
     mx = fmaxf(mx, e);
   }
@@ -196,7 +200,7 @@ favor_status run_decode(const Plan& s, const void* q, const void* k, const void*
                      static_cast<const T*>(v), W, s.Hkv, s.Hw, s.m, S, cst, count);
   if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
   hipLaunchKernelGGL((decode_readout<T, D>), dim3(s.B * s.Hq), dim3(kDecThreads), 0, st,
-                     static_cast<const T*>(q), W, S, s.Hq, s.Hkv, s.Hw, s.m, static_cast<T*>(out));
+                     static_cast<const T*>(q), W, S, cst, s.Hq, s.Hkv, s.Hw, s.m, static_cast<T*>(out));
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
@@ -204,18 +208,26 @@ favor_status run_decode(const Plan& s, const void* q, const void* k, const void*
 __global__ void __launch_bounds__(kDecThreads)
     prefill_state(const float* __restrict__ gs, const float* __restrict__ gc, int T, int d, int m, int L,
                   float* __restrict__ S, float* __restrict__ cst, unsigned* __restrict__ count) {
-  __shared__ float red[kDecThreads];
-  __shared__ float scale[512];
-  const int bh = blockIdx.x, t0 = threadIdx.x;
+  __shared__ float scale[512], cf[512], cs[kDecSplit];
+  const int bh = blockIdx.x, t0 = threadIdx.x, mf = m / kDecSplit;
   const float* gch = gc + (size_t)bh * T * m;
-  float mx = -INFINITY;
-  for (int i = t0; i < T * m; i += kDecThreads) mx = fmaxf(mx, gch[i]);
-  mx = block_max(mx, red);
+  for (int f = t0; f < m; f += kDecThreads) {
+    float c = -INFINITY;
+    for (int t = 0; t < T; ++t) c = fmaxf(c, gch[(size_t)t * m + f]);
+    cf[f] = c;
+  }
+  __syncthreads();
+  if (t0 < kDecSplit) {
+    float c = -INFINITY;
+    for (int f = t0 * mf; f < (t0 + 1) * mf; ++f) c = fmaxf(c, cf[f]);
+    cs[t0] = c;
+  }
+  __syncthreads();
   const int d1 = d + 1;
   const float* gsh = gs + (size_t)bh * T * d1 * m;
   float* Sh = S + (size_t)bh * m * d1;
   for (int t = 0; t < T; ++t) {
-    for (int f = t0; f < m; f += kDecThreads) scale[f] = fast_exp2(gch[(size_t)t * m + f] - mx);
+    for (int f = t0; f < m; f += kDecThreads) scale[f] = fast_exp2(gch[(size_t)t * m + f] - cs[f / mf]);
     __syncthreads();
     // element (f, col) of the state, f fastest (reads of the partial are contiguous)
     for (int e = t0; e < m * d1; e += kDecThreads) {
@@ -228,7 +240,7 @@ __global__ void __launch_bounds__(kDecThreads)
     __syncthreads();
   }
   if (t0 < kDecSplit) {
-    cst[bh * kDecSplit + t0] = mx;
+    cst[bh * kDecSplit + t0] = cs[t0];
     count[bh * kDecSplit + t0] = (unsigned)L;
   }
 }

@@ -161,11 +161,13 @@ favor_status favor_draw_features(int32_t heads_w, int32_t num_features, int32_t 
  *
  * State (device memory, caller-owned, favor_decode_state_bytes(p) bytes, 256-byte
  * aligned): float32 S[batch*heads_kv][m][d+1], float32 c[batch*heads_kv][8] and uint32
- * n[batch*heads_kv][8] (eight equal copies, one per slice of S updated in parallel), with
- *   S = sum_{j so far} 2^(e_j - c) [v_j, 1],  e_j,f = log2(e) (w_f . k_j - |k_j|^2 / 2),
- * i.e. the summary in log2 units scaled by 2^-c, and n the number of positions added.  c
- * starts at the first key's largest exponent and only grows (S is rescaled when it does).
- * A zero-filled buffer is the empty state.
+ * n[batch*heads_kv][8], one c and n per slice s of m/8 features (rows s m/8 .. (s+1) m/8 - 1
+ * of S, updated in parallel), with, for feature f of slice s,
+ *   S_f = sum_{j so far} 2^(e_j,f - c_s) [v_j, 1],  e_j,f = log2(e) (w_f . k_j - |k_j|^2 / 2),
+ * i.e. the summary in log2 units scaled by 2^-c_s, and n_s the number of positions added
+ * (the same in every slice).  c_s starts at the first key's largest exponent over the
+ * slice's features and only grows (the slice is rescaled when it does).  A zero-filled
+ * buffer is the empty state.
  *
  * favor_attn_decode: q [batch][heads_q][d], k and v [batch][heads_kv][d] (the new
  * position), W as for favor_attn_fwd, out [batch][heads_q][d] (device pointers; q, k, v,
@@ -178,7 +180,8 @@ size_t favor_decode_state_bytes(const favor_problem* p);
 
 /* Prompt prefill for decoding: writes the state (layout above) that holds the prompt's L =
  * p->seq_len positions, i.e. the state favor_attn_decode would reach after decoding them
- * one by one (up to rounding), with c the largest key exponent of the prompt and n = L.
+ * one by one (up to rounding), with c_s the largest key exponent of the prompt over the
+ * features of slice s and n = L.
  * p->mode must be FAVOR_CAUSAL (the state belongs to a causal sequence); the state buffer
  * has favor_decode_state_bytes of the same problem with seq_len 1 and is overwritten
  * whole.  K, V [batch][heads_kv][L][d] and W as for favor_attn_fwd.  The workspace

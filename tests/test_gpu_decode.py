@@ -80,8 +80,15 @@ def test_decode_first_step_returns_v():
     assert O.rowwise_rel_err(got, want) <= 2 ** -8
 
 
+def _slice_scale(cs, m):
+    """Per-feature factor 2^c_s / sqrt(m) of a state row (c_s: the stabiliser of slice s of
+    m / 8 features)."""
+    return np.repeat(2.0 ** cs, m // 8) / np.sqrt(m)
+
+
 def test_decode_state_is_the_summary():
-    """The state after L steps, times 2^c / sqrt(m), is phi(K)^T [V, 1] of the L positions."""
+    """The state after L steps, feature f times 2^c_s(f) / sqrt(m), is phi(K)^T [V, 1] of the
+    L positions."""
     w = CASES[4]  # float32
     Q, K, V, W = I.make_inputs(w, seed=1)
     _, state = _decode_all(w, Q, K, V, W)
@@ -90,20 +97,21 @@ def test_decode_state_is_the_summary():
     S = st[:BH * m * (d + 1)].reshape(BH, m, d + 1)
     off = BH * m * (d + 1)
     cs = st[off:off + 8 * BH].reshape(BH, 8)
-    assert (cs == cs[:, :1]).all()  # one copy per summary slice, all advanced alike
-    c = cs[:, 0]
     n = state.cpu()[off + 8 * BH:off + 16 * BH].view(torch.int32).numpy()
     assert (n == w.seq_len).all()
     for bh in range(BH):
         b, h = divmod(bh, w.heads_kv)
         Wh = W[0 if w.heads_w == 1 else h]
         Sv, S1 = O.kv_summary(O.feature_map(K[b, h], Wh), V[b, h])
-        scale = 2.0 ** c[bh] / np.sqrt(m)
-        got = np.concatenate([S[bh, :, :d], S[bh, :, d:]], axis=1) * scale
+        got = S[bh] * _slice_scale(cs[bh], m)[:, None]
         want = np.concatenate([Sv, S1[:, None]], axis=1)
         rel = np.abs(got - want).max() / np.abs(want).max()
-        _say(f"  state bh={bh}: rel err {rel:.2e}, c={c[bh]:.3f}")
+        _say(f"  state bh={bh}: rel err {rel:.2e}, c={cs[bh]}")
         assert rel <= 1e-5
+        # each slice's constant is the largest key exponent of its features (log2 units)
+        E = np.log2(np.e) * (K[b, h].astype(np.float64) @ Wh.astype(np.float64).T
+                             - 0.5 * np.sum(K[b, h].astype(np.float64) ** 2, axis=1)[:, None])
+        assert np.allclose(cs[bh], E.reshape(w.seq_len, 8, m // 8).max(axis=(0, 2)), atol=1e-3)
 
 
 def test_decode_deterministic():
@@ -172,14 +180,14 @@ def test_prefill_state_is_the_summary(w):
     state = api.decode_prefill(_dev(K, dt), _dev(V, dt), _dev(W, torch.float32), w.heads_q)
     torch.cuda.synchronize()
     S, cs, n = _state_parts(state, w)
-    assert (cs == cs[:, :1]).all() and (n == w.seq_len).all()
+    assert (n == w.seq_len).all()
     d, m = w.head_dim, w.num_features
     worst = 0.0
     for bh in range(w.batch * w.heads_kv):
         b, h = divmod(bh, w.heads_kv)
         Wh = W[0 if w.heads_w == 1 else h]
         Sv, S1 = O.kv_summary(O.feature_map(K[b, h], Wh), V[b, h])
-        got = S[bh] * 2.0 ** cs[bh, 0] / np.sqrt(m)
+        got = S[bh] * _slice_scale(cs[bh], m)[:, None]
         want = np.concatenate([Sv, S1[:, None]], axis=1)
         worst = max(worst, np.abs(got - want).max() / np.abs(want).max())
     _say(f"  state rel err {worst:.2e}")
