@@ -642,7 +642,9 @@ def approx_study(args, w):
     error).  Inputs: the workload's Q, K, V (Q and K times --qk-scale, which sets the kernel's
     temperature and so the features' variance); 256 sampled query rows; exact softmax on those
     rows in float32 on the GPU.  Metric per setting: RMS over the sampled rows' entries of
-    (FAVOR+ - softmax), mean and standard deviation over the draws.  One JSON line."""
+    (FAVOR+ - softmax), mean and standard deviation over the draws; and the relative mean
+    squared error of the kernel estimate phi(q) . phi(k) against exp(q . k) on 256 queries x
+    1024 keys of the first head (favor_features, stabilisers added back).  One JSON line."""
     import numpy as np
     import torch
 
@@ -664,19 +666,30 @@ def approx_study(args, w):
         exact.append(torch.softmax(s, dim=0) @ v[b, h // G, :n].float())
     exact = torch.stack(exact)
     bi, hi, ii = (torch.as_tensor(rows[:, j], device=dev) for j in range(3))
+    qs, ks = q[:1, :1, :256].contiguous(), k[:1, :1, :1024].contiguous()
+    kexact = torch.exp(qs[0, 0].double() @ ks[0, 0].double().T)
+
+    def kernel_rel_mse(Wd):
+        pq, cq = api.features(qs, Wd[:1].contiguous(), 0, 1, 1)
+        pk, ck = api.features(ks, Wd[:1].contiguous(), 1, 1, 1)
+        est = (pq.double() @ pk.double().T) * torch.exp(cq.double()[:, None] + ck.double()[0])
+        return float(torch.mean(((est - kexact) / kexact) ** 2))
+
     table = []
     for m in (64, 128, 256, 512):
         entry = {"m": m}
         for kind, orth in (("orf", True), ("iid", False)):
-            errs = []
+            errs, kmse = [], []
             for sd in range(args.seeds):
                 Wd = api.draw_features(w.heads_w, m, w.head_dim, 1000 * m + sd, orth)
                 y = api.attn_fwd(q, k, v, Wd, causal=w.causal)
                 got = y[bi, hi, ii].float()
                 errs.append(float(torch.sqrt(torch.mean((got - exact) ** 2))))
+                kmse.append(kernel_rel_mse(Wd))
                 del y
             entry[f"{kind}_rms"] = round(float(np.mean(errs)), 6)
             entry[f"{kind}_std"] = round(float(np.std(errs)), 6)
+            entry[f"{kind}_kernel_rel_mse"] = round(float(np.mean(kmse)), 6)
         entry["orf_over_iid"] = round(entry["orf_rms"] / entry["iid_rms"], 4)
         log(f"m={m}: {entry}")
         table.append(entry)
