@@ -1592,8 +1592,9 @@ favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const
     if constexpr (one_tile)
       hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, true>), dim3(s.T, s.B * s.Hq), dim3(kWave * (s.m / 32)), 0,
                          st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
-  } else if ((std::is_same<T, bf16>::value || D == 64) && s.m <= 256) {
-    // one 32-feature tile per wave without the register prefetch: no spills, two waves per SIMD
+  } else if (s.m <= 256) {
+    // one 32-feature tile per wave without the register prefetch: two waves per SIMD (a few
+    // spilled registers for float32 d = 128, still faster than two tiles per wave)
     hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false>), dim3(s.T, s.B * s.Hq), dim3(kWave * (s.m / 32)), 0,
                        st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
   } else if (nw <= 4)
