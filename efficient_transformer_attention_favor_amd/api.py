@@ -224,3 +224,25 @@ def draw_features(heads_w, num_features, head_dim, seed, orthogonal=True, device
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_draw_features")
     return W
+
+
+class _FavorAttention(torch.autograd.Function):
+    """favor_attn_fwd forward, favor_attn_bwd backward (W is a fixed input: no gradient)."""
+
+    @staticmethod
+    def forward(ctx, Q, K, V, W, causal):
+        ctx.causal = causal
+        ctx.save_for_backward(Q, K, V, W)
+        return attn_fwd(Q, K, V, W, causal=causal)
+
+    @staticmethod
+    def backward(ctx, dout):
+        Q, K, V, W = ctx.saved_tensors
+        dQ, dK, dV = attn_bwd(Q, K, V, W, dout.contiguous(), causal=ctx.causal)
+        return dQ, dK, dV, None, None
+
+
+def favor_attention(Q, K, V, W, causal=False):
+    """FAVOR+ attention as a differentiable op: out = attn_fwd(Q, K, V, W, causal), with the
+    gradients of Q, K and V from favor_attn_bwd (W gets none)."""
+    return _FavorAttention.apply(Q, K, V, W, causal)

@@ -160,3 +160,20 @@ def test_backward_full_size_one_head(name):
         err = _tensor_rel_err(g, r)
         _say(f"  {name_}: rel err {err:.3e}")
         assert err <= TOL[w.dtype], name_
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_autograd_function(causal):
+    """api.favor_attention through torch.autograd: .backward() of sum(dout * out) yields the
+    oracle's gradients."""
+    w = (CAUSAL_CASES if causal else CASES)[0]
+    Q, K, V, W = I.make_inputs(w, seed=9)
+    dO = _upstream(w, 9)
+    q, k, v = (_dev(x, torch.bfloat16).requires_grad_(True) for x in (Q, K, V))
+    out = api.favor_attention(q, k, v, _dev(W, torch.float32), causal=causal)
+    (out.float() * _dev(dO, torch.float32)).sum().backward()
+    ref = O.favor_grads(Q, K, V, W, dO, causal=causal)
+    for name, t, r in zip(("dQ", "dK", "dV"), (q, k, v), ref):
+        err = _tensor_rel_err(t.grad.float().cpu().numpy(), r)
+        _say(f"  autograd {name}: rel err {err:.3e}")
+        assert err <= TOL[w.dtype], name
