@@ -1174,11 +1174,15 @@ template <class T> struct CausalLd;
 template <> struct CausalLd<bf16> { static constexpr int PK = 48; };  // phi_K rows: 32 keys + pad
 template <> struct CausalLd<float> { static constexpr int PK = 33; };
 
-template <class T, int D, int NTC, int NWMAX, bool PF>
+// PART (wide heads, d = 128 with m > 256, whose two feature tiles per wave would spill):
+// the features run as two launches over feature ranges starting at fbase.  PART = 1 writes
+// each row's partial (numerators, denominator, row maximum) to part [rows][D+4]; PART = 2
+// merges its own with that partial (max-rescaled sum) and writes out.  PART = 0: one launch.
+template <class T, int D, int NTC, int NWMAX, bool PF, int PART = 0>
 __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ W,
     const float* __restrict__ prefix, const float* __restrict__ cstar_in, T* __restrict__ out, int L, int Hq,
-    int Hkv, int Hw, int m, int R, int T_ranges) {
+    int Hkv, int Hw, int m, int R, int T_ranges, int fbase = 0, float* __restrict__ part = nullptr) {
   using P = Prec<T>;
   using frag = typename P::frag;
   using wfrag = typename P::wfrag;
@@ -1209,7 +1213,7 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
   const int b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv), bh = b * Hkv + hkv;
   const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
-  const int f0 = wave * FW;
+  const int f0 = fbase + wave * FW;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
   const T* Qh = Q + (size_t)bhq * L * D;
   T* Oh = out + (size_t)bhq * L * D;
@@ -1476,6 +1480,24 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[i] += sc * v[i];
         }
+        if constexpr (PART != 0) {
+          float* prow = part + ((size_t)bhq * L + pos) * (D + 4);  // 16-byte aligned rows
+          if constexpr (PART == 1) {
+            *reinterpret_cast<f32x4*>(prow + c0) = acc;
+            if (c0 == 0) {
+              prow[D] = den;
+              prow[D + 1] = M;
+            }
+            continue;
+          } else {
+            const float den1 = prow[D], M1 = prow[D + 1];
+            const f32x4 acc1 = *reinterpret_cast<const f32x4*>(prow + c0);
+            const float Mn = fmaxf(M, M1), s0 = fast_exp2(M - Mn), s1 = fast_exp2(M1 - Mn);
+            den = den * s0 + den1 * s1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = acc[i] * s0 + acc1[i] * s1;
+          }
+        }
         const float inv = __builtin_amdgcn_rcpf(den);
         T* orow = Oh + (size_t)pos * D + c0;
         if constexpr (sizeof(T) == 2) {
@@ -1592,6 +1614,15 @@ favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const
     if constexpr (one_tile)
       hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, true>), dim3(s.T, s.B * s.Hq), dim3(kWave * (s.m / 32)), 0,
                          st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
+  } else if (D == 128 && s.m > 256) {
+    // two launches of one-tile waves over features [0, 256) and [256, m), merged per row
+    float* part = reinterpret_cast<float*>(ws + s.off_part);
+    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false, 1>), dim3(s.T, s.B * s.Hq), dim3(kWave * 8), 0, st, Q,
+                       K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, 0, part);
+    if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false, 2>), dim3(s.T, s.B * s.Hq),
+                       dim3(kWave * ((s.m - 256) / 32)), 0, st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv,
+                       s.Hw, s.m, s.R, s.T, 256, part);
   } else if (s.m <= 256) {
     // one 32-feature tile per wave without the register prefetch: two waves per SIMD (a few
     // spilled registers for float32 d = 128, still faster than two tiles per wave)

@@ -95,6 +95,9 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
   if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * (size_t)(q.d + 1) * q.m * q.BH * q.T);
   q.off_cstar = off;
   if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * q.BH);
+  q.off_part = off;
+  if (q.mode == FAVOR_CAUSAL && q.d == 128 && q.m > 256)
+    off = align256(off + sizeof(float) * (size_t)q.B * q.Hq * q.L * (q.d + 4));
   q.img = q.mode == FAVOR_BIDIRECTIONAL && q.dtype == FAVOR_BF16 && q.T == 1 && q.m <= kImgMP;
   q.off_img_w = q.off_img_s = q.off_img_cb = off;
   if (q.img) {

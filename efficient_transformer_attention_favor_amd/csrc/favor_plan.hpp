@@ -40,6 +40,7 @@ struct Plan {
   size_t off_gc;       // [BH][T][m] their per-feature stabilisers (log2 units)
   size_t off_p;        // [BH][T][d+1][m] exclusive prefixes of the segment summaries (causal)
   size_t off_cstar;    // [BH] global stabiliser per kv head (causal)
+  size_t off_part;     // [B Hq L][d+4] per-row partials of two feature ranges (causal, d = 128, m > 256)
   bool img;            // bf16 bidirectional, one range per head, m <= kImgMP: LDS images
   size_t off_img_w;    // [Hw] fp16 W images
   size_t off_img_s;    // [BH] bf16 S'^T images

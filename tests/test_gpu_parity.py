@@ -72,6 +72,19 @@ SMALL_CAUSAL = [
     _small("c1_bidir_f32", causal=True, seq_len=257),
     _small("c1_bidir_f32", causal=True, batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=100,
            head_dim=128, num_features=256),
+    # d = 128 with m > 256: two launches over feature ranges [0, 256) and [256, m), the
+    # second with (m - 256) / 32 waves, merged per row
+    _small("c3_causal_bf16", batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=301, head_dim=128,
+           num_features=320),
+    _small("c3_causal_bf16", batch=2, heads_q=2, heads_kv=2, heads_w=2, seq_len=95, head_dim=128,
+           num_features=384),
+    _small("c3_causal_bf16", batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=160, head_dim=128,
+           num_features=448),
+    _small("c5_causal_long_bf16", batch=1, heads_q=4, heads_kv=1, heads_w=1, seq_len=513, head_dim=128),
+    _small("c1_bidir_f32", causal=True, batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=130,
+           head_dim=128, num_features=384),
+    _small("c1_bidir_f32", causal=True, batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=67,
+           head_dim=128, num_features=512),
 ]
 SMALL = SMALL + SMALL_CAUSAL
 
