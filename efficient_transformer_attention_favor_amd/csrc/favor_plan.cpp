@@ -56,11 +56,17 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
   int T, unit;
   if (q.mode == FAVOR_CAUSAL) {
     // Segment count by a cost model in units of one 32-position block step: the chunk
-    // kernel runs one workgroup per CU (about twice the time per step of the key side),
+    // kernel runs one workgroup per CU (about twice the time per step of the key side;
+    // four times where d = 128 with m > 256 runs it as two launches over feature ranges),
     // the key side one wave per segment and 64-feature slice, one wave per SIMD, segments
-    // in groups of kSegGroup per workgroup.  Ties go to fewer segments.
+    // in groups of kSegGroup per workgroup.  The segment summaries cross HBM about four
+    // times (written by the key side, read and rewritten as prefixes by the scan, read by
+    // the chunk kernel); kSumUnitBytes of that traffic count as one unit.  Ties go to fewer
+    // segments.
     unit = q.chunk;
     const int max_t = ceil_div(q.L, unit);
+    const long long chunk_w = (q.d == 128 && q.m > 256) ? 4 : 2;
+    const long long sum_bytes = 4LL * sizeof(float) * (q.d + 1) * q.m * q.BH;  // per segment
     long long best = -1;
     T = 1;
     for (int t = 1; t <= max_t; ++t) {
@@ -70,7 +76,7 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
       const long long chunk_rounds = ceil_div((long long)q.B * q.Hq * t, kCUs);
       const long long key_waves = (long long)q.BH * ceil_div(t, kSegGroup) * kSegGroup * nfs;
       const long long key_rounds = ceil_div(key_waves, 4LL * kCUs);
-      const long long cost = (2 * chunk_rounds + key_rounds) * steps;
+      const long long cost = (chunk_w * chunk_rounds + key_rounds) * steps + sum_bytes * t / kSumUnitBytes;
       if (best < 0 || cost < best) {
         best = cost;
         T = t;

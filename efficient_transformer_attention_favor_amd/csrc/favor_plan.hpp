@@ -14,6 +14,7 @@ constexpr int kFeatPerWave = 64;   // features owned by one wave in the key-side
 constexpr int kKeyTarget = 256;     // key-side workgroups (4 waves each) a pass aims for
 constexpr int kCUs = 256;           // compute units of the MI355X (launch-geometry model only)
 constexpr int kSegGroup = 4;        // causal segments per key-side workgroup (d = 64; one per wave)
+constexpr long long kSumUnitBytes = 12LL << 20;  // summary traffic worth one block step (causal cost model)
 constexpr int kReadoutTarget = 256; // readout workgroups a pass aims for
 // Ready-to-copy LDS images for the bf16 bidirectional readout (one position range per kv
 // head): fp16 W rows of d+8, bf16 S'^T rows of kImgMP+8 (d+2 rows: values, ones, zeros),
