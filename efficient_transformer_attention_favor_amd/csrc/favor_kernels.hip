@@ -1268,18 +1268,25 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
   constexpr int MINT = NTC == 1 ? 128 : 64;  // fewest threads a block has (m >= 64)
   constexpr int PER = PF ? (NCH + MINT - 1) / MINT : 1;
   f32x4 pq[PER], pkk[PER], pv[PER];
+  // bf16: range-checked buffer loads (a head is under 2^31 elements, so its byte offsets
+  // fit 32 bits): a chunk of a row past L gets the head's size as offset and reads as zero,
+  // with no branch and no zero fill; a prefetch slot that no thread of the block uses is
+  // skipped.
+  const unsigned head_bytes = (unsigned)L * (unsigned)D * (unsigned)sizeof(T);
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Qh, (short)0, (int)head_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, (int)head_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, (int)head_bytes, kBufWord3);
   auto prefetch = [&](int q0) {
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
+      if (i * (int)blockDim.x >= NCH) break;  // uniform: no thread has a chunk in this slot
       const int c = threadIdx.x + i * blockDim.x;
       const int row = c / CPR, c0 = (c % CPR) * EPC;
-      pq[i] = pkk[i] = pv[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (c < NCH && q0 + row < L) {
-        const size_t off = (size_t)(q0 + row) * D + c0;
-        pq[i] = *reinterpret_cast<const f32x4*>(Qh + off);
-        pkk[i] = *reinterpret_cast<const f32x4*>(Kh + off);
-        pv[i] = *reinterpret_cast<const f32x4*>(Vh + off);
-      }
+      const unsigned off =
+          c < NCH && q0 + row < L ? ((unsigned)(q0 + row) * D + c0) * (unsigned)sizeof(T) : head_bytes;
+      pq[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)off, 0, 0));
+      pkk[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
+      pv[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
     }
   };
   auto put = [&](WE* dst, int ld, const f32x4& v, int row, int c0) {
@@ -1330,14 +1337,19 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
       for (int c = threadIdx.x; c < NCH; c += blockDim.x) {
         const int row = c / CPR, c0 = (c % CPR) * EPC;
         f32x4 q = {0.f, 0.f, 0.f, 0.f}, kk = {0.f, 0.f, 0.f, 0.f};
-        if (p0 + row < L) {
+        if constexpr (sizeof(T) == 2) {  // the range-checked loads of the prefetch
+          const unsigned off = p0 + row < L ? ((unsigned)(p0 + row) * D + c0) * (unsigned)sizeof(T) : head_bytes;
+          q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)off, 0, 0));
+          kk = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
+          put_v(__builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0)), row, c0);
+        } else if (p0 + row < L) {
           q = *reinterpret_cast<const f32x4*>(Qh + (size_t)(p0 + row) * D + c0);
           kk = *reinterpret_cast<const f32x4*>(Kh + (size_t)(p0 + row) * D + c0);
         }
         put(Ql, LDK, q, row, c0);
         put(Kl, LDK, kk, row, c0);
       }
-      stage_rows<T, D, true>(Vl, LDV, Vh, p0, L);
+      if constexpr (sizeof(T) != 2) stage_rows<T, D, true>(Vl, LDV, Vh, p0, L);
     }
     __syncthreads();
 
