@@ -101,6 +101,19 @@ def test_small_full_parity(w):
     assert err < TOL[w.dtype]
 
 
+@pytest.mark.parametrize("chunk", [64, 256])
+def test_causal_split_features_chunk_sizes(chunk):
+    """d = 128 with m > 256 (two launches over feature ranges) with segments of other lengths
+    and a ragged tail."""
+    w = _small("c3_causal_bf16", batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=777, head_dim=128,
+               num_features=384)
+    _say(f"case {w} chunk={chunk}")
+    Q, K, V, W = I.make_inputs(w, seed=4)
+    y = _run(w, Q, K, V, W, chunk=chunk).float().cpu().numpy()
+    ref = O.favor_attention(Q, K, V, W, causal=True)
+    assert O.rowwise_rel_err(y, ref) < TOL[w.dtype]
+
+
 @pytest.mark.parametrize("chunk", [0, 32, 64, 128, 256])
 def test_causal_chunk_sizes(chunk):
     w = _small("c3_causal_bf16", batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1111)
