@@ -83,6 +83,22 @@ def test_workspace_grows_with_problem():
     assert 0 < small <= big and causal > 0
 
 
+@pytest.mark.parametrize("m", [320, 512])
+def test_causal_wide_head_workspace_holds_row_partials(m):
+    """Causal d = 128 with m > 256 runs its chunk kernel as two launches over feature ranges,
+    the first writing a float32 partial of d + 4 values per output row: the workspace must
+    hold those B Hq L rows besides the segment summaries and their prefixes."""
+    # 16 query heads on one kv head and segments of >= 256 positions (at most 4): the
+    # summaries are small next to the row partials, so a layout without them falls short
+    B, Hq, Hkv, L, d = 2, 16, 1, 1000, 128
+    p = _p(batch=B, heads_q=Hq, heads_kv=Hkv, heads_w=Hkv, seq_len=L, head_dim=d, num_features=m,
+           mode=_lib.FAVOR_CAUSAL, chunk=256)
+    partials = 4 * B * Hq * L * (d + 4)
+    one_segment = 4 * (d + 1) * m * B * Hkv  # summaries (and again prefixes) of one segment
+    assert 2 * 4 * one_segment + 64 * 1024 < partials
+    assert _lib.workspace_bytes(p) >= partials + 2 * one_segment
+
+
 def test_status_strings():
     for s in range(5):
         assert isinstance(_lib.status_string(s), str) and _lib.status_string(s)
