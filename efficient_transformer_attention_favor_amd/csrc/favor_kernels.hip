@@ -97,7 +97,7 @@ __device__ __forceinline__ void stage_rows(T* dst, int ld, const T* src, int p0,
 // copy of K and V): block b runs on XCD b % 8.
 // ======================================================================================
 template <class T, int D> struct KvCfg;
-template <> struct KvCfg<bf16, 64> { static constexpr int KW = 4, NTW = 2; };
+template <> struct KvCfg<bf16, 64> { static constexpr int KW = 8, NTW = 2; };
 template <> struct KvCfg<bf16, 128> { static constexpr int KW = 4, NTW = 1; };
 template <> struct KvCfg<float, 64> { static constexpr int KW = 4, NTW = 1; };
 template <> struct KvCfg<float, 128> { static constexpr int KW = 4, NTW = 1; };
@@ -126,6 +126,12 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   __shared__ __attribute__((aligned(16))) T Vl[KW][32 * LDV];
   __shared__ __attribute__((aligned(16))) float Red[(PG / 2) * FG][ACC];
   __shared__ __attribute__((aligned(16))) float Cs[KW][32 * NTW];
+  // bf16, d = 64: the slice's fp16 W rows live in LDS (shared by the waves) and blocks are
+  // loaded at their start, not one block ahead, which keeps a wave within 256 registers
+  // (two waves per SIMD hide each other's latency)
+  constexpr bool WLDS = sizeof(T) == 2 && D == 64;
+  constexpr int LDWL = D + 8;
+  __shared__ __attribute__((aligned(16))) typename P::welem Wl[WLDS ? 64 * LDWL : 1];
 
   const int NFS = m / 64;
   const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3;
@@ -136,18 +142,43 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   const int TG = SEG ? (T_ranges + PG - 1) / PG : T_ranges;  // units per kv head
   const int bh = unit / TG, hkv = bh % Hkv;
   const int t = SEG ? (unit % TG) * PG + pgi : unit % TG;
-  if (SEG && t >= T_ranges) return;
   const int f0 = slice * 64 + fgi * 32 * NTW;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
   const T* Kh = K + (size_t)bh * L * D;
   const T* Vh = V + (size_t)bh * L * D;
   T* vl = Vl[wave];
 
-  wfrag wf[NTW][NKC];
+  wfrag wf[WLDS ? 1 : NTW][WLDS ? 1 : NKC];
+  if constexpr (WLDS) {
+    // rows slice*64 .. +63 scaled by log2 e, 8 elements per thread and step
+    for (int c = threadIdx.x; c < 64 * D / 8; c += blockDim.x) {
+      const int r = c / (D / 8), c0 = (c % (D / 8)) * 8;
+      const float* src = Wh + (size_t)(slice * 64 + r) * D + c0;
+      const f32x4 a = *reinterpret_cast<const f32x4*>(src), b = *reinterpret_cast<const f32x4*>(src + 4);
+      wfrag v;
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt)
+      for (int j = 0; j < 4; ++j) {
+        v[j] = (typename P::welem)(a[j] * kLog2e);
+        v[j + 4] = (typename P::welem)(b[j] * kLog2e);
+      }
+      *reinterpret_cast<wfrag*>(&Wl[r * LDWL + c0]) = v;
+    }
+    __syncthreads();
+  }
+  if (SEG && t >= T_ranges) return;  // after the workgroup-wide W staging
+  if constexpr (!WLDS) {
 #pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) load_w_frag(Wh + (size_t)(f0 + 32 * nt + col) * D, kc, g, wf[nt][kc]);
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) load_w_frag(Wh + (size_t)(f0 + 32 * nt + col) * D, kc, g, wf[nt][kc]);
+  }
+  // the W operand of feature tile nt, contraction slab kc
+  auto wop = [&](int nt, int kc) -> wfrag {
+    if constexpr (WLDS)
+      return *reinterpret_cast<const wfrag*>(&Wl[(f0 - slice * 64 + 32 * nt + col) * LDWL + 16 * kc + 8 * g]);
+    else
+      return wf[nt][kc];
+  };
 
   float cst[NTW];  // stabiliser of this lane's feature (log2 units)
   wfrag biasB[NTW];
@@ -206,6 +237,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   // 2 = fallback pass (running maximum, moved lazily, accumulators rescaled).
   auto block = [&](int p0, auto mode_tag) {
     constexpr int MODE = decltype(mode_tag)::value;
+    if constexpr (WLDS) fetch(p0);
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = l + 64 * i, row = c / CPR, c0 = (c % CPR) * EPC;
@@ -221,14 +253,14 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
     wfrag kf[NKC];
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) kf[kc] = to_wfrag(kn[kc]);
-    fetch(min(p0 + 32, we - 1));
+    if constexpr (!WLDS) fetch(min(p0 + 32, we - 1));
     // the W contraction first: the norm and the bias operand are built while it runs
     f32x16 c1[NTW];
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
       c1[nt] = zero16();
 #pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) c1[nt] = mma(kf[kc], wf[nt][kc], c1[nt]);
+      for (int kc = 0; kc < NKC; ++kc) c1[nt] = mma(kf[kc], wop(nt, kc), c1[nt]);
     }
     float nrm = sumsq(kf);
     nrm += partner32(nrm);
@@ -313,7 +345,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   // with the running maximum.
   reset();
   if (wb < we) {
-    fetch(wb);
+    if constexpr (!WLDS) fetch(wb);
     block(wb, std::integral_constant<int, 0>{});
     for (int p0 = wb + 32; p0 < we; p0 += 32) block(p0, std::integral_constant<int, 1>{});
   }
@@ -326,7 +358,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
       for (int r = 0; r < 16; ++r) chk += S[nt][dt][r];
   if (wave_any(!(chk - chk == 0.f))) {
     reset();
-    fetch(wb);
+    if constexpr (!WLDS) fetch(wb);
     for (int p0 = wb; p0 < we; p0 += 32) block(p0, std::integral_constant<int, 2>{});
   }
 
@@ -471,7 +503,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
         if (bh < Hkv && (Hw != 1 || bh == 0)) {
           f16* iw = reinterpret_cast<f16*>(img_w + (size_t)(Hw == 1 ? 0 : hkv) * img_w_bytes(D, m));
 #pragma unroll
-          for (int kc = 0; kc < NKC; ++kc) *reinterpret_cast<f16x8*>(iw + (size_t)f * LDW + 16 * kc + 8 * g) = wf[nt][kc];
+          for (int kc = 0; kc < NKC; ++kc) *reinterpret_cast<f16x8*>(iw + (size_t)f * LDW + 16 * kc + 8 * g) = wop(nt, kc);
         }
       }
       return;

@@ -13,7 +13,7 @@ constexpr int kTile = 32;          // MFMA tile edge (32x32 accumulators)
 constexpr int kFeatPerWave = 64;   // features owned by one wave in the key-side kernels
 constexpr int kKeyTarget = 256;     // key-side workgroups (4 waves each) a pass aims for
 constexpr int kCUs = 256;           // compute units of the MI355X (launch-geometry model only)
-constexpr int kSegGroup = 4;        // causal segments per key-side workgroup (d = 64; one per wave)
+constexpr int kSegGroup = 4;        // causal segments per key-side workgroup in the cost model
 constexpr long long kSumUnitBytes = 12LL << 20;  // summary traffic worth one block step (causal cost model)
 constexpr int kReadoutTarget = 256; // readout workgroups a pass aims for
 // Ready-to-copy LDS images for the bf16 bidirectional readout (one position range per kv
