@@ -1660,24 +1660,27 @@ favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const
                          st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
   } else if (D == 128 && s.m > 256) {
     // two launches of one-tile waves over features [0, 256) and [256, m), merged per row
-    float* part = reinterpret_cast<float*>(ws + s.off_part);
-    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false, 1>), dim3(s.T, s.B * s.Hq), dim3(kWave * 8), 0, st, Q,
-                       K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, 0, part);
-    if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
-    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false, 2>), dim3(s.T, s.B * s.Hq),
-                       dim3(kWave * ((s.m - 256) / 32)), 0, st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv,
-                       s.Hw, s.m, s.R, s.T, 256, part);
+    if constexpr (D == 128) {
+      float* part = reinterpret_cast<float*>(ws + s.off_part);
+      hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false, 1>), dim3(s.T, s.B * s.Hq), dim3(kWave * 8), 0, st,
+                         Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, 0, part);
+      if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+      hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false, 2>), dim3(s.T, s.B * s.Hq),
+                         dim3(kWave * ((s.m - 256) / 32)), 0, st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv,
+                         s.Hw, s.m, s.R, s.T, 256, part);
+    }
   } else if (s.m <= 256) {
     // one 32-feature tile per wave without the register prefetch: two waves per SIMD (a few
     // spilled registers for float32 d = 128, still faster than two tiles per wave)
     hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false>), dim3(s.T, s.B * s.Hq), dim3(kWave * (s.m / 32)), 0,
                        st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
-  } else if (nw <= 4)
-    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 2, 4, false>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
-                       prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
-  else
+  } else if constexpr (D == 64) {
+    // m > 256 (5 to 8 waves): two 32-feature tiles per wave
     hipLaunchKernelGGL((causal_chunk_kernel<T, D, 2, 8, false>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
                        prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
+  } else {
+    return FAVOR_ERR_UNSUPPORTED;  // not reached: d = 128 with m > 256 takes the split above
+  }
   if (hipGetLastError() != hipSuccess || !mk.mark(3, st)) return FAVOR_ERR_HIP;
   return FAVOR_OK;
 }
