@@ -87,7 +87,8 @@ __device__ __forceinline__ void stage_rows(T* dst, int ld, const T* src, int p0,
 // kv_summary: per (kv head bh, position range t, 64-feature slice) the partial summary
 //   S[f][c] = sum_{p in range} 2^(E_pf - c_f) [V, 1][p][c],   E_pf = log2e (w_f.k_p - |k_p|^2/2)
 // KW waves split the slice's features into NTW-tile groups and the range into position
-// groups; each wave streams 32-position blocks with its features' W in registers:
+// groups; each wave streams 32-position blocks with its features' W in registers (bf16
+// d = 64: the slice's W in LDS, shared by the workgroup's waves):
 // E = K_blk W^T (+ one bias MFMA carrying -|k|^2 log2e/2 - c_f), phi = 2^E,
 // S += phi^T [V, 1] (V transposed through wave-private LDS).  The wave partials of a
 // feature group are merged in LDS after rescaling to the largest c_f.  Output (float32):

@@ -58,8 +58,8 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
     // Segment count by a cost model in units of one 32-position block step: the chunk
     // kernel runs one workgroup per CU (about twice the time per step of the key side;
     // four times where d = 128 with m > 256 runs it as two launches over feature ranges),
-    // the key side one wave per segment and 64-feature slice, one wave per SIMD, segments
-    // in groups of kSegGroup per workgroup.  The segment summaries cross HBM about four
+    // the key side one wave per segment and 64-feature slice, taken as one wave per SIMD
+    // (bf16 d = 64 runs two), segments in groups of kSegGroup per workgroup.  The segment summaries cross HBM about four
     // times (written by the key side, read and rewritten as prefixes by the scan, read by
     // the chunk kernel); kSumUnitBytes of that traffic count as one unit.  Ties go to fewer
     // segments.

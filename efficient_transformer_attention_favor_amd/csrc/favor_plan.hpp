@@ -11,7 +11,7 @@ namespace favor {
 constexpr int kWave = 64;          // wavefront width on CDNA
 constexpr int kTile = 32;          // MFMA tile edge (32x32 accumulators)
 constexpr int kFeatPerWave = 64;   // features owned by one wave in the key-side kernels
-constexpr int kKeyTarget = 256;     // key-side workgroups (4 waves each) a pass aims for
+constexpr int kKeyTarget = 256;     // key-side workgroups a pass aims for (4 waves each, 8 for bf16 d = 64)
 constexpr int kCUs = 256;           // compute units of the MI355X (launch-geometry model only)
 constexpr int kSegGroup = 4;        // causal segments per key-side workgroup in the cost model
 constexpr long long kSumUnitBytes = 12LL << 20;  // summary traffic worth one block step (causal cost model)
