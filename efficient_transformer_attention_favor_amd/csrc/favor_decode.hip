@@ -82,36 +82,58 @@ template <class T, int D>
 __global__ void __launch_bounds__(kDecThreads)
     decode_update(const T* __restrict__ k, const T* __restrict__ v, const float* __restrict__ W, int Hkv, int Hw,
                   int m, float* __restrict__ S, float* __restrict__ cst, unsigned* __restrict__ count) {
-  __shared__ float kl[D], vl[D + 1], phi[512 / kDecSplit], red[kDecThreads];
+  static_assert(512 / kDecSplit <= 64, "a slice's features must fit one wave");
+  __shared__ float kl[D], vl[D + 1], phi[512 / kDecSplit], sc;
   const int bh = blockIdx.x / kDecSplit, part = blockIdx.x % kDecSplit, hkv = bh % Hkv;
-  const int mf = m / kDecSplit, fb = part * mf;  // this workgroup's features
+  const int mf = m / kDecSplit, fb = part * mf;  // this workgroup's features (at most 64)
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
   const int t = threadIdx.x;
+  // wave 0 owns the features, one per lane: its W row and the slice's stabiliser are
+  // loaded before the key arrives
+  const bool feat = t < mf;
+  f32x4 wr[D / 4];
+  if (feat) {
+#pragma unroll
+    for (int i = 0; i < D / 4; ++i) wr[i] = *reinterpret_cast<const f32x4*>(Wh + (size_t)(fb + t) * D + 4 * i);
+  }
+  const unsigned seen = count[bh * kDecSplit + part];
+  const float c_prev = cst[bh * kDecSplit + part];
   if (t < D) {
     kl[t] = to_f(k[(size_t)bh * D + t]);
     vl[t] = to_f(v[(size_t)bh * D + t]);
   }
   if (t == 0) vl[D] = 1.f;  // the ones column carries the normaliser
   __syncthreads();
-  float nrm = 0.f;
-  if (t < D) nrm = kl[t] * kl[t];
-  nrm = block_sum(nrm, red);
-
-  float mx = -INFINITY;
-  for (int f = t; f < mf; f += kDecThreads) {
-    const float e = kLog2e * (row_dot<D>(Wh + (size_t)(fb + f) * D, kl) - 0.5f * nrm);
-    phi[f] = e;
-    mx = fmaxf(mx, e);
+  if (t < 64) {  // wave 0: norm, exponents, maximum and stabiliser by shuffles
+    float nrm = 0.f;
+    for (int i = t; i < D; i += 64) nrm = fmaf(kl[i], kl[i], nrm);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) nrm += __shfl_xor(nrm, o);
+    float e = -INFINITY;
+    if (feat) {
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < D / 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = fmaf(wr[i][j], kl[4 * i + j], acc[j]);
+      e = kLog2e * (((acc[0] + acc[1]) + (acc[2] + acc[3])) - 0.5f * nrm);
+    }
+    float mx = e;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    // an empty state (no position yet) takes the new key's maximum as its constant; after
+    // that c only grows, so S never overflows and never has to be scaled up
+    const float c_old = seen ? c_prev : mx;
+    const float c_new = fmaxf(c_old, mx);
+    if (feat) phi[t] = fast_exp2(e - c_new);
+    if (t == 0) {
+      sc = fast_exp2(c_old - c_new);
+      cst[bh * kDecSplit + part] = c_new;
+      count[bh * kDecSplit + part] = seen + 1u;
+    }
   }
-  mx = block_max(mx, red);
-  // an empty state (no position yet) takes the new key's maximum as its constant; after
-  // that c only grows, so S never overflows and never has to be scaled up
-  const unsigned seen = count[bh * kDecSplit + part];
-  const float c_old = seen ? cst[bh * kDecSplit + part] : mx;
-  const float c_new = fmaxf(c_old, mx);
-  const float scale = fast_exp2(c_old - c_new);
-  for (int f = t; f < mf; f += kDecThreads) phi[f] = fast_exp2(phi[f] - c_new);
   __syncthreads();
+  const float scale = sc;
 
   // this workgroup's rows of S [m][D+1] (mf (D+1) floats, a multiple of 4): 4 consecutive
   // elements per thread and step, two steps' loads in flight
@@ -133,10 +155,6 @@ __global__ void __launch_bounds__(kDecThreads)
     upd(i + 4 * kDecThreads, b);
   }
   if (i < n) upd(i, *reinterpret_cast<const f32x4*>(Sh + i));
-  if (t == 0) {
-    cst[bh * kDecSplit + part] = c_new;
-    count[bh * kDecSplit + part] = seen + 1u;
-  }
 }
 
 template <class T, int D>
