@@ -208,6 +208,88 @@ __global__ void __launch_bounds__(kDecThreads)
   }
 }
 
+// d = 128: wave w takes features [w m/NW, (w+1) m/NW) for every value column (two per
+// lane), relative to its own maximum; the NW partials are merged by their maxima after one
+// barrier.  (For d = 64 the kernel above, which splits value columns over threads, is faster.)
+template <class T, int D>
+__global__ void __launch_bounds__(kDecThreads)
+    decode_readout_waves(const T* __restrict__ q, const float* __restrict__ W, const float* __restrict__ S,
+                         const float* __restrict__ cst, int Hq, int Hkv, int Hw, int m, T* __restrict__ out) {
+  constexpr int NW = kDecThreads / 64, CPL = D / 64;  // waves; value columns per lane
+  __shared__ float ql[D], p[512], part[NW][D + 2];
+  const int bhq = blockIdx.x, b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv);
+  const int bh = b * Hkv + hkv;
+  const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
+  const float* Sh = S + (size_t)bh * m * (D + 1);
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63;
+  if (t < D) ql[t] = to_f(q[(size_t)bhq * D + t]);
+  __syncthreads();
+
+  const int fpw = m / NW, f0 = w * fpw, mf = m / kDecSplit;  // fpw <= 128: two per lane
+  float e[2], Mw = -INFINITY;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int f = f0 + lane + 64 * h;
+    e[h] = -INFINITY;
+    if (lane + 64 * h < fpw) {
+      // the slice's stabiliser joins the query exponent
+      e[h] = kLog2e * row_dot<D>(Wh + (size_t)f * D, ql) + cst[bh * kDecSplit + f / mf];
+      Mw = fmaxf(Mw, e[h]);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) Mw = fmaxf(Mw, __shfl_xor(Mw, o));
+  float den = 0.f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    if (lane + 64 * h < fpw) {
+      const int f = f0 + lane + 64 * h;
+      const float pf = fast_exp2(e[h] - Mw);
+      p[f] = pf;
+      den = fmaf(pf, Sh[(size_t)f * (D + 1) + D], den);
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's p[] writes have landed
+  __builtin_amdgcn_wave_barrier();
+
+  // numerator columns lane + 64 c over the wave's features: rows of S read whole, 16 in flight
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int f = f0; f < f0 + fpw; f += 16) {  // fpw is a multiple of 16
+    float sv[16][CPL];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) sv[u][c] = Sh[(size_t)(f + u) * (D + 1) + lane + 64 * c];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int c = 0; c < CPL; ++c) acc[c] = fmaf(p[f + u], sv[u][c], acc[c]);
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) part[w][lane + 64 * c] = acc[c];
+  if (lane == 0) {
+    part[w][D] = den;
+    part[w][D + 1] = Mw;
+  }
+  __syncthreads();
+  if (t < D) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) M = fmaxf(M, part[v][D + 1]);
+    float num = 0.f, dsum = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      const float sc = fast_exp2(part[v][D + 1] - M);
+      num = fmaf(sc, part[v][t], num);
+      dsum = fmaf(sc, part[v][D], dsum);
+    }
+    out[(size_t)bhq * D + t] = (T)(num / dsum);
+  }
+}
+
 template <class T, int D>
 favor_status run_decode(const Plan& s, const void* q, const void* k, const void* v, const float* W, float* state,
                         void* out, hipStream_t st) {
@@ -217,8 +299,12 @@ favor_status run_decode(const Plan& s, const void* q, const void* k, const void*
   hipLaunchKernelGGL((decode_update<T, D>), dim3(s.BH * kDecSplit), dim3(kDecThreads), 0, st, static_cast<const T*>(k),
                      static_cast<const T*>(v), W, s.Hkv, s.Hw, s.m, S, cst, count);
   if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
-  hipLaunchKernelGGL((decode_readout<T, D>), dim3(s.B * s.Hq), dim3(kDecThreads), 0, st,
-                     static_cast<const T*>(q), W, S, cst, s.Hq, s.Hkv, s.Hw, s.m, static_cast<T*>(out));
+  if constexpr (D == 128)
+    hipLaunchKernelGGL((decode_readout_waves<T, D>), dim3(s.B * s.Hq), dim3(kDecThreads), 0, st,
+                       static_cast<const T*>(q), W, S, cst, s.Hq, s.Hkv, s.Hw, s.m, static_cast<T*>(out));
+  else
+    hipLaunchKernelGGL((decode_readout<T, D>), dim3(s.B * s.Hq), dim3(kDecThreads), 0, st,
+                       static_cast<const T*>(q), W, S, cst, s.Hq, s.Hkv, s.Hw, s.m, static_cast<T*>(out));
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
