@@ -308,44 +308,46 @@ favor_status run_decode(const Plan& s, const void* q, const void* k, const void*
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
-// One workgroup per (batch, kv head): the merged state of its T range partials.
+// One workgroup per (batch, kv head, slice of m/8 features): the merged state rows of its
+// T range partials.
 __global__ void __launch_bounds__(kDecThreads)
     prefill_state(const float* __restrict__ gs, const float* __restrict__ gc, int T, int d, int m, int L,
                   float* __restrict__ S, float* __restrict__ cst, unsigned* __restrict__ count) {
-  __shared__ float scale[512], cf[512], cs[kDecSplit];
-  const int bh = blockIdx.x, t0 = threadIdx.x, mf = m / kDecSplit;
+  // one workgroup per (batch, kv head, slice): the slice's mf <= 64 features, one per lane of
+  // the first wave for the maxima
+  __shared__ float scale[512 / kDecSplit], cs;
+  const int bh = blockIdx.x / kDecSplit, sl = blockIdx.x % kDecSplit, t0 = threadIdx.x;
+  const int mf = m / kDecSplit, fb = sl * mf;
   const float* gch = gc + (size_t)bh * T * m;
-  for (int f = t0; f < m; f += kDecThreads) {
+  if (t0 < 64) {
     float c = -INFINITY;
-    for (int t = 0; t < T; ++t) c = fmaxf(c, gch[(size_t)t * m + f]);
-    cf[f] = c;
+    if (t0 < mf)
+      for (int t = 0; t < T; ++t) c = fmaxf(c, gch[(size_t)t * m + fb + t0]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) c = fmaxf(c, __shfl_xor(c, o));
+    if (t0 == 0) cs = c;
   }
   __syncthreads();
-  if (t0 < kDecSplit) {
-    float c = -INFINITY;
-    for (int f = t0 * mf; f < (t0 + 1) * mf; ++f) c = fmaxf(c, cf[f]);
-    cs[t0] = c;
-  }
-  __syncthreads();
+  const float c_s = cs;
   const int d1 = d + 1;
   const float* gsh = gs + (size_t)bh * T * d1 * m;
   float* Sh = S + (size_t)bh * m * d1;
   for (int t = 0; t < T; ++t) {
-    for (int f = t0; f < m; f += kDecThreads) scale[f] = fast_exp2(gch[(size_t)t * m + f] - cs[f / mf]);
+    if (t0 < mf) scale[t0] = fast_exp2(gch[(size_t)t * m + fb + t0] - c_s);
     __syncthreads();
-    // element (f, col) of the state, f fastest (reads of the partial are contiguous)
-    for (int e = t0; e < m * d1; e += kDecThreads) {
-      const int col = e / m, f = e - col * m;
+    // element (f, col) of the slice's state rows, f fastest (reads of the partial are contiguous)
+    for (int e = t0; e < mf * d1; e += kDecThreads) {
+      const int col = e / mf, fl = e - col * mf, f = fb + fl;
       const int row = col == d ? d : 32 * (col >> 5) + vperm_inv(col & 31);
-      const float v = scale[f] * gsh[((size_t)t * d1 + row) * m + f];
+      const float v = scale[fl] * gsh[((size_t)t * d1 + row) * m + f];
       float* dst = Sh + (size_t)f * d1 + col;
       *dst = t == 0 ? v : *dst + v;
     }
     __syncthreads();
   }
-  if (t0 < kDecSplit) {
-    cst[bh * kDecSplit + t0] = cs[t0];
-    count[bh * kDecSplit + t0] = (unsigned)L;
+  if (t0 == 0) {
+    cst[bh * kDecSplit + sl] = c_s;
+    count[bh * kDecSplit + sl] = (unsigned)L;
   }
 }
 
@@ -398,8 +400,8 @@ extern "C" favor_status favor_decode_prefill(const favor_problem* p, const void*
   if (rc != FAVOR_OK) return rc;
   float* cst = state + (size_t)s.BH * s.m * (s.d + 1);
   unsigned* count = reinterpret_cast<unsigned*>(cst + (size_t)s.BH * favor::kDecSplit);
-  hipLaunchKernelGGL(favor::prefill_state, dim3(s.BH), dim3(favor::kDecThreads), 0, hs, gs, gc, s.T, s.d, s.m, s.L,
-                     state, cst, count);
+  hipLaunchKernelGGL(favor::prefill_state, dim3(s.BH * favor::kDecSplit), dim3(favor::kDecThreads), 0, hs, gs, gc,
+                     s.T, s.d, s.m, s.L, state, cst, count);
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
