@@ -1,15 +1,20 @@
 #!/usr/bin/env python3
 """Throughput of the FAVOR+ forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--also all|LIST]
 
 One step is one favor_attn_fwd call (every kernel of the path) over one batch of seeded
 synthetic input already resident in HBM.  W untimed warm-up steps, then exactly K timed
-steps between a synchronize on each side.  Prints one JSON line:
+steps between a synchronize on each side.  The headline workload is the largest one (the
+multi-query c4); the others, and the causal chunk sweep, follow under "also", each timed
+the same way.  Prints one JSON line:
   value          tokens/s = batch * heads_q * seq_len / step time
-  roofline       for the kernel with the longest average duration: algorithmic bytes or
-                 flops per launch over its average duration, from HIP events recorded by
-                 the library around each kernel on the stream it launches on
+  roofline       for the kernel with the longest duration: its algorithmic bytes or flops
+                 per launch over its duration.  The duration is the kernel's share of the
+                 plain-call step time, split in the ratio of per-kernel intervals that a
+                 second pass measures with HIP events recorded by the library between its
+                 kernels on its own stream (event_ms: the marked interval itself)
+  roofline_call  the whole call: its algorithmic bytes and flops against the step time
   cpu_baseline   the float64 CPU oracle timed on this host on a bounded sample of the same
                  workload (whole (batch, head) slices), scaled to tokens/s
 """
@@ -91,6 +96,23 @@ def algorithmic_work(w):
                 names[2]: (q_bytes + w_bytes + s_bytes, B * Hq * side)}
     return {names[0]: (k_bytes + w_bytes, B * Hkv * side), names[1]: (0, 0),
             names[2]: (q_bytes + k_bytes + w_bytes, B * Hq * side + B * Hkv * side)}
+
+
+def call_work(w):
+    """Algorithmic bytes and flops of one whole favor_attn_fwd call: Q, K, V read once, out
+    written once and W; the feature maps of Q and K (2 L d m per head) and the summary and
+    readout contractions (2 L m (d+1) per head)."""
+    e = 2 if w.dtype == "bf16" else 4
+    B, Hq, Hkv, Hw, L, d, m = (w.batch, w.heads_q, w.heads_kv, w.heads_w, w.seq_len, w.head_dim,
+                               w.num_features)
+    nbytes = e * L * d * (2 * B * Hq + 2 * B * Hkv) + 4 * Hw * m * d
+    flops = (B * Hq + B * Hkv) * (2 * L * d * m + 2 * L * m * (d + 1))
+    return nbytes, flops
+
+
+def kernel_names(w, p=None):
+    """Names of the kernel slots of one call (None for an empty slot)."""
+    return KERNELS[w.causal]
 
 
 # The sources the forward kernels (favor_attn_fwd) are built from.
@@ -226,7 +248,12 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2_bidir_bf16")
+    ap.add_argument("--workload", default="c4_mqa_bidir_bf16",
+                    help="the workload of the headline line (default: the largest, multi-query c4)")
+    ap.add_argument("--also", default="all",
+                    help="other workloads timed in the same run, reported under 'also': 'all' (every other "
+                         "workload; causal ones at the default chunk and 64, 128, 256), a comma-separated list, "
+                         "or '' for none")
     ap.add_argument("--chunk", type=int, default=0, help="causal chunk (0 = library default)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (at least)")
@@ -272,13 +299,66 @@ def main():
     if args.generalized:
         return generalized_main(args, w)
     Q, K, V, W = I.make_inputs(w, seed=0)
+    res = forward_record(w, Q, K, V, W, args.chunk, args.steps, args.warmup, graph=True,
+                         copy_probe_mb=args.copy_probe_mb)
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        res["cpu_baseline"] = cpu_baseline(w, Q, K, V, W, args.cpu_budget)
+    del Q, K, V, W
+    if args.also:
+        # the other benchmark workloads (and the causal chunk sweep) in the same run, each
+        # timed the same way on its own inputs; keys are workload names (with the chunk)
+        also = {}
+        for name, chunk in _also_list(args.also, w.name, args.chunk):
+            wa = I.workload(name)
+            log(f"also: {name} chunk {chunk}")
+            Qa, Ka, Va, Wa = I.make_inputs(wa, seed=0)
+            rec = forward_record(wa, Qa, Ka, Va, Wa, chunk, args.steps, args.warmup, graph=name.startswith("c1"))
+            del Qa, Ka, Va, Wa
+            keep = ("value", "ms_per_step", "dtype", "config", "roofline", "roofline_call", "kernels",
+                    "graph_ms_per_step")
+            also[f"{name}" + (f"/chunk{chunk}" if wa.causal else "")] = {k: rec[k] for k in keep if k in rec}
+        res["also"] = also
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(line + "\n")
+
+
+def _also_list(spec, main_name, main_chunk):
+    """(workload, chunk) pairs of --also: 'all' = every other workload, causal ones at the
+    library default and at chunks 64, 128, 256; else a comma-separated list of names."""
+    from efficient_transformer_attention_favor_amd import inputs as I
+
+    names = sorted(I.WORKLOADS) if spec == "all" else [n for n in spec.split(",") if n]
+    out = []
+    for n in names:
+        chunks = [0, 64, 128, 256] if I.workload(n).causal else [0]
+        for c in chunks:
+            if (n, c) != (main_name, main_chunk):
+                out.append((n, c))
+    return out
+
+
+def forward_record(w, Q, K, V, W, chunk, steps, warmup, graph=False, copy_probe_mb=0):
+    """Time `steps` plain favor_attn_fwd calls on workload w (inputs resident in HBM) and
+    return the JSON record: tokens/s, the whole-call roofline fraction, and per-kernel
+    durations from a second pass whose calls record HIP events between the kernels."""
+    import numpy as np
+    import torch
+
+    from efficient_transformer_attention_favor_amd import _lib, api
+
     dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(x).to(dev).to(dt) for x in (Q, K, V))
     wd = torch.from_numpy(W).to(dev)
     out = torch.empty_like(q)
-    p = api._problem(q, k, wd, w.causal, args.chunk)
+    p = api._problem(q, k, wd, w.causal, chunk)
     nbytes = _lib.workspace_bytes(p)
+    if nbytes == 0:
+        raise _lib.FavorError(_lib.attn_fwd(p, None, None, None, None, None, None, 0, None), "favor_attn_fwd")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), wd.data_ptr(), out.data_ptr(), ws.data_ptr())
@@ -288,72 +368,70 @@ def main():
         if st != _lib.FAVOR_OK:
             raise _lib.FavorError(st, "favor_attn_fwd")
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
 
-    # Timed region: exactly K plain calls between a synchronize on each side.
+    # Timed region: exactly `steps` plain calls between a synchronize on each side.
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_host = time.perf_counter()
     start.record(stream)
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     end.record(stream)
     torch.cuda.synchronize()
     t_host = time.perf_counter() - t_host
-    ms_step = start.elapsed_time(end) / args.steps
+    ms_step = start.elapsed_time(end) / steps
 
-    # The same K calls captured in one HIP graph and replayed (launch overhead removed; the
+    # The same calls captured in one HIP graph and replayed (launch overhead removed; the
     # library allocates nothing and issues no memset, so it captures as is).  Reported beside
     # the plain-call figure, not instead of it.
     graph_ms = None
-    try:
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            st = _lib.attn_fwd(p, *ptrs, nbytes, side.cuda_stream)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            cap = torch.cuda.current_stream(dev)
-            for _ in range(args.steps):
-                st = _lib.attn_fwd(p, *ptrs, nbytes, cap.cuda_stream)
-        if st == _lib.FAVOR_OK:
-            graph.replay()
+    if graph:
+        try:
+            side = torch.cuda.Stream()
+            side.wait_stream(stream)
+            with torch.cuda.stream(side):
+                st = _lib.attn_fwd(p, *ptrs, nbytes, side.cuda_stream)
+            stream.wait_stream(side)
             torch.cuda.synchronize()
-            g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            g0.record(stream)
-            graph.replay()
-            g1.record(stream)
-            torch.cuda.synchronize()
-            graph_ms = g0.elapsed_time(g1) / args.steps
-        del graph
-    except RuntimeError as e:  # capture unavailable: report the plain figure only
-        log(f"graph timing skipped: {e}")
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                cap = torch.cuda.current_stream(dev)
+                for _ in range(steps):
+                    st = _lib.attn_fwd(p, *ptrs, nbytes, cap.cuda_stream)
+            if st == _lib.FAVOR_OK:
+                g.replay()
+                torch.cuda.synchronize()
+                g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                g0.record(stream)
+                g.replay()
+                g1.record(stream)
+                torch.cuda.synchronize()
+                graph_ms = g0.elapsed_time(g1) / steps
+            del g
+        except RuntimeError as e:  # capture unavailable: report the plain figure only
+            log(f"graph timing skipped: {e}")
 
-    # Per-kernel durations: K more calls with the library recording HIP events between
+    # Per-kernel durations: `steps` more calls with the library recording HIP events between
     # its kernels on its own stream (outside the timed region above).
     hev = HipEvents()
     nk = _lib.FAVOR_FWD_KERNELS
-    evs = [hev.create(nk + 1) for _ in range(args.steps)]
-    for i in range(args.steps):
+    evs = [hev.create(nk + 1) for _ in range(steps)]
+    for i in range(steps):
         st = _lib.attn_fwd_timed(p, *ptrs, nbytes, stream.cuda_stream, evs[i])
         if st != _lib.FAVOR_OK:
             raise _lib.FavorError(st, "favor_attn_fwd_timed")
     torch.cuda.synchronize()
-    names = KERNELS[w.causal]
+    names = kernel_names(w, p)
     samples = {n: [hev.elapsed_ms(e[j], e[j + 1]) for e in evs] for j, n in enumerate(names) if n is not None}
-    kms = {n: float(np.mean(v)) for n, v in samples.items()}
-    kmin = {n: float(np.min(v)) for n, v in samples.items()}
-    kmed = {n: float(np.median(v)) for n, v in samples.items()}
     for e in evs:
         hev.destroy(e)
 
-    if args.copy_probe_mb > 0:
-        n = args.copy_probe_mb * (1 << 20)
+    if copy_probe_mb > 0:
+        n = copy_probe_mb * (1 << 20)
         src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
         torch.cuda.synchronize()
@@ -362,19 +440,24 @@ def main():
         log(f"copy probe: {n} bytes device-to-device")
 
     work = algorithmic_work(w)
+    peak_tf = PEAK_TFLOPS[w.dtype]
+    kms = {n: float(np.mean(v)) for n, v in samples.items()}
+    ev_total = sum(kms.values())
     kernels = {}
-    names = [n for n in names if n is not None]
-    for n in names:
-        b, f = work[n]
-        t = kms[n] * 1e-3
-        kernels[n] = {"ms": round(kms[n], 5), "median_ms": round(kmed[n], 5), "min_ms": round(kmin[n], 5),
+    for n in kms:
+        b, f = work.get(n, (0, 0))
+        # event markers between kernels add a gap to each interval: the kernel's share of the
+        # plain (unmarked) call time, split in the ratio of the marked intervals
+        t = ms_step * kms[n] / ev_total * 1e-3
+        kernels[n] = {"ms": round(t * 1e3, 5), "event_ms": round(kms[n], 5),
+                      "event_median_ms": round(float(np.median(samples[n])), 5),
+                      "event_min_ms": round(float(np.min(samples[n])), 5),
                       "alg_bytes": b, "alg_flops": f,
                       "GB/s": round(b / t / 1e9, 1) if b else None,
                       "TFLOP/s": round(f / t / 1e12, 2) if f else None}
-    dom = max(names, key=lambda n: kms[n])
-    b, f = work[dom]
-    t_dom = kms[dom] * 1e-3
-    peak_tf = PEAK_TFLOPS[w.dtype]
+    dom = max(kms, key=lambda n: kms[n])
+    b, f = work.get(dom, (0, 0))
+    t_dom = kernels[dom]["ms"] * 1e-3
     if b / (PEAK_HBM_GBS * 1e9) >= f / (peak_tf * 1e12):
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(b / t_dom / 1e9, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s"}
@@ -383,16 +466,26 @@ def main():
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     roof["traffic"] = measured_traffic(w.name, dom)
-    roof["per_launch"] = {"alg_bytes": b, "alg_flops": f, "avg_ms": round(kms[dom], 5)}
+    roof["per_launch"] = {"alg_bytes": b, "alg_flops": f, "avg_ms": round(t_dom * 1e3, 5),
+                          "event_ms": round(kms[dom], 5)}
+    # the whole call against the roofline of its algorithmic work (Q, K, V read once, out
+    # written once, W; the feature maps, the summary and the readout flops)
+    cb, cf = call_work(w)
+    t_call = ms_step * 1e-3
+    t_roof = max(cb / (PEAK_HBM_GBS * 1e9), cf / (peak_tf * 1e12))
+    call = {"bound": "hbm" if cb / (PEAK_HBM_GBS * 1e9) >= cf / (peak_tf * 1e12) else "mfma",
+            "alg_bytes": cb, "alg_flops": cf, "GB/s": round(cb / t_call / 1e9, 1),
+            "TFLOP/s": round(cf / t_call / 1e12, 2), "roofline_ms": round(t_roof * 1e3, 5),
+            "frac": round(t_roof / t_call, 4)}
 
     tokens = w.batch * w.heads_q * w.seq_len
-    res = {
+    return {
         "metric": METRIC,
         "value": round(tokens / (ms_step * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 5),
         "higher_is_better": True,
         "scaling": "weak",
@@ -402,20 +495,13 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "heads_q": w.heads_q, "heads_kv": w.heads_kv,
                    "heads_w": w.heads_w, "seq_len": w.seq_len, "head_dim": w.head_dim,
                    "num_features": w.num_features, "mode": "causal" if w.causal else "bidirectional",
-                   "chunk": args.chunk, "parallelism": "single GPU"},
+                   "chunk": chunk, "parallelism": "single GPU"},
         "roofline": roof,
+        "roofline_call": call,
         "kernels": kernels,
         "graph_ms_per_step": round(graph_ms, 5) if graph_ms is not None else None,
         "host_wall_s": round(t_host, 4),
     }
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle ...")
-        res["cpu_baseline"] = cpu_baseline(w, Q, K, V, W, args.cpu_budget)
-    line = json.dumps(res)
-    print(line, flush=True)
-    if args.out:
-        with open(args.out, "a") as f:
-            f.write(line + "\n")
 
 
 def decode_main(args, w0):

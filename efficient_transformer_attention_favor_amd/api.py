@@ -12,6 +12,15 @@ from . import _lib
 _DTYPES = {torch.float32: _lib.FAVOR_F32, torch.bfloat16: _lib.FAVOR_BF16}
 
 
+def _keep_alive(stream, *tensors):
+    """Tell the caching allocator that tensors allocated here are used on `stream` (which may
+    not be the current stream), so their memory is not handed out again before the queued
+    kernels have finished with it."""
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _problem(Q, K, W, causal, chunk):
     if Q.dim() != 4 or K.dim() != 4 or W.dim() != 3:
         raise ValueError("expected Q, K, V of shape (B, H, L, d) and W of shape (Hw, m, d)")
@@ -54,10 +63,13 @@ def attn_fwd(Q, K, V, W, causal=False, chunk=0, out=None, workspace=None, stream
     if nbytes == 0:
         st = _lib.attn_fwd(p, None, None, None, None, None, None, 0, None)
         raise _lib.FavorError(st, "favor_attn_fwd")
+    own = []
     if out is None:
         out = torch.empty_like(Q)
+        own.append(out)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+        own.append(workspace)
     if stream is None:
         stream = torch.cuda.current_stream(Q.device)
     st = _lib.attn_fwd(p, Q.data_ptr(), K.data_ptr(), V.data_ptr(), W.data_ptr(), out.data_ptr(),
@@ -65,6 +77,7 @@ def attn_fwd(Q, K, V, W, causal=False, chunk=0, out=None, workspace=None, stream
                        stream.cuda_stream)
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_attn_fwd")
+    _keep_alive(stream, *own)
     return out
 
 
@@ -80,10 +93,13 @@ def attn_fwd_generalized(Q, K, V, W, fn="relu", causal=False, out=None, workspac
     if nbytes == 0:
         st = _lib.attn_fwd_generalized(p, fns[fn], None, None, None, None, None, None, 0, None)
         raise _lib.FavorError(st, "favor_attn_fwd_generalized")
+    own = []
     if out is None:
         out = torch.empty_like(Q)
+        own.append(out)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+        own.append(workspace)
     if stream is None:
         stream = torch.cuda.current_stream(Q.device)
     st = _lib.attn_fwd_generalized(p, fns[fn], Q.data_ptr(), K.data_ptr(), V.data_ptr(), W.data_ptr(),
@@ -91,6 +107,7 @@ def attn_fwd_generalized(Q, K, V, W, fn="relu", causal=False, out=None, workspac
                                    workspace.numel() * workspace.element_size(), stream.cuda_stream)
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_attn_fwd_generalized")
+    _keep_alive(stream, *own)
     return out
 
 
@@ -119,6 +136,7 @@ def features(X, W, side, heads_q, heads_kv, stream=None):
                        stream.cuda_stream)
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_features")
+    _keep_alive(stream, phi, c)
     return phi, c
 
 
@@ -151,8 +169,10 @@ def decode_prefill(K, V, W, heads_q, state=None, stream=None):
     nbytes, sbytes = _lib.decode_prefill_workspace_bytes(p), _lib.decode_state_bytes(one)
     if nbytes == 0 or sbytes == 0:
         raise ValueError("unsupported prefill problem")
+    own = []
     if state is None:
         state = torch.empty(sbytes // 4, dtype=torch.float32, device=K.device)
+        own.append(state)
     elif state.dtype != torch.float32 or state.numel() * 4 < sbytes or not state.is_contiguous():
         raise ValueError("state must be a contiguous float32 tensor of favor_decode_state_bytes()")
     ws = torch.empty(nbytes, dtype=torch.uint8, device=K.device)
@@ -162,6 +182,7 @@ def decode_prefill(K, V, W, heads_q, state=None, stream=None):
                              stream.cuda_stream)
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_decode_prefill")
+    _keep_alive(stream, ws, *own)
     return state
 
 
@@ -180,14 +201,17 @@ def attn_decode(q, k, v, W, state, out=None, stream=None):
     p = _decode_problem(q, k, W)
     if state.numel() * 4 < _lib.decode_state_bytes(p):
         raise ValueError("state is smaller than favor_decode_state_bytes()")
+    own = []
     if out is None:
         out = torch.empty_like(q)
+        own.append(out)
     if stream is None:
         stream = torch.cuda.current_stream(q.device)
     st = _lib.attn_decode(p, q.data_ptr(), k.data_ptr(), v.data_ptr(), W.data_ptr(), state.data_ptr(),
                           out.data_ptr(), stream.cuda_stream)
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_attn_decode")
+    _keep_alive(stream, *own)
     return out
 
 
@@ -201,8 +225,10 @@ def attn_bwd(Q, K, V, W, dout, causal=False, workspace=None, stream=None):
     if nbytes == 0:
         st = _lib.attn_bwd(p, None, None, None, None, None, None, None, None, None, 0, None)
         raise _lib.FavorError(st, "favor_attn_bwd")
+    own = []
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+        own.append(workspace)
     if stream is None:
         stream = torch.cuda.current_stream(Q.device)
     dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
@@ -211,6 +237,7 @@ def attn_bwd(Q, K, V, W, dout, causal=False, workspace=None, stream=None):
                        workspace.numel() * workspace.element_size(), stream.cuda_stream)
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_attn_bwd")
+    _keep_alive(stream, dQ, dK, dV, *own)
     return dQ, dK, dV
 
 
@@ -223,6 +250,7 @@ def draw_features(heads_w, num_features, head_dim, seed, orthogonal=True, device
     st = _lib.draw_features(heads_w, num_features, head_dim, int(seed), orthogonal, W.data_ptr(), stream.cuda_stream)
     if st != _lib.FAVOR_OK:
         raise _lib.FavorError(st, "favor_draw_features")
+    _keep_alive(stream, W)
     return W
 
 

@@ -489,3 +489,42 @@ def test_generalized_zero_weights_give_zero_rows():
     assert np.all(out[0, 0, 0] == 0) and np.all(np.abs(out[0, 0, 1:]) > 0)
     one = O.generalized_attention(Q[:, :, 1:2], K[:, :, :1], V[:, :, :1], W)
     assert np.max(np.abs(one[0, 0, 0] - V[0, 0, 0])) < 1e-12
+
+
+# ---------------------------------------------------------------- the parity metric
+
+
+def test_rowwise_rel_err_hand_computed_rows():
+    """The pass/fail metric of every forward parity test: max over rows of
+    |y_i - r_i|_inf / |r_i|_inf, each row against its own largest magnitude.  Values worked
+    by hand; each case separates the metric from a plausible slip."""
+    # row 0: |y - r|_inf = 1 over |r|_inf = 1 -> 1.0;  row 1: 10 / 20 -> 0.5.  Result 1.0.
+    # The global ratio max|y - r| / max|r| (10 / 20 = 0.5) and the column-wise ratio
+    # (column 1: 10 / 20 = 0.5) both miss row 0.
+    assert O.rowwise_rel_err([[1.0, 2.0], [0.0, 10.0]], [[1.0, 1.0], [0.0, 20.0]]) == 1.0
+    # a row with a smaller maximum than another: row 0 0.1 / 0.2 = 0.5, row 1 0.5 / 5.5;
+    # normalising by the largest row maximum instead would give 0.1 / 5.5
+    assert O.rowwise_rel_err([[0.1, 0.0], [5.0, 5.0]], [[0.2, 0.0], [5.0, 5.5]]) == 0.5
+    # magnitudes, not signed values: |(-2) - (-4)| / |-4| = 0.5 (max(r) = 1 would give 2)
+    assert O.rowwise_rel_err([[-2.0, 1.0]], [[-4.0, 1.0]]) == 0.5
+    # the infinity norm of the difference, not its sum: |(0.3, -0.3)| -> 0.3 / 1
+    assert abs(O.rowwise_rel_err([[1.3, -0.3]], [[1.0, 0.0]]) - 0.3) < 1e-15
+    # exact agreement -> 0
+    assert O.rowwise_rel_err([[3.0, -4.0]], [[3.0, -4.0]]) == 0.0
+
+
+def test_rowwise_rel_err_rows_are_the_last_axis():
+    """(B, H, L, d) arrays: a row is one d-vector, whatever the leading shape."""
+    r = np.ones((2, 3, 4, 5))
+    y = r.copy()
+    y[1, 2, 3, 4] = 1.25                  # one entry of one row off by 0.25
+    y[0, 0, 0, :] = 1.1                   # every entry of another row off by 0.1
+    assert abs(O.rowwise_rel_err(y, r) - 0.25) < 1e-15
+    r2 = r.copy()
+    r2[1, 2, 3] = 100.0                   # the first row's own maximum now 100: 0.25 / 100 is
+    y2 = y.copy()                         # no longer the worst, the 0.1 row is
+    y2[1, 2, 3] = r2[1, 2, 3]
+    y2[1, 2, 3, 4] = 100.25
+    assert abs(O.rowwise_rel_err(y2, r2) - 0.1) < 1e-12
+    # float32 and bf16-valued inputs are compared in float64
+    assert O.rowwise_rel_err(np.float32([[1.0, 2.0]]), np.float64([[1.0, 2.0]])) == 0.0
