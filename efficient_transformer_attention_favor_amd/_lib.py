@@ -22,13 +22,14 @@ FAVOR_BIDIRECTIONAL = 0
 FAVOR_CAUSAL = 1
 
 FAVOR_FWD_KERNELS = 3
+FAVOR_NOALLOC_SCRATCH_BYTES = 64 << 20
 FAVOR_FEATURE_RELU = 1
 
 EXPORTED = ("favor_workspace_bytes", "favor_attn_fwd", "favor_attn_fwd_timed", "favor_features",
             "favor_decode_state_bytes", "favor_attn_decode", "favor_bwd_workspace_bytes", "favor_attn_bwd",
             "favor_draw_features", "favor_generalized_workspace_bytes", "favor_attn_fwd_generalized",
             "favor_decode_prefill_workspace_bytes", "favor_decode_prefill",
-            "favor_status_string", "favor_abi_version")
+            "favor_attn_fwd_noalloc", "favor_status_string", "favor_abi_version")
 
 
 class FavorProblem(ctypes.Structure):
@@ -63,6 +64,8 @@ def lib() -> ctypes.CDLL:
         L.favor_attn_fwd_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
                                            ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]
         L.favor_attn_fwd_timed.restype = ctypes.c_int
+        L.favor_attn_fwd_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp]
+        L.favor_attn_fwd_noalloc.restype = ctypes.c_int
         L.favor_features.argtypes = [P, ctypes.c_int32, vp, vp, vp, vp, vp]
         L.favor_features.restype = ctypes.c_int
         L.favor_decode_state_bytes.argtypes = [P]
@@ -121,6 +124,10 @@ def attn_fwd_timed(p: FavorProblem, q, k, v, w, out, workspace, workspace_nbytes
     return int(lib().favor_attn_fwd_timed(_ref(p), q, k, v, w, out, workspace,
                                           ctypes.c_size_t(workspace_nbytes), stream, arr,
                                           0 if events is None else len(events)))
+
+
+def attn_fwd_noalloc(p: FavorProblem, q, k, v, w, out, stream) -> int:
+    return int(lib().favor_attn_fwd_noalloc(_ref(p), q, k, v, w, out, stream))
 
 
 def features(p: FavorProblem, side, x, w, phi_out, c_out, stream) -> int:

@@ -26,6 +26,7 @@
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "favor_device.hpp"
@@ -1758,6 +1759,46 @@ static favor_status attn_fwd_impl(const favor_problem* p, const void* Q, const v
 favor_status favor_attn_fwd(const favor_problem* p, const void* Q, const void* K, const void* V, const float* W,
                             void* out, void* workspace, size_t workspace_bytes, void* stream) {
   return attn_fwd_impl(p, Q, K, V, W, out, workspace, workspace_bytes, stream, favor::Marks{nullptr, 0});
+}
+
+// ---- favor_attn_fwd_noalloc: the forward with the library's own device scratch ------
+// For callers that cannot allocate device memory.  The scratch is one file-scope device
+// array; every device the library runs on holds its own copy.  In host code `scratch` only
+// names the symbol: its device address is looked up once per device (with that device
+// current) and kept, and kernels and copies use that address only.
+namespace {
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) char scratch[FAVOR_NOALLOC_SCRATCH_BYTES];
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+favor_status favor_attn_fwd_noalloc(const favor_problem* p, const void* Q, const void* K, const void* V,
+                                    const float* W, void* out, void* stream) {
+  favor::Plan s;
+  const favor_status st = favor::make_plan(p, &s);
+  if (st != FAVOR_OK) return st;
+  if (Q == nullptr || K == nullptr || V == nullptr || W == nullptr || out == nullptr) return FAVOR_ERR_INVALID_ARG;
+  if (s.bytes > FAVOR_NOALLOC_SCRATCH_BYTES) return FAVOR_ERR_WORKSPACE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FAVOR_ERR_HIP;
+  hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (hs != nullptr) {  // the scratch of the current device serves work on that device only
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(hs, &sdev) != hipSuccess) return FAVOR_ERR_HIP;
+    if (sdev != dev) return FAVOR_ERR_INVALID_ARG;
+  }
+  void* ptr = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+      void* addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return FAVOR_ERR_HIP;
+      g_scratch_ptr[dev] = addr;
+    }
+    ptr = g_scratch_ptr[dev];
+  }
+  return attn_fwd_impl(p, Q, K, V, W, out, ptr, FAVOR_NOALLOC_SCRATCH_BYTES, stream, favor::Marks{nullptr, 0});
 }
 
 favor_status favor_attn_fwd_timed(const favor_problem* p, const void* Q, const void* K, const void* V,

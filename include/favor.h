@@ -103,6 +103,24 @@ favor_status favor_attn_fwd_timed(const favor_problem* p, const void* Q, const v
                                   size_t workspace_bytes, void* stream, void* const* events,
                                   int32_t n_events);
 
+/* favor_attn_fwd for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same kernels, with
+ * the workspace taken from a device array inside the library instead of the caller's.
+ * That array holds FAVOR_NOALLOC_SCRATCH_BYTES (64 MiB) on each device the library runs
+ * on, for the life of the process; a problem whose favor_workspace_bytes() exceeds it is
+ * rejected with FAVOR_ERR_WORKSPACE (nothing queued).  The entry point allocates nothing:
+ * no hipMalloc, hipFree or allocating library call.  Its first call on a device looks up
+ * that device's array address (hipGetSymbolAddress, FAVOR_ERR_HIP if that fails).  `stream`
+ * must belong to the current device (else FAVOR_ERR_INVALID_ARG); NULL is the current
+ * device's default stream.  Every call on a device shares that device's array: calls that
+ * overlap on one device (on different streams, or from several host threads without
+ * ordering) race and give undefined results; calls ordered on one stream do not.  No part
+ * of the array needs to start zeroed.  Other arguments, layouts and errors as for
+ * favor_attn_fwd. */
+#define FAVOR_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+favor_status favor_attn_fwd_noalloc(const favor_problem* p, const void* Q, const void* K, const void* V,
+                                    const float* W, void* out, void* stream);
+
 /* The positive feature map alone (Performer page, "제안 방법"), as a float32 tensor:
  *   side 0 (queries): X = Q, rows = batch*heads_q*seq_len, c per row (the row maximum of
  *                     the exponent), c_out [rows];

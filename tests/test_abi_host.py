@@ -194,3 +194,19 @@ def test_decode_prefill_validation():
     assert L.decode_prefill(causal, 8, 8, 8, 256, None, need, None) == L.FAVOR_ERR_WORKSPACE
     assert L.decode_prefill(_p(mode=L.FAVOR_CAUSAL, head_dim=32), 8, 8, 8, 256, 256, need, None) == \
         L.FAVOR_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects_before_any_hip_call():
+    """favor_attn_fwd_noalloc validates the problem, the pointers and the scratch limit before
+    it touches the GPU (these calls return without a device)."""
+    ok = _p()
+    fake = 256  # never dereferenced: every call below fails validation first
+    assert _lib.attn_fwd_noalloc(_p(batch=0), fake, fake, fake, fake, fake, None) == _lib.FAVOR_ERR_INVALID_ARG
+    assert _lib.attn_fwd_noalloc(_p(head_dim=32), fake, fake, fake, fake, fake, None) == _lib.FAVOR_ERR_UNSUPPORTED
+    assert _lib.attn_fwd_noalloc(ok, None, fake, fake, fake, fake, None) == _lib.FAVOR_ERR_INVALID_ARG
+    assert _lib.attn_fwd_noalloc(ok, fake, fake, fake, fake, None, None) == _lib.FAVOR_ERR_INVALID_ARG
+    # a problem whose workspace is larger than the library's scratch array
+    big = _p(batch=64, heads_q=16, heads_kv=16, heads_w=1, seq_len=8192, num_features=512,
+             mode=_lib.FAVOR_CAUSAL)
+    assert _lib.workspace_bytes(big) > _lib.FAVOR_NOALLOC_SCRATCH_BYTES
+    assert _lib.attn_fwd_noalloc(big, fake, fake, fake, fake, fake, None) == _lib.FAVOR_ERR_WORKSPACE
