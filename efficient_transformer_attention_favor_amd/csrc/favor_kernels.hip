@@ -514,6 +514,383 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   store_partial(unit_off, cmax);
 }
 
+// ======================================================================================
+// kv_summary_bf16: the bidirectional key side for bf16 problems.  Workgroup = (kv head bh,
+// position range t, 64-feature slice), 4 waves (one per SIMD).  The waves split the range
+// into contiguous position groups; each streams its 32-position blocks with the slice's two
+// feature tiles of W (fp16, x log2 e) in registers:
+//   E = K_blk W^T - |k|^2 log2e / 2 - c_f   (4 or 8 MFMAs per tile + one bias MFMA)
+//   phi = 2^E (bf16),  S_v += phi^T V  (V transposed through wave-private LDS),
+//   S_1 += sum over the block's keys of phi (VALU dot products of the same bf16 values).
+// K and V rows of the next NPF blocks are in flight in registers while a block is computed
+// (global-memory latency is several blocks' worth of work).  c_f is fixed at the first
+// block's per-feature maximum; only an overflow makes the fast pass non-finite, and then the
+// wave redoes its positions with a lazily moved running maximum.  The four waves' partials
+// are merged in LDS after rescaling to the largest c_f; wave 0 writes either the readout's
+// LDS images (one range per head) or float32 partials gs / gc in the layout of
+// kv_summary_kernel.
+// ======================================================================================
+template <int D> struct KvBf16 {
+  static constexpr int NW = 4;                    // waves per workgroup
+  static constexpr int NPF = D == 64 ? 3 : 2;     // blocks in flight per wave
+  static constexpr int NKC = D / 16;              // 16-deep contraction slabs over d
+  static constexpr int NDV = D / 32;              // value-column tiles
+  static constexpr int LDV = D + 16;              // V staging rows (transposed reads)
+  static constexpr int CPL = 32 * (D / 8) / 64;   // 16-byte V chunks per lane and block
+  static constexpr int PART = 2 * NDV * 16 + 2;   // floats of one lane's partial (S_v, S_1)
+  static constexpr int VBYTES = NW * 32 * LDV * 2;
+  static constexpr int MBYTES = (NW - 1) * 64 * PART * 4;
+  static constexpr int LDSB = VBYTES > MBYTES ? VBYTES : MBYTES;
+};
+
+template <int D>
+__global__ void __launch_bounds__(64 * KvBf16<D>::NW) kv_summary_bf16_kernel(
+    const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ W, int L, int Hkv, int Hw,
+    int m, int R, int T_ranges, int n_units, float* __restrict__ gs, float* __restrict__ gc, char* __restrict__ img_w,
+    char* __restrict__ img_s, char* __restrict__ img_cb) {
+  using Cfg = KvBf16<D>;
+  constexpr int NW = Cfg::NW, NPF = Cfg::NPF, NKC = Cfg::NKC, NDV = Cfg::NDV, LDV = Cfg::LDV, CPL = Cfg::CPL;
+  constexpr int PART = Cfg::PART;
+  // V staging during the stream; the merge buffers of waves 1..NW-1 afterwards
+  __shared__ __attribute__((aligned(16))) char Sh[Cfg::LDSB];
+  __shared__ __attribute__((aligned(16))) float Cs[NW][64];
+
+  const int NFS = m / 64;
+  const int xcd = blockIdx.x & 7, kq = blockIdx.x >> 3;
+  const int slice = kq % NFS, unit = (kq / NFS) * 8 + xcd;
+  if (unit >= n_units) return;
+  const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
+  const int bh = unit / T_ranges, hkv = bh % Hkv, t = unit % T_ranges;
+  const int f0 = slice * 64;
+  const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
+  bf16* vl = reinterpret_cast<bf16*>(Sh) + wave * 32 * LDV;
+
+  f16x8 wf[2][NKC];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) load_w_frag(Wh + (size_t)(f0 + 32 * nt + col) * D, kc, g, wf[nt][kc]);
+
+  const int pb = t * R, pe = min(pb + R, L);
+  const int Rw = ((R + 32 * NW - 1) / (32 * NW)) * 32;
+  const int wb = pb + wave * Rw, we = min(wb + Rw, pe);
+  const int nblk = wb < we ? (we - wb + 31) / 32 : 0;
+
+  // Raw buffer loads range-checked against the head (rows past L read as zero); a block's
+  // offset sits in the vector offset, which the check covers.
+  const bf16* Kh = K + (size_t)bh * L * D;
+  const bf16* Vh = V + (size_t)bh * L * D;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, L * D * 2, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, L * D * 2, kBufWord3);
+  struct Blk {
+    bf16x8 k[NKC];
+    f32x4 v[CPL];
+  };
+  auto fetch = [&](int p0, Blk& b) {
+    const int ko = (p0 + col) * D * 2 + 16 * g, vo = p0 * D * 2 + 16 * l;
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc)
+      b.k[kc] = __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(krs, ko + 32 * kc, 0, 0));
+#pragma unroll
+    for (int i = 0; i < CPL; ++i)
+      b.v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, vo + 1024 * i, 0, 0));
+  };
+
+  float cst[2];            // stabiliser of this lane's feature 32 nt + col (log2 units)
+  f16x8 biasB[2];
+  f32x16 S[2][NDV];
+  float s1[2];             // this lane's half of the block keys' sum of phi, feature 32 nt + col
+  auto reset = [&]() {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      cst[nt] = -INFINITY;
+      biasB[nt] = bias_cols(0.f, g, f16x8{});
+      s1[nt] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDV; ++dt) S[nt][dt] = zero16();
+    }
+  };
+  bf16x2 one2;
+  one2[0] = one2[1] = (bf16)1.f;
+
+  // One 32-position block.  MODE 0: first block (c_f := its per-feature maximum); 1: c_f
+  // fixed; 2: fallback, running maximum moved lazily with the accumulators rescaled.
+  auto block = [&](int p0, const Blk& b, auto mode_tag) {
+    constexpr int MODE = decltype(mode_tag)::value;
+    // V rows to LDS with the column permutation vperm_inv inside each 32-column tile
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = l + 64 * i, row = c / (D / 8), c0 = (c % (D / 8)) * 8;
+      bf16* drow = vl + row * LDV + (c0 & ~31);
+      *reinterpret_cast<float2*>(drow + vperm_inv(c0 & 31)) = float2{b.v[i][0], b.v[i][1]};
+      *reinterpret_cast<float2*>(drow + vperm_inv((c0 & 31) + 4)) = float2{b.v[i][2], b.v[i][3]};
+    }
+    f16x8 kf[NKC];
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) kf[kc] = to_wfrag(b.k[kc]);
+    f32x16 c1[2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      c1[nt] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) c1[nt] = mma(kf[kc], wf[nt][kc], c1[nt]);
+    }
+    float nrm = sumsq(kf);
+    nrm += partner32(nrm);
+    const float rb = p0 + col < we ? 0.5f * kLog2e * nrm : kMaskedRow;
+    const f16x8 biasA = bias_rows(rb, g, f16x8{});
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) c1[nt] = mma(biasA, biasB[nt], c1[nt]);
+
+    if constexpr (MODE == 0) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float mx = c1[nt][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, c1[nt][r]);
+        mx = fmaxf(mx, partner32(mx));
+        cst[nt] = mx;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) c1[nt][r] -= mx;
+        biasB[nt] = bias_cols(mx, g, f16x8{});
+      }
+    } else if constexpr (MODE == 2) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        float mx = c1[nt][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, c1[nt][r]);
+        mx = fmaxf(mx, partner32(mx));
+        const bool first = cst[nt] == -INFINITY;
+        float shift = 0.f;
+        if (first || mx > kTau) shift = mx;
+        if (wave_any(shift != 0.f)) {
+          const float base = first ? 0.f : cst[nt];
+          cst[nt] = base + shift;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) c1[nt][r] -= shift;
+          biasB[nt] = bias_cols(cst[nt], g, f16x8{});
+          if (!first) {
+            const float fct = fast_exp2(-shift);
+            s1[nt] *= fct;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const float fr = __shfl(fct, 8 * (r >> 2) + 4 * g + (r & 3));
+#pragma unroll
+              for (int dt = 0; dt < NDV; ++dt) S[nt][dt][r] *= fr;
+            }
+          }
+        } else if (first) {
+          cst[nt] = 0.f;  // block maximum is exactly 0
+        }
+      }
+    }
+
+    bf16x8 pa[2][2];
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x16 e;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(c1[nt][r]);
+      acc_to_frags(e, pa[nt]);
+      float sum = s1[nt];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          bf16x2 v2;
+          v2[0] = pa[nt][h][j];
+          v2[1] = pa[nt][h][j + 1];
+          sum = __builtin_amdgcn_fdot2_f32_bf16(v2, one2, sum, false);
+        }
+      s1[nt] = sum;
+    }
+#pragma unroll
+    for (int dt = 0; dt < NDV; ++dt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const bf16x8 vb = lds_frag_rows(vl, LDV, 0, 32 * dt, h);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) S[nt][dt] = mma(pa[nt][h], vb, S[nt][dt]);
+      }
+    asm volatile("" ::: "memory");  // this block's LDS reads before the next block's writes
+  };
+
+  // Fast pass: NPF blocks in flight, the ring of registers unrolled so that it rotates
+  // statically.  Every step issues its fetch (past the last block it re-reads the first),
+  // so the number of loads in flight is the same on every path and the waits for a block
+  // leave the later blocks' loads outstanding.
+  reset();
+  if (nblk > 0) {
+    auto pos = [&](int bi) { return bi < nblk ? wb + 32 * bi : wb; };
+    Blk ring[NPF];
+#pragma unroll
+    for (int j = 0; j < NPF; ++j) fetch(pos(j), ring[j]);
+    // block 0 sets the stabilisers
+    block(wb, ring[0], std::integral_constant<int, 0>{});
+    fetch(pos(NPF), ring[0]);
+    int bi = 1;
+    for (; bi + NPF <= nblk; bi += NPF) {
+#pragma unroll
+      for (int j = 0; j < NPF; ++j) {
+        const int slot = (1 + j) % NPF;  // block bi + j sits in slot (bi + j) % NPF, bi = 1 mod NPF
+        block(wb + 32 * (bi + j), ring[slot], std::integral_constant<int, 1>{});
+        fetch(pos(bi + j + NPF), ring[slot]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NPF; ++j)
+      if (bi + j < nblk) block(wb + 32 * (bi + j), ring[(1 + j) % NPF], std::integral_constant<int, 1>{});
+  }
+  float chk = s1[0] + s1[1];
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int dt = 0; dt < NDV; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) chk += S[nt][dt][r];
+  if (wave_any(!(chk - chk == 0.f))) {
+    reset();
+    for (int bi = 0; bi < nblk; ++bi) {
+      Blk bl;
+      fetch(wb + 32 * bi, bl);
+      block(wb + 32 * bi, bl, std::integral_constant<int, 2>{});
+    }
+  }
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) s1[nt] += partner32(s1[nt]);
+
+  // ---- merge the waves' partials (same features, different positions) ---------------
+  if (g == 0) {
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) Cs[wave][32 * nt + col] = cst[nt];
+  }
+  __syncthreads();  // also: every wave's V staging reads are done
+  float cmax[2];    // merged stabiliser of this lane's feature 32 nt + col
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+    cmax[nt] = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < NW; ++q) cmax[nt] = fmaxf(cmax[nt], Cs[q][32 * nt + col]);
+    s1[nt] *= cmax[nt] == -INFINITY ? 0.f : fast_exp2(cst[nt] - cmax[nt]);
+  }
+  // registers 4 r4 .. 4 r4 + 3 hold features 32 nt + 8 r4 + 4 g + (0..3)
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int fb = 32 * nt + 8 * r4 + 4 * g;
+      const f32x4 own = *reinterpret_cast<const f32x4*>(&Cs[wave][fb]);
+      f32x4 cm = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+#pragma unroll
+      for (int q = 0; q < NW; ++q) {
+        const f32x4 o = *reinterpret_cast<const f32x4*>(&Cs[q][fb]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cm[i] = fmaxf(cm[i], o[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = cm[i] == -INFINITY ? 0.f : fast_exp2(own[i] - cm[i]);
+#pragma unroll
+        for (int dt = 0; dt < NDV; ++dt) S[nt][dt][4 * r4 + i] *= sc;
+      }
+    }
+  // partial exchange: piece (nt, dt, r4) of lane l at ((nt NDV + dt) 4 + r4) 256 + 4 l, then
+  // s1 at 2 NDV 16 64 + 2 l
+  float* mb = reinterpret_cast<float*>(Sh);
+  if (wave > 0) {
+    float* dst = mb + (size_t)(wave - 1) * 64 * PART;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < NDV; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<f32x4*>(dst + ((nt * NDV + dt) * 4 + r4) * 256 + 4 * l) =
+              f32x4{S[nt][dt][4 * r4], S[nt][dt][4 * r4 + 1], S[nt][dt][4 * r4 + 2], S[nt][dt][4 * r4 + 3]};
+    *reinterpret_cast<float2*>(dst + 2 * NDV * 16 * 64 + 2 * l) = float2{s1[0], s1[1]};
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int q = 1; q < NW; ++q) {
+    const float* src = mb + (size_t)(q - 1) * 64 * PART;
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+      for (int dt = 0; dt < NDV; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(src + ((nt * NDV + dt) * 4 + r4) * 256 + 4 * l);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) S[nt][dt][4 * r4 + i] += v[i];
+        }
+    const float2 o = *reinterpret_cast<const float2*>(src + 2 * NDV * 16 * 64 + 2 * l);
+    s1[0] += o.x;
+    s1[1] += o.y;
+  }
+
+  const size_t unit_off = (size_t)bh * T_ranges + t;
+  if (img_s != nullptr) {
+    // The image holds S_v / S_1 per feature (rows already in vperm order: V was staged
+    // permuted, lane col is row 32 dt + col) and c'_f = c_f + log2 S_1,f, so the readout's
+    // denominator is the plain sum of its features.  S_1 of feature 32 nt + j sits in lane j.
+    constexpr int LDSS = kImgMP + 8, LDW = D + 8;
+    bf16* is = reinterpret_cast<bf16*>(img_s + (size_t)bh * img_s_bytes(D));
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      const int ftile = (f0 + 32 * nt) >> 5;
+      float rs1[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) rs1[r] = __builtin_amdgcn_rcpf(__shfl(s1[nt], 8 * (r >> 2) + 4 * g + (r & 3)));
+#pragma unroll
+      for (int dt = 0; dt < NDV; ++dt) {
+        const int row = 32 * dt + col;
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          bf16x4_t v;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = (bf16)(S[nt][dt][4 * a + j] * rs1[4 * a + j]);
+          *reinterpret_cast<bf16x4_t*>(is + (size_t)row * LDSS + 32 * ftile + 16 * (a >> 1) + 8 * g + 4 * (a & 1)) = v;
+        }
+      }
+      const int f = f0 + 32 * nt + col;
+      f16x8* icb = reinterpret_cast<f16x8*>(img_cb + (size_t)bh * img_cb_bytes(m));
+      if (g == 0) {
+        f16x8 cb = zero_frag(f16x8{});
+        split3(cmax[nt] + __builtin_amdgcn_logf(s1[nt]), cb, 0);
+        cb[3] = cb[4] = cb[5] = (f16)1.f;
+        icb[2 * f] = cb;
+        icb[2 * f + 1] = zero_frag(f16x8{});
+      }
+      // one writer per W head: batch 0 (kv head 0 when W is shared)
+      if (bh < Hkv && (Hw != 1 || bh == 0)) {
+        f16* iw = reinterpret_cast<f16*>(img_w + (size_t)(Hw == 1 ? 0 : hkv) * img_w_bytes(D, m));
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) *reinterpret_cast<f16x8*>(iw + (size_t)f * LDW + 16 * kc + 8 * g) = wf[nt][kc];
+      }
+    }
+    return;
+  }
+  // float32 partial: gs rows in vperm order (lane col is row 32 dt + col), row D the ones
+  // column (S_1), gc the stabilisers
+  float* out_s = gs + unit_off * (size_t)(D + 1) * m;
+#pragma unroll
+  for (int nt = 0; nt < 2; ++nt) {
+#pragma unroll
+    for (int dt = 0; dt < NDV; ++dt)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        f32x4 v = {S[nt][dt][4 * r4], S[nt][dt][4 * r4 + 1], S[nt][dt][4 * r4 + 2], S[nt][dt][4 * r4 + 3]};
+        *reinterpret_cast<f32x4*>(out_s + (size_t)(32 * dt + col) * m + f0 + 32 * nt + 8 * r4 + 4 * g) = v;
+      }
+    if (g == 0) {
+      out_s[(size_t)D * m + f0 + 32 * nt + col] = s1[nt];
+      gc[unit_off * m + f0 + 32 * nt + col] = cmax[nt];
+    }
+  }
+}
+
 // s_waitcnt immediate (gfx9 encoding) that waits for vector memory only: vmcnt <= n.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
@@ -1592,10 +1969,16 @@ favor_status launch_kv_summary(const Plan& s, const T* K, const T* V, const floa
     return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
   }
   const int units = s.BH * s.T;
-  hipLaunchKernelGGL((kv_summary_kernel<T, D, false>), dim3(8 * ceil_div_i(units, 8) * nfs), dim3(64 * KvCfg<T, D>::KW), 0,
-                     st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc, s.img ? ws + s.off_img_w : nullptr,
-                     s.img ? ws + s.off_img_s : nullptr, s.img ? ws + s.off_img_cb : nullptr);
-  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  if constexpr (std::is_same<T, bf16>::value) {
+    hipLaunchKernelGGL((kv_summary_bf16_kernel<D>), dim3(8 * ceil_div_i(units, 8) * nfs), dim3(64 * KvBf16<D>::NW), 0,
+                       st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc, s.img ? ws + s.off_img_w : nullptr,
+                       s.img ? ws + s.off_img_s : nullptr, s.img ? ws + s.off_img_cb : nullptr);
+    return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  } else {
+    hipLaunchKernelGGL((kv_summary_kernel<T, D, false>), dim3(8 * ceil_div_i(units, 8) * nfs), dim3(64 * KvCfg<T, D>::KW),
+                       0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc, nullptr, nullptr, nullptr);
+    return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  }
 }
 
 template <class T, int D>

@@ -28,6 +28,9 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
   const long long elems_q = (long long)p->batch * p->heads_q * p->seq_len * p->head_dim;
   const long long elems_kv = (long long)p->batch * p->heads_kv * p->seq_len * p->head_dim;
   if (elems_q >= (1LL << 31) || elems_kv >= (1LL << 31)) return FAVOR_ERR_UNSUPPORTED;
+  // one head's bytes index a buffer descriptor (a signed 32-bit byte count)
+  const long long esize = p->dtype == FAVOR_F32 ? 4 : 2;
+  if ((long long)p->seq_len * p->head_dim * esize >= (1LL << 31)) return FAVOR_ERR_UNSUPPORTED;
   // (batch, head) pairs index the second grid dimension of several launches
   if ((long long)p->batch * p->heads_q > 65535) return FAVOR_ERR_UNSUPPORTED;
 

@@ -64,7 +64,8 @@ typedef enum { FAVOR_BIDIRECTIONAL = 0, FAVOR_CAUSAL = 1 } favor_mode;
 
 /* Problem description.  Supported: head_dim in {64, 128}; num_features a multiple of 64
  * in [64, 512]; heads_q % heads_kv == 0; heads_w in {1, heads_kv}; seq_len >= 1;
- * batch * heads_q * seq_len * head_dim < 2^31; batch * heads_q <= 65535 (otherwise
+ * batch * heads_q * seq_len * head_dim < 2^31; one head's seq_len * head_dim elements under
+ * 2^31 bytes; batch * heads_q <= 65535 (otherwise
  * FAVOR_ERR_UNSUPPORTED).  chunk (causal only) is the granularity
  * of the sequence segments that run in parallel (each segment a multiple of it): 0
  * (library default, 32) or one of 32, 64, 128, 256; the result does not depend on it

@@ -51,6 +51,8 @@ BAD = [
      _lib.FAVOR_ERR_UNSUPPORTED),                           # more than 2^31 elements
     (dict(batch=1 << 12, heads_q=1 << 4, heads_kv=1 << 4, heads_w=1, seq_len=1),
      _lib.FAVOR_ERR_UNSUPPORTED),                           # more than 65535 (batch, head) pairs
+    (dict(batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=1 << 24, head_dim=64),
+     _lib.FAVOR_ERR_UNSUPPORTED),                           # one bf16 head of 2^31 bytes
 ]
 
 
