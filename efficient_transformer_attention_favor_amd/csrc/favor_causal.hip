@@ -1,0 +1,567 @@
+// Causal FAVOR+ for bf16 problems on gfx950: the chunked prefix pass with the value columns
+// split over the waves, and the exclusive scan of the segment summaries with one running
+// stabiliser per feature.
+//
+// Method: "Rethinking Attention with Performers" (review page), "제안 방법": attention in
+// linear order with positive random features; causal mode (inclusive mask j <= i) as the
+// running sum S_i = sum_{j <= i} phi(k_j) [v_j, 1]^T, out_i = phi(q_i) S_v,i / phi(q_i) S_1,i.
+// The sequence of one kv head is cut into segments; a segment starts from the exclusive
+// prefix of the summaries of the segments before it (causal_scan_pf_kernel) and walks its
+// 32-position blocks in order:
+//   out_blk = phi(Q_blk) S_carry + tril(phi(Q_blk) phi(K_blk)^T) [V_blk, 1]
+//   S_carry += phi(K_blk)^T [V_blk, 1]
+// Exponents are in log2 units (W scaled by log2 e).  Keys carry one stabiliser c_f per
+// feature: phi_K = 2^(w_f.k - |k|^2/2 - c_f), and c_f is added to the query exponent, so
+// every product phi_Q phi_K is exact whatever c_f is.  c_f starts at the largest exponent of
+// feature f over the earlier segments and rises (with the carry rescaled) when a block's
+// keys exceed it by more than kTau; the query rows use their own maximum over the features.
+#include <hip/hip_runtime.h>
+
+#include <math.h>
+
+#include <type_traits>
+
+#include "favor_device.hpp"
+#include "favor_ops.hpp"
+#include "favor_plan.hpp"
+
+namespace favor {
+
+// ======================================================================================
+// causal_scan_pf: per kv head bh and feature f, walking the segments in order,
+//   P_t = sum_{t' < t} 2^(c_t'f - C_tf) S_t'f,   C_tf = max_{t' < t} c_t'f   (-inf for t = 0)
+// in the summaries' layout [d+1][m] (rows in vperm order, row d the ones column).  Grid
+// (element groups of the [d+1][m] plane, B*Hkv); each thread owns 4 consecutive features of
+// one row and keeps the running maximum of those features itself; the threads of row 0
+// also write C_t.  TB segments' loads are in flight at a time.
+// ======================================================================================
+__global__ void __launch_bounds__(256) causal_scan_pf_kernel(const float* __restrict__ gs,
+                                                             const float* __restrict__ gc, int T_ranges, int m,
+                                                             int D, float* __restrict__ prefix,
+                                                             float* __restrict__ prefix_c) {
+  const int bh = blockIdx.y;
+  const int e4 = blockIdx.x * 256 + threadIdx.x;  // float4 index within the [d+1][m] plane
+  if (e4 >= (D + 1) * m / 4) return;
+  const int f = (e4 * 4) % m;
+  const bool row0 = e4 * 4 < m;
+  const size_t plane = (size_t)(D + 1) * m;
+  const float* pc = gc + (size_t)bh * T_ranges * m;
+  const f32x4* src = reinterpret_cast<const f32x4*>(gs + (size_t)bh * T_ranges * plane) + e4;
+  f32x4* dst = reinterpret_cast<f32x4*>(prefix + (size_t)bh * T_ranges * plane) + e4;
+  float* dc = prefix_c + (size_t)bh * T_ranges * m + f;
+  constexpr int TB = 8;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 run = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+  for (int t0 = 0; t0 < T_ranges; t0 += TB) {
+    f32x4 sv[TB], cv[TB];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int t = min(t0 + u, T_ranges - 1);
+      sv[u] = src[(size_t)t * (plane / 4)];
+      cv[u] = *reinterpret_cast<const f32x4*>(pc + (size_t)t * m + f);
+    }
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+      const int t = t0 + u;
+      if (t >= T_ranges) break;
+      dst[(size_t)t * (plane / 4)] = acc;
+      if (row0) *reinterpret_cast<f32x4*>(dc + (size_t)t * m) = run;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float nc = fmaxf(run[i], cv[u][i]);
+        if (nc == -INFINITY) continue;  // nothing seen yet (an empty segment summary is zero)
+        acc[i] = acc[i] * fast_exp2(run[i] - nc) + sv[u][i] * fast_exp2(cv[u][i] - nc);
+        run[i] = nc;
+      }
+    }
+  }
+}
+
+// ======================================================================================
+// causal_v: the chunked prefix pass.  Grid (segments, B*Hq); NW = 2 d/32 waves.
+//   Feature maps: the m/32 feature tiles are dealt to the waves (tile ft to wave ft % NW);
+//   a wave computes the key and query exponents of its tiles on the MFMA (fp16 W x log2 e
+//   in registers), the key features phi_K = 2^(. - c_f) into LDS as [feature][key], the
+//   query exponents' row maxima into LDS; after a barrier the rows' maxima M are known and
+//   phi_Q = 2^(. + c_f - M) goes to LDS in MFMA-operand order, with the wave's share of the
+//   inter-block denominator phi_Q . S_1 and of the intra-block matrix A^T = phi_K phi_Q^T.
+//   Products: wave (vt, fg) owns value columns [32 vt, 32 vt + 32) and group fg of the
+//   features (NFG groups): it keeps that part of the carry S_v in registers (float32) and forms
+//     num = S_v^T phi_Q^T (its features) [+ V^T tril(A)^T (fg = 0)],  S_v += phi_K^T V.
+//   The fg > 0 waves hand their numerators to the fg = 0 wave, which divides by
+//     den = sum of the waves' phi_Q . S_1 + the row sums of tril(A)
+//   and stores the bf16 output.  S_1 (the ones column) lives in LDS, one float per feature.
+// A block whose keys exceed their features' c_f by more than kTau raises those c_f first
+// (carry and S_1 rescaled); the first block of the sequence sets them.
+// ======================================================================================
+// Largest spread (log2 units) of one feature's key exponents taken in one block: beyond it,
+// or when a block's keys jump that far above c_f, the block runs one position at a time.
+// Within it every query's own terms stay above 2^-kSpread of the largest, far from float32
+// and bf16 underflow.
+constexpr float kSpread = 100.f;
+
+template <int D, int NFG> struct CausalV {
+  static constexpr int NV = D / 32;       // value tiles
+  static constexpr int NW = NFG * NV;     // waves: (value tile, feature group)
+  static constexpr int LDK = D + 8;       // fp16 Q / K staging rows
+  static constexpr int LDV = D + 16;      // bf16 V staging rows (transposed reads)
+  static constexpr int LDP = 40;          // phi_K rows: 32 keys + pad (bf16)
+  static constexpr int LDN = 36;          // numerator hand-over rows (float)
+  // LDS bytes for at most 32 nft features
+  static constexpr int bytes(int nft) {
+    return 2 * 32 * LDK * 2 + 32 * LDV * 2 + 32 * nft * LDP * 2 + 32 * (32 * nft + 8) * 2 + NW * 1024 * 4 +
+           NV * (NFG - 1) * 32 * LDN * 4 + 3 * 32 * nft * 4 + 2 * NW * 32 * 4 + 16;
+  }
+};
+
+template <int D, int NFTMAX, int NFG, bool REPAIR>
+__global__ void __launch_bounds__(64 * (D / 32) * NFG, (D / 32) * NFG == 4 && !REPAIR ? 2 : 1) causal_v_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ W,
+    const float* __restrict__ prefix, const float* __restrict__ prefix_c, bf16* __restrict__ out, int L, int Hq,
+    int Hkv, int Hw, int m, int R, int T_ranges, int* __restrict__ wide) {
+  using Cfg = CausalV<D, NFG>;
+  constexpr int NV = Cfg::NV, NW = Cfg::NW, LDK = Cfg::LDK, LDV = Cfg::LDV, LDP = Cfg::LDP, LDN = Cfg::LDN;
+  constexpr int NKC = D / 16;
+  constexpr int NMAP = (NFTMAX + NW - 1) / NW;  // feature tiles per wave in the map phase
+  constexpr int NCT = NFTMAX / NFG;             // carry tiles per wave (its feature group)
+  constexpr int NT = 64 * NW;
+  const int NFT = m / 32;
+  constexpr int LDQ = 32 * NFTMAX + 8;          // phi_Q rows (bf16)
+  constexpr int MMAX = 32 * NFTMAX;
+
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::bytes(NFTMAX)];
+  f16* Ql = reinterpret_cast<f16*>(smem);                       // [32][LDK]
+  f16* Kl = Ql + 32 * LDK;                                      // [32][LDK]
+  bf16* Vl = reinterpret_cast<bf16*>(Kl + 32 * LDK);            // [32][LDV]
+  bf16* Pk = Vl + 32 * LDV;                                     // [m][LDP]
+  bf16* Pq = Pk + (size_t)MMAX * LDP;                           // [32][LDQ]
+  float* Ap = reinterpret_cast<float*>(Pq + 32 * LDQ);          // [NW][16][64] partial A^T
+  float* Np = Ap + NW * 1024;                                   // [NV][NFG-1][32][LDN] numerator hand-over
+  float* S1 = Np + NV * (NFG - 1) * 32 * LDN;                   // [m]
+  float* Csh = S1 + MMAX;                                       // [m] c_f shift of the window
+  float* S1b = Csh + MMAX;                                      // [m] S_1 before the window, rescaled
+  float* Mr = S1b + MMAX;                                       // [NW][32] partial row maxima
+  float* Dp = Mr + NW * 32;                                     // [NW][32] partial denominators
+  int* flag = reinterpret_cast<int*>(Dp + NW * 32);             // [2]
+
+  const int seg = blockIdx.x, bhq = blockIdx.y;
+  // the repair pass redoes only the segments whose first pass met a wide block
+  if (REPAIR && wide[(size_t)bhq * T_ranges + seg] == 0) return;
+  const int b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv), bh = b * Hkv + hkv;
+  const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
+  const int vt = wave % NV, fg = wave / NV;
+  const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
+  const bf16* Qh = Q + (size_t)bhq * L * D;
+  bf16* Oh = out + (size_t)bhq * L * D;
+  const bf16* Kh = K + (size_t)bh * L * D;
+  const bf16* Vh = V + (size_t)bh * L * D;
+
+  // ---- state -------------------------------------------------------------------------
+  // map tiles of this wave: ft = wave + NW i; W fragments and c_f of feature 32 ft + col
+  f16x8 wf[NMAP][NKC];
+  float cf[NMAP];
+#pragma unroll
+  for (int i = 0; i < NMAP; ++i) {
+    const int ft = wave + NW * i;
+    if (ft < NFT) {
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) load_w_frag(Wh + (size_t)(32 * ft + col) * D, kc, g, wf[i][kc]);
+      cf[i] = prefix_c[((size_t)bh * T_ranges + seg) * m + 32 * ft + col];
+    }
+  }
+  // carry of value tile vt, features of group fg: tile ct covers features 32 (fg nct + ct) + ..
+  const int nct = NFT / NFG;
+  const float* Pp = prefix + ((size_t)bh * T_ranges + seg) * (size_t)(D + 1) * m;
+  f32x16 carry[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    carry[ct] = zero16();
+    if (ct < nct) {
+      const int fb = 32 * (fg * nct + ct);
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(Pp + (size_t)(32 * vt + col) * m + fb + 8 * r4 + 4 * g);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) carry[ct][4 * r4 + i] = v[i];
+      }
+    }
+  }
+  for (int f = threadIdx.x; f < m; f += NT) S1[f] = Pp[(size_t)D * m + f];
+
+  // ---- staging: the block's Q, K (fp16) and V (bf16, columns permuted) ----------------
+  // range-checked buffer loads: rows past L read as zero
+  const unsigned head_bytes = (unsigned)L * (unsigned)D * 2u;
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Qh, (short)0, (int)head_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, (int)head_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, (int)head_bytes, kBufWord3);
+  constexpr int CPR = D / 8, NCH = 32 * CPR;            // 16-byte chunks per row, per block
+  constexpr int PER = (NCH + NT - 1) / NT;
+  f32x4 pq_[PER], pk_[PER], pv_[PER];
+  auto prefetch = [&](int q0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NT;
+      const int row = c / CPR, c0 = (c % CPR) * 8;
+      const unsigned off = c < NCH && q0 + row < L ? ((unsigned)(q0 + row) * D + c0) * 2u : head_bytes;
+      pq_[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)off, 0, 0));
+      pk_[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
+      pv_[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
+    }
+  };
+  auto stage = [&]() {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NT;
+      if (c < NCH) {
+        const int row = c / CPR, c0 = (c % CPR) * 8;
+        *reinterpret_cast<f16x8*>(Ql + row * LDK + c0) = to_wfrag(__builtin_bit_cast(bf16x8, pq_[i]));
+        *reinterpret_cast<f16x8*>(Kl + row * LDK + c0) = to_wfrag(__builtin_bit_cast(bf16x8, pk_[i]));
+        bf16* drow = Vl + row * LDV + (c0 & ~31);
+        *reinterpret_cast<float2*>(drow + vperm_inv(c0 & 31)) = float2{pv_[i][0], pv_[i][1]};
+        *reinterpret_cast<float2*>(drow + vperm_inv((c0 & 31) + 4)) = float2{pv_[i][2], pv_[i][3]};
+      }
+    }
+  };
+
+  const int p_begin = seg * R, p_end = min(p_begin + R, L);
+  prefetch(p_begin);
+  int wide_any = 0;
+  bf16x2 one2;
+  one2[0] = one2[1] = (bf16)1.f;
+
+  for (int p0 = p_begin; p0 < p_end; p0 += 32) {
+    __syncthreads();  // the previous block's readers of Ql / Kl / Vl are done
+    stage();
+    if (p0 + 32 < p_end) prefetch(p0 + 32);
+    const int pend = min(p0 + 32, L);
+    // The block is taken whole, or -- when its keys' exponents spread (or jump above c_f) by
+    // more than kSpread for some feature -- one position at a time, so that no query's
+    // terms can underflow against a later key of its own block.  Keys and queries outside
+    // the window [lo, hi) are masked / not stored.
+    // step(lo, hi, check): the positions [lo, hi) of the block.  check: look for a wide
+    // block (see below); the repair pass then returns true having committed nothing, the
+    // first pass records it and goes on.  The repair pass rewrites every output of the
+    // segments it redoes.
+    auto step = [&](const int lo, const int hi, const bool check) -> bool {
+      if (threadIdx.x == 0) {
+        flag[0] = 0;
+        flag[1] = 0;
+      }
+      __syncthreads();  // staging done; the previous step's readers of Pk / Pq / Ap / Np done
+
+      // ---- map phase 1: key features, their maxima, query exponents -----------------
+      f16x8 kf[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) kf[kc] = load_frag_k(Kl + col * LDK, kc, g);
+      float nrm = sumsq(kf);
+      nrm += partner32(nrm);
+      const bool kin = p0 + col >= lo && p0 + col < hi;  // key col of the block in the window
+      const f16x8 biasA = bias_rows(kin ? 0.5f * kLog2e * nrm : kMaskedRow, g, f16x8{});
+      f32x16 cq[NMAP];
+      float s1inc[NMAP], cnew[NMAP];
+      float mloc = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NMAP; ++i) {
+        const int ft = wave + NW * i;
+        s1inc[i] = 0.f;
+        cnew[i] = cf[i];
+        if (ft >= NFT) continue;
+        // key exponents relative to c_f: C[key][feature], lane = feature
+        f32x16 ck = zero16();
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) ck = mma(kf[kc], wf[i][kc], ck);
+        const bool init = cf[i] == -INFINITY;
+        ck = mma(biasA, bias_cols(init ? 0.f : cf[i], g, f16x8{}), ck);
+        // masked keys sit near -kMaskedRow: far below any key in the window
+        float mx = ck[0], mn = ck[0] > -0.5f * kMaskedRow ? ck[0] : INFINITY;
+#pragma unroll
+        for (int r = 1; r < 16; ++r) {
+          mx = fmaxf(mx, ck[r]);
+          mn = fminf(mn, ck[r] > -0.5f * kMaskedRow ? ck[r] : INFINITY);
+        }
+        mx = fmaxf(mx, partner32(mx));
+        mn = fminf(mn, partner32(mn));
+        // wide: the first keys of the sequence spread too far (an early query could see only
+        // keys far below the block's largest), or a key jumps too far above c_f (the rescaled
+        // carry of the queries before it would underflow).  Keys far below c_f are harmless
+        // once there is a carry: it holds the key that set c_f.
+        if (check && (init ? mx - mn > kSpread : mx > kSpread) && g == 0) flag[1] = 1;
+        // c_f is set by the first keys of the sequence and raised when the window's keys
+        // pass it by more than kTau; the carry and S_1 of a raised feature are rescaled by
+        // 2^(old - new) (0 where it was unset).  Committed after the spread check.
+        float shift = 0.f;
+        if (init || mx > kTau) shift = mx;
+        if (shift != 0.f) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ck[r] -= shift;
+          if (g == 0) flag[0] = 1;
+        }
+        if (g == 0) {
+          Csh[32 * ft + col] = init ? -INFINITY : -shift;
+          S1b[32 * ft + col] = init ? 0.f : (shift != 0.f ? S1[32 * ft + col] * fast_exp2(-shift) : S1[32 * ft + col]);
+        }
+        cnew[i] = (init ? 0.f : cf[i]) + shift;
+        // key features to LDS [feature][key] and the window's S_1 increment of the feature
+        bf16x8 ka[2];
+        f32x16 e;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(ck[r]);
+        acc_to_frags(e, ka);
+        float sum = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int j = 0; j < 8; j += 2) {
+            bf16x2 v2;
+            v2[0] = ka[h][j];
+            v2[1] = ka[h][j + 1];
+            sum = __builtin_amdgcn_fdot2_f32_bf16(v2, one2, sum, false);
+          }
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            bf16x4_t v;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = ka[h][4 * hh + q];
+            *reinterpret_cast<bf16x4_t*>(Pk + (32 * ft + col) * LDP + 8 * (2 * h + hh) + 4 * g) = v;
+          }
+        }
+        s1inc[i] = sum + partner32(sum);
+      }
+      // query exponents + c_f: C[feature][query], lane = query
+      f16x8 qf[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) qf[kc] = load_frag_k(Ql + col * LDK, kc, g);
+#pragma unroll
+      for (int i = 0; i < NMAP; ++i) {
+        const int ft = wave + NW * i;
+        if (ft >= NFT) continue;
+        cq[i] = zero16();
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) cq[i] = mma(wf[i][kc], qf[kc], cq[i]);
+        cq[i] = mma(bias_rows(-cnew[i], g, f16x8{}), bias_cols(0.f, g, f16x8{}), cq[i]);
+        float qm = cq[i][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) qm = fmaxf(qm, cq[i][r]);
+        mloc = fmaxf(mloc, qm);
+      }
+      mloc = fmaxf(mloc, partner32(mloc));
+      if (g == 0) Mr[wave * 32 + col] = mloc;
+      __syncthreads();
+      if (check && __builtin_amdgcn_readfirstlane(flag[1]) != 0) {  // the same in every lane
+        if (REPAIR) return true;  // nothing committed: the caller redoes the block position by position
+        wide_any = 1;
+      }
+#pragma unroll
+      for (int i = 0; i < NMAP; ++i) cf[i] = cnew[i];
+
+      // ---- rescale the carry where c_f rose ---------------------------------------------
+      if (__builtin_amdgcn_readfirstlane(flag[0]) != 0) {
+#pragma unroll
+        for (int ct = 0; ct < NCT; ++ct) {
+          if (ct >= nct) continue;
+          const int fb = 32 * (fg * nct + ct);
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 sh = *reinterpret_cast<const f32x4*>(Csh + fb + 8 * r4 + 4 * g);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) carry[ct][4 * r4 + i] *= fast_exp2(sh[i]);
+          }
+        }
+      }
+
+      // ---- map phase 2: query features, the denominator share, A^T share --------------
+      float M = Mr[col];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) M = fmaxf(M, Mr[w * 32 + col]);
+      float dsh = 0.f;
+      f32x16 at = zero16();
+#pragma unroll
+      for (int i = 0; i < NMAP; ++i) {
+        const int ft = wave + NW * i;
+        if (ft >= NFT) continue;
+        bf16x8 qa[2];
+        f32x16 e;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(cq[i][r] - M);
+        acc_to_frags(e, qa);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) *reinterpret_cast<bf16x8*>(Pq + col * LDQ + 32 * ft + 16 * h + 8 * g) = qa[h];
+        // phi_Q . S_1 over this tile's features (the bf16 values the numerator uses); S_1
+        // of the positions before the window, relative to the window's c_f
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 sv = *reinterpret_cast<const f32x4*>(S1b + 32 * ft + 8 * r4 + 4 * g);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) dsh = __builtin_fmaf((float)qa[r4 >> 1][4 * (r4 & 1) + q], sv[q], dsh);
+        }
+        // A^T[key][query] += phi_K phi_Q^T over this tile's features (keys through a
+        // transposed read of the wave's own Pk rows)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) at = mma(lds_frag_rows(Pk, LDP, 32 * ft, 0, h), qa[h], at);
+      }
+      dsh += partner32(dsh);
+      if (g == 0) Dp[wave * 32 + col] = dsh;
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<f32x4*>(Ap + (wave * 4 + r4) * 256 + 4 * l) =
+            f32x4{at[4 * r4], at[4 * r4 + 1], at[4 * r4 + 2], at[4 * r4 + 3]};
+      __syncthreads();
+
+      // ---- S_1 of the positions up to the window's end (owners) -------------------------
+#pragma unroll
+      for (int i = 0; i < NMAP; ++i) {
+        const int ft = wave + NW * i;
+        if (ft < NFT && g == 0) S1[32 * ft + col] = S1b[32 * ft + col] + s1inc[i];
+      }
+
+      // ---- products of wave (vt, fg) ----------------------------------------------------
+      // tril(A)^T with the rows summed in fixed order, and its row sums (denominator)
+      f32x16 asum = zero16();
+#pragma unroll
+      for (int w = 0; w < NW; ++w)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(Ap + (w * 4 + r4) * 256 + 4 * l);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) asum[4 * r4 + q] += v[q];
+        }
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * g + (r & 3) > col) asum[r] = 0.f;
+      bf16x8 ab[2];
+      acc_to_frags(asum, ab);
+      f32x16 num = zero16();
+      // V^T operands of value tile vt (rows: keys in operand order)
+      bf16x8 vo[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) vo[h] = lds_frag_rows(Vl, LDV, 0, 32 * vt, h);
+      if (fg == 0) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) num = mma(vo[h], ab[h], num);
+      }
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct) {
+        if (ct >= nct) continue;
+        const int ftg = fg * nct + ct;
+        bf16x8 ca[2];
+        acc_to_frags(carry[ct], ca);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bf16x8 qb = *reinterpret_cast<const bf16x8*>(Pq + col * LDQ + 32 * ftg + 16 * h + 8 * g);
+          num = mma(ca[h], qb, num);
+        }
+        // carry += phi_K^T V: phi_K rows of these features, keys in operand order
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bf16* prow = Pk + (32 * ftg + col) * LDP + 16 * h + 4 * g;
+          const bf16x4_t plo = *reinterpret_cast<const bf16x4_t*>(prow);
+          const bf16x4_t phi = *reinterpret_cast<const bf16x4_t*>(prow + 8);
+          bf16x8 pa;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            pa[q] = plo[q];
+            pa[q + 4] = phi[q];
+          }
+          carry[ct] = mma(pa, vo[h], carry[ct]);
+        }
+      }
+      if (fg > 0) {
+        float* np = Np + ((vt * (NFG - 1) + fg - 1) * 32 + col) * LDN + 16 * g;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          *reinterpret_cast<f32x4*>(np + 4 * r4) = f32x4{num[4 * r4], num[4 * r4 + 1], num[4 * r4 + 2], num[4 * r4 + 3]};
+      }
+      float dintra = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dintra += asum[r];
+      dintra += partner32(dintra);
+      __syncthreads();
+      if (fg == 0) {
+        float den = dintra;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) den += Dp[w * 32 + col];
+        const int pos = p0 + col;
+        const float inv = __builtin_amdgcn_rcpf(den);
+        if (pos >= lo && pos < hi) {
+#pragma unroll
+          for (int u = 1; u < NFG; ++u) {
+            const float* np = Np + ((vt * (NFG - 1) + u - 1) * 32 + col) * LDN + 16 * g;
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 h = *reinterpret_cast<const f32x4*>(np + 4 * r4);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) num[4 * r4 + q] += h[q];
+            }
+          }
+          bf16x8 o0, o1;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            o0[j] = (bf16)(num[j] * inv);
+            o1[j] = (bf16)(num[8 + j] * inv);
+          }
+          bf16* orow = Oh + (size_t)pos * D + 32 * vt + 16 * g;
+          *reinterpret_cast<bf16x8*>(orow) = o0;
+          *reinterpret_cast<bf16x8*>(orow + 8) = o1;
+        }
+      }
+      return false;
+    };
+    if constexpr (REPAIR) {
+      if (step(p0, pend, true))
+        for (int q = p0; q < pend; ++q) step(q, q + 1, false);
+    } else {
+      step(p0, pend, true);
+    }
+  }
+  if (!REPAIR && threadIdx.x == 0) wide[(size_t)bhq * T_ranges + seg] = wide_any;
+}
+
+// Exclusive scan of the segment summaries gs / gc with per-feature stabilisers into the
+// prefix region of the workspace.
+favor_status launch_causal_scan_pf(const Plan& s, char* ws, hipStream_t st) {
+  const float* gs = reinterpret_cast<const float*>(ws + s.off_gs);
+  const float* gc = reinterpret_cast<const float*>(ws + s.off_gc);
+  float* prefix = reinterpret_cast<float*>(ws + s.off_p);
+  float* prefix_c = reinterpret_cast<float*>(ws + s.off_pc);
+  hipLaunchKernelGGL(causal_scan_pf_kernel, dim3((unsigned)(((size_t)(s.d + 1) * s.m / 4 + 255) / 256), s.BH), dim3(256),
+                     0, st, gs, gc, s.T, s.m, s.d, prefix, prefix_c);
+  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+bool causal_v_supported(const Plan& s) { return s.dtype == FAVOR_BF16 && (s.d == 64 || s.m <= 256); }
+
+// The chunked pass of causal_v_kernel from the prefixes launch_causal_scan_pf wrote.
+favor_status launch_causal_v(const Plan& s, const void* Q, const void* K, const void* V, const float* W, void* out,
+                             char* ws, hipStream_t st) {
+  if (!causal_v_supported(s)) return FAVOR_ERR_UNSUPPORTED;
+  const float* prefix = reinterpret_cast<const float*>(ws + s.off_p);
+  const float* prefix_c = reinterpret_cast<const float*>(ws + s.off_pc);
+  const bf16* q = static_cast<const bf16*>(Q);
+  const bf16* k = static_cast<const bf16*>(K);
+  const bf16* v = static_cast<const bf16*>(V);
+  bf16* o = static_cast<bf16*>(out);
+  int* wide = reinterpret_cast<int*>(ws + s.off_wide);
+  const dim3 grid(s.T, s.B * s.Hq);
+  // first pass, then the repair pass (its workgroups return at once unless their segment
+  // met a wide block)
+  auto run = [&](auto repair) -> bool {
+    constexpr bool RP = decltype(repair)::value;
+    if (s.d == 64) {
+      if (s.m <= 256)
+        hipLaunchKernelGGL((causal_v_kernel<64, 8, 2, RP>), grid, dim3(64 * 2 * 2), 0, st, q, k, v, W, prefix,
+                           prefix_c, o, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, wide);
+      else
+        hipLaunchKernelGGL((causal_v_kernel<64, 16, 4, RP>), grid, dim3(64 * 2 * 4), 0, st, q, k, v, W, prefix,
+                           prefix_c, o, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, wide);
+    } else {
+      hipLaunchKernelGGL((causal_v_kernel<128, 8, 2, RP>), grid, dim3(64 * 4 * 2), 0, st, q, k, v, W, prefix,
+                         prefix_c, o, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, wide);
+    }
+    return hipGetLastError() == hipSuccess;
+  };
+  if (!run(std::false_type{})) return FAVOR_ERR_HIP;
+  if (!run(std::true_type{})) return FAVOR_ERR_HIP;
+  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+}  // namespace favor

@@ -2034,6 +2034,15 @@ favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const
   if (!mk.mark(0, st)) return FAVOR_ERR_HIP;
   favor_status rc = launch_kv_summary<T, D>(s, K, V, W, gs, gc, ws, st);
   if (rc != FAVOR_OK || !mk.mark(1, st)) return rc != FAVOR_OK ? rc : FAVOR_ERR_HIP;
+  if (causal_v_supported(s)) {
+    // per-feature stabilisers, the value columns split over the waves
+    rc = launch_causal_scan_pf(s, ws, st);
+    if (rc != FAVOR_OK) return rc;
+    if (!mk.mark(2, st)) return FAVOR_ERR_HIP;
+    rc = launch_causal_v(s, Q, K, V, W, out, ws, st);
+    if (rc != FAVOR_OK) return rc;
+    return mk.mark(3, st) ? FAVOR_OK : FAVOR_ERR_HIP;
+  }
   hipLaunchKernelGGL(causal_scan_kernel, dim3(ceil_div_i((long long)(s.d + 1) * s.m / 4, 256), s.BH), dim3(256), 0,
                      st, gs, gc, s.T, s.m, s.d, prefix, cstar);
   if (hipGetLastError() != hipSuccess || !mk.mark(2, st)) return FAVOR_ERR_HIP;

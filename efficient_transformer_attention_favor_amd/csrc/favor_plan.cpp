@@ -104,6 +104,10 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
   if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * (size_t)(q.d + 1) * q.m * q.BH * q.T);
   q.off_cstar = off;
   if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * q.BH);
+  q.off_pc = off;
+  if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * (size_t)q.m * q.BH * q.T);
+  q.off_wide = off;
+  if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(int) * (size_t)q.B * q.Hq * q.T);
   q.off_part = off;
   if (q.mode == FAVOR_CAUSAL && q.d == 128 && q.m > 256)
     off = align256(off + sizeof(float) * (size_t)q.B * q.Hq * q.L * (q.d + 4));

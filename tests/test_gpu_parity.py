@@ -174,3 +174,24 @@ def test_large_norm_inputs(causal, dtype):
     _say(f"  rowwise rel err {err:.3e}")
     assert np.isfinite(y).all()
     assert err < TOL[w.dtype]
+
+
+@pytest.mark.parametrize("base,kw", [
+    ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1000)),
+    ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=301, head_dim=128)),
+    ("c5_causal_long_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=700, heavy_fraction=0.0)),
+], ids=["d64m256", "d128m256", "d64m512"])
+def test_causal_keys_far_apart(base, kw):
+    """K scaled by 8 (exact in bf16): |k|^2 / 2 alone spreads the key exponents over hundreds
+    of log2 units, so early queries whose keys all sit far below a later key of the same block
+    (or of the sequence) must not lose their terms to underflow."""
+    w = _small(base, **kw)
+    _say(f"case {w} K x8")
+    Q, K, V, W = I.make_inputs(w, seed=4)
+    K = K * np.float32(8)
+    y = _run(w, Q, K, V, W).float().cpu().numpy()
+    ref = O.favor_attention(Q, K, V, W, causal=True)
+    err = O.rowwise_rel_err(y, ref)
+    _say(f"  rowwise rel err {err:.3e}")
+    assert np.isfinite(y).all()
+    assert err < TOL[w.dtype]
