@@ -328,13 +328,16 @@ def main():
 
 def _also_list(spec, main_name, main_chunk):
     """(workload, chunk) pairs of --also: 'all' = every other workload, causal ones at the
-    library default and at chunks 64, 128, 256; else a comma-separated list of names."""
+    library default and at intra-chunk blocks 64, 128, 256 (256 where the problem has at most
+    256 features); else a comma-separated list of names."""
     from efficient_transformer_attention_favor_amd import inputs as I
 
     names = sorted(I.WORKLOADS) if spec == "all" else [n for n in spec.split(",") if n]
     out = []
     for n in names:
-        chunks = [0, 64, 128, 256] if I.workload(n).causal else [0]
+        w = I.workload(n)
+        # the 256-position intra-chunk block is built up to 256 features
+        chunks = [c for c in (0, 64, 128, 256) if c < 256 or w.num_features <= 256] if w.causal else [0]
         for c in chunks:
             if (n, c) != (main_name, main_chunk):
                 out.append((n, c))

@@ -516,6 +516,533 @@ __global__ void __launch_bounds__(64 * (D / 32) * NFG, (D / 32) * NFG == 4 && !R
   if (!REPAIR && threadIdx.x == 0) wide[(size_t)bhq * T_ranges + seg] = wide_any;
 }
 
+// ======================================================================================
+// causal_fg (d = 64): the chunked prefix pass with the features split over the waves.
+// Grid (segments, B*Hq); NW waves, wave w owns features [64 w, 64 w + 64) (none when
+// 64 w >= m) and works on them alone through a 32-position block:
+//   key features  phi_K = 2^(w_f.k - |k|^2/2 - c_f), c_f per feature (set by the first keys
+//                 of the sequence, raised with its carry rescaled when the block's keys pass
+//                 it by more than kTau);
+//   query features relative to the wave's own row maxima: phi_Q = 2^(w_f.q + c_f - M_w);
+//   num_w = S_v,w^T phi_Q^T + V^T tril(phi_K phi_Q^T)^T    (its features, all 64 columns)
+//   den_w = phi_Q . S_1,w + row sums of tril(phi_Q phi_K^T)
+//   S_v,w += phi_K^T V,  S_1,w += the keys' sum of phi_K.
+// The partials meet in LDS once per block: with M = max_w M_w,
+//   out = sum_w 2^(M_w - M) num_w / sum_w 2^(M_w - M) den_w,
+// each wave finishing 8 / NW of the block's eight 4-column groups of each value tile pair.
+// Two barriers per block (staged Q / K / V ready; partials ready).  phi_K reaches the
+// intra-block product through the wave's own LDS rows (a transposed read), which needs no
+// barrier: one wave's LDS accesses complete in issue order.
+// ======================================================================================
+template <int NW, int NB> struct CausalFg {
+  static constexpr int D = 64, LDK = D + 8, LDV = D + 16, LDP = 40;
+  // Q (fp16) of a block; K (fp16) and V (bf16) of the NB blocks of a chunk
+  static constexpr int STAGE = 32 * LDK * 2 + NB * (32 * LDK * 2 + 32 * LDV * 2);
+  static constexpr int PK = 64 * LDP * 2;                        // per wave: phi_K [64 features][keys]
+  static constexpr int RED = 2 * 4 * 64 * 16;                    // per wave: numerator partial
+  static constexpr int DM = 32 * 8;                              // per wave: (den_w, M_w) per query
+  static constexpr int VEC = 2 * 64 * 4;                         // per wave: S_1 before the block, c_f shifts
+  static constexpr int BYTES = STAGE + NW * (PK + RED + DM + VEC) + 64;
+};
+
+template <int NW, int NB, bool REPAIR>
+__global__ void __launch_bounds__(64 * NW, REPAIR || NW < 4 || NB > 1 ? 1 : 8 / NW) causal_fg_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ W,
+    const float* __restrict__ prefix, const float* __restrict__ prefix_c, bf16* __restrict__ out, int L, int Hq,
+    int Hkv, int Hw, int m, int R, int T_ranges, int* __restrict__ wide, int n_units) {
+  using Cfg = CausalFg<NW, NB>;
+  static_assert(NB == 1 || !REPAIR, "the repair pass takes the chunk as 32 positions");
+  constexpr int D = 64, NKC = D / 16, LDK = Cfg::LDK, LDV = Cfg::LDV, LDP = Cfg::LDP, NT = 64 * NW;
+  constexpr int UPW = 8 / NW;  // 4-column output groups a wave finishes per block
+  __shared__ __attribute__((aligned(16))) char smem[Cfg::BYTES];
+  const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
+  f16* Ql = reinterpret_cast<f16*>(smem);                            // [32][LDK]
+  f16* Kc = Ql + 32 * LDK;                                           // [NB][32][LDK]
+  bf16* Vc = reinterpret_cast<bf16*>(Kc + NB * 32 * LDK);            // [NB][32][LDV], columns permuted
+  char* wb = smem + Cfg::STAGE;
+  bf16* Pk = reinterpret_cast<bf16*>(wb + wave * Cfg::PK);           // own [64][LDP]
+  float* Red = reinterpret_cast<float*>(wb + NW * Cfg::PK);          // [NW][2][4][64] x f32x4
+  float2* Dm = reinterpret_cast<float2*>(wb + NW * (Cfg::PK + Cfg::RED));  // [NW][32]
+  float* S1v = reinterpret_cast<float*>(wb + NW * (Cfg::PK + Cfg::RED + Cfg::DM)) + wave * 128;  // own [64]
+  float* Csh = S1v + 64;                                                                          // own [64]
+  int* flagw = reinterpret_cast<int*>(wb + NW * (Cfg::PK + Cfg::RED + Cfg::DM + Cfg::VEC));       // [NW]
+
+  // One segment (seg, bhq) from its prefix.  First pass: one per workgroup.  Repair pass:
+  // the workgroups walk the n_units = B Hq T flags and redo the segments whose first pass
+  // met a wide block.
+  auto run_segment = [&](const int seg, const int bhq) {
+  const int b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv), bh = b * Hkv + hkv;
+  const int f0 = 64 * wave;
+  const bool active = f0 < m;
+  const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
+  const bf16* Qh = Q + (size_t)bhq * L * D;
+  bf16* Oh = out + (size_t)bhq * L * D;
+  const bf16* Kh = K + (size_t)bh * L * D;
+  const bf16* Vh = V + (size_t)bh * L * D;
+
+  // ---- state of the wave's features: W x log2 e (fp16), c_f, S_1 (lane = feature
+  // 32 i + col), the carry S_v [feature][value] of tile i and value tile vt --------------
+  f16x8 wf[2][NKC];
+  float cf[2], s1r[2];
+  f32x16 carry[2][2];
+  // bias operands of c_f: key side -(c_f) on the feature columns (0 while c_f is unset),
+  // query side +c_f on the feature rows; rebuilt only when c_f moves
+  f16x8 bk[2], bq[2];
+  const float* Pp = prefix + ((size_t)bh * T_ranges + seg) * (size_t)(D + 1) * m;
+  const float* Pc = prefix_c + ((size_t)bh * T_ranges + seg) * m;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    cf[i] = 0.f;
+    s1r[i] = 0.f;
+#pragma unroll
+    for (int vt = 0; vt < 2; ++vt) carry[i][vt] = zero16();
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) wf[i][kc] = zero_frag(f16x8{});
+    if (active) {
+      const int f = f0 + 32 * i;
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) load_w_frag(Wh + (size_t)(f + col) * D, kc, g, wf[i][kc]);
+      cf[i] = Pc[f + col];
+      s1r[i] = Pp[(size_t)D * m + f + col];
+#pragma unroll
+      for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(Pp + (size_t)(32 * vt + col) * m + f + 8 * r4 + 4 * g);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) carry[i][vt][4 * r4 + q] = v[q];
+        }
+    }
+    bk[i] = bias_cols(cf[i] == -INFINITY ? 0.f : cf[i], g, f16x8{});
+    bq[i] = bias_rows(cf[i] == -INFINITY ? 0.f : -cf[i], g, f16x8{});
+  }
+
+  // ---- staging: the block's Q, K (fp16) and V (bf16, columns permuted) ----------------
+  // range-checked buffer loads: rows past L read as zero
+  const unsigned head_bytes = (unsigned)L * (unsigned)D * 2u;
+  const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Qh, (short)0, (int)head_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, (int)head_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, (int)head_bytes, kBufWord3);
+  constexpr int CPR = D / 8, NCH = 32 * CPR;  // 16-byte chunks per row, per block
+  constexpr int PER = (NCH + NT - 1) / NT;
+  f32x4 pq_[PER], pk_[PER], pv_[PER];
+  auto prefetch = [&](int q0) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NT;
+      const int row = c / CPR, c0 = (c % CPR) * 8;
+      const unsigned off = c < NCH && q0 + row < L ? ((unsigned)(q0 + row) * D + c0) * 2u : head_bytes;
+      pq_[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)off, 0, 0));
+      pk_[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
+      pv_[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
+    }
+  };
+  auto stage = [&](f16* Kl, bf16* Vl) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int c = threadIdx.x + i * NT;
+      if (c < NCH) {
+        const int row = c / CPR, c0 = (c % CPR) * 8;
+        *reinterpret_cast<f16x8*>(Ql + row * LDK + c0) = to_wfrag(__builtin_bit_cast(bf16x8, pq_[i]));
+        *reinterpret_cast<f16x8*>(Kl + row * LDK + c0) = to_wfrag(__builtin_bit_cast(bf16x8, pk_[i]));
+        bf16* drow = Vl + row * LDV + (c0 & ~31);
+        *reinterpret_cast<float2*>(drow + vperm_inv(c0 & 31)) = float2{pv_[i][0], pv_[i][1]};
+        *reinterpret_cast<float2*>(drow + vperm_inv((c0 & 31) + 4)) = float2{pv_[i][2], pv_[i][3]};
+      }
+    }
+  };
+
+  bf16x2 one2;
+  one2[0] = one2[1] = (bf16)1.f;
+  bool wide_w = false;  // first pass: a block of this wave's features was wide
+
+  // Key exponents of tile i relative to c_f (C[key][feature], lane = feature).
+  auto key_exp = [&](const f16x8 (&kf)[NKC], const f16x8& biasA, int i) {
+    f32x16 ck = zero16();
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) ck = mma(kf[kc], wf[i][kc], ck);
+    return mma(biasA, bk[i], ck);
+  };
+  // A block is wide when one feature's key exponents spread by more than kSpread over the
+  // first keys of the sequence (an early query may see only keys far below the block's
+  // largest), or when a key passes c_f by more than kSpread (the rescaled carry of the
+  // queries before it would underflow).  Keys far below c_f are harmless once there is a
+  // carry: it holds the key that set c_f.  Masked keys sit near -kMaskedRow.
+  auto is_wide = [&](const f32x16& ck, float mx, bool init) {
+    if (!init) return mx > kSpread;
+    float mn = INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mn = fminf(mn, ck[r] > -0.5f * kMaskedRow ? ck[r] : INFINITY);
+    mn = pair_min(mn);
+    return mx - mn > kSpread;
+  };
+  auto row_max = [&](const f32x16& c) {
+    float mx = c[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, c[r]);
+    return pair_max(mx);
+  };
+
+  // bf16 operands of the chunk-start carry S_v (NB > 1): converted once per chunk
+  bf16x8 ca[2][2][2];
+
+  const int p_begin = seg * R, p_end = min(p_begin + R, L);
+  prefetch(p_begin);
+
+  for (int p0 = p_begin; p0 < p_end; p0 += 32) {
+    // block `slot` of its chunk (segments start on chunk boundaries)
+    const int slot = NB == 1 ? 0 : ((p0 - p_begin) >> 5) % NB;
+    f16* Kl = Kc + slot * 32 * LDK;
+    bf16* Vl = Vc + slot * 32 * LDV;
+    // every wave is past the previous block's second barrier: its staging reads are done
+    stage(Kl, Vl);
+    if (p0 + 32 < p_end) prefetch(p0 + 32);
+    __syncthreads();
+    const int pend = min(p0 + 32, L);
+    // step(lo, hi, check): the positions [lo, hi) of the block (keys outside masked, rows
+    // outside not stored).  The repair pass first tests the whole block (check) and
+    // returns true, having changed nothing, when it is wide; the caller then takes the
+    // block one position at a time.
+    auto step = [&](const int lo, const int hi, const bool check) -> bool {
+      if (REPAIR && !check) __syncthreads();  // the previous position's partials are read
+      f16x8 kf[NKC];
+#pragma unroll
+      for (int kc = 0; kc < NKC; ++kc) kf[kc] = load_frag_k(Kl + col * LDK, kc, g);
+      const float nrm = pair_sum(sumsq(kf));
+      const bool kin = p0 + col >= lo && p0 + col < hi;
+      const f16x8 biasA = bias_rows(kin ? 0.5f * kLog2e * nrm : kMaskedRow, g, f16x8{});
+      if (REPAIR && check) {
+        bool wd = false;
+        if (active) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const bool init = cf[i] == -INFINITY;
+            const f32x16 ck = key_exp(kf, biasA, i);
+            wd = wd || is_wide(ck, row_max(ck), init);
+          }
+        }
+        const bool any = wave_any(wd);
+        if (l == 0) flagw[wave] = any ? 1 : 0;
+        __syncthreads();
+        int a = 0;
+#pragma unroll
+        for (int p = 0; p < NW; ++p) a |= flagw[p];
+        if (a != 0) return true;
+      }
+
+      // the wave's partial to LDS: numerator (registers 4 r4 .. of value tile vt), den_w, M_w
+      auto put = [&](const f32x16 (&num)[2], float den, float Mw) {
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<f32x4*>(Red + ((size_t)((wave * 2 + vt) * 4 + r4) * 64 + l) * 4) =
+                f32x4{num[vt][4 * r4], num[vt][4 * r4 + 1], num[vt][4 * r4 + 2], num[vt][4 * r4 + 3]};
+        if (g == 0) Dm[wave * 32 + col] = float2{den, Mw};
+      };
+      if (!active) {
+        f32x16 num[2];
+        num[0] = num[1] = zero16();
+        put(num, 0.f, -INFINITY);
+      } else {
+        f32x16 num[2];
+        float Mw = -INFINITY;
+        // ---- key features: c_f, phi_K to the wave's LDS rows, S_1 ------------------------
+        bool shifted = false;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const bool init = cf[i] == -INFINITY;
+          f32x16 ck = key_exp(kf, biasA, i);
+          const float mx = row_max(ck);
+          if (!REPAIR && check) wide_w = wide_w || is_wide(ck, mx, init);
+          // c_f := c_f + shift; the carry and S_1 of the feature scale by 2^-shift (0 when
+          // it was unset)
+          const float shift = init || mx > kTau ? mx : 0.f;
+          if (g == 0) Csh[32 * i + col] = init ? -INFINITY : -shift;
+          s1r[i] = init ? 0.f : (shift != 0.f ? s1r[i] * fast_exp2(-shift) : s1r[i]);
+          // S_1 at the chunk start (the query side's inter-chunk denominator)
+          if (g == 0) {
+            if (slot == 0)
+              S1v[32 * i + col] = s1r[i];
+            else if (shift != 0.f)
+              S1v[32 * i + col] *= fast_exp2(-shift);
+          }
+          if (init || shift != 0.f) {
+            cf[i] = (init ? 0.f : cf[i]) + shift;
+            bk[i] = bias_cols(cf[i], g, f16x8{});
+            bq[i] = bias_rows(-cf[i], g, f16x8{});
+          }
+          shifted = shifted || shift != 0.f;
+          if (shift != 0.f) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) ck[r] -= shift;
+          }
+          f32x16 e;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) e[r] = fast_exp2(ck[r]);
+          bf16x8 ka[2];
+          acc_to_frags(e, ka);
+          float sum = 0.f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+              bf16x2 v2;
+              v2[0] = ka[h][j];
+              v2[1] = ka[h][j + 1];
+              sum = __builtin_amdgcn_fdot2_f32_bf16(v2, one2, sum, false);
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              bf16x4_t v;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) v[q] = ka[h][4 * hh + q];
+              *reinterpret_cast<bf16x4_t*>(Pk + (32 * i + col) * LDP + 8 * (2 * h + hh) + 4 * g) = v;
+            }
+          }
+          s1r[i] += pair_sum(sum);
+        }
+        asm volatile("" ::: "memory");  // the wave's LDS writes above before its reads below
+        if (wave_any(shifted)) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4 sh = *reinterpret_cast<const f32x4*>(Csh + 32 * i + 8 * r4 + 4 * g);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                const float fct = fast_exp2(sh[q]);
+#pragma unroll
+                for (int vt = 0; vt < 2; ++vt) {
+                  carry[i][vt][4 * r4 + q] *= fct;
+                  // element 4 (r4 % 2) + q of operand r4 / 2 is carry register 4 r4 + q
+                  if (NB > 1 && slot > 0) {
+                    const int j = 4 * (r4 & 1) + q;
+                    ca[i][vt][r4 >> 1][j] = (bf16)((float)ca[i][vt][r4 >> 1][j] * fct);
+                  }
+                }
+              }
+            }
+        }
+        if (NB > 1 && slot == 0) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int vt = 0; vt < 2; ++vt) acc_to_frags(carry[i][vt], ca[i][vt]);
+        }
+
+        // ---- query features (C[feature][query], lane = query) ----------------------------
+        f16x8 qf[NKC];
+#pragma unroll
+        for (int kc = 0; kc < NKC; ++kc) qf[kc] = load_frag_k(Ql + col * LDK, kc, g);
+        f32x16 cq[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          cq[i] = zero16();
+#pragma unroll
+          for (int kc = 0; kc < NKC; ++kc) cq[i] = mma(wf[i][kc], qf[kc], cq[i]);
+          cq[i] = mma(bq[i], bias_cols(0.f, g, f16x8{}), cq[i]);
+          Mw = fmaxf(Mw, row_max(cq[i]));
+        }
+        bf16x8 qa[2][2];
+        float dsh = 0.f;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          f32x16 e;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) e[r] = fast_exp2(cq[i][r] - Mw);
+          acc_to_frags(e, qa[i]);
+          // phi_Q . S_1 (S_1 of the positions before the block, at the block's c_f)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 sv = *reinterpret_cast<const f32x4*>(S1v + 32 * i + 8 * r4 + 4 * g);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) dsh = __builtin_fmaf(e[4 * r4 + q], sv[q], dsh);
+          }
+        }
+        dsh = pair_sum(dsh);
+
+        // ---- tril(phi_K phi_Q^T) over the wave's features: C[key][query] -----------------
+        f32x16 at = zero16();
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int h = 0; h < 2; ++h) at = mma(lds_frag_rows(Pk, LDP, 32 * i, 0, h), qa[i][h], at);
+        float dint = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          if (8 * (r >> 2) + 4 * g + (r & 3) > col) at[r] = 0.f;
+          dint += at[r];
+        }
+        {
+          bf16x8 ab[2];
+          acc_to_frags(at, ab);
+#pragma unroll
+          for (int vt = 0; vt < 2; ++vt)
+            num[vt] = mma(lds_frag_rows(Vl, LDV, 0, 32 * vt, 1), ab[1],
+                          mma(lds_frag_rows(Vl, LDV, 0, 32 * vt, 0), ab[0], zero16()));
+        }
+        // ---- the chunk's earlier blocks i < slot (NB > 1): phi_Q phi_K,i^T [V_i, 1] ------
+        // phi_K,i comes straight in the operand layout (C[feature][key], lane = key) from
+        // the chunk's staged K at the current c_f.
+        if constexpr (NB > 1) {
+          if (slot > 0) {
+            f16x8 br[2];
+#pragma unroll
+            for (int t = 0; t < 2; ++t) br[t] = bias_rows(cf[t], g, f16x8{});
+            for (int bi = 0; bi < slot; ++bi) {
+              const f16* Ki = Kc + bi * 32 * LDK;
+              f16x8 kfi[NKC];
+#pragma unroll
+              for (int kc = 0; kc < NKC; ++kc) kfi[kc] = load_frag_k(Ki + col * LDK, kc, g);
+              const f16x8 bcol = bias_cols(0.5f * kLog2e * pair_sum(sumsq(kfi)), g, f16x8{});
+              f32x16 ai = zero16();
+#pragma unroll
+              for (int t = 0; t < 2; ++t) {
+                f32x16 e = zero16();
+#pragma unroll
+                for (int kc = 0; kc < NKC; ++kc) e = mma(wf[t][kc], kfi[kc], e);
+                e = mma(br[t], bcol, e);
+#pragma unroll
+                for (int r = 0; r < 16; ++r) e[r] = fast_exp2(e[r]);
+                bf16x8 kt[2];
+                acc_to_frags(e, kt);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) ai = mma(kt[h], qa[t][h], ai);
+              }
+#pragma unroll
+              for (int r = 0; r < 16; ++r) dint += ai[r];
+              bf16x8 abi[2];
+              acc_to_frags(ai, abi);
+              const bf16* Vi = Vc + bi * 32 * LDV;
+#pragma unroll
+              for (int vt = 0; vt < 2; ++vt)
+                num[vt] = mma(lds_frag_rows(Vi, LDV, 0, 32 * vt, 1), abi[1],
+                              mma(lds_frag_rows(Vi, LDV, 0, 32 * vt, 0), abi[0], num[vt]));
+            }
+          }
+        }
+        const float den = dsh + pair_sum(dint);
+
+        // ---- inter-chunk numerator and carry update per value tile -------------------------
+#pragma unroll
+        for (int vt = 0; vt < 2; ++vt) {
+          bf16x8 vo[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) vo[h] = lds_frag_rows(Vl, LDV, 0, 32 * vt, h);
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            if constexpr (NB == 1) {
+              bf16x8 cb[2];
+              acc_to_frags(carry[i][vt], cb);
+#pragma unroll
+              for (int h = 0; h < 2; ++h) num[vt] = mma(cb[h], qa[i][h], num[vt]);
+            } else {
+#pragma unroll
+              for (int h = 0; h < 2; ++h) num[vt] = mma(ca[i][vt][h], qa[i][h], num[vt]);
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const bf16* prow = Pk + (32 * i + col) * LDP + 16 * h + 4 * g;
+              const bf16x4_t plo = *reinterpret_cast<const bf16x4_t*>(prow);
+              const bf16x4_t phi = *reinterpret_cast<const bf16x4_t*>(prow + 8);
+              bf16x8 pa;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                pa[q] = plo[q];
+                pa[q + 4] = phi[q];
+              }
+              carry[i][vt] = mma(pa, vo[h], carry[i][vt]);
+            }
+        }
+        asm volatile("" ::: "memory");  // this block's LDS reads before the next block's writes
+        put(num, den, Mw);
+      }
+      // ---- the partials meet ----------------------------------------------------------------
+      __syncthreads();
+      float M = -INFINITY;
+#pragma unroll
+      for (int p = 0; p < NW; ++p) M = fmaxf(M, Dm[p * 32 + col].y);
+      float sc[NW];
+      float dd = 0.f;
+#pragma unroll
+      for (int p = 0; p < NW; ++p) {
+        const float2 dm = Dm[p * 32 + col];
+        sc[p] = fast_exp2(dm.y - M);  // 0 for a wave without features (M_w = -inf)
+        dd = __builtin_fmaf(sc[p], dm.x, dd);
+      }
+      const float inv = __builtin_amdgcn_rcpf(dd);
+      const int pos = p0 + col;
+      if (pos >= lo && pos < hi) {
+        // group u = wave UPW + j: value tile u / 4, registers 4 (u % 4) .. + 3 = columns
+        // 32 (u / 4) + 16 g + 4 (u % 4) .. + 3
+        bf16x4_t o[UPW];
+#pragma unroll
+        for (int j = 0; j < UPW; ++j) {
+          const int u = wave * UPW + j, vt = u >> 2, r4 = u & 3;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int p = 0; p < NW; ++p) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(Red + ((size_t)((p * 2 + vt) * 4 + r4) * 64 + l) * 4);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] = __builtin_fmaf(sc[p], v[q], acc[q]);
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[j][q] = (bf16)(acc[q] * inv);
+        }
+        bf16* orow = Oh + (size_t)pos * D + 16 * g;
+        if constexpr (UPW == 1) {
+          const int u = wave;
+          *reinterpret_cast<bf16x4_t*>(orow + 32 * (u >> 2) + 4 * (u & 3)) = o[0];
+        } else {
+#pragma unroll
+          for (int j = 0; j < UPW; j += 2) {
+            const int u = wave * UPW + j;
+            bf16x8 o8;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              o8[q] = o[j][q];
+              o8[q + 4] = o[j + 1][q];
+            }
+            *reinterpret_cast<bf16x8*>(orow + 32 * (u >> 2) + 4 * (u & 3)) = o8;
+          }
+        }
+      }
+      return false;
+    };
+    if constexpr (REPAIR) {
+      // the whole block with the wide test, then (when wide) its positions one at a time
+      for (int q = p0 - 1; q < pend; ++q) {
+        const bool whole = q < p0;
+        if (!step(whole ? p0 : q, whole ? pend : q + 1, whole) && whole) break;
+      }
+    } else {
+      step(p0, pend, true);
+    }
+  }
+  if (!REPAIR) {
+    const bool any = wave_any(wide_w);
+    if (l == 0) flagw[wave] = any ? 1 : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int a = 0;
+#pragma unroll
+      for (int p = 0; p < NW; ++p) a |= flagw[p];
+      wide[(size_t)bhq * T_ranges + seg] = a;
+    }
+  }
+  };
+  if constexpr (REPAIR) {
+    for (int u = blockIdx.x; u < n_units; u += gridDim.x)
+      if (wide[u] != 0) run_segment(u % T_ranges, u / T_ranges);
+  } else {
+    run_segment(blockIdx.x, blockIdx.y);
+  }
+}
+
 // Exclusive scan of the segment summaries gs / gc with per-feature stabilisers into the
 // prefix region of the workspace.
 favor_status launch_causal_scan_pf(const Plan& s, char* ws, hipStream_t st) {
@@ -530,10 +1057,49 @@ favor_status launch_causal_scan_pf(const Plan& s, char* ws, hipStream_t st) {
 
 bool causal_v_supported(const Plan& s) { return s.dtype == FAVOR_BF16 && (s.d == 64 || s.m <= 256); }
 
-// The chunked pass of causal_v_kernel from the prefixes launch_causal_scan_pf wrote.
+bool causal_chunk_supported(const Plan& s) {
+  if (s.chunk == 32) return true;
+  // intra-chunk blocks above 32 positions: bf16 d = 64, and 256 only up to m = 256 (the
+  // chunk's staged K and V beside the partials of eight waves do not fit in LDS)
+  return s.dtype == FAVOR_BF16 && s.d == 64 && (s.chunk < 256 || s.m <= 256);
+}
+
+namespace {
+
+template <int NW, int NB, bool RP>
+void launch_fg(const Plan& s, dim3 grid, const bf16* q, const bf16* k, const bf16* v, const float* W,
+               const float* prefix, const float* prefix_c, bf16* o, int* wide, hipStream_t st) {
+  const int n_units = s.T * s.B * s.Hq;
+  // the repair pass: one workgroup per CU at most, walking the segment flags
+  const dim3 g = RP ? dim3((unsigned)(n_units < kCUs ? n_units : kCUs)) : grid;
+  hipLaunchKernelGGL((causal_fg_kernel<NW, NB, RP>), g, dim3(64 * NW), 0, st, q, k, v, W, prefix, prefix_c, o, s.L,
+                     s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, wide, n_units);
+}
+
+template <int NB, bool RP>
+void launch_fg_nw(const Plan& s, dim3 grid, const bf16* q, const bf16* k, const bf16* v, const float* W,
+                  const float* prefix, const float* prefix_c, bf16* o, int* wide, hipStream_t st) {
+  // one wave per 64 features, NW rounded up to 1, 2, 4 or 8
+  const int nw = s.m / 64;
+  if (nw <= 1)
+    launch_fg<1, NB, RP>(s, grid, q, k, v, W, prefix, prefix_c, o, wide, st);
+  else if (nw <= 2)
+    launch_fg<2, NB, RP>(s, grid, q, k, v, W, prefix, prefix_c, o, wide, st);
+  else if (nw <= 4)
+    launch_fg<4, NB, RP>(s, grid, q, k, v, W, prefix, prefix_c, o, wide, st);
+  else if constexpr (NB < 8)
+    launch_fg<8, NB, RP>(s, grid, q, k, v, W, prefix, prefix_c, o, wide, st);
+}
+
+}  // namespace
+
+// The chunked pass (causal_fg_kernel for d = 64, causal_v_kernel for d = 128) from the
+// prefixes launch_causal_scan_pf wrote: the first pass over every segment, then the repair
+// pass (its workgroups return at once unless their segment met a wide block), which takes
+// the chunk as 32 positions.
 favor_status launch_causal_v(const Plan& s, const void* Q, const void* K, const void* V, const float* W, void* out,
                              char* ws, hipStream_t st) {
-  if (!causal_v_supported(s)) return FAVOR_ERR_UNSUPPORTED;
+  if (!causal_v_supported(s) || !causal_chunk_supported(s)) return FAVOR_ERR_UNSUPPORTED;
   const float* prefix = reinterpret_cast<const float*>(ws + s.off_p);
   const float* prefix_c = reinterpret_cast<const float*>(ws + s.off_pc);
   const bf16* q = static_cast<const bf16*>(Q);
@@ -542,25 +1108,22 @@ favor_status launch_causal_v(const Plan& s, const void* Q, const void* K, const 
   bf16* o = static_cast<bf16*>(out);
   int* wide = reinterpret_cast<int*>(ws + s.off_wide);
   const dim3 grid(s.T, s.B * s.Hq);
-  // first pass, then the repair pass (its workgroups return at once unless their segment
-  // met a wide block)
-  auto run = [&](auto repair) -> bool {
-    constexpr bool RP = decltype(repair)::value;
-    if (s.d == 64) {
-      if (s.m <= 256)
-        hipLaunchKernelGGL((causal_v_kernel<64, 8, 2, RP>), grid, dim3(64 * 2 * 2), 0, st, q, k, v, W, prefix,
-                           prefix_c, o, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, wide);
-      else
-        hipLaunchKernelGGL((causal_v_kernel<64, 16, 4, RP>), grid, dim3(64 * 2 * 4), 0, st, q, k, v, W, prefix,
-                           prefix_c, o, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, wide);
-    } else {
-      hipLaunchKernelGGL((causal_v_kernel<128, 8, 2, RP>), grid, dim3(64 * 4 * 2), 0, st, q, k, v, W, prefix,
-                         prefix_c, o, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, wide);
+  if (s.d == 64) {
+    switch (s.chunk) {
+      case 32: launch_fg_nw<1, false>(s, grid, q, k, v, W, prefix, prefix_c, o, wide, st); break;
+      case 64: launch_fg_nw<2, false>(s, grid, q, k, v, W, prefix, prefix_c, o, wide, st); break;
+      case 128: launch_fg_nw<4, false>(s, grid, q, k, v, W, prefix, prefix_c, o, wide, st); break;
+      default: launch_fg_nw<8, false>(s, grid, q, k, v, W, prefix, prefix_c, o, wide, st); break;
     }
-    return hipGetLastError() == hipSuccess;
-  };
-  if (!run(std::false_type{})) return FAVOR_ERR_HIP;
-  if (!run(std::true_type{})) return FAVOR_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+    launch_fg_nw<1, true>(s, grid, q, k, v, W, prefix, prefix_c, o, wide, st);
+    return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+  }
+  hipLaunchKernelGGL((causal_v_kernel<128, 8, 2, false>), grid, dim3(64 * 4 * 2), 0, st, q, k, v, W, prefix, prefix_c,
+                     o, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, wide);
+  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  hipLaunchKernelGGL((causal_v_kernel<128, 8, 2, true>), grid, dim3(64 * 4 * 2), 0, st, q, k, v, W, prefix, prefix_c,
+                     o, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, wide);
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 

@@ -25,6 +25,10 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
   if (p->num_features % 64 != 0 || p->num_features > 512) return FAVOR_ERR_UNSUPPORTED;
   if (p->chunk != 0 && p->chunk != 32 && p->chunk != 64 && p->chunk != 128 && p->chunk != 256)
     return FAVOR_ERR_UNSUPPORTED;
+  // intra-chunk blocks above 32 positions: bf16 with d = 64 only, C = 256 up to m = 256
+  if (p->mode == FAVOR_CAUSAL && p->chunk > 32 &&
+      (p->dtype != FAVOR_BF16 || p->head_dim != 64 || (p->chunk == 256 && p->num_features > 256)))
+    return FAVOR_ERR_UNSUPPORTED;
   const long long elems_q = (long long)p->batch * p->heads_q * p->seq_len * p->head_dim;
   const long long elems_kv = (long long)p->batch * p->heads_kv * p->seq_len * p->head_dim;
   if (elems_q >= (1LL << 31) || elems_kv >= (1LL << 31)) return FAVOR_ERR_UNSUPPORTED;

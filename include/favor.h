@@ -66,10 +66,14 @@ typedef enum { FAVOR_BIDIRECTIONAL = 0, FAVOR_CAUSAL = 1 } favor_mode;
  * in [64, 512]; heads_q % heads_kv == 0; heads_w in {1, heads_kv}; seq_len >= 1;
  * batch * heads_q * seq_len * head_dim < 2^31; one head's seq_len * head_dim elements under
  * 2^31 bytes; batch * heads_q <= 65535 (otherwise
- * FAVOR_ERR_UNSUPPORTED).  chunk (causal only) is the granularity
- * of the sequence segments that run in parallel (each segment a multiple of it): 0
- * (library default, 32) or one of 32, 64, 128, 256; the result does not depend on it
- * beyond rounding.  Ignored for bidirectional problems. */
+ * FAVOR_ERR_UNSUPPORTED).  chunk (causal only) is the intra-chunk block C of the chunked
+ * prefix scan: the positions of one chunk see each other through a masked C x C product
+ * tril(phi(Q_c) phi(K_c)^T) [V_c, 1] and the earlier chunks through the carried state
+ * S_<c, which is updated once per chunk.  0 (library default, 32) or one of 32, 64, 128,
+ * 256; C above 32 is built for bf16 problems with head_dim 64 (and C = 256 for
+ * num_features <= 256), other causal problems take 0 or 32 (otherwise
+ * FAVOR_ERR_UNSUPPORTED).  The sequence segments that run in parallel are multiples of C.
+ * The result does not depend on C beyond rounding.  Ignored for bidirectional problems. */
 typedef struct {
   int32_t batch, heads_q, heads_kv, heads_w;
   int32_t seq_len, head_dim, num_features;

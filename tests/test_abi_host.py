@@ -47,6 +47,10 @@ BAD = [
     (dict(dtype=7), _lib.FAVOR_ERR_UNSUPPORTED),
     (dict(mode=2), _lib.FAVOR_ERR_UNSUPPORTED),
     (dict(mode=_lib.FAVOR_CAUSAL, chunk=48), _lib.FAVOR_ERR_UNSUPPORTED),
+    # intra-chunk blocks above 32 positions: bf16 d = 64 only, 256 up to m = 256
+    (dict(mode=_lib.FAVOR_CAUSAL, chunk=64, head_dim=128), _lib.FAVOR_ERR_UNSUPPORTED),
+    (dict(mode=_lib.FAVOR_CAUSAL, chunk=128, dtype=_lib.FAVOR_F32), _lib.FAVOR_ERR_UNSUPPORTED),
+    (dict(mode=_lib.FAVOR_CAUSAL, chunk=256, num_features=320), _lib.FAVOR_ERR_UNSUPPORTED),
     (dict(batch=1 << 12, heads_q=1 << 8, heads_kv=1 << 8, heads_w=1, seq_len=1 << 14),
      _lib.FAVOR_ERR_UNSUPPORTED),                           # more than 2^31 elements
     (dict(batch=1 << 12, heads_q=1 << 4, heads_kv=1 << 4, heads_w=1, seq_len=1),
@@ -54,6 +58,17 @@ BAD = [
     (dict(batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=1 << 24, head_dim=64),
      _lib.FAVOR_ERR_UNSUPPORTED),                           # one bf16 head of 2^31 bytes
 ]
+
+
+GOOD_CAUSAL_CHUNKS = [
+    dict(chunk=0, head_dim=128), dict(chunk=32, dtype=_lib.FAVOR_F32), dict(chunk=64),
+    dict(chunk=128, num_features=512), dict(chunk=256, num_features=256),
+]
+
+
+@pytest.mark.parametrize("kw", GOOD_CAUSAL_CHUNKS)
+def test_causal_chunk_values_accepted(kw):
+    assert _lib.workspace_bytes(_p(mode=_lib.FAVOR_CAUSAL, **kw)) > 0
 
 
 @pytest.mark.parametrize("kw,status", BAD)
@@ -90,11 +105,11 @@ def test_causal_wide_head_workspace_holds_row_partials(m):
     """Causal d = 128 with m > 256 runs its chunk kernel as two launches over feature ranges,
     the first writing a float32 partial of d + 4 values per output row: the workspace must
     hold those B Hq L rows besides the segment summaries and their prefixes."""
-    # 16 query heads on one kv head and segments of >= 256 positions (at most 4): the
-    # summaries are small next to the row partials, so a layout without them falls short
+    # 16 query heads on one kv head: the summaries of one segment are small next to the
+    # row partials, so a layout without them falls short
     B, Hq, Hkv, L, d = 2, 16, 1, 1000, 128
     p = _p(batch=B, heads_q=Hq, heads_kv=Hkv, heads_w=Hkv, seq_len=L, head_dim=d, num_features=m,
-           mode=_lib.FAVOR_CAUSAL, chunk=256)
+           mode=_lib.FAVOR_CAUSAL, chunk=0)
     partials = 4 * B * Hq * L * (d + 4)
     one_segment = 4 * (d + 1) * m * B * Hkv  # summaries (and again prefixes) of one segment
     assert 2 * 4 * one_segment + 64 * 1024 < partials

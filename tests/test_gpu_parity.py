@@ -101,17 +101,39 @@ def test_small_full_parity(w):
     assert err < TOL[w.dtype]
 
 
-@pytest.mark.parametrize("chunk", [64, 256])
-def test_causal_split_features_chunk_sizes(chunk):
-    """d = 128 with m > 256 (two launches over feature ranges) with segments of other lengths
-    and a ragged tail."""
-    w = _small("c3_causal_bf16", batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=777, head_dim=128,
+@pytest.mark.parametrize("L", [777, 2900])
+def test_causal_split_features_ragged(L):
+    """d = 128 with m > 256 (two launches over feature ranges) with one and several segments
+    and a ragged tail (its intra-chunk block is 32 positions)."""
+    w = _small("c3_causal_bf16", batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=L, head_dim=128,
                num_features=384)
-    _say(f"case {w} chunk={chunk}")
+    _say(f"case {w}")
     Q, K, V, W = I.make_inputs(w, seed=4)
-    y = _run(w, Q, K, V, W, chunk=chunk).float().cpu().numpy()
+    y = _run(w, Q, K, V, W, chunk=32).float().cpu().numpy()
     ref = O.favor_attention(Q, K, V, W, causal=True)
     assert O.rowwise_rel_err(y, ref) < TOL[w.dtype]
+
+
+# intra-chunk blocks of 64-256 positions over feature counts that give 1, 2, 3 (of 4) and
+# 8 waves, ragged tails, MQA groups; chunk 256 only up to m = 256
+CHUNK_SHAPES = [
+    (64, 64, 301, 1, 1), (128, 128, 700, 2, 2), (256, 192, 999, 4, 2), (64, 512, 640, 2, 1),
+    (128, 512, 1001, 1, 1), (256, 256, 97, 2, 2), (128, 64, 1300, 3, 3),
+]
+
+
+@pytest.mark.parametrize("chunk,m,L,hq,hkv", CHUNK_SHAPES,
+                         ids=[f"C{c}-m{m}-L{L}-G{hq // hkv}" for c, m, L, hq, hkv in CHUNK_SHAPES])
+def test_causal_intra_chunk_blocks(chunk, m, L, hq, hkv):
+    w = _small("c3_causal_bf16", batch=1, heads_q=hq, heads_kv=hkv, heads_w=hkv, seq_len=L, num_features=m)
+    _say(f"case {w} chunk={chunk}")
+    Q, K, V, W = I.make_inputs(w, seed=6)
+    y = _run(w, Q, K, V, W, chunk=chunk).float().cpu().numpy()
+    ref = O.favor_attention(Q, K, V, W, causal=True)
+    err = O.rowwise_rel_err(y, ref)
+    _say(f"  rowwise rel err {err:.3e}")
+    assert np.isfinite(y).all()
+    assert err < TOL[w.dtype]
 
 
 @pytest.mark.parametrize("chunk", [0, 32, 64, 128, 256])
@@ -176,20 +198,23 @@ def test_large_norm_inputs(causal, dtype):
     assert err < TOL[w.dtype]
 
 
-@pytest.mark.parametrize("base,kw", [
-    ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1000)),
-    ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=301, head_dim=128)),
-    ("c5_causal_long_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=700, heavy_fraction=0.0)),
-], ids=["d64m256", "d128m256", "d64m512"])
-def test_causal_keys_far_apart(base, kw):
+@pytest.mark.parametrize("base,kw,chunk", [
+    ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1000), 0),
+    ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=301, head_dim=128), 0),
+    ("c5_causal_long_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=700, heavy_fraction=0.0), 0),
+    ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1000), 128),
+    ("c5_causal_long_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=700, heavy_fraction=0.0), 64),
+], ids=["d64m256", "d128m256", "d64m512", "d64m256-C128", "d64m512-C64"])
+def test_causal_keys_far_apart(base, kw, chunk):
     """K scaled by 8 (exact in bf16): |k|^2 / 2 alone spreads the key exponents over hundreds
     of log2 units, so early queries whose keys all sit far below a later key of the same block
-    (or of the sequence) must not lose their terms to underflow."""
+    (or of the sequence) must not lose their terms to underflow.  With intra-chunk blocks
+    above 32 positions the stabilisers also move in the middle of a chunk."""
     w = _small(base, **kw)
-    _say(f"case {w} K x8")
+    _say(f"case {w} K x8 chunk={chunk}")
     Q, K, V, W = I.make_inputs(w, seed=4)
     K = K * np.float32(8)
-    y = _run(w, Q, K, V, W).float().cpu().numpy()
+    y = _run(w, Q, K, V, W, chunk=chunk).float().cpu().numpy()
     ref = O.favor_attention(Q, K, V, W, causal=True)
     err = O.rowwise_rel_err(y, ref)
     _say(f"  rowwise rel err {err:.3e}")
