@@ -1947,15 +1947,6 @@ namespace {
 
 inline int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// Records ev[i] (if given) before the i-th kernel of a call and after the last one.
-struct Marks {
-  hipEvent_t* ev;
-  int n;
-  bool mark(int i, hipStream_t st) const {
-    return ev == nullptr || i >= n || hipEventRecord(ev[i], st) == hipSuccess;
-  }
-};
-
 template <class T, int D>
 favor_status launch_kv_summary(const Plan& s, const T* K, const T* V, const float* W, float* gs, float* gc,
                                char* ws, hipStream_t st) {
@@ -1984,6 +1975,10 @@ favor_status launch_kv_summary(const Plan& s, const T* K, const T* V, const floa
 template <class T, int D>
 favor_status run_bidirectional(const Plan& s, const T* Q, const T* K, const T* V, const float* W, T* out,
                                char* ws, hipStream_t st, const Marks& mk) {
+  if constexpr (std::is_same<T, float>::value) {
+    // float32: the key side and the readout spread over feature tiles
+    return launch_small_f32(s, Q, K, V, W, out, ws, st, mk);
+  }
   float* gs = reinterpret_cast<float*>(ws + s.off_gs);
   float* gc = reinterpret_cast<float*>(ws + s.off_gc);
   if (!mk.mark(0, st)) return FAVOR_ERR_HIP;

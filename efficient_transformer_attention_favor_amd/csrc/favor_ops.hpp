@@ -7,6 +7,15 @@
 
 namespace favor {
 
+// Records ev[i] (if given) before the i-th kernel of a call and after the last one.
+struct Marks {
+  hipEvent_t* ev;
+  int n;
+  bool mark(int i, hipStream_t st) const {
+    return ev == nullptr || i >= n || hipEventRecord(ev[i], st) == hipSuccess;
+  }
+};
+
 // The feature map of the queries (side 0, row stabilisers) or keys (side 1, one stabiliser
 // per (batch, kv head)) as float32 [rows][m], stabilisers in natural-log units in c.  With
 // Lo > L each head gets Lo rows of phi (and of c for queries), rows L..Lo-1 written as zero.
@@ -32,5 +41,10 @@ bool causal_v_supported(const Plan& s);
 favor_status launch_causal_scan_pf(const Plan& s, char* ws, hipStream_t st);
 favor_status launch_causal_v(const Plan& s, const void* Q, const void* K, const void* V, const float* W, void* out,
                              char* ws, hipStream_t st);
+
+// Bidirectional float32 forward: the key side per (kv head, range, 32-feature tile), then
+// the readout with the feature tiles over the waves (ranges merged in the readout).
+favor_status launch_small_f32(const Plan& s, const float* Q, const float* K, const float* V, const float* W,
+                              float* out, char* ws, hipStream_t st, const Marks& mk);
 
 }  // namespace favor

@@ -89,6 +89,15 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
         T = t;
       }
     }
+  } else if (q.dtype == FAVOR_F32) {
+    // float32: about kSmallKeyTarget key-side workgroups of one 32-feature tile each, every
+    // range at least 4 x 32 positions (one block per wave), and at most kSmallRanges ranges:
+    // each range the readout merges costs it about one dependent round of loads
+    unit = 4 * kTile;
+    T = ceil_div(kSmallKeyTarget, (long long)q.BH * (q.m / kTile));
+    const int max_t = ceil_div(q.L, unit);
+    if (T > max_t) T = max_t;
+    if (T > kSmallRanges) T = kSmallRanges;
   } else {
     unit = 4 * kTile;
     T = (int)((kKeyTarget + (long long)q.BH * nfs / 2) / ((long long)q.BH * nfs));

@@ -16,6 +16,8 @@ constexpr int kCUs = 256;           // compute units of the MI355X (launch-geome
 constexpr int kSegGroup = 4;        // causal segments per key-side workgroup in the cost model
 constexpr long long kSumUnitBytes = 12LL << 20;  // summary traffic worth one block step (causal cost model)
 constexpr int kReadoutTarget = 256; // readout workgroups a pass aims for
+constexpr int kSmallKeyTarget = 512;  // float32 key-side workgroups (one 32-feature tile each)
+constexpr int kSmallRanges = 4;       // float32 position ranges per kv head at most
 // Ready-to-copy LDS images for the bf16 bidirectional readout (one position range per kv
 // head): fp16 W rows of d+8, bf16 S'^T rows of kImgMP+8 (d+2 rows: values, ones, zeros),
 // and two 16-byte bias operands per feature.  Sizes are whole 1 KB blocks (LDS DMA unit).
