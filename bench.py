@@ -116,7 +116,8 @@ def kernel_names(w, p=None):
 
 
 # The sources the forward kernels (favor_attn_fwd) are built from.
-FORWARD_SOURCES = ("favor_device.hpp", "favor_kernels.hip", "favor_plan.cpp", "favor_plan.hpp")
+FORWARD_SOURCES = ("favor_device.hpp", "favor_kernels.hip", "favor_causal.hip", "favor_small.hip", "favor_ops.hpp",
+                   "favor_plan.cpp", "favor_plan.hpp")
 
 
 def source_digest():
@@ -305,6 +306,7 @@ def main():
         log("timing the CPU oracle ...")
         res["cpu_baseline"] = cpu_baseline(w, Q, K, V, W, args.cpu_budget)
     del Q, K, V, W
+    res["launch_floor_us"] = launch_floor_us()
     if args.also:
         # the other benchmark workloads (and the causal chunk sweep) in the same run, each
         # timed the same way on its own inputs; keys are workload names (with the chunk)
@@ -324,6 +326,24 @@ def main():
     if args.out:
         with open(args.out, "a") as f:
             f.write(line + "\n")
+
+
+def launch_floor_us(n=2000):
+    """Microseconds per launch of a one-element fill kernel issued back to back on the current
+    stream: the floor under any kernel of a call (a call with k kernels costs at least k of
+    these)."""
+    import torch
+    x = torch.zeros(1, device="cuda")
+    for _ in range(50):
+        x.fill_(1.0)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(n):
+        x.fill_(1.0)
+    e.record()
+    torch.cuda.synchronize()
+    return round(s.elapsed_time(e) / n * 1e3, 3)
 
 
 def _also_list(spec, main_name, main_chunk):
