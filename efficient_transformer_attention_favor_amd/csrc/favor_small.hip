@@ -17,7 +17,7 @@
 //   ps[D + 1][32] (value rows in natural order, row D the ones column), pc[32] = c_f.
 //
 // Readout (small_readout_f32_kernel): one workgroup per (kv head, 32-row tile of the G
-// query heads' rows); wave w owns feature tiles w, w + NW, ...  It merges the ranges'
+// query heads' rows); wave w owns feature tiles w, w + NW, ... (NW = 4)  It merges the ranges'
 // partials of its tiles into MFMA operands (S_f rescaled to the largest c_f), then
 //   C[feature][query] = W Q^T + c_f,  M_w = the row maxima over its features,
 //   phi = 2^(C - M_w),  num_w = S_v^T phi,  den_w = S_1 . phi,
@@ -217,7 +217,9 @@ __global__ void __launch_bounds__(256) small_kv_f32_kernel(const float* __restri
 // readout
 // ======================================================================================
 template <int D> struct SmallRo {
-  static constexpr int NW = D == 64 ? 8 : 4;  // waves at most (feature tiles beyond go round)
+  // waves at most (feature tiles beyond go round); four waves leave each one the whole
+  // register file of its SIMD, which the merged partials and two accumulator chains need
+  static constexpr int NW = 4;
   static constexpr int NDT = D / 32;
   static constexpr int LDQ = D + 1;
 };
@@ -242,6 +244,78 @@ __global__ void __launch_bounds__(64 * SmallRo<D>::NW) small_readout_f32_kernel(
   float* Ob = out + ((size_t)b * Hq + (size_t)hkv * G) * L * D;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
 
+  // ---- per feature tile: the W operand and the ranges' partials merged at the largest c_f
+  // (A operand: step s carries contraction index 2 s + g; register r of this lane group is
+  // feature 8 (r/4) + 4 g + r%4 of the tile).  The loads of TG ranges and RB register groups
+  // go out together (past the last range the last one is re-read with weight 0).
+  float wv[NS], cf[16], sv[NDT][16], s1[16];
+  auto prep = [&](int ft) {
+    const float* wr = Wh + (size_t)(32 * ft + col) * D;
+#pragma unroll
+    for (int c = 0; c < D / 4; ++c) {
+      const f32x4 w4 = *reinterpret_cast<const f32x4*>(wr + 4 * c);
+      wv[2 * c] = g == 0 ? w4[0] : w4[1];
+      wv[2 * c + 1] = g == 0 ? w4[2] : w4[3];
+    }
+    constexpr int TG = 4, RB = D == 64 ? 4 : 1;
+    const float* pch = pc + (size_t)bh * T_ranges * m + 32 * ft;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cf[r] = -INFINITY;
+    for (int t0 = 0; t0 < T_ranges; t0 += TG) {
+      f32x4 cv[TG][4];
+#pragma unroll
+      for (int u = 0; u < TG; ++u)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+          cv[u][r4] = *reinterpret_cast<const f32x4*>(pch + (size_t)min(t0 + u, T_ranges - 1) * m + 8 * r4 + 4 * g);
+#pragma unroll
+      for (int u = 0; u < TG; ++u)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) cf[4 * r4 + q] = fmaxf(cf[4 * r4 + q], cv[u][r4][q]);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s1[r] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) sv[dt][r] = 0.f;
+    }
+    for (int t0 = 0; t0 < T_ranges; t0 += TG) {
+#pragma unroll
+      for (int rb = 0; rb < 4; rb += RB) {
+        f32x4 cv[RB][TG], ov[RB][TG], vv[RB][TG][NDT];
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+#pragma unroll
+          for (int u = 0; u < TG; ++u) {
+            const int r4 = rb + j, t = min(t0 + u, T_ranges - 1);
+            const float* src = ps + (((size_t)bh * T_ranges + t) * NFT + ft) * (size_t)(D + 1) * 32;
+            cv[j][u] = *reinterpret_cast<const f32x4*>(pch + (size_t)t * m + 8 * r4 + 4 * g);
+            ov[j][u] = *reinterpret_cast<const f32x4*>(src + (size_t)D * 32 + 8 * r4 + 4 * g);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+              vv[j][u][dt] = *reinterpret_cast<const f32x4*>(src + (size_t)(32 * dt + col) * 32 + 8 * r4 + 4 * g);
+          }
+#pragma unroll
+        for (int j = 0; j < RB; ++j)
+#pragma unroll
+          for (int u = 0; u < TG; ++u)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int r = 4 * (rb + j) + q;
+              const float f = t0 + u < T_ranges ? fast_exp2(cv[j][u][q] - cf[r]) : 0.f;
+              s1[r] = __builtin_fmaf(f, ov[j][u][q], s1[r]);
+#pragma unroll
+              for (int dt = 0; dt < NDT; ++dt) sv[dt][r] = __builtin_fmaf(f, vv[j][u][dt][q], sv[dt][r]);
+            }
+      }
+    }
+  };
+  // one feature tile per wave: prepared once for all row tiles of the workgroup
+  const bool once = NFT <= nw;
+  if (once) prep(wave);
+
   for (size_t tile = tile0; tile * 32 < rows; tile += tiles_per_head) {
     const size_t row0 = tile * 32;
     __syncthreads();  // the previous tile's readers of Ql, Red, Dm are done
@@ -260,60 +334,7 @@ __global__ void __launch_bounds__(64 * SmallRo<D>::NW) small_readout_f32_kernel(
     for (int dt = 0; dt < NDT; ++dt) num[dt] = zero16();
     float den = 0.f, Mw = -INFINITY;
     for (int ft = wave; ft < NFT; ft += nw) {
-      // W operand (A, lane = feature): step s carries contraction index 2 s + g; its loads
-      // go out first and overlap the merge below
-      float wv[NS];
-      {
-        const float* wr = Wh + (size_t)(32 * ft + col) * D;
-#pragma unroll
-        for (int c = 0; c < D / 4; ++c) {
-          const f32x4 w4 = *reinterpret_cast<const f32x4*>(wr + 4 * c);
-          wv[2 * c] = g == 0 ? w4[0] : w4[1];
-          wv[2 * c + 1] = g == 0 ? w4[2] : w4[3];
-        }
-      }
-      // ---- the ranges' partials of tile ft, merged at the largest c_f -------------------
-      // register r of this lane group: feature 8 (r/4) + 4 g + r%4 of the tile
-      float cf[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) cf[r] = -INFINITY;
-      const float* pch = pc + (size_t)bh * T_ranges * m + 32 * ft;
-#pragma unroll 4
-      for (int t = 0; t < T_ranges; ++t)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 c = *reinterpret_cast<const f32x4*>(pch + (size_t)t * m + 8 * r4 + 4 * g);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) cf[4 * r4 + q] = fmaxf(cf[4 * r4 + q], c[q]);
-        }
-      float sv[NDT][16], s1[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s1[r] = 0.f;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) sv[dt][r] = 0.f;
-      }
-#pragma unroll 2
-      for (int t = 0; t < T_ranges; ++t) {
-        const float* src = ps + (((size_t)bh * T_ranges + t) * NFT + ft) * (size_t)(D + 1) * 32;
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 c = *reinterpret_cast<const f32x4*>(pch + (size_t)t * m + 8 * r4 + 4 * g);
-          const f32x4 o = *reinterpret_cast<const f32x4*>(src + (size_t)D * 32 + 8 * r4 + 4 * g);
-          float f[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            f[q] = fast_exp2(c[q] - cf[4 * r4 + q]);
-            s1[4 * r4 + q] = __builtin_fmaf(f[q], o[q], s1[4 * r4 + q]);
-          }
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(src + (size_t)(32 * dt + col) * 32 + 8 * r4 + 4 * g);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) sv[dt][4 * r4 + q] = __builtin_fmaf(f[q], v[q], sv[dt][4 * r4 + q]);
-          }
-        }
-      }
+      if (!once) prep(ft);
       // ---- C[feature][query] = W Q^T + c_f (lane = query) ---------------------------------
       f32x16 e0 = zero16(), e1 = zero16();
 #pragma unroll
