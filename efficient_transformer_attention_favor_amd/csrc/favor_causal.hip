@@ -1,6 +1,8 @@
-// Causal FAVOR+ for bf16 problems on gfx950: the chunked prefix pass with the value columns
-// split over the waves, and the exclusive scan of the segment summaries with one running
-// stabiliser per feature.
+// Causal FAVOR+ for bf16 problems on gfx950: the exclusive scan of the segment summaries
+// with one running stabiliser per feature, and the chunked prefix pass -- causal_fg_kernel
+// (d = 64: features split over the waves, intra-chunk blocks of 32..256 positions) and
+// causal_v_kernel (d = 128, m <= 256: value columns and feature groups over the waves) --
+// each followed by a repair pass for segments whose keys spread too far within a block.
 //
 // Method: "Rethinking Attention with Performers" (review page), "제안 방법": attention in
 // linear order with positive random features; causal mode (inclusive mask j <= i) as the

@@ -35,8 +35,9 @@ favor_status launch_key_summaries(const Plan& s, const void* K, const void* V, c
                                   float* gc, hipStream_t st);
 
 // The causal pass of bf16 problems after the key side has written the segment summaries:
-// the exclusive scan with per-feature stabilisers, then the chunked pass with the value
-// columns split over the waves (for the shapes causal_v_supported accepts).
+// the exclusive scan with per-feature stabilisers, then the chunked pass (features over the
+// waves for d = 64, value columns and feature groups for d = 128) and its repair pass, for
+// the shapes causal_v_supported accepts.
 bool causal_v_supported(const Plan& s);
 favor_status launch_causal_scan_pf(const Plan& s, char* ws, hipStream_t st);
 favor_status launch_causal_v(const Plan& s, const void* Q, const void* K, const void* V, const float* W, void* out,
