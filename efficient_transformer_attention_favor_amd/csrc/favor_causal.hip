@@ -656,6 +656,16 @@ __global__ void __launch_bounds__(64 * NW, REPAIR || NW < 4 || NB > 1 ? 1 : 8 / 
 
   bf16x2 one2;
   one2[0] = one2[1] = (bf16)1.f;
+  // tril masks of the intra-block product's operand words: slot j of operand h carries key
+  // 16 h + 8 (j/4) + 4 g + j%4 of query col; a 16-bit half is kept when key <= col
+  u32x4 tril[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int k0 = 16 * h + 8 * ((2 * j) >> 2) + 4 * g + ((2 * j) & 3);
+      tril[h][j] = (k0 <= col ? 0x0000FFFFu : 0u) | (k0 + 1 <= col ? 0xFFFF0000u : 0u);
+    }
   bool wide_w = false;  // first pass: a block of this wave's features was wide
 
   // Key exponents of tile i relative to c_f (C[key][feature], lane = feature).
@@ -848,11 +858,14 @@ __global__ void __launch_bounds__(64 * NW, REPAIR || NW < 4 || NB > 1 ? 1 : 8 / 
         }
         bf16x8 qa[2][2];
         float dsh = 0.f;
+        // -M_w enters as one more MFMA per tile (the query columns' bias)
+        const f16x8 bm = bias_cols(Mw, g, f16x8{});
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
+          cq[i] = mma(bias_unit_rows(g, f16x8{}), bm, cq[i]);
           f32x16 e;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) e[r] = fast_exp2(cq[i][r] - Mw);
+          for (int r = 0; r < 16; ++r) e[r] = fast_exp2(cq[i][r]);
           acc_to_frags(e, qa[i]);
           // phi_Q . S_1 (S_1 of the positions before the block, at the block's c_f)
 #pragma unroll
@@ -870,15 +883,26 @@ __global__ void __launch_bounds__(64 * NW, REPAIR || NW < 4 || NB > 1 ? 1 : 8 / 
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int h = 0; h < 2; ++h) at = mma(lds_frag_rows(Pk, LDP, 32 * i, 0, h), qa[i][h], at);
+        // keep key <= query: the bf16 operand masked word by word, its row sums by dot2 (the
+        // values the numerator uses)
         float dint = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          if (8 * (r >> 2) + 4 * g + (r & 3) > col) at[r] = 0.f;
-          dint += at[r];
-        }
         {
           bf16x8 ab[2];
           acc_to_frags(at, ab);
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            u32x4 w = __builtin_bit_cast(u32x4, ab[h]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) w[j] &= tril[h][j];
+            ab[h] = __builtin_bit_cast(bf16x8, w);
+#pragma unroll
+            for (int j = 0; j < 8; j += 2) {
+              bf16x2 v2;
+              v2[0] = ab[h][j];
+              v2[1] = ab[h][j + 1];
+              dint = __builtin_amdgcn_fdot2_f32_bf16(v2, one2, dint, false);
+            }
+          }
 #pragma unroll
           for (int vt = 0; vt < 2; ++vt)
             num[vt] = mma(lds_frag_rows(Vl, LDV, 0, 32 * vt, 1), ab[1],
