@@ -119,6 +119,8 @@ def test_causal_split_features_ragged(L):
 CHUNK_SHAPES = [
     (64, 64, 301, 1, 1), (128, 128, 700, 2, 2), (256, 192, 999, 4, 2), (64, 512, 640, 2, 1),
     (128, 512, 1001, 1, 1), (256, 256, 97, 2, 2), (128, 64, 1300, 3, 3),
+    # shorter than one block, one position, one block and one more
+    (32, 256, 1, 2, 2), (256, 256, 1, 1, 1), (64, 256, 31, 2, 1), (64, 128, 33, 1, 1), (256, 64, 33, 2, 2),
 ]
 
 
@@ -204,7 +206,10 @@ def test_large_norm_inputs(causal, dtype):
     ("c5_causal_long_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=700, heavy_fraction=0.0), 0),
     ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1000), 128),
     ("c5_causal_long_bf16", dict(batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=700, heavy_fraction=0.0), 64),
-], ids=["d64m256", "d128m256", "d64m512", "d64m256-C128", "d64m512-C64"])
+    # one wave (m = 64); four waves of which the last has no features (m = 192)
+    ("c3_causal_bf16", dict(batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=500, num_features=64), 0),
+    ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=650, num_features=192), 64),
+], ids=["d64m256", "d128m256", "d64m512", "d64m256-C128", "d64m512-C64", "d64m64", "d64m192-C64"])
 def test_causal_keys_far_apart(base, kw, chunk):
     """K scaled by 8 (exact in bf16): |k|^2 / 2 alone spreads the key exponents over hundreds
     of log2 units, so early queries whose keys all sit far below a later key of the same block
