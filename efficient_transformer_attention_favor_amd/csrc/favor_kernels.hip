@@ -1513,87 +1513,35 @@ __global__ void __launch_bounds__(64 * RoBf16<D>::NWAVE)
 }
 
 // ======================================================================================
-// causal_scan: per kv head, c* = max over segments and features of the segment
-// stabilisers, and the exclusive prefix P_t = sum_{t' < t} 2^(c_t',f - c*) S_t' of the
-// segment summaries, in the summaries' own layout [d+1][m] (rows in vperm order, row d the
-// ones column).  Grid (element groups, B*Hkv); each thread owns 4 consecutive features of
-// one row and walks the segments in order, TB segments' loads in flight at a time.
-// ======================================================================================
-__global__ void __launch_bounds__(256) causal_scan_kernel(const float* __restrict__ gs,
-                                                          const float* __restrict__ gc, int T_ranges, int m,
-                                                          int D, float* __restrict__ prefix,
-                                                          float* __restrict__ cstar_out) {
-  __shared__ float red[256];
-  const int bh = blockIdx.y;
-  const float* pc = gc + (size_t)bh * T_ranges * m;
-  // c*: 8 float4 loads in flight per thread
-  float cm = -INFINITY;
-  const int n4 = T_ranges * m / 4;
-  for (int i0 = threadIdx.x; i0 < n4; i0 += 8 * 256) {
-    f32x4 v[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = reinterpret_cast<const f32x4*>(pc)[min(i0 + 256 * u, n4 - 1)];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) cm = fmaxf(cm, fmaxf(fmaxf(v[u][0], v[u][1]), fmaxf(v[u][2], v[u][3])));
-  }
-  red[threadIdx.x] = cm;
-  __syncthreads();
-  for (int s = 128; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + s]);
-    __syncthreads();
-  }
-  const float cstar = red[0];
-  if (blockIdx.x == 0 && threadIdx.x == 0) cstar_out[bh] = cstar;
-  const int e4 = blockIdx.x * 256 + threadIdx.x;  // float4 index within the [d+1][m] plane
-  if (e4 >= (D + 1) * m / 4) return;
-  const int f = (e4 * 4) % m;
-  const size_t plane = (size_t)(D + 1) * m;
-  const f32x4* src = reinterpret_cast<const f32x4*>(gs + (size_t)bh * T_ranges * plane) + e4;
-  f32x4* dst = reinterpret_cast<f32x4*>(prefix + (size_t)bh * T_ranges * plane) + e4;
-  constexpr int TB = 8;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int t0 = 0; t0 < T_ranges; t0 += TB) {
-    f32x4 sv[TB], cv[TB];
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      const int t = min(t0 + u, T_ranges - 1);
-      sv[u] = src[(size_t)t * (plane / 4)];
-      cv[u] = *reinterpret_cast<const f32x4*>(pc + (size_t)t * m + f);
-    }
-#pragma unroll
-    for (int u = 0; u < TB; ++u) {
-      const int t = t0 + u;
-      if (t >= T_ranges) break;
-      dst[(size_t)t * (plane / 4)] = acc;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] += fast_exp2(cv[u][i] - cstar) * sv[u][i];
-    }
-  }
-}
-
-// ======================================================================================
-// causal_chunk: grid (segments, B*Hq), m/(32 NTC) waves; wave w owns NTC 32-feature tiles.
-// Per 32-position block p0 of the segment, in order:
-//   phi_Q,w  = 2^(W_w Q^T - M_w)             (M_w: this wave's row maximum)
-//   phi_K,w  = 2^(K W_w^T - |k|^2 log2e/2 - c*) (c*: global per kv head, from the scan)
+// causal_chunk (float32 problems, and bf16 with d = 128 and m > 256): grid (segments,
+// B*Hq), m/(32 NTC) waves; wave w owns NTC 32-feature tiles.  Per 32-position block p0 of
+// the segment, in order:
+//   phi_K,w  = 2^(K W_w^T - |k|^2 log2e/2 - c_f)  (c_f per feature: the scan's prefix
+//              maximum, raised with the carry rescaled when the block's keys pass it by kTau)
+//   phi_Q,w  = 2^(W_w Q^T + c_f - M_w)            (M_w: this wave's row maximum)
 //   num_w^T  = carry_w^T phi_Q,w^T + [V,1]^T tril(phi_K,w phi_Q,w^T)
 //   carry_w += phi_K,w^T [V, 1]
 // then out = sum_w 2^(M_w - M) num_w / sum_w 2^(M_w - M) den_w across the waves (LDS).
-// The carry of a segment starts at the scan's exclusive prefix.
+// The carry of a segment starts at the scan's exclusive prefix.  A block whose keys spread
+// by more than kSpreadChunk for one feature (over the first keys of the sequence), or pass
+// c_f by more than kSpreadChunk, is wide: the first pass records it per segment and the repair pass
+// (REPAIR) redoes those segments, taking each wide block one position at a time.
 // ======================================================================================
 template <class T> struct CausalLd;
 template <> struct CausalLd<bf16> { static constexpr int PK = 48; };  // phi_K rows: 32 keys + pad
 template <> struct CausalLd<float> { static constexpr int PK = 33; };
+constexpr float kSpreadChunk = 100.f;  // as kSpread of the bf16 causal kernels (log2 units)
 
 // PART (wide heads, d = 128 with m > 256, whose two feature tiles per wave would spill):
 // the features run as two launches over feature ranges starting at fbase.  PART = 1 writes
 // each row's partial (numerators, denominator, row maximum) to part [rows][D+4]; PART = 2
 // merges its own with that partial (max-rescaled sum) and writes out.  PART = 0: one launch.
-template <class T, int D, int NTC, int NWMAX, bool PF, int PART = 0>
+template <class T, int D, int NTC, int NWMAX, int PART, bool REPAIR>
 __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ W,
-    const float* __restrict__ prefix, const float* __restrict__ cstar_in, T* __restrict__ out, int L, int Hq,
-    int Hkv, int Hw, int m, int R, int T_ranges, int fbase = 0, float* __restrict__ part = nullptr) {
+    const float* __restrict__ prefix, const float* __restrict__ prefix_c, T* __restrict__ out, int L, int Hq,
+    int Hkv, int Hw, int m, int R, int T_ranges, int fbase, float* __restrict__ part, int* __restrict__ wide,
+    int n_units) {
   using P = Prec<T>;
   using frag = typename P::frag;
   using wfrag = typename P::wfrag;
@@ -1606,7 +1554,7 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
   // The cross-wave reduction handles 32 / QSPLIT query rows at a time so that the LDS
   // footprint stays within 160 KB for wide heads and many waves.
   constexpr int FW = 32 * NTC;  // features per wave
-  constexpr int BASE_LDS = (2 * 32 * LDK + 32 * LDV + NWMAX * FW * LDP) * (int)sizeof(T);
+  constexpr int BASE_LDS = (2 * 32 * LDK + 32 * LDV + NWMAX * FW * LDP) * (int)sizeof(T) + NWMAX * FW * 4 + 64;
   constexpr int QSPLIT = BASE_LDS + NWMAX * 32 * LDR * 4 <= 160 * 1024       ? 1
                          : BASE_LDS + NWMAX * 16 * LDR * 4 <= 160 * 1024 ? 2
                                                                          : 4;
@@ -1619,12 +1567,18 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
   __shared__ __attribute__((aligned(16))) T Vl[32 * LDV];
   __shared__ __attribute__((aligned(16))) T Pk[NWMAX][FW * LDP];
   __shared__ __attribute__((aligned(16))) float Red[NWMAX][QR * LDR];
+  __shared__ __attribute__((aligned(16))) float CshL[NWMAX][FW];  // the block's c_f moves
+  __shared__ int flagw[NWMAX];
 
-  const int seg = blockIdx.x, bhq = blockIdx.y;
-  const int b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv), bh = b * Hkv + hkv;
   const int nw = blockDim.x >> 6;
   const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
   const int f0 = fbase + wave * FW;
+  float* Csh = CshL[wave];
+  T* pk = Pk[wave];
+  float* red = Red[wave];
+
+  auto run_segment = [&](const int seg, const int bhq) {
+  const int b = bhq / Hq, hq = bhq % Hq, hkv = hq / (Hq / Hkv), bh = b * Hkv + hkv;
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
   const T* Qh = Q + (size_t)bhq * L * D;
   T* Oh = out + (size_t)bhq * L * D;
@@ -1636,8 +1590,12 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
   for (int nt = 0; nt < NTC; ++nt)
 #pragma unroll
     for (int kc = 0; kc < NKC; ++kc) load_w_frag(Wh + (size_t)(f0 + 32 * nt + col) * D, kc, g, wf[nt][kc]);
-  const float cstar = cstar_in[bh];
-  const wfrag biasB = bias_cols(cstar, g, wfrag{});
+  // c_f of this lane's feature 32 nt + col (-inf while no key has set it); its bias
+  // operands are built where they are used (keys: -c_f, 0 while unset; queries: +c_f)
+  float cf[NTC];
+  const float* pcs = prefix_c + ((size_t)bh * T_ranges + seg) * m;
+#pragma unroll
+  for (int nt = 0; nt < NTC; ++nt) cf[nt] = pcs[f0 + 32 * nt + col];
 
   // carry of this wave's features, from the exclusive prefix of the segment ([d+1][m]:
   // lane col takes row 32 dt + col, register r feature 8(r/4) + 4g + r%4 of the tile)
@@ -1668,38 +1626,16 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
       ones = 1.f;
     }
   }
-  T* pk = Pk[wave];
-  float* red = Red[wave];
 
   const int p_begin = seg * R;
   const int p_end = min(p_begin + R, L);
-  // The next block's Q, K, V rows are loaded into registers while the current block is
-  // computed, and written to LDS at the top of the next iteration (zeros past L).
   constexpr int EPC = 16 / (int)sizeof(T), CPR = D / EPC, NCH = 32 * CPR;
-  constexpr int MINT = NTC == 1 ? 128 : 64;  // fewest threads a block has (m >= 64)
-  constexpr int PER = PF ? (NCH + MINT - 1) / MINT : 1;
-  f32x4 pq[PER], pkk[PER], pv[PER];
-  // bf16: range-checked buffer loads (a head is under 2^31 elements, so its byte offsets
-  // fit 32 bits): a chunk of a row past L gets the head's size as offset and reads as zero,
-  // with no branch and no zero fill; a prefetch slot that no thread of the block uses is
-  // skipped.
+  // bf16: range-checked buffer loads (a head is under 2^31 bytes, so its byte offsets fit
+  // 32 bits): a chunk of a row past L gets the head's size as offset and reads as zero
   const unsigned head_bytes = (unsigned)L * (unsigned)D * (unsigned)sizeof(T);
   const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc((void*)Qh, (short)0, (int)head_bytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)Kh, (short)0, (int)head_bytes, kBufWord3);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)Vh, (short)0, (int)head_bytes, kBufWord3);
-  auto prefetch = [&](int q0) {
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (i * (int)blockDim.x >= NCH) break;  // uniform: no thread has a chunk in this slot
-      const int c = threadIdx.x + i * blockDim.x;
-      const int row = c / CPR, c0 = (c % CPR) * EPC;
-      const unsigned off =
-          c < NCH && q0 + row < L ? ((unsigned)(q0 + row) * D + c0) * (unsigned)sizeof(T) : head_bytes;
-      pq[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)off, 0, 0));
-      pkk[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
-      pv[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0));
-    }
-  };
   auto put = [&](WE* dst, int ld, const f32x4& v, int row, int c0) {
     WE* drow = dst + row * ld;
     if constexpr (sizeof(T) == 2) {
@@ -1726,214 +1662,294 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
       d[3] = v[3];
     }
   };
-  if constexpr (PF) prefetch(p_begin);
-  // The carry (and first block) loads complete here: otherwise the compiler's wait for the
-  // carry registers, merged over the loop back edge, also waits for every later prefetch.
+  auto row_max = [&](const f32x16& c) {
+    float mx = c[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, c[r]);
+    return pair_max(mx);
+  };
+  // wide block: see the kernel's comment (masked keys sit near -kMaskedRow)
+  auto is_wide = [&](const f32x16& ck, float mx, bool init) {
+    if (!init) return mx > kSpreadChunk;
+    float mn = INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mn = fminf(mn, ck[r] > -0.5f * kMaskedRow ? ck[r] : INFINITY);
+    return mx - pair_min(mn) > kSpreadChunk;
+  };
+  auto key_exp = [&](const wfrag (&kf)[NKC], const wfrag& biasA, int nt) {
+    f32x16 ck = zero16();
+#pragma unroll
+    for (int kc = 0; kc < NKC; ++kc) ck = mma(kf[kc], wf[nt][kc], ck);
+    return mma(biasA, bias_cols(cf[nt] == -INFINITY ? 0.f : cf[nt], g, wfrag{}), ck);
+  };
+  bool wide_w = false;
+
+  // The carry loads complete here: otherwise the compiler's wait for the carry registers,
+  // merged over the loop back edge, also waits for every later load.
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
   for (int p0 = p_begin; p0 < p_end; p0 += 32) {
-    __syncthreads();
-    if constexpr (PF) {
-#pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int c = threadIdx.x + i * blockDim.x;
-        if (c < NCH) {
-          const int row = c / CPR, c0 = (c % CPR) * EPC;
-          put(Ql, LDK, pq[i], row, c0);
-          put(Kl, LDK, pkk[i], row, c0);
-          put_v(pv[i], row, c0);
-        }
-      }
-      if (p0 + 32 < p_end) prefetch(p0 + 32);
-    } else {
-      for (int c = threadIdx.x; c < NCH; c += blockDim.x) {
-        const int row = c / CPR, c0 = (c % CPR) * EPC;
-        f32x4 q = {0.f, 0.f, 0.f, 0.f}, kk = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (sizeof(T) == 2) {  // the range-checked loads of the prefetch
-          const unsigned off = p0 + row < L ? ((unsigned)(p0 + row) * D + c0) * (unsigned)sizeof(T) : head_bytes;
-          q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)off, 0, 0));
-          kk = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
-          put_v(__builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0)), row, c0);
-        } else if (p0 + row < L) {
-          q = *reinterpret_cast<const f32x4*>(Qh + (size_t)(p0 + row) * D + c0);
-          kk = *reinterpret_cast<const f32x4*>(Kh + (size_t)(p0 + row) * D + c0);
-        }
-        put(Ql, LDK, q, row, c0);
-        put(Kl, LDK, kk, row, c0);
-      }
-      if constexpr (sizeof(T) != 2) stage_rows<T, D, true>(Vl, LDV, Vh, p0, L);
-    }
-    __syncthreads();
-
-    // phi_Q of this wave's features: C = W_w Q^T (features x queries), lane = query.
-    wfrag qf[NKC];
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) qf[kc] = load_frag_k(Ql + col * LDK, kc, g);
-    f32x16 cq[NTC];
-#pragma unroll
-    for (int nt = 0; nt < NTC; ++nt) {
-      cq[nt] = zero16();
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) cq[nt] = mma(wf[nt][kc], qf[kc], cq[nt]);
-    }
-    float Mw = cq[0][0];
-#pragma unroll
-    for (int nt = 0; nt < NTC; ++nt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Mw = fmaxf(Mw, cq[nt][r]);
-    Mw = fmaxf(Mw, partner32(Mw));
-    frag qb[NTC][P::NF32];
-#pragma unroll
-    for (int nt = 0; nt < NTC; ++nt) {
-      f32x16 e;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(cq[nt][r] - Mw);
-      acc_to_frags(e, qb[nt]);
-    }
-
-    // phi_K of this wave's features: C = K W_w^T (keys x features), lane = feature.
-    wfrag kf[NKC];
-#pragma unroll
-    for (int kc = 0; kc < NKC; ++kc) kf[kc] = load_frag_k(Kl + col * LDK, kc, g);
-    float nrm = sumsq(kf);
-    nrm += partner32(nrm);
-    // keys past L (zero rows in LDS) get the masking row bias: their features are exactly 0
-    const wfrag biasA = bias_rows(p0 + col < L ? 0.5f * kLog2e * nrm : kMaskedRow, g, wfrag{});
-    frag ka[NTC][P::NF32];
-#pragma unroll
-    for (int nt = 0; nt < NTC; ++nt) {
-      f32x16 ck = zero16();
-#pragma unroll
-      for (int kc = 0; kc < NKC; ++kc) ck = mma(kf[kc], wf[nt][kc], ck);
-      ck = mma(biasA, biasB, ck);
-      f32x16 e;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(ck[r]);
-      acc_to_frags(e, ka[nt]);
-      // phi_K to LDS as [feature][key] for the transposed read below (the operand values:
-      // register r holds key 8(r/4) + 4g + r%4)
+    __syncthreads();  // the previous block's readers of Ql / Kl / Vl are done
+    for (int c = threadIdx.x; c < NCH; c += blockDim.x) {
+      const int row = c / CPR, c0 = (c % CPR) * EPC;
+      f32x4 q = {0.f, 0.f, 0.f, 0.f}, kk = {0.f, 0.f, 0.f, 0.f};
       if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            bf16x4_t v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = ka[nt][h][4 * hh + i];
-            *reinterpret_cast<bf16x4_t*>(pk + (32 * nt + col) * LDP + 8 * (2 * h + hh) + 4 * g) = v;
-          }
-      } else {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          T* dst = pk + (32 * nt + col) * LDP + 8 * r4 + 4 * g;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) dst[i] = e[4 * r4 + i];
-        }
+        const unsigned off = p0 + row < L ? ((unsigned)(p0 + row) * D + c0) * (unsigned)sizeof(T) : head_bytes;
+        q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qrs, (int)off, 0, 0));
+        kk = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, (int)off, 0, 0));
+        put_v(__builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)off, 0, 0)), row, c0);
+      } else if (p0 + row < L) {
+        q = *reinterpret_cast<const f32x4*>(Qh + (size_t)(p0 + row) * D + c0);
+        kk = *reinterpret_cast<const f32x4*>(Kh + (size_t)(p0 + row) * D + c0);
       }
+      put(Ql, LDK, q, row, c0);
+      put(Kl, LDK, kk, row, c0);
     }
+    if constexpr (sizeof(T) != 2) stage_rows<T, D, true>(Vl, LDV, Vh, p0, L);
+    __syncthreads();
+    const int pend = min(p0 + 32, L);
 
-    // num^T = carry^T phi_Q^T  (rows: value columns, lanes: queries)
-    f32x16 num[NDT];
+    // step(lo, hi, check): the positions [lo, hi) of the block (keys outside masked, rows
+    // outside not stored).  The repair pass first tests the whole block (check) and returns
+    // true, having changed nothing, when it is wide; the caller then takes the block one
+    // position at a time.
+    auto step = [&](const int lo, const int hi, const bool check) -> bool {
+      if (REPAIR && !check) __syncthreads();  // the previous position's reduction is read
+      wfrag kf[NKC];
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) {
-      num[dt] = zero16();
+      for (int kc = 0; kc < NKC; ++kc) kf[kc] = load_frag_k(Kl + col * LDK, kc, g);
+      const float nrm = pair_sum(sumsq(kf));
+      // keys outside the window (and past L: zero rows in LDS) get the masking row bias:
+      // their features are exactly 0
+      const bool kin = p0 + col >= lo && p0 + col < hi;
+      const wfrag biasA = bias_rows(kin ? 0.5f * kLog2e * nrm : kMaskedRow, g, wfrag{});
+      if (REPAIR && check) {
+        bool wd = false;
+#pragma unroll
+        for (int nt = 0; nt < NTC; ++nt) {
+          const f32x16 ck = key_exp(kf, biasA, nt);
+          wd = wd || is_wide(ck, row_max(ck), cf[nt] == -INFINITY);
+        }
+        const bool any = wave_any(wd);
+        if (l == 0) flagw[wave] = any ? 1 : 0;
+        __syncthreads();
+        int a = 0;
+        for (int w = 0; w < nw; ++w) a |= flagw[w];
+        if (a != 0) return true;
+      }
+
+      // phi_K of this wave's features: C = K W_w^T (keys x features), lane = feature; c_f
+      // raised first where the block's keys pass it
+      frag ka[NTC][P::NF32];
+      bool shifted = false;
 #pragma unroll
       for (int nt = 0; nt < NTC; ++nt) {
-        frag ca[P::NF32];
-        acc_to_frags(carry[nt][dt], ca);
+        f32x16 ck = key_exp(kf, biasA, nt);
+        const float mx = row_max(ck);
+        const bool init = cf[nt] == -INFINITY;
+        if (!REPAIR && check) wide_w = wide_w || is_wide(ck, mx, init);
+        const float shift = init || mx > kTau ? mx : 0.f;
+        Csh[32 * nt + col] = init ? -INFINITY : -shift;  // both lane halves write the same value
+        if (init || shift != 0.f) cf[nt] = (init ? 0.f : cf[nt]) + shift;
+        shifted = shifted || shift != 0.f;
+        f32x16 e;
 #pragma unroll
-        for (int h = 0; h < P::NF32; ++h) num[dt] = mma(ca[h], qb[nt][h], num[dt]);
+        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(ck[r] - shift);
+        acc_to_frags(e, ka[nt]);
+        // phi_K to LDS as [feature][key] for the transposed read below (the operand values:
+        // register r holds key 8(r/4) + 4g + r%4)
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              bf16x4_t v;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) v[i] = ka[nt][h][4 * hh + i];
+              *reinterpret_cast<bf16x4_t*>(pk + (32 * nt + col) * LDP + 8 * (2 * h + hh) + 4 * g) = v;
+            }
+        } else {
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            T* dst = pk + (32 * nt + col) * LDP + 8 * r4 + 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dst[i] = e[4 * r4 + i];
+          }
+        }
       }
-    }
-    // intra-block triangle: A^T = phi_K phi_Q^T (keys x queries), keep key <= query
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only: the prefetch stays in flight
-    __builtin_amdgcn_wave_barrier();
-    f32x16 at = zero16();
+      asm volatile("" ::: "memory");  // the wave's LDS writes above before its reads below
+      // the carry (ones column included) of a raised feature scales by 2^(old - new), 0
+      // where it was unset
+      if (wave_any(shifted)) {
 #pragma unroll
-    for (int nt = 0; nt < NTC; ++nt)
+        for (int nt = 0; nt < NTC; ++nt)
 #pragma unroll
-      for (int h = 0; h < P::NF32; ++h) at = mma(lds_frag_rows(pk, LDP, 32 * nt, 0, h), qb[nt][h], at);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 sh = *reinterpret_cast<const f32x4*>(Csh + 32 * nt + 8 * r4 + 4 * g);
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (8 * (r >> 2) + 4 * g + (r & 3) > col) at[r] = 0.f;
-    frag ab[P::NF32];
-    acc_to_frags(at, ab);
+            for (int q = 0; q < 4; ++q) {
+              const float fct = fast_exp2(sh[q]);
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-      for (int h = 0; h < P::NF32; ++h) {
-        const frag va = dt < NDT - 1 ? lds_frag_rows(Vl, LDV, 0, 32 * dt, h) : ones;
-        num[dt] = mma(va, ab[h], num[dt]);
-#pragma unroll
-        for (int nt = 0; nt < NTC; ++nt) carry[nt][dt] = mma(ka[nt][h], va, carry[nt][dt]);
+              for (int dt = 0; dt < NDT; ++dt) carry[nt][dt][4 * r4 + q] *= fct;
+            }
+          }
       }
 
-    // this wave's partial to LDS (D values, den, row maximum per query), then the
-    // cross-wave sum; one reduction item = (query, 4 value columns), spread over all threads.
+      // phi_Q of this wave's features: C = W_w Q^T + c_f (features x queries), lane = query
+      wfrag qf[NKC];
 #pragma unroll
-    for (int qh = 0; qh < QSPLIT; ++qh) {
-      const int qrow = col - qh * QR;
-      if (qrow >= 0 && qrow < QR) {
+      for (int kc = 0; kc < NKC; ++kc) qf[kc] = load_frag_k(Ql + col * LDK, kc, g);
+      f32x16 cq[NTC];
+      float Mw = -INFINITY;
 #pragma unroll
-        for (int dt = 0; dt < NDT - 1; ++dt)
+      for (int nt = 0; nt < NTC; ++nt) {
+        cq[nt] = zero16();
 #pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            f32x4 v = {num[dt][4 * q4], num[dt][4 * q4 + 1], num[dt][4 * q4 + 2], num[dt][4 * q4 + 3]};
-            *reinterpret_cast<f32x4*>(red + qrow * LDR + 32 * dt + 16 * g + 4 * q4) = v;
-          }
-        if (g == 0) {
-          red[qrow * LDR + D] = num[NDT - 1][0];
-          red[qrow * LDR + D + 1] = Mw;
+        for (int kc = 0; kc < NKC; ++kc) cq[nt] = mma(wf[nt][kc], qf[kc], cq[nt]);
+        // every c_f is set once the block's keys are in (each feature saw a key)
+        cq[nt] = mma(bias_rows(-cf[nt], g, wfrag{}), bias_cols(0.f, g, wfrag{}), cq[nt]);
+        Mw = fmaxf(Mw, row_max(cq[nt]));
+      }
+      frag qb[NTC][P::NF32];
+#pragma unroll
+      for (int nt = 0; nt < NTC; ++nt) {
+        f32x16 e;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) e[r] = fast_exp2(cq[nt][r] - Mw);
+        acc_to_frags(e, qb[nt]);
+      }
+
+      // num^T = carry^T phi_Q^T  (rows: value columns, lanes: queries)
+      f32x16 num[NDT];
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        num[dt] = zero16();
+#pragma unroll
+        for (int nt = 0; nt < NTC; ++nt) {
+          frag ca[P::NF32];
+          acc_to_frags(carry[nt][dt], ca);
+#pragma unroll
+          for (int h = 0; h < P::NF32; ++h) num[dt] = mma(ca[h], qb[nt][h], num[dt]);
         }
       }
-      __syncthreads();
-      for (int it = threadIdx.x; it < QR * (D / 4); it += blockDim.x) {
-        const int q = it / (D / 4), c0 = (it % (D / 4)) * 4;
-        const int pos = p0 + qh * QR + q;
-        if (pos >= L) continue;
-        float M = -INFINITY;
-        for (int w = 0; w < nw; ++w) M = fmaxf(M, Red[w][q * LDR + D + 1]);
-        float den = 0.f;
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        for (int w = 0; w < nw; ++w) {
-          const float* rw = Red[w] + q * LDR;
-          const float2 dm = *reinterpret_cast<const float2*>(rw + D);  // den, row maximum
-          const f32x4 v = *reinterpret_cast<const f32x4*>(rw + c0);
-          const float sc = fast_exp2(dm.y - M);
-          den += sc * dm.x;
+      // intra-block triangle: A^T = phi_K phi_Q^T (keys x queries), keep key <= query
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+      __builtin_amdgcn_wave_barrier();
+      f32x16 at = zero16();
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[i] += sc * v[i];
+      for (int nt = 0; nt < NTC; ++nt)
+#pragma unroll
+        for (int h = 0; h < P::NF32; ++h) at = mma(lds_frag_rows(pk, LDP, 32 * nt, 0, h), qb[nt][h], at);
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (8 * (r >> 2) + 4 * g + (r & 3) > col) at[r] = 0.f;
+      frag ab[P::NF32];
+      acc_to_frags(at, ab);
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int h = 0; h < P::NF32; ++h) {
+          const frag va = dt < NDT - 1 ? lds_frag_rows(Vl, LDV, 0, 32 * dt, h) : ones;
+          num[dt] = mma(va, ab[h], num[dt]);
+#pragma unroll
+          for (int nt = 0; nt < NTC; ++nt) carry[nt][dt] = mma(ka[nt][h], va, carry[nt][dt]);
         }
-        if constexpr (PART != 0) {
-          float* prow = part + ((size_t)bhq * L + pos) * (D + 4);  // 16-byte aligned rows
-          if constexpr (PART == 1) {
-            *reinterpret_cast<f32x4*>(prow + c0) = acc;
-            if (c0 == 0) {
-              prow[D] = den;
-              prow[D + 1] = M;
+
+      // this wave's partial to LDS (D values, den, row maximum per query), then the
+      // cross-wave sum; one reduction item = (query, 4 value columns), spread over all threads.
+#pragma unroll
+      for (int qh = 0; qh < QSPLIT; ++qh) {
+        const int qrow = col - qh * QR;
+        if (qrow >= 0 && qrow < QR) {
+#pragma unroll
+          for (int dt = 0; dt < NDT - 1; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+              f32x4 v = {num[dt][4 * q4], num[dt][4 * q4 + 1], num[dt][4 * q4 + 2], num[dt][4 * q4 + 3]};
+              *reinterpret_cast<f32x4*>(red + qrow * LDR + 32 * dt + 16 * g + 4 * q4) = v;
             }
-            continue;
-          } else {
-            const float den1 = prow[D], M1 = prow[D + 1];
-            const f32x4 acc1 = *reinterpret_cast<const f32x4*>(prow + c0);
-            const float Mn = fmaxf(M, M1), s0 = fast_exp2(M - Mn), s1 = fast_exp2(M1 - Mn);
-            den = den * s0 + den1 * s1;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = acc[i] * s0 + acc1[i] * s1;
+          if (g == 0) {
+            red[qrow * LDR + D] = num[NDT - 1][0];
+            red[qrow * LDR + D + 1] = Mw;
           }
         }
-        const float inv = __builtin_amdgcn_rcpf(den);
-        T* orow = Oh + (size_t)pos * D + c0;
-        if constexpr (sizeof(T) == 2) {
-          bf16x4_t o;
+        __syncthreads();
+        for (int it = threadIdx.x; it < QR * (D / 4); it += blockDim.x) {
+          const int q = it / (D / 4), c0 = (it % (D / 4)) * 4;
+          const int pos = p0 + qh * QR + q;
+          if (pos < lo || pos >= hi) continue;
+          float M = -INFINITY;
+          for (int w = 0; w < nw; ++w) M = fmaxf(M, Red[w][q * LDR + D + 1]);
+          float den = 0.f;
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+          for (int w = 0; w < nw; ++w) {
+            const float* rw = Red[w] + q * LDR;
+            const float2 dm = *reinterpret_cast<const float2*>(rw + D);  // den, row maximum
+            const f32x4 v = *reinterpret_cast<const f32x4*>(rw + c0);
+            const float sc = fast_exp2(dm.y - M);
+            den += sc * dm.x;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) o[i] = (bf16)(acc[i] * inv);
-          *reinterpret_cast<bf16x4_t*>(orow) = o;
-        } else {
-          *reinterpret_cast<f32x4*>(orow) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+            for (int i = 0; i < 4; ++i) acc[i] += sc * v[i];
+          }
+          if constexpr (PART != 0) {
+            float* prow = part + ((size_t)bhq * L + pos) * (D + 4);  // 16-byte aligned rows
+            if constexpr (PART == 1) {
+              *reinterpret_cast<f32x4*>(prow + c0) = acc;
+              if (c0 == 0) {
+                prow[D] = den;
+                prow[D + 1] = M;
+              }
+              continue;
+            } else {
+              const float den1 = prow[D], M1 = prow[D + 1];
+              const f32x4 acc1 = *reinterpret_cast<const f32x4*>(prow + c0);
+              const float Mn = fmaxf(M, M1), s0 = fast_exp2(M - Mn), s1 = fast_exp2(M1 - Mn);
+              den = den * s0 + den1 * s1;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) acc[i] = acc[i] * s0 + acc1[i] * s1;
+            }
+          }
+          const float inv = __builtin_amdgcn_rcpf(den);
+          T* orow = Oh + (size_t)pos * D + c0;
+          if constexpr (sizeof(T) == 2) {
+            bf16x4_t o;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = (bf16)(acc[i] * inv);
+            *reinterpret_cast<bf16x4_t*>(orow) = o;
+          } else {
+            *reinterpret_cast<f32x4*>(orow) = f32x4{acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv};
+          }
         }
+        if (QSPLIT > 1) __syncthreads();
       }
-      if (QSPLIT > 1) __syncthreads();
+      return false;
+    };
+    if constexpr (REPAIR) {
+      // the whole block with the wide test, then (when wide) its positions one at a time
+      for (int q = p0 - 1; q < pend; ++q) {
+        const bool whole = q < p0;
+        if (!step(whole ? p0 : q, whole ? pend : q + 1, whole) && whole) break;
+      }
+    } else {
+      step(p0, pend, true);
     }
+  }
+  if (!REPAIR) {
+    const bool any = wave_any(wide_w);
+    __syncthreads();  // flagw is free
+    if (l == 0) flagw[wave] = any ? 1 : 0;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int a = 0;
+      for (int w = 0; w < nw; ++w) a |= flagw[w];
+      wide[(size_t)bhq * T_ranges + seg] = a;
+    }
+  }
+  };
+  if constexpr (REPAIR) {
+    for (int u = blockIdx.x; u < n_units; u += gridDim.x)
+      if (wide[u] != 0) run_segment(u % T_ranges, u / T_ranges);
+  } else {
+    run_segment(blockIdx.x, blockIdx.y);
   }
 }
 
@@ -2023,54 +2039,62 @@ favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const
                         hipStream_t st, const Marks& mk) {
   float* gs = reinterpret_cast<float*>(ws + s.off_gs);
   float* gc = reinterpret_cast<float*>(ws + s.off_gc);
-  float* prefix = reinterpret_cast<float*>(ws + s.off_p);
-  float* cstar = reinterpret_cast<float*>(ws + s.off_cstar);
-  const int nw = s.m / kFeatPerWave;
   if (!mk.mark(0, st)) return FAVOR_ERR_HIP;
   favor_status rc = launch_kv_summary<T, D>(s, K, V, W, gs, gc, ws, st);
   if (rc != FAVOR_OK || !mk.mark(1, st)) return rc != FAVOR_OK ? rc : FAVOR_ERR_HIP;
+  // per-feature stabilisers: the scan's prefix maxima start each segment
+  rc = launch_causal_scan_pf(s, ws, st);
+  if (rc != FAVOR_OK) return rc;
+  if (!mk.mark(2, st)) return FAVOR_ERR_HIP;
   if (causal_v_supported(s)) {
-    // per-feature stabilisers, the value columns split over the waves
-    rc = launch_causal_scan_pf(s, ws, st);
-    if (rc != FAVOR_OK) return rc;
-    if (!mk.mark(2, st)) return FAVOR_ERR_HIP;
+    // bf16 (d = 64, or m <= 256): the value columns split over the waves
     rc = launch_causal_v(s, Q, K, V, W, out, ws, st);
     if (rc != FAVOR_OK) return rc;
     return mk.mark(3, st) ? FAVOR_OK : FAVOR_ERR_HIP;
   }
-  hipLaunchKernelGGL(causal_scan_kernel, dim3(ceil_div_i((long long)(s.d + 1) * s.m / 4, 256), s.BH), dim3(256), 0,
-                     st, gs, gc, s.T, s.m, s.d, prefix, cstar);
-  if (hipGetLastError() != hipSuccess || !mk.mark(2, st)) return FAVOR_ERR_HIP;
-  // bf16, d = 64: one 32-feature tile per wave up to m = 256 (two waves per SIMD), else two
-  constexpr bool one_tile = std::is_same<T, bf16>::value && D == 64;
-  if (one_tile && s.m <= 256) {
-    if constexpr (one_tile)
-      hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, true>), dim3(s.T, s.B * s.Hq), dim3(kWave * (s.m / 32)), 0,
-                         st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
-  } else if (D == 128 && s.m > 256) {
-    // two launches of one-tile waves over features [0, 256) and [256, m), merged per row
+  const float* prefix = reinterpret_cast<const float*>(ws + s.off_p);
+  const float* prefix_c = reinterpret_cast<const float*>(ws + s.off_pc);
+  int* wide = reinterpret_cast<int*>(ws + s.off_wide);
+  const int n_units = s.T * s.B * s.Hq;
+  const dim3 grid(s.T, s.B * s.Hq);
+  // the repair pass: one workgroup per CU at most, walking the segment flags
+  const dim3 rgrid((unsigned)(n_units < kCUs ? n_units : kCUs));
+  // one launch pair (first pass, repair) over nw waves from feature fbase
+  auto pair = [&](auto first, auto repair, int nw, int fbase, float* part) {
+    hipLaunchKernelGGL(first, grid, dim3(kWave * nw), 0, st, Q, K, V, W, prefix, prefix_c, out, s.L, s.Hq, s.Hkv,
+                       s.Hw, s.m, s.R, s.T, fbase, part, wide, n_units);
+    if (hipGetLastError() != hipSuccess) return false;
+    hipLaunchKernelGGL(repair, rgrid, dim3(kWave * nw), 0, st, Q, K, V, W, prefix, prefix_c, out, s.L, s.Hq, s.Hkv,
+                       s.Hw, s.m, s.R, s.T, fbase, part, wide, n_units);
+    return hipGetLastError() == hipSuccess;
+  };
+  bool ok = false;
+  if (D == 128 && s.m > 256) {
+    // two launch pairs of one-tile waves over features [0, 256) and [256, m), merged per row
+    // (the second pair's flags replace the first's once its repair has read them)
     if constexpr (D == 128) {
       float* part = reinterpret_cast<float*>(ws + s.off_part);
-      hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false, 1>), dim3(s.T, s.B * s.Hq), dim3(kWave * 8), 0, st,
-                         Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, 0, part);
-      if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
-      hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false, 2>), dim3(s.T, s.B * s.Hq),
-                         dim3(kWave * ((s.m - 256) / 32)), 0, st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv,
-                         s.Hw, s.m, s.R, s.T, 256, part);
+      ok = pair(causal_chunk_kernel<T, D, 1, 8, 1, false>, causal_chunk_kernel<T, D, 1, 8, 1, true>, 8, 0, part) &&
+           pair(causal_chunk_kernel<T, D, 1, 8, 2, false>, causal_chunk_kernel<T, D, 1, 8, 2, true>,
+                (s.m - 256) / 32, 256, part);
     }
-  } else if (s.m <= 256) {
-    // one 32-feature tile per wave without the register prefetch: two waves per SIMD (a few
-    // spilled registers for float32 d = 128, still faster than two tiles per wave)
-    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 1, 8, false>), dim3(s.T, s.B * s.Hq), dim3(kWave * (s.m / 32)), 0,
-                       st, Q, K, V, W, prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
-  } else if constexpr (D == 64) {
-    // m > 256 (5 to 8 waves): two 32-feature tiles per wave
-    hipLaunchKernelGGL((causal_chunk_kernel<T, D, 2, 8, false>), dim3(s.T, s.B * s.Hq), dim3(kWave * nw), 0, st, Q, K, V, W,
-                       prefix, cstar, out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T);
+  } else if constexpr (std::is_same<T, float>::value) {
+    if (s.m <= 256) {
+      // one 32-feature tile per wave: two waves per SIMD (a few spilled registers for d =
+      // 128, still faster than two tiles per wave)
+      ok = pair(causal_chunk_kernel<T, D, 1, 8, 0, false>, causal_chunk_kernel<T, D, 1, 8, 0, true>, s.m / 32, 0,
+                nullptr);
+    } else if constexpr (D == 64) {
+      // m > 256 (5 to 8 waves): two 32-feature tiles per wave
+      ok = pair(causal_chunk_kernel<T, D, 2, 8, 0, false>, causal_chunk_kernel<T, D, 2, 8, 0, true>, s.m / 64, 0,
+                nullptr);
+    } else {
+      return FAVOR_ERR_UNSUPPORTED;  // not reached: d = 128 with m > 256 takes the split above
+    }
   } else {
-    return FAVOR_ERR_UNSUPPORTED;  // not reached: d = 128 with m > 256 takes the split above
+    return FAVOR_ERR_UNSUPPORTED;  // not reached: the other bf16 shapes take launch_causal_v
   }
-  if (hipGetLastError() != hipSuccess || !mk.mark(3, st)) return FAVOR_ERR_HIP;
+  if (!ok || !mk.mark(3, st)) return FAVOR_ERR_HIP;
   return FAVOR_OK;
 }
 

@@ -115,8 +115,6 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
   off = align256(off + sizeof(float) * (size_t)q.m * q.BH * q.T);
   q.off_p = off;
   if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * (size_t)(q.d + 1) * q.m * q.BH * q.T);
-  q.off_cstar = off;
-  if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * q.BH);
   q.off_pc = off;
   if (q.mode == FAVOR_CAUSAL) off = align256(off + sizeof(float) * (size_t)q.m * q.BH * q.T);
   q.off_wide = off;

@@ -42,7 +42,6 @@ struct Plan {
   size_t off_gs;       // [BH][T][d+1][m] range / segment summaries (float)
   size_t off_gc;       // [BH][T][m] their per-feature stabilisers (log2 units)
   size_t off_p;        // [BH][T][d+1][m] exclusive prefixes of the segment summaries (causal)
-  size_t off_cstar;    // [BH] global stabiliser per kv head (causal)
   size_t off_pc;       // [BH][T][m] per-feature stabilisers of the exclusive prefixes (causal)
   size_t off_wide;     // [B Hq][T] int: segment met a block of widely spread keys (causal)
   size_t off_part;     // [B Hq L][d+4] per-row partials of two feature ranges (causal, d = 128, m > 256)

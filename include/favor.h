@@ -92,8 +92,9 @@ size_t favor_workspace_bytes(const favor_problem* p);
 
 /* FAVOR+ forward (Performer page, "제안 방법"): out = D^-1 A_hat V in linear order,
  * bidirectional or causal (inclusive mask j <= i) per p->mode.  Queues 2 (bidirectional)
- * or 3-4 (causal: key-side summaries, their prefix scan, the chunked pass and, for bf16
- * problems, its repair launch) kernels on `stream`. */
+ * or 4 (causal: key-side summaries, their prefix scan, the chunked pass and its repair
+ * launch; 6 where d = 128 with m > 256 in bf16 or float32, whose chunked pass and repair
+ * run once per feature range) kernels on `stream`. */
 favor_status favor_attn_fwd(const favor_problem* p, const void* Q, const void* K, const void* V,
                             const float* W, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);

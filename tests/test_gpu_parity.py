@@ -209,12 +209,22 @@ def test_large_norm_inputs(causal, dtype):
     # one wave (m = 64); four waves of which the last has no features (m = 192)
     ("c3_causal_bf16", dict(batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=500, num_features=64), 0),
     ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=650, num_features=192), 64),
-], ids=["d64m256", "d128m256", "d64m512", "d64m256-C128", "d64m512-C64", "d64m64", "d64m192-C64"])
+    # d = 128 with m > 256: two launches over feature ranges, merged per row
+    ("c3_causal_bf16", dict(batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=700, head_dim=128, num_features=384), 0),
+    # float32: one 32-feature tile per wave, two tiles per wave (m > 256), d = 128 split in two
+    ("c1_bidir_f32", dict(heads_q=2, heads_kv=2, heads_w=2, seq_len=700, num_features=256, causal=True), 0),
+    ("c1_bidir_f32", dict(heads_q=2, heads_kv=1, heads_w=1, seq_len=533, num_features=512, causal=True), 0),
+    ("c1_bidir_f32", dict(heads_q=1, heads_kv=1, heads_w=1, seq_len=600, head_dim=128, num_features=128, causal=True), 0),
+    ("c1_bidir_f32", dict(heads_q=2, heads_kv=1, heads_w=1, seq_len=417, head_dim=128, num_features=384, causal=True), 0),
+], ids=["d64m256", "d128m256", "d64m512", "d64m256-C128", "d64m512-C64", "d64m64", "d64m192-C64", "d128m384",
+        "f32-d64m256", "f32-d64m512", "f32-d128m128", "f32-d128m384"])
 def test_causal_keys_far_apart(base, kw, chunk):
     """K scaled by 8 (exact in bf16): |k|^2 / 2 alone spreads the key exponents over hundreds
     of log2 units, so early queries whose keys all sit far below a later key of the same block
     (or of the sequence) must not lose their terms to underflow.  With intra-chunk blocks
-    above 32 positions the stabilisers also move in the middle of a chunk."""
+    above 32 positions the stabilisers also move in the middle of a chunk.  Every causal
+    kernel family is covered: bf16 d = 64 (by intra-chunk block), bf16 d = 128 (m <= 256 and
+    the two-range split above), and float32."""
     w = _small(base, **kw)
     _say(f"case {w} K x8 chunk={chunk}")
     Q, K, V, W = I.make_inputs(w, seed=4)
