@@ -709,8 +709,9 @@ def backward_main(args, w):
 def generalized_main(args, w):
     """Kernelised attention with the ReLU feature map (favor_attn_fwd_generalized): one step =
     one call on the workload (inputs resident).  Algorithmic flops as for the softmax forward
-    (features of Q and K, S, phi(Q) S); float32 MFMA products, so the roofline is the float32
-    matrix peak."""
+    (features of Q and K, S, phi(Q) S).  Bidirectional problems run fused MFMA kernels in the
+    input's precision (bf16: fp16 W contraction, bf16 products), so the roofline is that
+    dtype's matrix peak; causal problems run float32 products (the float32 peak)."""
     import numpy as np
     import torch
 
@@ -750,19 +751,20 @@ def generalized_main(args, w):
     Rq, Rk = B * Hq * L, B * Hkv * L
     flops = 2 * m * ((Rq + Rk) * d + (Rq + Rk) * (d + 1))
     achieved = flops / (ms_step * 1e-3) / 1e12
+    cdt = "f32" if w.causal else w.dtype
     res = {
         "metric": "kernelised attention (ReLU random features) fwd tokens/s (B*H*L/s), 1 GPU",
         "value": round(Rq / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32",
+        "vs_baseline": None, "dtype": cdt,
         "data": "synthetic (seeded Gaussian Q, K, V; orthogonal random features W)",
         "config": {"workload": f"{w.name} relu features", "batch": B, "heads_q": Hq, "heads_kv": Hkv,
                    "heads_w": w.heads_w, "seq_len": L, "head_dim": d, "num_features": m,
                    "input_dtype": w.dtype, "mode": "causal" if w.causal else "bidirectional",
                    "parallelism": "single GPU"},
         "roofline": {"kernel": "favor_attn_fwd_generalized (all kernels)", "bound": "mfma",
-                     "achieved": round(achieved, 2), "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_TFLOPS["f32"], 4), "traffic": None,
+                     "achieved": round(achieved, 2), "peak": PEAK_TFLOPS[cdt], "unit": "TFLOP/s",
+                     "frac": round(achieved / PEAK_TFLOPS[cdt], 4), "traffic": None,
                      "per_launch": {"alg_flops": flops, "avg_ms": round(ms_step, 5)}},
     }
     if not args.no_cpu_baseline:

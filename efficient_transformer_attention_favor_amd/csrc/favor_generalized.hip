@@ -9,12 +9,14 @@
 // stabiliser, and a row whose weights are all zero (every feature of its query, or of its
 // keys, zero) gets a zero output.
 //
-// Implementation: the feature matrices are materialised in float32 (the features kernel in
-// its ReLU mode), then float32 batched products:
-//   bidirectional: S = phi(K)^T [V, 1] (split contraction), [N, D] = phi(Q) S per kv head,
-//   causal: 64-position chunks, S_<c the exclusive prefix of the chunk summaries,
-//           [N, D]_c = tril(phi(Q_c) phi(K_c)^T) [V_c, 1] + phi(Q_c) S_<c,
-// and a row kernel writes out = N / D in the problem's dtype.
+// Implementation.  Bidirectional: the softmax forward's generic key-side and readout
+// kernels with ReLU in place of the exponential -- the features stay on chip, S =
+// phi(K)^T [V, 1] per position range by MFMA (bf16 problems: fp16 W contraction, bf16
+// features and products, float32 accumulation), then out = phi(Q) S_v / phi(Q) S_1.
+// Causal: the feature matrices are materialised in float32 (the features kernel in its
+// ReLU mode), then float32 batched products over 64-position chunks, S_<c the exclusive
+// prefix of the chunk summaries, [N, D]_c = tril(phi(Q_c) phi(K_c)^T) [V_c, 1] +
+// phi(Q_c) S_<c, and a row kernel writes out = N / D in the problem's dtype.
 #include <hip/hip_runtime.h>
 
 #include "favor_device.hpp"
@@ -28,18 +30,20 @@ namespace {
 constexpr int kGenChunk = GT;
 
 struct GenLayout {
-  size_t phq, phk, v1, S, part, Pm, ND, bytes;
-  int Lp, NC, split;
+  size_t phq, phk, v1, S, Pm, ND, bytes;
+  int Lp, NC;
 };
 
 GenLayout gen_layout(const Plan& s) {
-  GenLayout w;
-  const bool causal = s.mode == FAVOR_CAUSAL;
-  w.NC = causal ? (s.L + kGenChunk - 1) / kGenChunk : 1;
-  w.Lp = causal ? w.NC * kGenChunk : s.L;
+  GenLayout w{};
+  if (s.mode != FAVOR_CAUSAL) {  // bidirectional: the plan's range summaries gs and gc
+    w.bytes = s.off_p;
+    return w;
+  }
+  w.NC = (s.L + kGenChunk - 1) / kGenChunk;
+  w.Lp = w.NC * kGenChunk;
   const size_t Rq = (size_t)s.B * s.Hq * w.Lp, Rk = (size_t)s.B * s.Hkv * w.Lp;
   const size_t m = s.m, d1 = s.d + 1, f = sizeof(float);
-  w.split = causal ? 1 : ksplit_for(s.m, s.d + 1, s.L, s.BH);
   size_t off = 0;
   auto take = [&](size_t n) {
     const size_t o = off;
@@ -50,8 +54,7 @@ GenLayout gen_layout(const Plan& s) {
   w.phk = take(Rk * m);
   w.v1 = take(Rk * d1);
   w.S = take((size_t)s.BH * w.NC * m * d1);
-  w.part = causal ? off : take((size_t)w.split * s.BH * m * d1);
-  w.Pm = causal ? take(Rq * kGenChunk) : off;
+  w.Pm = take(Rq * kGenChunk);
   w.ND = take(Rq * d1);
   w.bytes = off;
   return w;
@@ -78,9 +81,10 @@ __global__ void __launch_bounds__(256)
 template <class T, int D>
 favor_status run_generalized(const Plan& s, const void* Q, const void* K, const void* V, const float* W, void* out,
                              char* ws, hipStream_t st) {
+  if (s.mode != FAVOR_CAUSAL) return launch_relu_bidirectional(s, Q, K, V, W, out, ws, st);
   const GenLayout w = gen_layout(s);
   auto F = [&](size_t off) { return reinterpret_cast<float*>(ws + off); };
-  float *phq = F(w.phq), *phk = F(w.phk), *v1 = F(w.v1), *S = F(w.S), *ND = F(w.ND);
+  float *phq = F(w.phq), *phk = F(w.phk), *v1 = F(w.v1), *S = F(w.S), *ND = F(w.ND), *Pm = F(w.Pm);
   const int L = s.L, Lp = w.Lp, NC = w.NC, m = s.m, D1 = D + 1, G = s.G, BH = s.BH;
   const long long Rq = (long long)s.B * s.Hq * L, Rkp = (long long)BH * Lp;
   const long long sm = (long long)m * D1;
@@ -90,26 +94,16 @@ favor_status run_generalized(const Plan& s, const void* Q, const void* K, const 
   hipLaunchKernelGGL((ones_column<T, D>), dim3(row_blocks(Rkp)), dim3(256), 0, st, static_cast<const T*>(V), v1,
                      Rkp, L, Lp);
   FAVOR_LAUNCHED();
-  if (s.mode != FAVOR_CAUSAL) {
-    const int GL = G * L;
-    // S = phi(K)^T [V, 1] per kv head; [N, D] = phi(Q) S over the G L query rows of the head
-    FAVOR_TRY((gemm_split<true, false>(phk, v1, S, F(w.part), m, D1, L, m, D1, (long long)L * m, (long long)L * D1,
-                                       kIdent, kIdent, BH, w.split, st)));
-    FAVOR_TRY((gemm<false, false>(phq, S, ND, GL, D1, m, m, D1, D1, (long long)GL * m, sm, (long long)GL * D1,
-                                  kIdent, kIdent, BH, st)));
-  } else {
-    const int C = kGenChunk, Zq = s.B * s.Hq * NC, Zk = BH * NC;
-    const long long cm = (long long)C * m, cd1 = (long long)C * D1, cc = (long long)C * C;
-    const BMap key_of_q{G * NC, 0x7fffffff, NC, NC};
-    float* Pm = F(w.Pm);
-    FAVOR_TRY((gemm<true, false>(phk, v1, S, m, D1, C, m, D1, D1, cm, cd1, sm, kIdent, kIdent, Zk, st)));
-    hipLaunchKernelGGL(chunk_prefix, dim3((unsigned)((sm + 255) / 256), (unsigned)BH), dim3(256), 0, st, S, NC,
-                       (int)sm);
-    FAVOR_LAUNCHED();
-    FAVOR_TRY((gemm<false, true>(phq, phk, Pm, C, C, m, m, m, C, cm, cm, cc, kIdent, key_of_q, Zq, st, kTril)));
-    FAVOR_TRY((gemm<false, false>(Pm, v1, ND, C, D1, C, C, D1, D1, cc, cd1, cd1, kIdent, key_of_q, Zq, st)));
-    FAVOR_TRY((gemm<false, false>(phq, S, ND, C, D1, m, m, D1, D1, cm, sm, cd1, kIdent, key_of_q, Zq, st, kAccum)));
-  }
+  const int C = kGenChunk, Zq = s.B * s.Hq * NC, Zk = BH * NC;
+  const long long cm = (long long)C * m, cd1 = (long long)C * D1, cc = (long long)C * C;
+  const BMap key_of_q{G * NC, 0x7fffffff, NC, NC};
+  FAVOR_TRY((gemm<true, false>(phk, v1, S, m, D1, C, m, D1, D1, cm, cd1, sm, kIdent, kIdent, Zk, st)));
+  hipLaunchKernelGGL(chunk_prefix, dim3((unsigned)((sm + 255) / 256), (unsigned)BH), dim3(256), 0, st, S, NC,
+                     (int)sm);
+  FAVOR_LAUNCHED();
+  FAVOR_TRY((gemm<false, true>(phq, phk, Pm, C, C, m, m, m, C, cm, cm, cc, kIdent, key_of_q, Zq, st, kTril)));
+  FAVOR_TRY((gemm<false, false>(Pm, v1, ND, C, D1, C, C, D1, D1, cc, cd1, cd1, kIdent, key_of_q, Zq, st)));
+  FAVOR_TRY((gemm<false, false>(phq, S, ND, C, D1, m, m, D1, D1, cm, sm, cd1, kIdent, key_of_q, Zq, st, kAccum)));
   hipLaunchKernelGGL((ratio_out<T, D>), dim3(row_blocks(Rq)), dim3(256), 0, st, ND, static_cast<T*>(out), Rq, L,
                      Lp);
   FAVOR_LAUNCHED();

@@ -110,7 +110,10 @@ template <> struct KvCfg<float, 128> { static constexpr int KW = 4, NTW = 1; };
 // SEG (causal segments): each wave owns one whole segment instead of a share of a range,
 // so the position groups of a workgroup are PG consecutive segments and every wave writes
 // its own partial with its own stabilisers (no merge, no workgroup barrier).
-template <class T, int D, bool SEG>
+// RELU: the feature map ReLU(W k) in place of the exponential (no norm term, no
+// stabiliser: c_f = 0 throughout, so the partials merge as plain sums).  W keeps its
+// log2 e scale, which both sides share and the ratio cancels.
+template <class T, int D, bool SEG, bool RELU = false>
 __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
     const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ W, int L, int Hkv, int Hw, int m,
     int R, int T_ranges, int n_units, float* __restrict__ gs, float* __restrict__ gc, char* __restrict__ img_w,
@@ -264,14 +267,21 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) c1[nt] = mma(kf[kc], wop(nt, kc), c1[nt]);
     }
-    float nrm = sumsq(kf);
-    nrm += partner32(nrm);
-    const float rb = p0 + col < we ? 0.5f * kLog2e * nrm : kMaskedRow;
+    float rb = kMaskedRow;  // keys past the range: features exactly 0
+    if constexpr (RELU) {
+      if (p0 + col < we) rb = 0.f;
+    } else {
+      float nrm = sumsq(kf);
+      nrm += partner32(nrm);
+      if (p0 + col < we) rb = 0.5f * kLog2e * nrm;
+    }
     const wfrag biasA = bias_rows(rb, g, wfrag{});
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) c1[nt] = mma(biasA, biasB[nt], c1[nt]);
 
-    if constexpr (MODE == 0) {
+    if constexpr (RELU) {
+      // no stabiliser
+    } else if constexpr (MODE == 0) {
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         float mx = c1[nt][0];
@@ -319,7 +329,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
     for (int nt = 0; nt < NTW; ++nt) {
       f32x16 e;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) e[r] = fast_exp2(c1[nt][r]);
+      for (int r = 0; r < 16; ++r) e[r] = RELU ? fmaxf(c1[nt][r], 0.f) : fast_exp2(c1[nt][r]);
       acc_to_frags(e, pa[nt]);
     }
 #pragma unroll
@@ -335,7 +345,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   auto reset = [&]() {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
-      cst[nt] = -INFINITY;
+      cst[nt] = RELU ? 0.f : -INFINITY;
       biasB[nt] = bias_cols(0.f, g, wfrag{});
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) S[nt][dt] = zero16();
@@ -358,7 +368,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) chk += S[nt][dt][r];
-  if (wave_any(!(chk - chk == 0.f))) {
+  if (!RELU && wave_any(!(chk - chk == 0.f))) {
     reset();
     if constexpr (!WLDS) fetch(wb);
     for (int p0 = wb; p0 < we; p0 += 32) block(p0, std::integral_constant<int, 2>{});
@@ -459,7 +469,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   if (pgi != 0) return;
 
   const size_t unit_off = (size_t)bh * T_ranges + t;
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (sizeof(T) == 2 && !RELU) {
     if (img_s != nullptr) {
       // The image holds S_v / S_1 per feature (rows already in vperm order: V was staged
       // permuted, lane col is row 32 dt + col) and c'_f = c_f + log2 S_1,f, so the readout's
@@ -937,7 +947,9 @@ __device__ __forceinline__ float s_frag(const float* Sl, int ld, int row, int ft
   return Sl[row * ld + 32 * ft + 8 * (r >> 2) + 4 * g + (r & 3)];
 }
 
-template <class T, int D>
+// RELU: the feature map ReLU(W q) with the key side's RELU partials (no stabilisers); a
+// row whose denominator is 0 (no positive weight) is written as zeros.
+template <class T, int D, bool RELU = false>
 __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
     readout_kernel(const T* __restrict__ Q, const float* __restrict__ W, const float* __restrict__ gs,
                    const float* __restrict__ gc, T* __restrict__ out, int L, int Hq, int Hkv, int Hw, int m,
@@ -949,7 +961,10 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
   using Cfg = ReadoutCfg<T, D>;
   constexpr int NKC = D / P::KS;
   constexpr int NDT = D / 32 + 1;
-  constexpr int MP = Cfg::MP, LDW = Cfg::LDW, LDSS = Cfg::LDS, QN = Cfg::QN;
+  // RELU with bf16 data stages up to 256 features per pass (W and S^T in 140 KB of LDS at
+  // d = 128): with m <= 256 they are staged once, not once per query tile
+  constexpr int MP = RELU && sizeof(T) == 2 ? 256 : Cfg::MP;
+  constexpr int LDW = Cfg::LDW, LDSS = RELU && sizeof(T) == 2 ? MP + 8 : Cfg::LDS, QN = Cfg::QN;
   constexpr int NT = 64 * Cfg::NWAVE;
   constexpr int SROWS = D + 1;
   constexpr int TILE = Cfg::NWAVE * QN * 32;
@@ -1077,7 +1092,7 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
         f32x16 e;
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          e[r] = fast_exp2(decltype(sub_tag)::value ? c1[q][r] - M[q] : c1[q][r]);
+          e[r] = RELU ? fmaxf(c1[q][r], 0.f) : fast_exp2(decltype(sub_tag)::value ? c1[q][r] - M[q] : c1[q][r]);
         acc_to_frags(e, pf[q]);
       }
 #pragma unroll
@@ -1118,7 +1133,13 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
           __syncthreads();
         }
         const int nft = min(MP, m - pass * MP) / 32;
-        if (fast) {
+        if (RELU) {
+          for (int ft = 0; ft < nft; ++ft) {
+            f32x16 c1[QN];
+            c1_tile(ft, c1, No{});
+            readout_tile(ft, c1, No{});
+          }
+        } else if (fast) {
           int ft = 0;
           if (pass == 0) {
             f32x16 c1[QN];
@@ -1164,14 +1185,14 @@ __global__ void __launch_bounds__((64 * ReadoutCfg<T, D>::NWAVE))
       const float dq = acc[q][NDT - 1][0];
       bad |= !(dq - dq == 0.f);
     }
-    if (__syncthreads_or(bad)) run(false);
+    if (!RELU && __syncthreads_or(bad)) run(false);
 
 #pragma unroll
     for (int q = 0; q < QN; ++q) {
       float den = acc[q][NDT - 1][0];
       const float dp = partner32(den);
       den = g ? dp : den;
-      const float inv = 1.f / den;
+      const float inv = RELU ? (den > 0.f ? 1.f / den : 0.f) : 1.f / den;
       if (!valid[q]) continue;
       T* orow = Ob + myrow[q] * D;
 #pragma unroll
@@ -2035,6 +2056,27 @@ favor_status run_bidirectional(const Plan& s, const T* Q, const T* K, const T* V
 }
 
 template <class T, int D>
+favor_status run_relu_bidirectional(const Plan& s, const T* Q, const T* K, const T* V, const float* W, T* out,
+                                    char* ws, hipStream_t st) {
+  float* gs = reinterpret_cast<float*>(ws + s.off_gs);
+  float* gc = reinterpret_cast<float*>(ws + s.off_gc);
+  const int units = s.BH * s.T, nfs = s.m / kFeatPerWave;
+  hipLaunchKernelGGL((kv_summary_kernel<T, D, false, true>), dim3(8 * ceil_div_i(units, 8) * nfs),
+                     dim3(64 * KvCfg<T, D>::KW), 0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc,
+                     nullptr, nullptr, nullptr);
+  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
+  using Cfg = ReadoutCfg<T, D>;
+  const long long rows = (long long)s.G * s.L;
+  const int tiles = ceil_div_i(rows, Cfg::NWAVE * Cfg::QN * 32);
+  int per_head = ceil_div_i(kReadoutTarget, s.BH);
+  if (per_head > tiles) per_head = tiles;
+  if (per_head < 1) per_head = 1;
+  hipLaunchKernelGGL((readout_kernel<T, D, true>), dim3(per_head, s.BH), dim3(64 * Cfg::NWAVE), 0, st, Q, W, gs, gc,
+                     out, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.T);
+  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
+template <class T, int D>
 favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const float* W, T* out, char* ws,
                         hipStream_t st, const Marks& mk) {
   float* gs = reinterpret_cast<float*>(ws + s.off_gs);
@@ -2128,6 +2170,21 @@ favor_status launch_key_summaries(const Plan& plan, const void* K, const void* V
                                                   gs, gc, nullptr, st)
                    : launch_kv_summary<float, 128>(s, static_cast<const float*>(K), static_cast<const float*>(V), W,
                                                    gs, gc, nullptr, st);
+}
+
+favor_status launch_relu_bidirectional(const Plan& s, const void* Q, const void* K, const void* V, const float* W,
+                                       void* out, char* ws, hipStream_t st) {
+  if (s.mode != FAVOR_BIDIRECTIONAL) return FAVOR_ERR_INVALID_ARG;
+  if (s.dtype == FAVOR_BF16) {
+    const bf16 *q = static_cast<const bf16*>(Q), *k = static_cast<const bf16*>(K), *v = static_cast<const bf16*>(V);
+    bf16* o = static_cast<bf16*>(out);
+    return s.d == 64 ? run_relu_bidirectional<bf16, 64>(s, q, k, v, W, o, ws, st)
+                     : run_relu_bidirectional<bf16, 128>(s, q, k, v, W, o, ws, st);
+  }
+  const float *q = static_cast<const float*>(Q), *k = static_cast<const float*>(K), *v = static_cast<const float*>(V);
+  float* o = static_cast<float*>(out);
+  return s.d == 64 ? run_relu_bidirectional<float, 64>(s, q, k, v, W, o, ws, st)
+                   : run_relu_bidirectional<float, 128>(s, q, k, v, W, o, ws, st);
 }
 
 }  // namespace favor

@@ -34,6 +34,13 @@ favor_status launch_relu_features(const Plan& s, int side, const void* X, const 
 favor_status launch_key_summaries(const Plan& s, const void* K, const void* V, const float* W, float* gs,
                                   float* gc, hipStream_t st);
 
+// Bidirectional attention with the ReLU feature map: the key side's range summaries of
+// ReLU(W k) [v, 1] into gs (gc = 0: no stabilisers), then a readout of ReLU(W q) against
+// them (rows with a zero denominator written as zeros).  Workspace: gs and gc of the plan
+// (s.off_p bytes).
+favor_status launch_relu_bidirectional(const Plan& s, const void* Q, const void* K, const void* V, const float* W,
+                                       void* out, char* ws, hipStream_t st);
+
 // The causal pass of bf16 problems after the key side has written the segment summaries:
 // the exclusive scan with per-feature stabilisers, then the chunked pass (features over the
 // waves for d = 64, value columns and feature groups for d = 128) and its repair pass, for

@@ -45,6 +45,13 @@ CASES = [
     _small("c2_bidir_bf16", False, batch=2, heads_q=6, heads_kv=2, heads_w=2, seq_len=129),
     _small("c4_mqa_bidir_bf16", False, batch=2, heads_q=4, heads_kv=1, heads_w=1, seq_len=300),
     _small("c1_bidir_f32", False, seq_len=333),
+    # fused path: three readout passes over m = 384 features, float32 d = 128, one position,
+    # one kv head with many position ranges
+    _small("c4_mqa_bidir_bf16", False, batch=1, heads_q=3, heads_kv=1, heads_w=1, seq_len=1500, num_features=384),
+    _small("c1_bidir_f32", False, batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=333, head_dim=128,
+           num_features=192),
+    _small("c2_bidir_bf16", False, batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=1, num_features=64),
+    _small("c2_bidir_bf16", False, batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=5000, num_features=128),
     _small("c3_causal_bf16", True, batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1000),
     _small("c3_causal_bf16", True, batch=2, heads_q=4, heads_kv=2, heads_w=2, seq_len=65, num_features=64),
     _small("c3_causal_bf16", True, batch=1, heads_q=2, heads_kv=1, heads_w=1, seq_len=300, head_dim=128),
@@ -81,24 +88,27 @@ def test_relu_attention_full_size_sampled_rows(name):
     assert err < TOL[w.dtype]
 
 
-def test_relu_attention_ones_and_zero_rows():
+@pytest.mark.parametrize("base", ["c1_bidir_f32", "c2_bidir_bf16"])
+def test_relu_attention_ones_and_zero_rows(base):
     """V = 1 gives 1; a query with no positive feature gets a zero row."""
-    w = _small("c1_bidir_f32", True, batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=130, num_features=64)
+    w = _small(base, True, batch=1, heads_q=1, heads_kv=1, heads_w=1, seq_len=130, num_features=64)
+    tol = TOL[w.dtype] if w.dtype == "bf16" else 1e-5
     Q, K, V, W = I.make_inputs(w, seed=1)
     W, K, Q = np.abs(W), np.abs(K), np.abs(Q)  # every other row and key has positive features
     Q[0, 0, 5] = -Q[0, 0, 5]                    # W q < 0 for every feature
-    y = _run(w, Q, K, np.ones_like(V), W).cpu().numpy()
+    y = _run(w, Q, K, np.ones_like(V), W).float().cpu().numpy()
     assert np.all(y[0, 0, 5] == 0)
     keep = np.ones(w.seq_len, bool)
     keep[5] = False
-    assert np.max(np.abs(y[0, 0, keep] - 1)) < 1e-5
+    assert np.max(np.abs(y[0, 0, keep] - 1)) < tol
     for causal in (False, True):
-        y = _run(w.replace(causal=causal), Q, K, V, W).cpu().numpy()
+        y = _run(w.replace(causal=causal), Q, K, V, W).float().cpu().numpy()
         ref = O.generalized_attention(Q, K, V, W, causal=causal)
-        assert np.all(y[0, 0, 5] == 0) and O.rowwise_rel_err(y[0, 0, keep], ref[0, 0, keep]) < TOL["f32"]
+        assert np.all(y[0, 0, 5] == 0) and O.rowwise_rel_err(y[0, 0, keep], ref[0, 0, keep]) < TOL[w.dtype]
 
 
-def test_relu_attention_deterministic():
-    w = CASES[4]
+@pytest.mark.parametrize("causal", [False, True])
+def test_relu_attention_deterministic(causal):
+    w = _small("c2_bidir_bf16", causal, batch=1, heads_q=2, heads_kv=2, heads_w=2, seq_len=1000)
     Q, K, V, W = I.make_inputs(w, seed=5)
     assert torch.equal(_run(w, Q, K, V, W), _run(w, Q, K, V, W))
