@@ -709,9 +709,8 @@ def backward_main(args, w):
 def generalized_main(args, w):
     """Kernelised attention with the ReLU feature map (favor_attn_fwd_generalized): one step =
     one call on the workload (inputs resident).  Algorithmic flops as for the softmax forward
-    (features of Q and K, S, phi(Q) S).  Bidirectional problems run fused MFMA kernels in the
-    input's precision (bf16: fp16 W contraction, bf16 products), so the roofline is that
-    dtype's matrix peak; causal problems run float32 products (the float32 peak)."""
+    (features of Q and K, S, phi(Q) S).  The kernels run MFMA in the input's precision (bf16:
+    fp16 W contraction, bf16 products), so the roofline is that dtype's matrix peak."""
     import numpy as np
     import torch
 
@@ -751,7 +750,7 @@ def generalized_main(args, w):
     Rq, Rk = B * Hq * L, B * Hkv * L
     flops = 2 * m * ((Rq + Rk) * d + (Rq + Rk) * (d + 1))
     achieved = flops / (ms_step * 1e-3) / 1e12
-    cdt = "f32" if w.causal else w.dtype
+    cdt = w.dtype
     res = {
         "metric": "kernelised attention (ReLU random features) fwd tokens/s (B*H*L/s), 1 GPU",
         "value": round(Rq / (ms_step * 1e-3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,

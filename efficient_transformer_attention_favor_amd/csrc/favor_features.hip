@@ -45,8 +45,7 @@ __device__ __forceinline__ float dec_order(unsigned k) {
 }
 
 // MODE 0: queries (row stabiliser, two passes in the kernel); 1: keys, head-maximum pass;
-// 2: keys, writing pass with the head maximum from pass 1; 3: the ReLU feature map
-// ReLU(W x) / sqrt(m) of queries or keys (no norm term, no stabiliser; c_out unused).
+// 2: keys, writing pass with the head maximum from pass 1.
 template <class T, int D, int MODE, bool LW>
 __global__ void __launch_bounds__(64 * (LW ? kFeatLdsWaves : kFeatWaves))
     features_kernel(const T* __restrict__ X, const float* __restrict__ W, int L, int Lo, int H, int G, int Hw,
@@ -100,10 +99,8 @@ __global__ void __launch_bounds__(64 * (LW ? kFeatLdsWaves : kFeatWaves))
         load_w_frag(Wh + (size_t)(32 * ft + col) * D, kc, g, wp);
       c = mma(wp, xf[kc], c);
     }
-    if constexpr (MODE != 3) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) c[r] -= half_norm;
-    }
+    for (int r = 0; r < 16; ++r) c[r] -= half_norm;
     return c;
   };
   const float inv_sqrt_m = 1.0f / sqrtf((float)m);
@@ -117,12 +114,7 @@ __global__ void __launch_bounds__(64 * (LW ? kFeatLdsWaves : kFeatWaves))
         f32x4 v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          float x;
-          if constexpr (MODE == 3)
-            x = fmaxf(e[4 * r4 + i], 0.f) * (inv_sqrt_m / kLog2e);  // the W operand carries log2 e
-          else
-            x = fast_exp2(e[4 * r4 + i] - cst) * inv_sqrt_m;
-          v[i] = valid ? x : 0.f;
+          v[i] = valid ? fast_exp2(e[4 * r4 + i] - cst) * inv_sqrt_m : 0.f;
         }
         *reinterpret_cast<f32x4*>(dst + 8 * r4) = v;
       }
@@ -131,10 +123,6 @@ __global__ void __launch_bounds__(64 * (LW ? kFeatLdsWaves : kFeatWaves))
 
   if constexpr (MODE == 2) {
     write(dec_order(reinterpret_cast<const unsigned*>(c_out)[bh]));
-    return;
-  }
-  if constexpr (MODE == 3) {
-    write(0.f);
     return;
   }
   float mx = -INFINITY;
@@ -202,25 +190,7 @@ favor_status run_features(const Plan& s, int side, const void* Xv, const float* 
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
-template <class T, int D>
-favor_status run_relu_features(const Plan& s, int side, const void* Xv, const float* W, float* phi, int Lo,
-                               hipStream_t st) {
-  const int H = side == 0 ? s.Hq : s.Hkv, G = side == 0 ? s.G : 1;
-  return launch_mode<T, D, 3>(s, static_cast<const T*>(Xv), W, Lo, H, G, phi, nullptr, st) ? FAVOR_OK
-                                                                                            : FAVOR_ERR_HIP;
-}
-
 }  // namespace
-
-favor_status launch_relu_features(const Plan& s, int side, const void* X, const float* W, float* phi,
-                                  hipStream_t st, int Lo) {
-  if (Lo < s.L) Lo = s.L;
-  if (s.dtype == FAVOR_BF16)
-    return s.d == 64 ? run_relu_features<bf16, 64>(s, side, X, W, phi, Lo, st)
-                     : run_relu_features<bf16, 128>(s, side, X, W, phi, Lo, st);
-  return s.d == 64 ? run_relu_features<float, 64>(s, side, X, W, phi, Lo, st)
-                   : run_relu_features<float, 128>(s, side, X, W, phi, Lo, st);
-}
 
 favor_status launch_features(const Plan& s, int side, const void* X, const float* W, float* phi, float* c,
                              hipStream_t st, int Lo) {

@@ -22,11 +22,6 @@ struct Marks {
 favor_status launch_features(const Plan& s, int side, const void* X, const float* W, float* phi, float* c,
                              hipStream_t st, int Lo = 0);
 
-// The ReLU feature map ReLU(W x) / sqrt(m) of the queries (side 0) or keys (side 1) as
-// float32 [rows][m], Lo rows per head as above.
-favor_status launch_relu_features(const Plan& s, int side, const void* X, const float* W, float* phi,
-                                  hipStream_t st, int Lo = 0);
-
 // The key-side range summaries of a bidirectional plan as float32 partials:
 // gs [BH][T][d+1][m] (value rows in the permuted order vperm within each 32-column tile, row d
 // the ones column) and gc [BH][T][m], the per-feature stabilisers in log2 units, with
@@ -34,12 +29,14 @@ favor_status launch_relu_features(const Plan& s, int side, const void* X, const 
 favor_status launch_key_summaries(const Plan& s, const void* K, const void* V, const float* W, float* gs,
                                   float* gc, hipStream_t st);
 
-// Bidirectional attention with the ReLU feature map: the key side's range summaries of
-// ReLU(W k) [v, 1] into gs (gc = 0: no stabilisers), then a readout of ReLU(W q) against
-// them (rows with a zero denominator written as zeros).  Workspace: gs and gc of the plan
-// (s.off_p bytes).
-favor_status launch_relu_bidirectional(const Plan& s, const void* Q, const void* K, const void* V, const float* W,
-                                       void* out, char* ws, hipStream_t st);
+// Attention with the ReLU feature map, on the softmax forward's kernels in their ReLU mode:
+// bidirectional, the key side's range summaries of ReLU(W k) [v, 1] (no stabilisers), then
+// a readout of ReLU(W q) against them; causal, the segment summaries, their exclusive
+// prefix and the chunk kernel.  Rows with a zero denominator are written as zeros.
+// Workspace: relu_workspace_bytes(s) bytes laid out as the plan's.
+size_t relu_workspace_bytes(const Plan& s);
+favor_status launch_relu_attention(const Plan& s, const void* Q, const void* K, const void* V, const float* W,
+                                   void* out, char* ws, hipStream_t st);
 
 // The causal pass of bf16 problems after the key side has written the segment summaries:
 // the exclusive scan with per-feature stabilisers, then the chunked pass (features over the

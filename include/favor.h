@@ -148,10 +148,12 @@ favor_status favor_features(const favor_problem* p, int32_t side, const void* X,
  * order like favor_attn_fwd.  fn selects phi:
  *   FAVOR_FEATURE_RELU  phi(x) = ReLU(W x) / sqrt(m)  (the first-order arc-cosine kernel).
  * A row whose weights are all zero gets a zero output.  Arguments, layouts and errors as
- * for favor_attn_fwd (an unknown fn is FAVOR_ERR_UNSUPPORTED); the workspace
- * (favor_generalized_workspace_bytes(p, fn) bytes, 256-byte aligned) holds the float32
- * feature matrices, about m (B Hq + B Hkv) L floats.  The features are materialised and
- * the products run in float32 (about 8 kernels on `stream`). */
+ * for favor_attn_fwd (an unknown fn is FAVOR_ERR_UNSUPPORTED, also p->chunk as there); the
+ * workspace (favor_generalized_workspace_bytes(p, fn) bytes, 256-byte aligned) holds the
+ * float32 range or segment summaries, as favor_attn_fwd's does.  The features stay on chip;
+ * the arithmetic is favor_attn_fwd's (bf16 problems: fp16 W contraction, bf16 features and
+ * products, float32 accumulation).  Queues 2 (bidirectional) or 3-4 (causal: key side,
+ * prefix scan, one or two chunked passes) kernels on `stream`. */
 typedef enum { FAVOR_FEATURE_RELU = 1 } favor_feature_fn;
 size_t favor_generalized_workspace_bytes(const favor_problem* p, int32_t fn);
 favor_status favor_attn_fwd_generalized(const favor_problem* p, int32_t fn, const void* Q, const void* K,
