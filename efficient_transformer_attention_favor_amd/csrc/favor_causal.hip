@@ -32,24 +32,24 @@ namespace favor {
 // ======================================================================================
 // causal_scan_pf: per kv head bh and feature f, walking the segments in order,
 //   P_t = sum_{t' < t} 2^(c_t'f - C_tf) S_t'f,   C_tf = max_{t' < t} c_t'f   (-inf for t = 0)
-// in the summaries' layout [d+1][m] (rows in vperm order, row d the ones column).  Grid
-// (element groups of the [d+1][m] plane, B*Hkv); each thread owns 4 consecutive features of
+// in the summaries' layout [d+1][m] (rows in vperm order, row d the ones column; float32 or
+// bf16 elements, accumulated in float32).  Grid (element groups of the [d+1][m] plane, B*Hkv); each thread owns 4 consecutive features of
 // one row and keeps the running maximum of those features itself; the threads of row 0
 // also write C_t.  TB segments' loads are in flight at a time.
 // ======================================================================================
-__global__ void __launch_bounds__(256) causal_scan_pf_kernel(const float* __restrict__ gs,
-                                                             const float* __restrict__ gc, int T_ranges, int m,
-                                                             int D, float* __restrict__ prefix,
+template <class ST>
+__global__ void __launch_bounds__(256) causal_scan_pf_kernel(const ST* __restrict__ gs, const float* __restrict__ gc,
+                                                             int T_ranges, int m, int D, ST* __restrict__ prefix,
                                                              float* __restrict__ prefix_c) {
   const int bh = blockIdx.y;
-  const int e4 = blockIdx.x * 256 + threadIdx.x;  // float4 index within the [d+1][m] plane
+  const int e4 = blockIdx.x * 256 + threadIdx.x;  // group of 4 elements within the [d+1][m] plane
   if (e4 >= (D + 1) * m / 4) return;
   const int f = (e4 * 4) % m;
   const bool row0 = e4 * 4 < m;
   const size_t plane = (size_t)(D + 1) * m;
   const float* pc = gc + (size_t)bh * T_ranges * m;
-  const f32x4* src = reinterpret_cast<const f32x4*>(gs + (size_t)bh * T_ranges * plane) + e4;
-  f32x4* dst = reinterpret_cast<f32x4*>(prefix + (size_t)bh * T_ranges * plane) + e4;
+  const ST* src = gs + (size_t)bh * T_ranges * plane + 4 * (size_t)e4;
+  ST* dst = prefix + (size_t)bh * T_ranges * plane + 4 * (size_t)e4;
   float* dc = prefix_c + (size_t)bh * T_ranges * m + f;
   constexpr int TB = 8;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -59,14 +59,14 @@ __global__ void __launch_bounds__(256) causal_scan_pf_kernel(const float* __rest
 #pragma unroll
     for (int u = 0; u < TB; ++u) {
       const int t = min(t0 + u, T_ranges - 1);
-      sv[u] = src[(size_t)t * (plane / 4)];
+      sv[u] = load_sum4(src + (size_t)t * plane);
       cv[u] = *reinterpret_cast<const f32x4*>(pc + (size_t)t * m + f);
     }
 #pragma unroll
     for (int u = 0; u < TB; ++u) {
       const int t = t0 + u;
       if (t >= T_ranges) break;
-      dst[(size_t)t * (plane / 4)] = acc;
+      store_sum4(dst + (size_t)t * plane, acc);
       if (row0) *reinterpret_cast<f32x4*>(dc + (size_t)t * m) = run;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -119,7 +119,7 @@ template <int D, int NFG> struct CausalV {
 template <int D, int NFTMAX, int NFG, bool REPAIR>
 __global__ void __launch_bounds__(64 * (D / 32) * NFG, (D / 32) * NFG == 4 && !REPAIR ? 2 : 1) causal_v_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ W,
-    const float* __restrict__ prefix, const float* __restrict__ prefix_c, bf16* __restrict__ out, int L, int Hq,
+    const bf16* __restrict__ prefix, const float* __restrict__ prefix_c, bf16* __restrict__ out, int L, int Hq,
     int Hkv, int Hw, int m, int R, int T_ranges, int* __restrict__ wide) {
   using Cfg = CausalV<D, NFG>;
   constexpr int NV = Cfg::NV, NW = Cfg::NW, LDK = Cfg::LDK, LDV = Cfg::LDV, LDP = Cfg::LDP, LDN = Cfg::LDN;
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(64 * (D / 32) * NFG, (D / 32) * NFG == 4 && !R
   }
   // carry of value tile vt, features of group fg: tile ct covers features 32 (fg nct + ct) + ..
   const int nct = NFT / NFG;
-  const float* Pp = prefix + ((size_t)bh * T_ranges + seg) * (size_t)(D + 1) * m;
+  const bf16* Pp = prefix + ((size_t)bh * T_ranges + seg) * (size_t)(D + 1) * m;
   f32x16 carry[NCT];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -182,13 +182,13 @@ __global__ void __launch_bounds__(64 * (D / 32) * NFG, (D / 32) * NFG == 4 && !R
       const int fb = 32 * (fg * nct + ct);
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(Pp + (size_t)(32 * vt + col) * m + fb + 8 * r4 + 4 * g);
+        const f32x4 v = load_sum4(Pp + (size_t)(32 * vt + col) * m + fb + 8 * r4 + 4 * g);
 #pragma unroll
         for (int i = 0; i < 4; ++i) carry[ct][4 * r4 + i] = v[i];
       }
     }
   }
-  for (int f = threadIdx.x; f < m; f += NT) S1[f] = Pp[(size_t)D * m + f];
+  for (int f = threadIdx.x; f < m; f += NT) S1[f] = (float)Pp[(size_t)D * m + f];
 
   // ---- staging: the block's Q, K (fp16) and V (bf16, columns permuted) ----------------
   // range-checked buffer loads: rows past L read as zero
@@ -550,7 +550,7 @@ template <int NW, int NB> struct CausalFg {
 template <int NW, int NB, bool REPAIR>
 __global__ void __launch_bounds__(64 * NW, REPAIR || NW < 4 || NB > 1 ? 1 : 8 / NW) causal_fg_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V, const float* __restrict__ W,
-    const float* __restrict__ prefix, const float* __restrict__ prefix_c, bf16* __restrict__ out, int L, int Hq,
+    const bf16* __restrict__ prefix, const float* __restrict__ prefix_c, bf16* __restrict__ out, int L, int Hq,
     int Hkv, int Hw, int m, int R, int T_ranges, int* __restrict__ wide, int n_units) {
   using Cfg = CausalFg<NW, NB>;
   static_assert(NB == 1 || !REPAIR, "the repair pass takes the chunk as 32 positions");
@@ -590,7 +590,7 @@ __global__ void __launch_bounds__(64 * NW, REPAIR || NW < 4 || NB > 1 ? 1 : 8 / 
   // bias operands of c_f: key side -(c_f) on the feature columns (0 while c_f is unset),
   // query side +c_f on the feature rows; rebuilt only when c_f moves
   f16x8 bk[2], bq[2];
-  const float* Pp = prefix + ((size_t)bh * T_ranges + seg) * (size_t)(D + 1) * m;
+  const bf16* Pp = prefix + ((size_t)bh * T_ranges + seg) * (size_t)(D + 1) * m;
   const float* Pc = prefix_c + ((size_t)bh * T_ranges + seg) * m;
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -605,12 +605,12 @@ __global__ void __launch_bounds__(64 * NW, REPAIR || NW < 4 || NB > 1 ? 1 : 8 / 
 #pragma unroll
       for (int kc = 0; kc < NKC; ++kc) load_w_frag(Wh + (size_t)(f + col) * D, kc, g, wf[i][kc]);
       cf[i] = Pc[f + col];
-      s1r[i] = Pp[(size_t)D * m + f + col];
+      s1r[i] = (float)Pp[(size_t)D * m + f + col];
 #pragma unroll
       for (int vt = 0; vt < 2; ++vt)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4 v = *reinterpret_cast<const f32x4*>(Pp + (size_t)(32 * vt + col) * m + f + 8 * r4 + 4 * g);
+          const f32x4 v = load_sum4(Pp + (size_t)(32 * vt + col) * m + f + 8 * r4 + 4 * g);
 #pragma unroll
           for (int q = 0; q < 4; ++q) carry[i][vt][4 * r4 + q] = v[q];
         }
@@ -1072,12 +1072,15 @@ __global__ void __launch_bounds__(64 * NW, REPAIR || NW < 4 || NB > 1 ? 1 : 8 / 
 // Exclusive scan of the segment summaries gs / gc with per-feature stabilisers into the
 // prefix region of the workspace.
 favor_status launch_causal_scan_pf(const Plan& s, char* ws, hipStream_t st) {
-  const float* gs = reinterpret_cast<const float*>(ws + s.off_gs);
   const float* gc = reinterpret_cast<const float*>(ws + s.off_gc);
-  float* prefix = reinterpret_cast<float*>(ws + s.off_p);
   float* prefix_c = reinterpret_cast<float*>(ws + s.off_pc);
-  hipLaunchKernelGGL(causal_scan_pf_kernel, dim3((unsigned)(((size_t)(s.d + 1) * s.m / 4 + 255) / 256), s.BH), dim3(256),
-                     0, st, gs, gc, s.T, s.m, s.d, prefix, prefix_c);
+  const dim3 grid((unsigned)(((size_t)(s.d + 1) * s.m / 4 + 255) / 256), s.BH);
+  if (s.dtype == FAVOR_BF16)
+    hipLaunchKernelGGL(causal_scan_pf_kernel<bf16>, grid, dim3(256), 0, st, reinterpret_cast<const bf16*>(ws + s.off_gs),
+                       gc, s.T, s.m, s.d, reinterpret_cast<bf16*>(ws + s.off_p), prefix_c);
+  else
+    hipLaunchKernelGGL(causal_scan_pf_kernel<float>, grid, dim3(256), 0, st, reinterpret_cast<const float*>(ws + s.off_gs),
+                       gc, s.T, s.m, s.d, reinterpret_cast<float*>(ws + s.off_p), prefix_c);
   return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
 }
 
@@ -1094,7 +1097,7 @@ namespace {
 
 template <int NW, int NB, bool RP>
 void launch_fg(const Plan& s, dim3 grid, const bf16* q, const bf16* k, const bf16* v, const float* W,
-               const float* prefix, const float* prefix_c, bf16* o, int* wide, hipStream_t st) {
+               const bf16* prefix, const float* prefix_c, bf16* o, int* wide, hipStream_t st) {
   const int n_units = s.T * s.B * s.Hq;
   // the repair pass: one workgroup per CU at most, walking the segment flags
   const dim3 g = RP ? dim3((unsigned)(n_units < kCUs ? n_units : kCUs)) : grid;
@@ -1104,7 +1107,7 @@ void launch_fg(const Plan& s, dim3 grid, const bf16* q, const bf16* k, const bf1
 
 template <int NB, bool RP>
 void launch_fg_nw(const Plan& s, dim3 grid, const bf16* q, const bf16* k, const bf16* v, const float* W,
-                  const float* prefix, const float* prefix_c, bf16* o, int* wide, hipStream_t st) {
+                  const bf16* prefix, const float* prefix_c, bf16* o, int* wide, hipStream_t st) {
   // one wave per 64 features, NW rounded up to 1, 2, 4 or 8
   const int nw = s.m / 64;
   if (nw <= 1)
@@ -1126,7 +1129,7 @@ void launch_fg_nw(const Plan& s, dim3 grid, const bf16* q, const bf16* k, const 
 favor_status launch_causal_v(const Plan& s, const void* Q, const void* K, const void* V, const float* W, void* out,
                              char* ws, hipStream_t st) {
   if (!causal_v_supported(s) || !causal_chunk_supported(s)) return FAVOR_ERR_UNSUPPORTED;
-  const float* prefix = reinterpret_cast<const float*>(ws + s.off_p);
+  const bf16* prefix = reinterpret_cast<const bf16*>(ws + s.off_p);
   const float* prefix_c = reinterpret_cast<const float*>(ws + s.off_pc);
   const bf16* q = static_cast<const bf16*>(Q);
   const bf16* k = static_cast<const bf16*>(K);

@@ -62,6 +62,24 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ bool wave_any(bool p) { return __ballot(p) != 0; }
 
+// Causal segment summaries and their prefixes are stored in float32 for float32 problems and
+// in bf16 for bf16 problems (their consumers accumulate in float32 either way).
+template <class T> struct SumOf { using type = float; };
+template <> struct SumOf<bf16> { using type = bf16; };
+// four consecutive elements (16-byte aligned for float32, 8-byte for bf16)
+__device__ __forceinline__ f32x4 load_sum4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ f32x4 load_sum4(const bf16* p) {
+  const bf16x4_t v = *reinterpret_cast<const bf16x4_t*>(p);
+  return f32x4{(float)v[0], (float)v[1], (float)v[2], (float)v[3]};
+}
+__device__ __forceinline__ void store_sum4(float* p, const f32x4& v) { *reinterpret_cast<f32x4*>(p) = v; }
+__device__ __forceinline__ void store_sum4(bf16* p, const f32x4& v) {
+  bf16x4_t h;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) h[i] = (bf16)v[i];
+  *reinterpret_cast<bf16x4_t*>(p) = h;
+}
+
 __device__ __forceinline__ f32x16 mma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }

@@ -376,8 +376,11 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
 
   // The partial of unit_off (float32 gs rows in vperm order, row D the ones column, and
   // gc) relative to the stabilisers cmx of this lane's C1 features.
+  // causal segment summaries (SEG) are stored in the problem's summary type (bf16 for bf16
+  // problems), range partials in float32
   auto store_partial = [&](size_t unit_off, const float (&cmx)[NTW]) {
-    float* out_s = gs + unit_off * (size_t)(D + 1) * m;
+    using GST = std::conditional_t<SEG, typename SumOf<T>::type, float>;
+    GST* out_s = reinterpret_cast<GST*>(gs) + unit_off * (size_t)(D + 1) * m;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
@@ -385,14 +388,14 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           f32x4 v = {S[nt][dt][4 * r4], S[nt][dt][4 * r4 + 1], S[nt][dt][4 * r4 + 2], S[nt][dt][4 * r4 + 3]};
-          *reinterpret_cast<f32x4*>(out_s + (size_t)(32 * dt + col) * m + f0 + 32 * nt + 8 * r4 + 4 * g) = v;
+          store_sum4(out_s + (size_t)(32 * dt + col) * m + f0 + 32 * nt + 8 * r4 + 4 * g, v);
         }
       if (col == 0)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           f32x4 v = {S[nt][NDT - 1][4 * r4], S[nt][NDT - 1][4 * r4 + 1], S[nt][NDT - 1][4 * r4 + 2],
                      S[nt][NDT - 1][4 * r4 + 3]};
-          *reinterpret_cast<f32x4*>(out_s + (size_t)D * m + f0 + 32 * nt + 8 * r4 + 4 * g) = v;
+          store_sum4(out_s + (size_t)D * m + f0 + 32 * nt + 8 * r4 + 4 * g, v);
         }
       if (g == 0) gc[unit_off * m + f0 + 32 * nt + col] = cmx[nt];
     }
@@ -1563,7 +1566,8 @@ constexpr float kSpreadChunk = 100.f;  // as kSpread of the bf16 causal kernels 
 template <class T, int D, int NTC, int NWMAX, int PART, bool REPAIR, bool RELU = false>
 __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ W,
-    const float* __restrict__ prefix, const float* __restrict__ prefix_c, T* __restrict__ out, int L, int Hq,
+    const typename SumOf<T>::type* __restrict__ prefix, const float* __restrict__ prefix_c, T* __restrict__ out,
+    int L, int Hq,
     int Hkv, int Hw, int m, int R, int T_ranges, int fbase, float* __restrict__ part, int* __restrict__ wide,
     int n_units) {
   using P = Prec<T>;
@@ -1625,7 +1629,7 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
   // lane col takes row 32 dt + col, register r feature 8(r/4) + 4g + r%4 of the tile)
   f32x16 carry[NTC][NDT];
   {
-    const float* pf = prefix + ((size_t)bh * T_ranges + seg) * (size_t)(D + 1) * m;
+    const typename SumOf<T>::type* pf = prefix + ((size_t)bh * T_ranges + seg) * (size_t)(D + 1) * m;
 #pragma unroll
     for (int nt = 0; nt < NTC; ++nt)
 #pragma unroll
@@ -1635,7 +1639,7 @@ __global__ void __launch_bounds__(64 * NWMAX) causal_chunk_kernel(
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           f32x4 v = {0.f, 0.f, 0.f, 0.f};
-          if (live) v = *reinterpret_cast<const f32x4*>(pf + (size_t)row * m + f0 + 32 * nt + 8 * r4 + 4 * g);
+          if (live) v = load_sum4(pf + (size_t)row * m + f0 + 32 * nt + 8 * r4 + 4 * g);
 #pragma unroll
           for (int i = 0; i < 4; ++i) carry[nt][dt][4 * r4 + i] = v[i];
         }
@@ -2111,7 +2115,7 @@ favor_status run_causal(const Plan& s, const T* Q, const T* K, const T* V, const
     if (rc != FAVOR_OK) return rc;
     return mk.mark(3, st) ? FAVOR_OK : FAVOR_ERR_HIP;
   }
-  const float* prefix = reinterpret_cast<const float*>(ws + s.off_p);
+  const auto* prefix = reinterpret_cast<const typename SumOf<T>::type*>(ws + s.off_p);
   const float* prefix_c = reinterpret_cast<const float*>(ws + s.off_pc);
   int* wide = reinterpret_cast<int*>(ws + s.off_wide);
   const int n_units = s.T * s.B * s.Hq;
@@ -2173,7 +2177,7 @@ favor_status run_relu_causal(const Plan& s, const T* Q, const T* K, const T* V, 
   if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
   favor_status rc = launch_causal_scan_pf(s, ws, st);
   if (rc != FAVOR_OK) return rc;
-  const float* prefix = reinterpret_cast<const float*>(ws + s.off_p);
+  const auto* prefix = reinterpret_cast<const typename SumOf<T>::type*>(ws + s.off_p);
   const float* prefix_c = reinterpret_cast<const float*>(ws + s.off_pc);
   int* wide = reinterpret_cast<int*>(ws + s.off_wide);
   const int n_units = s.T * s.B * s.Hq;
