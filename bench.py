@@ -131,16 +131,18 @@ def source_digest():
     return h.hexdigest()
 
 
-def measured_traffic(workload, kernel):
+def measured_traffic(workload, kernel, chunk=0):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
-    for this workload, or None if there is none or the kernels changed since it was taken."""
+    for this workload at this chunk setting (the summaries are taken at the default, 0), or None
+    if there is none or the kernels changed since it was taken."""
     import glob
     for path in glob.glob(os.path.join(ROOT, "profiles", f"*_{workload}_traffic.txt")):
         with open(path) as f:
             for line in f:
                 if line.startswith("json: "):
                     rec = json.loads(line[6:])
-                    if rec.get("workload") == workload and rec.get("source_sha256") == source_digest():
+                    if (rec.get("workload") == workload and rec.get("chunk", 0) == chunk
+                            and rec.get("source_sha256") == source_digest()):
                         return rec["traffic_bytes"].get(kernel)
     return None
 
@@ -488,7 +490,7 @@ def forward_record(w, Q, K, V, W, chunk, steps, warmup, graph=False, copy_probe_
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(f / t_dom / 1e12, 2), "peak": peak_tf,
                 "unit": "TFLOP/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["traffic"] = measured_traffic(w.name, dom)
+    roof["traffic"] = measured_traffic(w.name, dom, chunk)
     roof["per_launch"] = {"alg_bytes": b, "alg_flops": f, "avg_ms": round(t_dom * 1e3, 5),
                           "event_ms": round(kms[dom], 5)}
     # the whole call against the roofline of its algorithmic work (Q, K, V read once, out

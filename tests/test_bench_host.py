@@ -49,3 +49,22 @@ def test_bench_refuses_more_than_one_gpu():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_traffic_only_for_the_profiled_setting(tmp_path, monkeypatch):
+    """A committed traffic summary is used for its workload at the chunk it was taken with,
+    and only while the kernel sources hash to its digest."""
+    prof = tmp_path / "profiles"
+    prof.mkdir()
+    rec = {"workload": "c3_causal_bf16", "source_sha256": bench.source_digest(),
+           "traffic_bytes": {"causal_chunk": 123}}
+    (prof / "x_c3_causal_bf16_traffic.txt").write_text("json: " + __import__("json").dumps(rec) + "\n")
+    digest = bench.source_digest()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "source_digest", lambda: digest)
+    assert bench.measured_traffic("c3_causal_bf16", "causal_chunk") == 123
+    assert bench.measured_traffic("c3_causal_bf16", "causal_chunk", 64) is None
+    assert bench.measured_traffic("c5_causal_long_bf16", "causal_chunk") is None
+    rec["source_sha256"] = "0" * 64
+    (prof / "x_c3_causal_bf16_traffic.txt").write_text("json: " + __import__("json").dumps(rec) + "\n")
+    assert bench.measured_traffic("c3_causal_bf16", "causal_chunk") is None
