@@ -124,7 +124,8 @@ def test_status_strings():
 
 def test_decode_validation():
     """favor_attn_decode takes causal problems of one position; its state size is the
-    summaries [B*Hkv][m][d+1] plus one stabiliser per kv head, 256-byte aligned."""
+    summaries [B*Hkv][m][d+1] plus a stabiliser and a count per slice of m/8 features,
+    256-byte aligned."""
     p = _p(mode=_lib.FAVOR_CAUSAL, seq_len=1, chunk=48)  # the chunk is ignored when decoding
     n = _lib.decode_state_bytes(p)
     assert n == ((2 * 2 * 128 * 65 + 2 * 2 * 8 * 2) * 4 + 255) // 256 * 256
