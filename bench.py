@@ -33,7 +33,9 @@ sys.path.insert(0, ROOT)
 METRIC = "FAVOR+ attention fwd tokens/s (B*H*L/s) and % MFMA/HBM roofline, 1 GPU"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA
-# Kernel slots of one call (the bidirectional path has no middle kernel).
+# Kernel slots of one call (the bidirectional path has no middle kernel; a small float32
+# call that runs as one launch fills the first slot only).
+FUSED_NAME = "small_fused"
 KERNELS = {
     False: ("kv_summary", None, "readout"),
     True: ("kv_summary", "causal_scan", "causal_chunk"),
@@ -74,7 +76,7 @@ class HipEvents:
             self.rt.hipEventDestroy(ctypes.c_void_p(e))
 
 
-def algorithmic_work(w):
+def algorithmic_work(w, fused=False):
     """Per-kernel algorithmic bytes and flops of one call (what FAVOR+ itself must move and do).
 
     Bytes: Q, K, V read once and out written once, plus W (and S where a kernel reads the
@@ -91,6 +93,8 @@ def algorithmic_work(w):
     k_bytes = 2 * e * B * Hkv * L * d
     q_bytes = 2 * e * B * Hq * L * d
     names = KERNELS[w.causal]
+    if fused:  # one launch: the whole call's reads, writes and flops
+        return {FUSED_NAME: (k_bytes + q_bytes + w_bytes, B * Hkv * side + B * Hq * side)}
     if not w.causal:
         return {names[0]: (k_bytes + w_bytes, B * Hkv * side),
                 names[2]: (q_bytes + w_bytes + s_bytes, B * Hq * side)}
@@ -111,7 +115,12 @@ def call_work(w):
 
 
 def kernel_names(w, p=None):
-    """Names of the kernel slots of one call (None for an empty slot)."""
+    """Names of the kernel slots of one call (None for an empty slot).  A call the library
+    runs as one launch (small float32 bidirectional problems) fills the first slot only."""
+    if p is not None and not w.causal:
+        from efficient_transformer_attention_favor_amd import _lib
+        if _lib.attn_fwd_launches(p) == 1:
+            return (FUSED_NAME, None, None)
     return KERNELS[w.causal]
 
 
@@ -464,7 +473,7 @@ def forward_record(w, Q, K, V, W, chunk, steps, warmup, graph=False, copy_probe_
         torch.cuda.synchronize()
         log(f"copy probe: {n} bytes device-to-device")
 
-    work = algorithmic_work(w)
+    work = algorithmic_work(w, fused=names[0] == FUSED_NAME)
     peak_tf = PEAK_TFLOPS[w.dtype]
     kms = {n: float(np.mean(v)) for n, v in samples.items()}
     ev_total = sum(kms.values())

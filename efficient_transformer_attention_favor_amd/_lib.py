@@ -29,7 +29,7 @@ EXPORTED = ("favor_workspace_bytes", "favor_attn_fwd", "favor_attn_fwd_timed", "
             "favor_decode_state_bytes", "favor_attn_decode", "favor_bwd_workspace_bytes", "favor_attn_bwd",
             "favor_draw_features", "favor_generalized_workspace_bytes", "favor_attn_fwd_generalized",
             "favor_decode_prefill_workspace_bytes", "favor_decode_prefill",
-            "favor_attn_fwd_noalloc", "favor_status_string", "favor_abi_version")
+            "favor_attn_fwd_noalloc", "favor_attn_fwd_launches", "favor_status_string", "favor_abi_version")
 
 
 class FavorProblem(ctypes.Structure):
@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         vp = ctypes.c_void_p
         L.favor_workspace_bytes.argtypes = [P]
         L.favor_workspace_bytes.restype = ctypes.c_size_t
+        L.favor_attn_fwd_launches.argtypes = [P]
+        L.favor_attn_fwd_launches.restype = ctypes.c_int32
         L.favor_attn_fwd.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.favor_attn_fwd.restype = ctypes.c_int
         L.favor_attn_fwd_timed.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp,
@@ -111,6 +113,10 @@ def _ref(p):
 
 def workspace_bytes(p: FavorProblem) -> int:
     return int(lib().favor_workspace_bytes(_ref(p)))
+
+
+def attn_fwd_launches(p: FavorProblem) -> int:
+    return int(lib().favor_attn_fwd_launches(_ref(p)))
 
 
 def attn_fwd(p: FavorProblem, q, k, v, w, out, workspace, workspace_nbytes, stream) -> int:

@@ -2282,6 +2282,13 @@ const char* favor_status_string(favor_status s) {
 
 int32_t favor_abi_version(void) { return FAVOR_ABI_VERSION; }
 
+int32_t favor_attn_fwd_launches(const favor_problem* p) {
+  favor::Plan s;
+  if (favor::make_plan(p, &s) != FAVOR_OK) return 0;
+  if (s.mode == FAVOR_BIDIRECTIONAL) return s.dtype == FAVOR_F32 && favor::small_f32_fused(s) ? 1 : 2;
+  return s.d == 128 && s.m > 256 ? 6 : 4;
+}
+
 static favor_status attn_fwd_impl(const favor_problem* p, const void* Q, const void* K, const void* V,
                                   const float* W, void* out, void* workspace, size_t workspace_bytes, void* stream,
                                   const favor::Marks& mk) {

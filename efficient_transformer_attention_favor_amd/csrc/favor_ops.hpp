@@ -49,6 +49,10 @@ favor_status launch_causal_v(const Plan& s, const void* Q, const void* K, const 
 
 // Bidirectional float32 forward: the key side per (kv head, range, 32-feature tile), then
 // the readout with the feature tiles over the waves (ranges merged in the readout).
+// Whether launch_small_f32 runs *s as one launch (key side, grid barrier, readout) on the
+// current device.
+bool small_f32_fused(const Plan& s);
+
 favor_status launch_small_f32(const Plan& s, const float* Q, const float* K, const float* V, const float* W,
                               float* out, char* ws, hipStream_t st, const Marks& mk);
 

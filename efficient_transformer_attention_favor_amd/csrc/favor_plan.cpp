@@ -131,6 +131,8 @@ favor_status make_plan(const favor_problem* p, Plan* s) {
     q.off_img_cb = off;
     off = align256(off + img_cb_bytes(q.m) * q.BH);
   }
+  q.off_bar = off;
+  if (q.dtype == FAVOR_F32 && q.mode == FAVOR_BIDIRECTIONAL) off = align256(off + sizeof(unsigned long long) * (1 + kCUs));
   q.bytes = off;
   return FAVOR_OK;
 }

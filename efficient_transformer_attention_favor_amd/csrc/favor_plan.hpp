@@ -49,6 +49,7 @@ struct Plan {
   size_t off_img_w;    // [Hw] fp16 W images
   size_t off_img_s;    // [BH] bf16 S'^T images
   size_t off_img_cb;   // [BH] bias-operand images
+  size_t off_bar;      // one-launch float32 path's grid barrier: epoch word + kCUs arrival flags (64-bit)
   size_t bytes;        // total workspace bytes
 };
 

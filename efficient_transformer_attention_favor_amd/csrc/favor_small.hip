@@ -26,6 +26,8 @@
 
 #include <math.h>
 
+#include <atomic>
+
 #include "favor_device.hpp"
 #include "favor_ops.hpp"
 #include "favor_plan.hpp"
@@ -35,18 +37,28 @@ namespace favor {
 // ======================================================================================
 // key side
 // ======================================================================================
+template <int D> struct SmallKv {
+  static constexpr int NW = 4, NDT = D / 32;
+  // LDS in floats: the waves' key row norms, their stabilisers, and the partials of waves
+  // 1..3 for the merge
+  static constexpr int NR = NW * 32, CS = NW * 32, RED = (NW - 1) * (NDT * 16 * 64 + 64);
+  static constexpr size_t LDS = sizeof(float) * (NR + CS + RED);
+};
+
+// One key-side unit (kv head, range, 32-feature tile) on the workgroup's four waves; sm is
+// SmallKv<D>::LDS bytes of LDS.  Every thread of the workgroup takes part (workgroup barriers).
 template <int D>
-__global__ void __launch_bounds__(256) small_kv_f32_kernel(const float* __restrict__ K, const float* __restrict__ V,
-                                                           const float* __restrict__ W, int L, int Hkv, int Hw,
-                                                           int m, int R, int T_ranges, float* __restrict__ ps,
-                                                           float* __restrict__ pc) {
-  constexpr int NW = 4, NDT = D / 32, LDK = D + 1, NS = D / 2;
-  __shared__ float Kl[NW][32 * LDK];           // the wave's block of keys
-  __shared__ float Nr[NW][32];                 // -|k|^2/2 log2 e of those keys (-inf past the range)
-  __shared__ float Cs[NW][32];                 // the waves' stabilisers, then the merged ones
-  __shared__ float Red[NW - 1][NDT * 16 * 64 + 64];  // partials of waves 1..3
+__device__ __forceinline__ void small_kv_unit(float* sm, int id, const float* __restrict__ K,
+                                              const float* __restrict__ V, const float* __restrict__ W, int L,
+                                              int Hkv, int Hw, int m, int R, int T_ranges, float* __restrict__ ps,
+                                              float* __restrict__ pc) {
+  using Cfg = SmallKv<D>;
+  constexpr int NW = Cfg::NW, NDT = Cfg::NDT, NS = D / 2;
+  float(*Nr)[32] = reinterpret_cast<float(*)[32]>(sm);                       // -|k|^2/2 log2 e (-inf past the range)
+  float(*Cs)[32] = reinterpret_cast<float(*)[32]>(sm + Cfg::NR);             // stabilisers, then the merged ones
+  float(*Red)[NDT * 16 * 64 + 64] =
+      reinterpret_cast<float(*)[NDT * 16 * 64 + 64]>(sm + Cfg::NR + Cfg::CS);  // partials of waves 1..3
   const int NFT = m / 32;
-  int id = blockIdx.x;
   const int ft = id % NFT;
   id /= NFT;
   const int t = id % T_ranges, bh = id / T_ranges, hkv = bh % Hkv;
@@ -55,13 +67,14 @@ __global__ void __launch_bounds__(256) small_kv_f32_kernel(const float* __restri
   const float* Vh = V + (size_t)bh * L * D;
   const float* Wr = W + ((size_t)(Hw == 1 ? 0 : hkv) * m + 32 * ft + col) * D;
 
-  // W operand (B, lane = feature): step s carries contraction index 2 s + g
+  // W operand (B, lane = feature): step s carries contraction index (D/2) g + s, so each
+  // lane holds one contiguous half of its feature's row (and of each key's row below)
   float wreg[NS];
 #pragma unroll
-  for (int c = 0; c < D / 4; ++c) {
-    const f32x4 w4 = *reinterpret_cast<const f32x4*>(Wr + 4 * c);
-    wreg[2 * c] = (g == 0 ? w4[0] : w4[1]) * kLog2e;
-    wreg[2 * c + 1] = (g == 0 ? w4[2] : w4[3]) * kLog2e;
+  for (int c = 0; c < NS / 4; ++c) {
+    const f32x4 w4 = *reinterpret_cast<const f32x4*>(Wr + (D / 2) * g + 4 * c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wreg[4 * c + i] = w4[i] * kLog2e;
   }
 
   const int pb = t * R, pe = min(pb + R, L);
@@ -69,35 +82,33 @@ __global__ void __launch_bounds__(256) small_kv_f32_kernel(const float* __restri
 #pragma unroll
   for (int dt = 0; dt < NDT; ++dt) S[dt] = zero16();
   float s1 = 0.f, crun = -INFINITY;  // this lane's feature 32 ft + col (both lane halves)
-  float* kl = Kl[wave];
-  for (int p0 = pb + 32 * wave; p0 < pe; p0 += 32 * NW) {
-    // V operands of the block (B, lane = value): step r contracts key 8 (r/4) + 4 g + r%4;
-    // rows past the range are read clamped to its last row (their phi is 0)
-    float vop[NDT][16];
+
+  // One 32-key block in registers: the A operand (key col, half g of its row) and the V
+  // operands (B, lane = value): step r contracts key 8 (r/4) + 4 g + r%4.  Rows past the
+  // range are read clamped to its last row; their row bias is -inf, so their phi is 0.
+  struct Blk {
+    f32x4 k[NS / 4];
+    float v[NDT][16];
+  };
+  auto fetch = [&](int p0, Blk& b) {
+    const float* kr = Kh + (size_t)min(p0 + col, pe - 1) * D + (D / 2) * g;
+#pragma unroll
+    for (int c = 0; c < NS / 4; ++c) b.k[c] = *reinterpret_cast<const f32x4*>(kr + 4 * c);
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = min(p0 + 8 * (r >> 2) + 4 * g + (r & 3), pe - 1);
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) vop[dt][r] = Vh[(size_t)key * D + 32 * dt + col];
+      for (int dt = 0; dt < NDT; ++dt) b.v[dt][r] = Vh[(size_t)key * D + 32 * dt + col];
     }
-    // keys of the block into the wave's LDS rows (rows past the range read as zero)
-#pragma unroll
-    for (int j = 0; j < D / 8; ++j) {
-      const int c = l + 64 * j, row = c / (D / 4), c4 = (c % (D / 4)) * 4;
-      const f32x4 v = p0 + row < pe ? *reinterpret_cast<const f32x4*>(Kh + (size_t)(p0 + row) * D + c4)
-                                     : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) kl[row * LDK + c4 + i] = v[i];
-    }
-    asm volatile("" ::: "memory");  // the wave's LDS writes above before its reads below
+  };
+  auto block = [&](int p0, const Blk& b) {
     {
-      // |k|^2 of key col: each lane half sums half of the row
+      // |k|^2 of key col: each lane half sums its half of the row
       float n = 0.f;
-#pragma unroll 16
-      for (int k = 0; k < D / 2; ++k) {
-        const float x = kl[col * LDK + g * (D / 2) + k];
-        n = __builtin_fmaf(x, x, n);
-      }
+#pragma unroll
+      for (int c = 0; c < NS / 4; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) n = __builtin_fmaf(b.k[c][i], b.k[c][i], n);
       n = pair_sum(n);
       if (g == 0) Nr[wave][col] = p0 + col < pe ? -0.5f * kLog2e * n : -INFINITY;
     }
@@ -105,9 +116,11 @@ __global__ void __launch_bounds__(256) small_kv_f32_kernel(const float* __restri
     // E = K W^T as two independent chains (even and odd steps)
     f32x16 e0 = zero16(), e1 = zero16();
 #pragma unroll
-    for (int s = 0; s < NS; s += 2) {
-      e0 = mma(kl[col * LDK + 2 * s + g], wreg[s], e0);
-      e1 = mma(kl[col * LDK + 2 * s + 2 + g], wreg[s + 1], e1);
+    for (int c = 0; c < NS / 4; ++c) {
+      e0 = mma(b.k[c][0], wreg[4 * c], e0);
+      e1 = mma(b.k[c][1], wreg[4 * c + 1], e1);
+      e0 = mma(b.k[c][2], wreg[4 * c + 2], e0);
+      e1 = mma(b.k[c][3], wreg[4 * c + 3], e1);
     }
     // row bias -|k|^2/2 of key 8 (r/4) + 4 g + r%4, block maximum per feature
     float mx = -INFINITY;
@@ -151,8 +164,27 @@ __global__ void __launch_bounds__(256) small_kv_f32_kernel(const float* __restri
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) S[dt] = mma(e0[r], vop[dt][r], S[dt]);
+      for (int r = 0; r < 16; ++r) S[dt] = mma(e0[r], b.v[dt][r], S[dt]);
     asm volatile("" ::: "memory");  // this block's LDS reads before the next block's writes
+  };
+
+  // the wave's blocks p0 = pb + 32 (wave + NW i); for d = 64 the next block's rows are in
+  // flight while one is computed (d = 128 leaves no registers for a second block)
+  int p0 = pb + 32 * wave;
+  if constexpr (D == 64) {
+    Blk cur, nxt;
+    if (p0 < pe) fetch(p0, cur);
+    for (; p0 < pe; p0 += 32 * NW) {
+      if (p0 + 32 * NW < pe) fetch(p0 + 32 * NW, nxt);
+      block(p0, cur);
+      cur = nxt;
+    }
+  } else {
+    for (; p0 < pe; p0 += 32 * NW) {
+      Blk cur;
+      fetch(p0, cur);
+      block(p0, cur);
+    }
   }
 
   // ---- the four partials meet at the range's largest c_f ------------------------------
@@ -186,31 +218,41 @@ __global__ void __launch_bounds__(256) small_kv_f32_kernel(const float* __restri
     dst[NDT * 16 * 64 + l] = s1;
   }
   __syncthreads();
-  if (wave != 0) return;
+  if (wave == 0) {
 #pragma unroll
-  for (int w = 1; w < NW; ++w) {
+    for (int w = 1; w < NW; ++w) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4 v = *reinterpret_cast<const f32x4*>(&Red[w - 1][((dt * 4 + r4) * 64 + l) * 4]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) S[dt][4 * r4 + q] += v[q];
+        }
+      s1 += Red[w - 1][NDT * 16 * 64 + l];
+    }
+    const size_t unit = ((size_t)bh * T_ranges + t) * NFT + ft;
+    float* out_s = ps + unit * (size_t)(D + 1) * 32;
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-      for (int r4 = 0; r4 < 4; ++r4) {
-        const f32x4 v = *reinterpret_cast<const f32x4*>(&Red[w - 1][((dt * 4 + r4) * 64 + l) * 4]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) S[dt][4 * r4 + q] += v[q];
-      }
-    s1 += Red[w - 1][NDT * 16 * 64 + l];
+      for (int r4 = 0; r4 < 4; ++r4)
+        *reinterpret_cast<f32x4*>(out_s + (size_t)(32 * dt + col) * 32 + 8 * r4 + 4 * g) =
+            f32x4{S[dt][4 * r4], S[dt][4 * r4 + 1], S[dt][4 * r4 + 2], S[dt][4 * r4 + 3]};
+    if (g == 0) {
+      out_s[(size_t)D * 32 + col] = s1;
+      pc[((size_t)bh * T_ranges + t) * m + 32 * ft + col] = cm;
+    }
   }
-  const size_t unit = ((size_t)bh * T_ranges + t) * NFT + ft;
-  float* out_s = ps + unit * (size_t)(D + 1) * 32;
-#pragma unroll
-  for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4)
-      *reinterpret_cast<f32x4*>(out_s + (size_t)(32 * dt + col) * 32 + 8 * r4 + 4 * g) =
-          f32x4{S[dt][4 * r4], S[dt][4 * r4 + 1], S[dt][4 * r4 + 2], S[dt][4 * r4 + 3]};
-  if (g == 0) {
-    out_s[(size_t)D * 32 + col] = s1;
-    pc[((size_t)bh * T_ranges + t) * m + 32 * ft + col] = cm;
-  }
+}
+
+template <int D>
+__global__ void __launch_bounds__(256) small_kv_f32_kernel(const float* __restrict__ K, const float* __restrict__ V,
+                                                           const float* __restrict__ W, int L, int Hkv, int Hw,
+                                                           int m, int R, int T_ranges, float* __restrict__ ps,
+                                                           float* __restrict__ pc) {
+  __shared__ __attribute__((aligned(16))) float sm[SmallKv<D>::LDS / sizeof(float)];
+  small_kv_unit<D>(sm, blockIdx.x, K, V, W, L, Hkv, Hw, m, R, T_ranges, ps, pc);
 }
 
 // ======================================================================================
@@ -221,22 +263,27 @@ template <int D> struct SmallRo {
   // register file of its SIMD, which the merged partials and two accumulator chains need
   static constexpr int NW = 4;
   static constexpr int NDT = D / 32;
-  static constexpr int LDQ = D + 1;
+  // LDS: the waves' numerator partials, their (den, max) pairs
+  static constexpr int RED = NW * NDT * 16 * 64;
+  static constexpr size_t LDS = sizeof(float) * RED + sizeof(float2) * NW * 32;
 };
 
+// The readout of workgroup blk's 32-row tiles; nw waves (min(m / 32, 4)) own the feature
+// tiles, further waves of the workgroup only join its barriers.  sm is SmallRo<D>::LDS
+// bytes of LDS.  poison multiplies the reciprocal denominators (1, or NaN to mark the rows
+// of a launch whose key-side partials are not known to be complete).
 template <int D>
-__global__ void __launch_bounds__(64 * SmallRo<D>::NW) small_readout_f32_kernel(
-    const float* __restrict__ Q, const float* __restrict__ W, const float* __restrict__ ps,
-    const float* __restrict__ pc, float* __restrict__ out, int L, int Hq, int Hkv, int Hw, int m, int T_ranges,
-    int tiles_per_head) {
+__device__ __forceinline__ void small_readout_body(float* sm, int blk, int nw, const float* __restrict__ Q,
+                                                   const float* __restrict__ W, const float* __restrict__ ps,
+                                                   const float* __restrict__ pc, float* __restrict__ out, int L,
+                                                   int Hq, int Hkv, int Hw, int m, int T_ranges, int tiles_per_head,
+                                                   float poison) {
   using Cfg = SmallRo<D>;
-  constexpr int NWM = Cfg::NW, NDT = Cfg::NDT, LDQ = Cfg::LDQ, NS = D / 2, NU = NDT * 4;
-  __shared__ float Ql[32 * LDQ];
-  __shared__ float Red[NWM][NDT * 16 * 64];
-  __shared__ float2 Dm[NWM][32];
+  constexpr int NWM = Cfg::NW, NDT = Cfg::NDT, NS = D / 2, NU = NDT * 4;
+  float(*Red)[NDT * 16 * 64] = reinterpret_cast<float(*)[NDT * 16 * 64]>(sm);
+  float2(*Dm)[32] = reinterpret_cast<float2(*)[32]>(sm + Cfg::RED);
   const int NFT = m / 32;
-  const int nw = blockDim.x >> 6;  // waves: min(NFT, NWM)
-  const int bh = blockIdx.x / tiles_per_head, tile0 = blockIdx.x % tiles_per_head;
+  const int bh = blk / tiles_per_head, tile0 = blk % tiles_per_head;
   const int b = bh / Hkv, hkv = bh % Hkv, G = Hq / Hkv;
   const int wave = threadIdx.x >> 6, l = lane_id(), col = l & 31, g = l >> 5;
   const size_t rows = (size_t)G * L;
@@ -250,12 +297,12 @@ __global__ void __launch_bounds__(64 * SmallRo<D>::NW) small_readout_f32_kernel(
   // go out together (past the last range the last one is re-read with weight 0).
   float wv[NS], cf[16], sv[NDT][16], s1[16];
   auto prep = [&](int ft) {
-    const float* wr = Wh + (size_t)(32 * ft + col) * D;
+    const float* wr = Wh + (size_t)(32 * ft + col) * D + (D / 2) * g;
 #pragma unroll
-    for (int c = 0; c < D / 4; ++c) {
+    for (int c = 0; c < NS / 4; ++c) {
       const f32x4 w4 = *reinterpret_cast<const f32x4*>(wr + 4 * c);
-      wv[2 * c] = g == 0 ? w4[0] : w4[1];
-      wv[2 * c + 1] = g == 0 ? w4[2] : w4[3];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[4 * c + i] = w4[i] * kLog2e;
     }
     constexpr int TG = 4, RB = D == 64 ? 4 : 1;
     const float* pch = pc + (size_t)bh * T_ranges * m + 32 * ft;
@@ -313,21 +360,23 @@ __global__ void __launch_bounds__(64 * SmallRo<D>::NW) small_readout_f32_kernel(
     }
   };
   // one feature tile per wave: prepared once for all row tiles of the workgroup
+  // B operand of the exponents: query row0 + col, half g of its row (rows past the end are
+  // read clamped to the last row and never stored); the first tile's rows are in flight
+  // while the partials are merged
+  f32x4 qv[NS / 4];
+  auto load_q = [&](size_t row0) {
+    const float* qr = Qb + min(row0 + col, rows - 1) * D + (D / 2) * g;
+#pragma unroll
+    for (int c = 0; c < NS / 4; ++c) qv[c] = *reinterpret_cast<const f32x4*>(qr + 4 * c);
+  };
+  if ((size_t)tile0 * 32 < rows) load_q((size_t)tile0 * 32);
   const bool once = NFT <= nw;
-  if (once) prep(wave);
+  if (once && wave < NFT) prep(wave);
 
   for (size_t tile = tile0; tile * 32 < rows; tile += tiles_per_head) {
     const size_t row0 = tile * 32;
-    __syncthreads();  // the previous tile's readers of Ql, Red, Dm are done
-    // the tile's queries (rows past the end read as zero)
-    for (int c = threadIdx.x; c < 32 * (D / 4); c += blockDim.x) {
-      const int row = c / (D / 4), c4 = (c % (D / 4)) * 4;
-      const f32x4 v = row0 + row < rows ? *reinterpret_cast<const f32x4*>(Qb + (row0 + row) * D + c4)
-                                         : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Ql[row * LDQ + c4 + i] = v[i];
-    }
-    __syncthreads();
+    if (tile != (size_t)tile0) load_q(row0);
+    __syncthreads();  // the previous tile's readers of Red, Dm are done
 
     f32x16 num[NDT];
 #pragma unroll
@@ -338,9 +387,11 @@ __global__ void __launch_bounds__(64 * SmallRo<D>::NW) small_readout_f32_kernel(
       // ---- C[feature][query] = W Q^T + c_f (lane = query) ---------------------------------
       f32x16 e0 = zero16(), e1 = zero16();
 #pragma unroll
-      for (int s2 = 0; s2 < NS; s2 += 2) {
-        e0 = mma(wv[s2] * kLog2e, Ql[col * LDQ + 2 * s2 + g], e0);
-        e1 = mma(wv[s2 + 1] * kLog2e, Ql[col * LDQ + 2 * s2 + 2 + g], e1);
+      for (int c = 0; c < NS / 4; ++c) {
+        e0 = mma(wv[4 * c], qv[c][0], e0);
+        e1 = mma(wv[4 * c + 1], qv[c][1], e1);
+        e0 = mma(wv[4 * c + 2], qv[c][2], e0);
+        e1 = mma(wv[4 * c + 3], qv[c][3], e1);
       }
       float mt = -INFINITY;
 #pragma unroll
@@ -386,9 +437,9 @@ __global__ void __launch_bounds__(64 * SmallRo<D>::NW) small_readout_f32_kernel(
       const float2 dm = Dm[w][col];
       dd = __builtin_fmaf(dm.y == -INFINITY ? 0.f : fast_exp2(dm.y - M), dm.x, dd);
     }
-    const float inv = 1.f / dd;
+    const float inv = poison / dd;
     const size_t row = row0 + col;
-    if (row < rows) {
+    if (row < rows && wave < nw) {
       // group u: value tile u / 4, registers 4 (u % 4) .. = values 32 (u / 4) + 8 (u % 4) + 4 g ..
       for (int u = wave; u < NU; u += nw) {
         const int dt = u >> 2, r4 = u & 3;
@@ -407,10 +458,141 @@ __global__ void __launch_bounds__(64 * SmallRo<D>::NW) small_readout_f32_kernel(
   }
 }
 
+template <int D>
+__global__ void __launch_bounds__(64 * SmallRo<D>::NW) small_readout_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ W, const float* __restrict__ ps,
+    const float* __restrict__ pc, float* __restrict__ out, int L, int Hq, int Hkv, int Hw, int m, int T_ranges,
+    int tiles_per_head) {
+  __shared__ __attribute__((aligned(16))) float sm[SmallRo<D>::LDS / sizeof(float)];
+  small_readout_body<D>(sm, blockIdx.x, blockDim.x >> 6, Q, W, ps, pc, out, L, Hq, Hkv, Hw, m, T_ranges,
+                        tiles_per_head, 1.f);
+}
+
+
+// ======================================================================================
+// one launch for small problems: the key-side units, a grid-wide barrier, the readout
+// ======================================================================================
+// Polls before a workgroup gives up waiting at the barrier (about a second); a launch whose
+// workgroups are all resident passes it in microseconds.
+constexpr int kBarrierPolls = 1 << 20;
+
+// Grid-wide barrier for a launch of n <= 256 workgroups that are all resident at once.
+// bar[0] is an epoch the workgroups read as e at the start of the launch (before any of
+// them can pass the barrier); bar[1 + b] is workgroup b's arrival flag.  Workgroup b
+// arrives by storing (e + 1) ^ tag in its flag and waits until every flag holds that value;
+// workgroup 0 then moves the epoch to e + 1.  Flags left by an earlier launch hold another
+// value (a replayed launch with the same tag has moved on by one epoch; a fresh workspace
+// matches only by accident of 2^-64), so nothing needs clearing between calls.  No
+// read-modify-write: each workgroup writes its own word.  Ordering: every wave waits for
+// its stores, one agent-scope release (the XCD's L2 written back) precedes the flag, and
+// the polling wave takes one agent-scope acquire after the last flag.  The wait is bounded:
+// returns false if the flags did not all arrive in kBarrierPolls polls.
+__device__ __forceinline__ unsigned long long barrier_epoch(const unsigned long long* bar) {
+  return __hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ bool grid_barrier(unsigned long long* bar, unsigned long long epoch, unsigned tag,
+                                             unsigned n) {
+  __shared__ int ok_s;
+  const unsigned long long want = (epoch + 1) ^ tag;
+  // vmcnt(0): the wave's stores have reached the L2 before the release writes it back
+  __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    if (threadIdx.x == 0) {
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_store(bar + 1 + blockIdx.x, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // lane i watches flags i, i + 64, ...
+    bool mine = true;
+    for (unsigned j = threadIdx.x; j < n; j += 64) {
+      int i = 0;
+      while (__hip_atomic_load(bar + 1 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want && ++i < kBarrierPolls)
+        __builtin_amdgcn_s_sleep(1);
+      mine = mine && i < kBarrierPolls;
+    }
+    const bool ok = !wave_any(!mine);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (threadIdx.x == 0) {
+      ok_s = ok ? 1 : 0;
+      if (blockIdx.x == 0 && ok) __hip_atomic_store(bar, epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  return ok_s != 0;
+}
+
+// Workgroup b runs key-side unit b (b < n_kv), waits for every unit, then reads out its
+// 32-row tile (one tile per workgroup: tiles_per_head = all tiles of a head).  Rows of a
+// launch whose barrier gave up are written as NaN.
+template <int D>
+__global__ void __launch_bounds__(256) small_fused_f32_kernel(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ W, float* __restrict__ ps, float* __restrict__ pc, float* __restrict__ out,
+    unsigned long long* __restrict__ bar, unsigned tag, int L, int Hq, int Hkv, int Hw, int m, int R, int T_ranges,
+    int n_kv, int tiles_per_head, int n_ro) {
+  constexpr size_t LDS = SmallKv<D>::LDS > SmallRo<D>::LDS ? SmallKv<D>::LDS : SmallRo<D>::LDS;
+  __shared__ __attribute__((aligned(16))) float sm[LDS / sizeof(float)];
+  const unsigned long long epoch = barrier_epoch(bar);
+  for (int u = blockIdx.x; u < n_kv; u += gridDim.x) {
+    small_kv_unit<D>(sm, u, K, V, W, L, Hkv, Hw, m, R, T_ranges, ps, pc);
+    __syncthreads();  // LDS free for the next unit
+  }
+  const bool ok = grid_barrier(bar, epoch, tag, gridDim.x);
+  const int NFT = m / 32;
+  const int nw = NFT < SmallRo<D>::NW ? NFT : SmallRo<D>::NW;
+  for (int u = blockIdx.x; u < n_ro; u += gridDim.x) {
+    small_readout_body<D>(sm, u, nw, Q, W, ps, pc, out, L, Hq, Hkv, Hw, m, T_ranges, tiles_per_head,
+                          ok ? 1.f : __builtin_nanf(""));
+    __syncthreads();
+  }
+}
+
 // ======================================================================================
 // launchers
 // ======================================================================================
+namespace {
+
+// Compute units of the current device (0 if the query fails), cached per device.
+int device_cu_count() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// A fresh 32-bit tag per launch of the one-launch path (odd, mixed so that it is unlikely
+// to match stale workspace contents).
+unsigned next_barrier_tag() {
+  static std::atomic<unsigned> counter{0};
+  unsigned x = counter.fetch_add(1, std::memory_order_relaxed) * 0x9E3779B9u + 0x7F4A7C15u;
+  x ^= x >> 16;
+  x *= 0x85EBCA6Bu;
+  x ^= x >> 13;
+  return x | 1u;
+}
+
+}  // namespace
+
 bool small_f32_path(const Plan& s) { return s.dtype == FAVOR_F32 && s.mode == FAVOR_BIDIRECTIONAL; }
+
+// One launch when every key-side unit and every 32-row tile has a workgroup of its own and
+// all of them can be resident at once on the current device (one per CU).
+bool small_f32_fused(const Plan& s) {
+  if (!small_f32_path(s)) return false;
+  const long long kv_wg = (long long)s.BH * s.T * (s.m / 32);
+  const long long n_ro = (long long)s.BH * (((long long)s.G * s.L + 31) / 32);
+  const int cus = device_cu_count();
+  const long long lim = cus < kCUs ? cus : kCUs;  // the workspace holds kCUs arrival flags
+  return lim > 0 && kv_wg <= lim && n_ro <= lim;
+}
 
 favor_status launch_small_f32(const Plan& s, const float* Q, const float* K, const float* V, const float* W,
                               float* out, char* ws, hipStream_t st, const Marks& mk) {
@@ -419,6 +601,23 @@ favor_status launch_small_f32(const Plan& s, const float* Q, const float* K, con
   const int NFT = s.m / 32;
   if (!mk.mark(0, st)) return FAVOR_ERR_HIP;
   const unsigned kv_wg = (unsigned)(s.BH * s.T * NFT);
+  const long long tiles = ((long long)s.G * s.L + 31) / 32;
+  const long long n_ro = (long long)s.BH * tiles;
+  if (small_f32_fused(s)) {
+    const unsigned grid = (unsigned)(n_ro > (long long)kv_wg ? n_ro : (long long)kv_wg);
+    unsigned long long* bar = reinterpret_cast<unsigned long long*>(ws + s.off_bar);
+    const unsigned tag = next_barrier_tag();
+    if (s.d == 64)
+      hipLaunchKernelGGL(small_fused_f32_kernel<64>, dim3(grid), dim3(256), 0, st, Q, K, V, W, ps, pc, out, bar, tag,
+                         s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, (int)kv_wg, (int)tiles, (int)n_ro);
+    else
+      hipLaunchKernelGGL(small_fused_f32_kernel<128>, dim3(grid), dim3(256), 0, st, Q, K, V, W, ps, pc, out, bar,
+                         tag, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, (int)kv_wg, (int)tiles, (int)n_ro);
+    // one kernel: the key-side slot holds it, the readout slot is empty
+    if (hipGetLastError() != hipSuccess || !mk.mark(1, st) || !mk.mark(2, st) || !mk.mark(3, st))
+      return FAVOR_ERR_HIP;
+    return FAVOR_OK;
+  }
   if (s.d == 64)
     hipLaunchKernelGGL(small_kv_f32_kernel<64>, dim3(kv_wg), dim3(256), 0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R,
                        s.T, ps, pc);
@@ -427,7 +626,6 @@ favor_status launch_small_f32(const Plan& s, const float* Q, const float* K, con
                        s.R, s.T, ps, pc);
   if (hipGetLastError() != hipSuccess || !mk.mark(1, st) || !mk.mark(2, st)) return FAVOR_ERR_HIP;
   // about kReadoutTarget workgroups, one 32-row tile each at most
-  const long long tiles = ((long long)s.G * s.L + 31) / 32;
   long long per_head = (2LL * kReadoutTarget + s.BH - 1) / s.BH;
   if (per_head > tiles) per_head = tiles;
   const int nwm = s.d == 64 ? SmallRo<64>::NW : SmallRo<128>::NW;

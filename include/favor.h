@@ -25,9 +25,10 @@
  *    last:  Q [batch][heads_q][seq_len][head_dim],  K and V [batch][heads_kv][seq_len][head_dim],
  *    W [heads_w][num_features][head_dim] (float32, host-generated),
  *    out [batch][heads_q][seq_len][head_dim].  Q, K, V and out share `dtype`.
- *  - The caller owns every buffer; the library allocates and frees no device memory and
- *    keeps no global state.  Scratch space is the caller's `workspace`, at least
- *    favor_workspace_bytes() bytes, 256-byte aligned.
+ *  - The caller owns every buffer; the library allocates and frees no device memory.
+ *    Scratch space is the caller's `workspace`, at least favor_workspace_bytes() bytes,
+ *    256-byte aligned.  Host-side state is limited to a cached compute-unit count per
+ *    device and a launch counter (see favor_attn_fwd).
  *  - `stream` is a hipStream_t (NULL = default stream).  Work is queued asynchronously;
  *    no entry point synchronises the host.
  *  - Arguments are checked before any HIP call.  On an error status nothing has been
@@ -87,14 +88,27 @@ size_t favor_workspace_bytes(const favor_problem* p);
 
 /* Kernel slots of one favor_attn_fwd call: the key/value summary per position range (or
  * segment); the prefix scan of the segment summaries (causal; empty for bidirectional
- * problems); the query readout (bidirectional) or chunked causal pass. */
+ * problems); the query readout (bidirectional) or chunked causal pass.  A one-launch
+ * float32 call fills the first slot only. */
 #define FAVOR_FWD_KERNELS 3
+
+/* Number of kernels one favor_attn_fwd call for *p queues on the current device (1, 2, 4
+ * or 6; 0 if *p is invalid).  Reads the device's compute-unit count (a HIP query); without
+ * a usable device the one-launch path is off and the count says so. */
+int32_t favor_attn_fwd_launches(const favor_problem* p);
 
 /* FAVOR+ forward (Performer page, "제안 방법"): out = D^-1 A_hat V in linear order,
  * bidirectional or causal (inclusive mask j <= i) per p->mode.  Queues 2 (bidirectional)
  * or 4 (causal: key-side summaries, their prefix scan, the chunked pass and its repair
  * launch; 6 where d = 128 with m > 256 in bf16 or float32, whose chunked pass and repair
- * run once per feature range) kernels on `stream`. */
+ * run once per feature range) kernels on `stream`.  A float32 bidirectional problem whose
+ * key-side units (kv head x position range x 32 features) and 32-row query tiles each
+ * number at most the device's compute units runs as ONE kernel: the key side, a grid-wide
+ * barrier on a 64-bit word in the workspace (tagged per launch from a host counter, so
+ * it needs no clearing), then the readout.  Its wait is bounded; rows of a launch whose
+ * barrier gave up (not every workgroup resident, e.g. beside other work holding the
+ * compute units) are written as NaN.  Two such calls in flight at once on one device must
+ * not share a workspace. */
 favor_status favor_attn_fwd(const favor_problem* p, const void* Q, const void* K, const void* V,
                             const float* W, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);

@@ -228,3 +228,15 @@ def test_noalloc_rejects_before_any_hip_call():
              mode=_lib.FAVOR_CAUSAL)
     assert _lib.workspace_bytes(big) > _lib.FAVOR_NOALLOC_SCRATCH_BYTES
     assert _lib.attn_fwd_noalloc(big, fake, fake, fake, fake, fake, None) == _lib.FAVOR_ERR_WORKSPACE
+
+
+def test_fwd_launch_count_query():
+    """favor_attn_fwd_launches: 0 for an invalid problem, 4 / 6 kernels for causal problems,
+    1 or 2 for float32 bidirectional ones (1 only where a device reports enough compute
+    units), 2 for bf16 bidirectional ones."""
+    assert _lib.attn_fwd_launches(None) == 0
+    assert _lib.attn_fwd_launches(_p(head_dim=32)) == 0
+    assert _lib.attn_fwd_launches(_p(mode=_lib.FAVOR_CAUSAL)) == 4
+    assert _lib.attn_fwd_launches(_p(mode=_lib.FAVOR_CAUSAL, head_dim=128, num_features=384)) == 6
+    assert _lib.attn_fwd_launches(_p(dtype=_lib.FAVOR_BF16)) == 2
+    assert _lib.attn_fwd_launches(_p(dtype=_lib.FAVOR_F32, seq_len=1024)) in (1, 2)
