@@ -292,9 +292,8 @@ __device__ __forceinline__ void small_readout_body(float* sm, int blk, int nw, c
   const float* Wh = W + (size_t)(Hw == 1 ? 0 : hkv) * m * D;
 
   // ---- per feature tile: the W operand and the ranges' partials merged at the largest c_f
-  // (A operand: step s carries contraction index 2 s + g; register r of this lane group is
-  // feature 8 (r/4) + 4 g + r%4 of the tile).  The loads of TG ranges and RB register groups
-  // go out together (past the last range the last one is re-read with weight 0).
+  // (A operand: step s carries contraction index (D/2) g + s; register r of this lane group is
+  // feature 8 (r/4) + 4 g + r%4 of the tile).
   float wv[NS], cf[16], sv[NDT][16], s1[16];
   auto prep = [&](int ft) {
     const float* wr = Wh + (size_t)(32 * ft + col) * D + (D / 2) * g;
@@ -304,62 +303,52 @@ __device__ __forceinline__ void small_readout_body(float* sm, int blk, int nw, c
 #pragma unroll
       for (int i = 0; i < 4; ++i) wv[4 * c + i] = w4[i] * kLog2e;
     }
-    constexpr int TG = 4, RB = D == 64 ? 4 : 1;
+    // Online merge over the ranges (running maximum per feature, earlier sums rescaled when
+    // it rises), so the loads of TG ranges -- stabilisers and partials alike -- go out
+    // together in one round (past the last range the last one is re-read with weight 0).
+    constexpr int TG = D == 64 ? 4 : 2;
     const float* pch = pc + (size_t)bh * T_ranges * m + 32 * ft;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) cf[r] = -INFINITY;
-    for (int t0 = 0; t0 < T_ranges; t0 += TG) {
-      f32x4 cv[TG][4];
-#pragma unroll
-      for (int u = 0; u < TG; ++u)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-          cv[u][r4] = *reinterpret_cast<const f32x4*>(pch + (size_t)min(t0 + u, T_ranges - 1) * m + 8 * r4 + 4 * g);
-#pragma unroll
-      for (int u = 0; u < TG; ++u)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) cf[4 * r4 + q] = fmaxf(cf[4 * r4 + q], cv[u][r4][q]);
-    }
-#pragma unroll
     for (int r = 0; r < 16; ++r) {
+      cf[r] = -INFINITY;
       s1[r] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) sv[dt][r] = 0.f;
     }
     for (int t0 = 0; t0 < T_ranges; t0 += TG) {
+      f32x4 cv[TG][4], ov[TG][4], vv[TG][4][NDT];
 #pragma unroll
-      for (int rb = 0; rb < 4; rb += RB) {
-        f32x4 cv[RB][TG], ov[RB][TG], vv[RB][TG][NDT];
+      for (int u = 0; u < TG; ++u) {
+        const int t = min(t0 + u, T_ranges - 1);
+        const float* src = ps + (((size_t)bh * T_ranges + t) * NFT + ft) * (size_t)(D + 1) * 32;
 #pragma unroll
-        for (int j = 0; j < RB; ++j)
+        for (int r4 = 0; r4 < 4; ++r4) {
+          cv[u][r4] = *reinterpret_cast<const f32x4*>(pch + (size_t)t * m + 8 * r4 + 4 * g);
+          ov[u][r4] = *reinterpret_cast<const f32x4*>(src + (size_t)D * 32 + 8 * r4 + 4 * g);
 #pragma unroll
-          for (int u = 0; u < TG; ++u) {
-            const int r4 = rb + j, t = min(t0 + u, T_ranges - 1);
-            const float* src = ps + (((size_t)bh * T_ranges + t) * NFT + ft) * (size_t)(D + 1) * 32;
-            cv[j][u] = *reinterpret_cast<const f32x4*>(pch + (size_t)t * m + 8 * r4 + 4 * g);
-            ov[j][u] = *reinterpret_cast<const f32x4*>(src + (size_t)D * 32 + 8 * r4 + 4 * g);
+          for (int dt = 0; dt < NDT; ++dt)
+            vv[u][r4][dt] = *reinterpret_cast<const f32x4*>(src + (size_t)(32 * dt + col) * 32 + 8 * r4 + 4 * g);
+        }
+      }
 #pragma unroll
-            for (int dt = 0; dt < NDT; ++dt)
-              vv[j][u][dt] = *reinterpret_cast<const f32x4*>(src + (size_t)(32 * dt + col) * 32 + 8 * r4 + 4 * g);
+      for (int u = 0; u < TG; ++u) {
+        if (t0 + u >= T_ranges) break;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = 4 * r4 + q;
+            const float c = cv[u][r4][q], nm = fmaxf(cf[r], c);
+            const float a = cf[r] == -INFINITY ? 0.f : fast_exp2(cf[r] - nm);
+            const float b = fast_exp2(c - nm);
+            cf[r] = nm;
+            s1[r] = __builtin_fmaf(b, ov[u][r4][q], s1[r] * a);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) sv[dt][r] = __builtin_fmaf(b, vv[u][r4][dt][q], sv[dt][r] * a);
           }
-#pragma unroll
-        for (int j = 0; j < RB; ++j)
-#pragma unroll
-          for (int u = 0; u < TG; ++u)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int r = 4 * (rb + j) + q;
-              const float f = t0 + u < T_ranges ? fast_exp2(cv[j][u][q] - cf[r]) : 0.f;
-              s1[r] = __builtin_fmaf(f, ov[j][u][q], s1[r]);
-#pragma unroll
-              for (int dt = 0; dt < NDT; ++dt) sv[dt][r] = __builtin_fmaf(f, vv[j][u][dt][q], sv[dt][r]);
-            }
       }
     }
   };
-  // one feature tile per wave: prepared once for all row tiles of the workgroup
   // B operand of the exponents: query row0 + col, half g of its row (rows past the end are
   // read clamped to the last row and never stored); the first tile's rows are in flight
   // while the partials are merged
@@ -370,6 +359,7 @@ __device__ __forceinline__ void small_readout_body(float* sm, int blk, int nw, c
     for (int c = 0; c < NS / 4; ++c) qv[c] = *reinterpret_cast<const f32x4*>(qr + 4 * c);
   };
   if ((size_t)tile0 * 32 < rows) load_q((size_t)tile0 * 32);
+  // one feature tile per wave: prepared once for all row tiles of the workgroup
   const bool once = NFT <= nw;
   if (once && wave < NFT) prep(wave);
 
