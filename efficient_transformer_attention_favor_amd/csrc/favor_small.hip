@@ -6,22 +6,30 @@
 // features phi(x) = exp(W x - |x|^2 / 2) / sqrt(m) (the 1/sqrt(m) cancels in the ratio),
 // attention in linear order out = phi(Q) S_v / phi(Q) S_1 with S = phi(K)^T [V, 1].
 // Exponents are in log2 units (W scaled by log2 e); every contraction runs on
-// v_mfma_f32_32x32x2_f32 (float32 operands, float32 accumulation).
+// v_mfma_f32_32x32x2_f32 (float32 operands, float32 accumulation).  The contraction index
+// of the exponent products is split by lane half (lane group g supplies indices
+// (d/2) g + s), so a lane holds one contiguous half of a key, query or W row and loads it
+// straight into operand registers.
 //
-// Key side (small_kv_f32_kernel): one workgroup per (kv head, position range, 32-feature
-// tile); its four waves take the range's 32-position blocks in turn.  Per block a wave forms
-// E = K W^T - |k|^2/2 (C[key][feature], lane = feature), keeps a running maximum c_f per
-// feature (moved lazily by kTau, the partial rescaled), and adds phi^T [V, 1] with the
-// accumulator registers as the A operand and V read straight from global memory.  The four
-// partials meet in LDS at the range's largest c_f.  Output per (head, range, tile):
-//   ps[D + 1][32] (value rows in natural order, row D the ones column), pc[32] = c_f.
+// Key side (small_kv_unit): per (kv head, position range, 32-feature tile), four waves
+// taking the range's 32-position blocks in turn (the next block's rows in flight for
+// d = 64).  Per block a wave forms E = K W^T - |k|^2/2 (C[key][feature], lane = feature),
+// keeps a running maximum c_f per feature (moved lazily by kTau, the partial rescaled), and
+// adds phi^T [V, 1] with the accumulator registers as the A operand and V read straight
+// from global memory.  The four partials meet in LDS at the range's largest c_f.  Output
+// per (head, range, tile): ps[D + 1][32] (value rows in natural order, row D the ones
+// column), pc[32] = c_f.
 //
-// Readout (small_readout_f32_kernel): one workgroup per (kv head, 32-row tile of the G
-// query heads' rows); wave w owns feature tiles w, w + NW, ... (NW = 4)  It merges the ranges'
-// partials of its tiles into MFMA operands (S_f rescaled to the largest c_f), then
+// Readout (small_readout_body): per (kv head, 32-row tile of the G query heads' rows); wave
+// w owns feature tiles w, w + NW, ... (NW = 4).  It merges the ranges' partials of its tile
+// online (running maximum per feature, earlier sums rescaled), then
 //   C[feature][query] = W Q^T + c_f,  M_w = the row maxima over its features,
 //   phi = 2^(C - M_w),  num_w = S_v^T phi,  den_w = S_1 . phi,
 // and the waves' partials meet in LDS: out = sum_w 2^(M_w - M) num_w / sum_w 2^(M_w - M) den_w.
+//
+// Launches: small_fused_f32_kernel runs both in one launch (workgroup b: key-side unit b,
+// a grid barrier, then row tile b) when every unit and tile has a workgroup of its own on
+// the device's compute units; otherwise small_kv_f32_kernel then small_readout_f32_kernel.
 #include <hip/hip_runtime.h>
 
 #include <math.h>
