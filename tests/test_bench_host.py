@@ -68,3 +68,14 @@ def test_traffic_only_for_the_profiled_setting(tmp_path, monkeypatch):
     rec["source_sha256"] = "0" * 64
     (prof / "x_c3_causal_bf16_traffic.txt").write_text("json: " + __import__("json").dumps(rec) + "\n")
     assert bench.measured_traffic("c3_causal_bf16", "causal_chunk") is None
+
+
+@pytest.mark.parametrize("name", ["c1_bidir_f32", "c2_bidir_bf16"])
+def test_one_launch_slot_carries_the_whole_call(name):
+    """A call the library runs as one launch is timed as one slot; its algorithmic bytes and
+    flops are those of the whole call (Q, K, V read once, out written once, W; both sides'
+    feature maps and contractions)."""
+    w = I.workload(name)
+    work = bench.algorithmic_work(w, fused=True)
+    assert list(work) == [bench.FUSED_NAME]
+    assert work[bench.FUSED_NAME] == bench.call_work(w)
