@@ -35,6 +35,7 @@
 #include <math.h>
 
 #include <atomic>
+#include <type_traits>
 
 #include "favor_device.hpp"
 #include "favor_ops.hpp"
@@ -273,8 +274,16 @@ template <int D> struct SmallRo {
   static constexpr int NDT = D / 32;
   // LDS: the waves' numerator partials, their (den, max) pairs
   static constexpr int RED = NW * NDT * 16 * 64;
-  static constexpr size_t LDS = sizeof(float) * RED + sizeof(float2) * NW * 32;
+  static constexpr size_t LDS_RED = sizeof(float) * RED + sizeof(float2) * NW * 32;
+  // d = 64: the ranges' partials of a wave's feature tile staged in LDS by DMA before the
+  // merge (up to kSmallRanges ranges: S rows, then the stabilisers), aliased with the above
+  static constexpr bool STAGE = D == 64;
+  static constexpr int SW = kSmallRanges * ((D + 1) * 32 + 32);  // floats per wave
+  static constexpr size_t LDS_STAGE = STAGE ? sizeof(float) * NW * SW : 0;
+  static constexpr size_t LDS = LDS_RED > LDS_STAGE ? LDS_RED : LDS_STAGE;
 };
+
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 // The readout of workgroup blk's 32-row tiles; nw waves (min(m / 32, 4)) own the feature
 // tiles, further waves of the workgroup only join its barriers.  sm is SmallRo<D>::LDS
@@ -303,7 +312,26 @@ __device__ __forceinline__ void small_readout_body(float* sm, int blk, int nw, c
   // (A operand: step s carries contraction index (D/2) g + s; register r of this lane group is
   // feature 8 (r/4) + 4 g + r%4 of the tile).
   float wv[NS], cf[16], sv[NDT][16], s1[16];
-  auto prep = [&](int ft) {
+  // The ranges' partials of tile ft (S rows, then the stabilisers) into the wave's LDS
+  // staging rows by DMA, 1 KB per instruction (the 128-byte tails by lanes 0..7).
+  float* stg = sm + (size_t)wave * Cfg::SW;
+  auto stage = [&](int ft) {
+    constexpr int UB = (D + 1) * 32 * 4, NB = UB / 1024, TAIL = (UB - NB * 1024) / 16;
+    const float* pcs = pc + (size_t)bh * T_ranges * m + 32 * ft;
+    for (int t = 0; t < T_ranges; ++t) {
+      const float* src = ps + (((size_t)bh * T_ranges + t) * NFT + ft) * (size_t)(D + 1) * 32;
+      float* dst = stg + (size_t)t * (D + 1) * 32;
+#pragma unroll
+      for (int k = 0; k < NB; ++k)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 256 * k + 4 * l), (lds_void_t*)(dst + 256 * k), 16, 0, 0);
+      if (l < TAIL)
+        __builtin_amdgcn_global_load_lds((const void*)(src + 256 * NB + 4 * l), (lds_void_t*)(dst + 256 * NB), 16, 0, 0);
+      if (l < 8)
+        __builtin_amdgcn_global_load_lds((const void*)(pcs + (size_t)t * m + 4 * l),
+                                         (lds_void_t*)(stg + kSmallRanges * (D + 1) * 32 + 32 * t), 16, 0, 0);
+    }
+  };
+  auto load_w = [&](int ft) {
     const float* wr = Wh + (size_t)(32 * ft + col) * D + (D / 2) * g;
 #pragma unroll
     for (int c = 0; c < NS / 4; ++c) {
@@ -311,6 +339,11 @@ __device__ __forceinline__ void small_readout_body(float* sm, int blk, int nw, c
 #pragma unroll
       for (int i = 0; i < 4; ++i) wv[4 * c + i] = w4[i] * kLog2e;
     }
+  };
+  // the W operand of tile ft and the merge of its ranges' partials
+  auto prep = [&](int ft, auto staged_tag) {
+    constexpr bool STG = decltype(staged_tag)::value;
+    load_w(ft);
     // Online merge over the ranges (running maximum per feature, earlier sums rescaled when
     // it rises), so the loads of TG ranges -- stabilisers and partials alike -- go out
     // together in one round (past the last range the last one is re-read with weight 0).
@@ -328,10 +361,12 @@ __device__ __forceinline__ void small_readout_body(float* sm, int blk, int nw, c
 #pragma unroll
       for (int u = 0; u < TG; ++u) {
         const int t = min(t0 + u, T_ranges - 1);
-        const float* src = ps + (((size_t)bh * T_ranges + t) * NFT + ft) * (size_t)(D + 1) * 32;
+        const float* src = STG ? stg + (size_t)t * (D + 1) * 32
+                               : ps + (((size_t)bh * T_ranges + t) * NFT + ft) * (size_t)(D + 1) * 32;
+        const float* csrc = STG ? stg + kSmallRanges * (D + 1) * 32 + 32 * t : pch + (size_t)t * m;
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          cv[u][r4] = *reinterpret_cast<const f32x4*>(pch + (size_t)t * m + 8 * r4 + 4 * g);
+          cv[u][r4] = *reinterpret_cast<const f32x4*>(csrc + 8 * r4 + 4 * g);
           ov[u][r4] = *reinterpret_cast<const f32x4*>(src + (size_t)D * 32 + 8 * r4 + 4 * g);
 #pragma unroll
           for (int dt = 0; dt < NDT; ++dt)
@@ -367,9 +402,18 @@ __device__ __forceinline__ void small_readout_body(float* sm, int blk, int nw, c
     for (int c = 0; c < NS / 4; ++c) qv[c] = *reinterpret_cast<const f32x4*>(qr + 4 * c);
   };
   if ((size_t)tile0 * 32 < rows) load_q((size_t)tile0 * 32);
-  // one feature tile per wave: prepared once for all row tiles of the workgroup
+  // one feature tile per wave: prepared once for all row tiles of the workgroup (for
+  // d = 64 from the LDS-staged partials: every range's loads in one DMA round, no registers
+  // held while they are in flight)
   const bool once = NFT <= nw;
-  if (once && wave < NFT) prep(wave);
+  if (Cfg::STAGE && once && T_ranges <= kSmallRanges) {
+    if (wave < NFT) stage(wave);
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));  // vmcnt(0): the DMA has landed
+    __syncthreads();
+    if (wave < NFT) prep(wave, std::true_type{});
+  } else if (once && wave < NFT) {
+    prep(wave, std::false_type{});
+  }
 
   for (size_t tile = tile0; tile * 32 < rows; tile += tiles_per_head) {
     const size_t row0 = tile * 32;
@@ -381,7 +425,7 @@ __device__ __forceinline__ void small_readout_body(float* sm, int blk, int nw, c
     for (int dt = 0; dt < NDT; ++dt) num[dt] = zero16();
     float den = 0.f, Mw = -INFINITY;
     for (int ft = wave; ft < NFT; ft += nw) {
-      if (!once) prep(ft);
+      if (!once) prep(ft, std::false_type{});
       // ---- C[feature][query] = W Q^T + c_f (lane = query) ---------------------------------
       f32x16 e0 = zero16(), e1 = zero16();
 #pragma unroll
