@@ -34,6 +34,8 @@
 
 #include <math.h>
 
+#include <stdlib.h>
+
 #include <atomic>
 #include <type_traits>
 
@@ -515,7 +517,9 @@ __global__ void __launch_bounds__(64 * SmallRo<D>::NW) small_readout_f32_kernel(
 // one launch for small problems: the key-side units, a grid-wide barrier, the readout
 // ======================================================================================
 // Polls before a workgroup gives up waiting at the barrier (about a second); a launch whose
-// workgroups are all resident passes it in microseconds.
+// workgroups are all resident passes it in microseconds.  The environment variable
+// FAVOR_BARRIER_POLLS_FOR_TESTS lowers the limit, so a test can make the wait give up (the
+// kernel still finishes; the rows of the workgroups that gave up are NaN).
 constexpr int kBarrierPolls = 1 << 20;
 
 // Grid-wide barrier for a launch of n <= 256 workgroups that are all resident at once.
@@ -528,13 +532,13 @@ constexpr int kBarrierPolls = 1 << 20;
 // read-modify-write: each workgroup writes its own word.  Ordering: every wave waits for
 // its stores, one agent-scope release (the XCD's L2 written back) precedes the flag, and
 // the polling wave takes one agent-scope acquire after the last flag.  The wait is bounded:
-// returns false if the flags did not all arrive in kBarrierPolls polls.
+// returns false if the flags did not all arrive within max_polls polls.
 __device__ __forceinline__ unsigned long long barrier_epoch(const unsigned long long* bar) {
   return __hip_atomic_load(bar, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 __device__ __forceinline__ bool grid_barrier(unsigned long long* bar, unsigned long long epoch, unsigned tag,
-                                             unsigned n) {
+                                             unsigned n, int max_polls) {
   __shared__ int ok_s;
   const unsigned long long want = (epoch + 1) ^ tag;
   // vmcnt(0): the wave's stores have reached the L2 before the release writes it back
@@ -549,9 +553,13 @@ __device__ __forceinline__ bool grid_barrier(unsigned long long* bar, unsigned l
     bool mine = true;
     for (unsigned j = threadIdx.x; j < n; j += 64) {
       int i = 0;
-      while (__hip_atomic_load(bar + 1 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want && ++i < kBarrierPolls)
+      bool seen = __hip_atomic_load(bar + 1 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
+      while (!seen && i < max_polls) {
         __builtin_amdgcn_s_sleep(1);
-      mine = mine && i < kBarrierPolls;
+        seen = __hip_atomic_load(bar + 1 + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == want;
+        ++i;
+      }
+      mine = mine && seen;
     }
     const bool ok = !wave_any(!mine);
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -571,8 +579,8 @@ template <int D>
 __global__ void __launch_bounds__(256) small_fused_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     const float* __restrict__ W, float* __restrict__ ps, float* __restrict__ pc, float* __restrict__ out,
-    unsigned long long* __restrict__ bar, unsigned tag, int L, int Hq, int Hkv, int Hw, int m, int R, int T_ranges,
-    int n_kv, int tiles_per_head, int n_ro) {
+    unsigned long long* __restrict__ bar, unsigned tag, int max_polls, int L, int Hq, int Hkv, int Hw, int m, int R,
+    int T_ranges, int n_kv, int tiles_per_head, int n_ro) {
   constexpr size_t LDS = SmallKv<D>::LDS > SmallRo<D>::LDS ? SmallKv<D>::LDS : SmallRo<D>::LDS;
   __shared__ __attribute__((aligned(16))) float sm[LDS / sizeof(float)];
   const unsigned long long epoch = barrier_epoch(bar);
@@ -580,7 +588,7 @@ __global__ void __launch_bounds__(256) small_fused_f32_kernel(
     small_kv_unit<D>(sm, u, K, V, W, L, Hkv, Hw, m, R, T_ranges, ps, pc);
     __syncthreads();  // LDS free for the next unit
   }
-  const bool ok = grid_barrier(bar, epoch, tag, gridDim.x);
+  const bool ok = grid_barrier(bar, epoch, tag, gridDim.x, max_polls);
   const int NFT = m / 32;
   const int nw = NFT < SmallRo<D>::NW ? NFT : SmallRo<D>::NW;
   for (int u = blockIdx.x; u < n_ro; u += gridDim.x) {
@@ -649,12 +657,17 @@ favor_status launch_small_f32(const Plan& s, const float* Q, const float* K, con
     const unsigned grid = (unsigned)(n_ro > (long long)kv_wg ? n_ro : (long long)kv_wg);
     unsigned long long* bar = reinterpret_cast<unsigned long long*>(ws + s.off_bar);
     const unsigned tag = next_barrier_tag();
+    int polls = kBarrierPolls;
+    if (const char* e = getenv("FAVOR_BARRIER_POLLS_FOR_TESTS")) {
+      const long v = strtol(e, nullptr, 10);
+      polls = v < 0 ? 0 : (v < kBarrierPolls ? (int)v : kBarrierPolls);
+    }
     if (s.d == 64)
       hipLaunchKernelGGL(small_fused_f32_kernel<64>, dim3(grid), dim3(256), 0, st, Q, K, V, W, ps, pc, out, bar, tag,
-                         s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, (int)kv_wg, (int)tiles, (int)n_ro);
+                         polls, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, (int)kv_wg, (int)tiles, (int)n_ro);
     else
       hipLaunchKernelGGL(small_fused_f32_kernel<128>, dim3(grid), dim3(256), 0, st, Q, K, V, W, ps, pc, out, bar,
-                         tag, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, (int)kv_wg, (int)tiles, (int)n_ro);
+                         tag, polls, s.L, s.Hq, s.Hkv, s.Hw, s.m, s.R, s.T, (int)kv_wg, (int)tiles, (int)n_ro);
     // one kernel: the key-side slot holds it, the readout slot is empty
     if (hipGetLastError() != hipSuccess || !mk.mark(1, st) || !mk.mark(2, st) || !mk.mark(3, st))
       return FAVOR_ERR_HIP;

@@ -129,3 +129,31 @@ def test_one_launch_graph_replays_match_eager():
         other = api.attn_fwd(q, v, k, wd, workspace=ws)  # eager work on the same workspace in between
         torch.cuda.synchronize()
         del other
+
+
+def test_barrier_that_gives_up_writes_nan_rows(monkeypatch):
+    """The barrier's wait is bounded.  With the poll limit forced to zero from the host
+    (FAVOR_BARRIER_POLLS_FOR_TESTS), workgroups that reach the barrier before the others give
+    up at once: the kernel still finishes, and every output row is either all NaN (its
+    workgroup gave up) or correct -- never silently wrong.  The next call on the same
+    workspace, with the limit restored, is correct again."""
+    w = _w()
+    Q, K, V, W = I.make_inputs(w, seed=7)
+    q, k, v, wd = _dev(Q), _dev(K), _dev(V), _dev(W)
+    p = api._problem(q, k, wd, False, 0)
+    assert _lib.attn_fwd_launches(p) == 1
+    ws = torch.empty(_lib.workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    ref = O.favor_attention(Q, K, V, W)[0, 0]
+    monkeypatch.setenv("FAVOR_BARRIER_POLLS_FOR_TESTS", "0")
+    y = api.attn_fwd(q, k, v, wd, workspace=ws).cpu().numpy()[0, 0]
+    torch.cuda.synchronize()
+    nan_rows = np.isnan(y).all(axis=1)
+    _say(f"  poll limit 0: {int(nan_rows.sum())} of {len(nan_rows)} rows NaN")
+    assert nan_rows.any()  # the workgroups without a key-side unit arrive first and give up
+    assert not np.isnan(y[~nan_rows]).any()
+    if (~nan_rows).any():
+        assert O.rowwise_rel_err(y[~nan_rows], ref[~nan_rows]) < TOL
+    monkeypatch.delenv("FAVOR_BARRIER_POLLS_FOR_TESTS")
+    y2 = api.attn_fwd(q, k, v, wd, workspace=ws).cpu().numpy()[0, 0]
+    torch.cuda.synchronize()
+    assert np.isfinite(y2).all() and O.rowwise_rel_err(y2, ref) < TOL
