@@ -108,7 +108,8 @@ int32_t favor_attn_fwd_launches(const favor_problem* p);
  * it needs no clearing), then the readout.  Its wait is bounded; rows of a launch whose
  * barrier gave up (not every workgroup resident, e.g. beside other work holding the
  * compute units) are written as NaN.  Two such calls in flight at once on one device must
- * not share a workspace. */
+ * not share a workspace.  The environment variable FAVOR_BARRIER_POLLS_FOR_TESTS (a test
+ * hook, read per call) lowers the barrier's poll limit so that path can be exercised. */
 favor_status favor_attn_fwd(const favor_problem* p, const void* Q, const void* K, const void* V,
                             const float* W, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
