@@ -98,11 +98,16 @@ __device__ __forceinline__ void stage_rows(T* dst, int ld, const T* src, int p0,
 // Workgroup ids are laid out so the feature slices of one (bh, t) share an XCD (and its L2
 // copy of K and V): block b runs on XCD b % 8.
 // ======================================================================================
-template <class T, int D> struct KvCfg;
-template <> struct KvCfg<bf16, 64> { static constexpr int KW = 8, NTW = 2; };
-template <> struct KvCfg<bf16, 128> { static constexpr int KW = 4, NTW = 1; };
-template <> struct KvCfg<float, 64> { static constexpr int KW = 4, NTW = 1; };
-template <> struct KvCfg<float, 128> { static constexpr int KW = 4, NTW = 1; };
+// KW waves per workgroup, NTW 32-feature tiles per wave, MINB workgroups per CU the
+// registers must allow.  OCC: the causal bf16 d = 64 key side as four-wave workgroups at
+// three waves per SIMD (the compiler spills a few registers to fit); its default runs
+// eight-wave workgroups at two waves per SIMD.  Each wave's arithmetic is the same in both.
+template <class T, int D, bool OCC = false> struct KvCfg;
+template <> struct KvCfg<bf16, 64, false> { static constexpr int KW = 8, NTW = 2, MINB = 1; };
+template <> struct KvCfg<bf16, 64, true> { static constexpr int KW = 4, NTW = 2, MINB = 3; };
+template <bool O> struct KvCfg<bf16, 128, O> { static constexpr int KW = 4, NTW = 1, MINB = 1; };
+template <bool O> struct KvCfg<float, 64, O> { static constexpr int KW = 4, NTW = 1, MINB = 1; };
+template <bool O> struct KvCfg<float, 128, O> { static constexpr int KW = 4, NTW = 1, MINB = 1; };
 
 // With one range per kv head and bf16 data (img_s != nullptr) the workgroup writes, instead
 // of gs / gc, the readout's LDS images of its 64 features: S'^T rows in readout order, the
@@ -113,19 +118,23 @@ template <> struct KvCfg<float, 128> { static constexpr int KW = 4, NTW = 1; };
 // RELU: the feature map ReLU(W k) in place of the exponential (no norm term, no
 // stabiliser: c_f = 0 throughout, so the partials merge as plain sums).  W keeps its
 // log2 e scale, which both sides share and the ratio cancels.
-template <class T, int D, bool SEG, bool RELU = false>
-__global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
+template <class T, int D, bool SEG, bool RELU = false, bool OCC = false>
+__global__ void __launch_bounds__((64 * KvCfg<T, D, OCC>::KW), (KvCfg<T, D, OCC>::MINB)) kv_summary_kernel(
     const T* __restrict__ K, const T* __restrict__ V, const float* __restrict__ W, int L, int Hkv, int Hw, int m,
     int R, int T_ranges, int n_units, float* __restrict__ gs, float* __restrict__ gc, char* __restrict__ img_w,
     char* __restrict__ img_s, char* __restrict__ img_cb) {
   using P = Prec<T>;
   using frag = typename P::frag;
   using wfrag = typename P::wfrag;
-  constexpr int KW = KvCfg<T, D>::KW, NTW = KvCfg<T, D>::NTW;
+  static_assert(SEG || !OCC, "the three-waves-per-SIMD form is the segment path's");
+  constexpr int KW = KvCfg<T, D, OCC>::KW, NTW = KvCfg<T, D, OCC>::NTW;
   constexpr int FG = 2 / NTW;   // feature groups per workgroup (64 features)
   constexpr int PG = KW / FG;   // position groups
   constexpr int NKC = D / P::KS;
-  constexpr int NDT = D / 32 + 1;
+  // MFMA accumulator tiles: the value columns, then (except in the OCC form, which sums
+  // S_1 by dot products to free the tile's registers) the ones column
+  constexpr int NDV = D / 32;
+  constexpr int NDT = NDV + (OCC ? 0 : 1);
   constexpr int LDV = Ld<T>::template V<D>;
   constexpr int ACC = NTW * NDT * 1024;  // floats of one wave's partial (fragment order)
   __shared__ __attribute__((aligned(16))) T Vl[KW][32 * LDV];
@@ -188,6 +197,25 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   float cst[NTW];  // stabiliser of this lane's feature (log2 units)
   wfrag biasB[NTW];
   f32x16 S[NTW][NDT];
+  // OCC: S_1 of feature 32 nt + col over this lane half's keys, summing the same rounded phi
+  // values the S_v products take; the two lane halves are added at the end
+  float s1[NTW];
+  auto frag_sum = [](const frag& x, float acc) {
+    if constexpr (sizeof(T) == 2) {
+      bf16x2 one2;
+      one2[0] = one2[1] = (bf16)1.f;
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        bf16x2 v2;
+        v2[0] = x[j];
+        v2[1] = x[j + 1];
+        acc = __builtin_amdgcn_fdot2_f32_bf16(v2, one2, acc, false);
+      }
+      return acc;
+    } else {
+      return acc + x;
+    }
+  };
   frag ones = zero_frag(frag{});
   if (col == 0) {
     if constexpr (sizeof(T) == 2) {
@@ -311,6 +339,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
           biasB[nt] = bias_cols(cst[nt], g, wfrag{});
           if (!first) {
             const float fct = fast_exp2(-shift);
+            if constexpr (OCC) s1[nt] *= fct;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
               const float fr = __shfl(fct, 8 * (r >> 2) + 4 * g + (r & 3));
@@ -331,12 +360,18 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) e[r] = RELU ? fmaxf(c1[nt][r], 0.f) : fast_exp2(c1[nt][r]);
       acc_to_frags(e, pa[nt]);
+      if constexpr (OCC) {
+        float sum = s1[nt];
+#pragma unroll
+        for (int h = 0; h < P::NF32; ++h) sum = frag_sum(pa[nt][h], sum);
+        s1[nt] = sum;
+      }
     }
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int h = 0; h < P::NF32; ++h) {
-        const frag vb = dt < NDT - 1 ? lds_frag_rows(vl, LDV, 0, 32 * dt, h) : ones;
+        const frag vb = dt < NDV ? lds_frag_rows(vl, LDV, 0, 32 * dt, h) : ones;
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) S[nt][dt] = mma(pa[nt][h], vb, S[nt][dt]);
       }
@@ -347,6 +382,7 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
     for (int nt = 0; nt < NTW; ++nt) {
       cst[nt] = RELU ? 0.f : -INFINITY;
       biasB[nt] = bias_cols(0.f, g, wfrag{});
+      s1[nt] = 0.f;
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) S[nt][dt] = zero16();
     }
@@ -363,11 +399,13 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   }
   float chk = 0.f;
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt)
+  for (int nt = 0; nt < NTW; ++nt) {
+    if constexpr (OCC) chk += s1[nt];
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) chk += S[nt][dt][r];
+  }
   if (!RELU && wave_any(!(chk - chk == 0.f))) {
     reset();
     if constexpr (!WLDS) fetch(wb);
@@ -375,33 +413,39 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
   }
 
   // The partial of unit_off (float32 gs rows in vperm order, row D the ones column, and
-  // gc) relative to the stabilisers cmx of this lane's C1 features.
+  // gc) relative to the stabilisers cmx of this lane's C1 features; in the OCC form s1t holds
+  // S_1 of feature 32 nt + col with both lane halves added.
   // causal segment summaries (SEG) are stored in the problem's summary type (bf16 for bf16
   // problems), range partials in float32
-  auto store_partial = [&](size_t unit_off, const float (&cmx)[NTW]) {
+  auto store_partial = [&](size_t unit_off, const float (&cmx)[NTW], const float (&s1t)[NTW]) {
     using GST = std::conditional_t<SEG, typename SumOf<T>::type, float>;
     GST* out_s = reinterpret_cast<GST*>(gs) + unit_off * (size_t)(D + 1) * m;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) {
 #pragma unroll
-      for (int dt = 0; dt < NDT - 1; ++dt)
+      for (int dt = 0; dt < NDV; ++dt)
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
           f32x4 v = {S[nt][dt][4 * r4], S[nt][dt][4 * r4 + 1], S[nt][dt][4 * r4 + 2], S[nt][dt][4 * r4 + 3]};
           store_sum4(out_s + (size_t)(32 * dt + col) * m + f0 + 32 * nt + 8 * r4 + 4 * g, v);
         }
-      if (col == 0)
+      if constexpr (OCC) {
+        if (g == 0) out_s[(size_t)D * m + f0 + 32 * nt + col] = (GST)s1t[nt];
+      } else if (col == 0) {
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
-          f32x4 v = {S[nt][NDT - 1][4 * r4], S[nt][NDT - 1][4 * r4 + 1], S[nt][NDT - 1][4 * r4 + 2],
-                     S[nt][NDT - 1][4 * r4 + 3]};
+          f32x4 v = {S[nt][NDV][4 * r4], S[nt][NDV][4 * r4 + 1], S[nt][NDV][4 * r4 + 2], S[nt][NDV][4 * r4 + 3]};
           store_sum4(out_s + (size_t)D * m + f0 + 32 * nt + 8 * r4 + 4 * g, v);
         }
+      }
       if (g == 0) gc[unit_off * m + f0 + 32 * nt + col] = cmx[nt];
     }
   };
   if constexpr (SEG) {
-    store_partial((size_t)bh * T_ranges + t, cst);
+    float s1t[NTW];
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) s1t[nt] = OCC ? s1[nt] + partner32(s1[nt]) : 0.f;
+    store_partial((size_t)bh * T_ranges + t, cst, s1t);
     return;
   }
 
@@ -524,7 +568,8 @@ __global__ void __launch_bounds__((64 * KvCfg<T, D>::KW)) kv_summary_kernel(
       return;
     }
   }
-  store_partial(unit_off, cmax);
+  const float no_s1[NTW] = {};  // the range path keeps S_1 in its ones tile
+  store_partial(unit_off, cmax, no_s1);
 }
 
 // ======================================================================================
@@ -2005,18 +2050,40 @@ namespace {
 
 inline int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b); }
 
+// The causal key side: one wave per segment and 64-feature slice.  Where the three-waves-
+// per-SIMD form holds all of them in fewer resident rounds (one wave slot per SIMD of the
+// kCUs model per unit of occupancy), it is taken; otherwise its spills cost more than the
+// occupancy gains.  The choice depends on the problem only, and the bits do not depend on it.
+template <class T, int D, bool RELU>
+favor_status launch_kv_segments(const Plan& s, const T* K, const T* V, const float* W, float* gs, float* gc,
+                                hipStream_t st) {
+  using A = KvCfg<T, D, false>;
+  using B = KvCfg<T, D, true>;
+  const int nfs = s.m / kFeatPerWave;
+  if constexpr (A::KW != B::KW || A::MINB != B::MINB) {
+    const long long waves = (long long)s.BH * s.T * nfs, slots = 4LL * kCUs;
+    if (ceil_div_i(waves, 3 * slots) < ceil_div_i(waves, 2 * slots)) {
+      constexpr int PG = B::KW * B::NTW / 2;  // segments per workgroup
+      const int units = s.BH * ceil_div_i(s.T, PG);
+      hipLaunchKernelGGL((kv_summary_kernel<T, D, true, RELU, true>), dim3(8 * ceil_div_i(units, 8) * nfs),
+                         dim3(64 * B::KW), 0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc, nullptr,
+                         nullptr, nullptr);
+      return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+    }
+  }
+  constexpr int PG = A::KW * A::NTW / 2;
+  const int units = s.BH * ceil_div_i(s.T, PG);
+  hipLaunchKernelGGL((kv_summary_kernel<T, D, true, RELU, false>), dim3(8 * ceil_div_i(units, 8) * nfs),
+                     dim3(64 * A::KW), 0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc, nullptr,
+                     nullptr, nullptr);
+  return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
+}
+
 template <class T, int D>
 favor_status launch_kv_summary(const Plan& s, const T* K, const T* V, const float* W, float* gs, float* gc,
                                char* ws, hipStream_t st) {
   const int nfs = s.m / kFeatPerWave;
-  if (s.mode == FAVOR_CAUSAL) {
-    constexpr int PG = KvCfg<T, D>::KW * KvCfg<T, D>::NTW / 2;  // segments per workgroup
-    const int units = s.BH * ceil_div_i(s.T, PG);
-    hipLaunchKernelGGL((kv_summary_kernel<T, D, true>), dim3(8 * ceil_div_i(units, 8) * nfs),
-                       dim3(64 * KvCfg<T, D>::KW), 0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc,
-                       nullptr, nullptr, nullptr);
-    return hipGetLastError() == hipSuccess ? FAVOR_OK : FAVOR_ERR_HIP;
-  }
+  if (s.mode == FAVOR_CAUSAL) return launch_kv_segments<T, D, false>(s, K, V, W, gs, gc, st);
   const int units = s.BH * s.T;
   if constexpr (std::is_same<T, bf16>::value) {
     hipLaunchKernelGGL((kv_summary_bf16_kernel<D>), dim3(8 * ceil_div_i(units, 8) * nfs), dim3(64 * KvBf16<D>::NW), 0,
@@ -2169,13 +2236,9 @@ favor_status run_relu_causal(const Plan& s, const T* Q, const T* K, const T* V, 
                              hipStream_t st) {
   float* gs = reinterpret_cast<float*>(ws + s.off_gs);
   float* gc = reinterpret_cast<float*>(ws + s.off_gc);
-  constexpr int PG = KvCfg<T, D>::KW * KvCfg<T, D>::NTW / 2;  // segments per workgroup
-  const int units = s.BH * ceil_div_i(s.T, PG), nfs = s.m / kFeatPerWave;
-  hipLaunchKernelGGL((kv_summary_kernel<T, D, true, true>), dim3(8 * ceil_div_i(units, 8) * nfs),
-                     dim3(64 * KvCfg<T, D>::KW), 0, st, K, V, W, s.L, s.Hkv, s.Hw, s.m, s.R, s.T, units, gs, gc,
-                     nullptr, nullptr, nullptr);
-  if (hipGetLastError() != hipSuccess) return FAVOR_ERR_HIP;
-  favor_status rc = launch_causal_scan_pf(s, ws, st);
+  favor_status rc = launch_kv_segments<T, D, true>(s, K, V, W, gs, gc, st);
+  if (rc != FAVOR_OK) return rc;
+  rc = launch_causal_scan_pf(s, ws, st);
   if (rc != FAVOR_OK) return rc;
   const auto* prefix = reinterpret_cast<const typename SumOf<T>::type*>(ws + s.off_p);
   const float* prefix_c = reinterpret_cast<const float*>(ws + s.off_pc);
