@@ -100,8 +100,9 @@ __device__ __forceinline__ void stage_rows(T* dst, int ld, const T* src, int p0,
 // ======================================================================================
 // KW waves per workgroup, NTW 32-feature tiles per wave, MINB workgroups per CU the
 // registers must allow.  OCC: the causal bf16 d = 64 key side as four-wave workgroups at
-// three waves per SIMD (the compiler spills a few registers to fit); its default runs
-// eight-wave workgroups at two waves per SIMD.  Each wave's arithmetic is the same in both.
+// three waves per SIMD, which sum S_1 by bf16 dot products instead of a ones-column MFMA
+// tile to free that tile's registers (the compiler still spills a few); its default runs
+// eight-wave workgroups at two waves per SIMD.
 template <class T, int D, bool OCC = false> struct KvCfg;
 template <> struct KvCfg<bf16, 64, false> { static constexpr int KW = 8, NTW = 2, MINB = 1; };
 template <> struct KvCfg<bf16, 64, true> { static constexpr int KW = 4, NTW = 2, MINB = 3; };
@@ -2050,10 +2051,11 @@ namespace {
 
 inline int ceil_div_i(long long a, long long b) { return (int)((a + b - 1) / b); }
 
-// The causal key side: one wave per segment and 64-feature slice.  Where the three-waves-
-// per-SIMD form holds all of them in fewer resident rounds (one wave slot per SIMD of the
-// kCUs model per unit of occupancy), it is taken; otherwise its spills cost more than the
-// occupancy gains.  The choice depends on the problem only, and the bits do not depend on it.
+// The causal key side: one wave per segment and 64-feature slice.  The three-waves-per-SIMD
+// form is taken where it holds all of them in fewer resident rounds than the default's two
+// waves per SIMD (rounds counted on the kCUs model); elsewhere its spills cost more than
+// the occupancy gains.  The choice rests on the problem alone, never the device, so a
+// problem's result bits (S_1 is summed differently in the two forms) do not depend on it.
 template <class T, int D, bool RELU>
 favor_status launch_kv_segments(const Plan& s, const T* K, const T* V, const float* W, float* gs, float* gc,
                                 hipStream_t st) {
